@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of the Engram forward pass on one MI355X.
+
+One step = one engram_forward call per Engram layer of the workload over one
+batch of synthetic tokens (hash, gather, projections with the fused gate
+partials, gate + conv + residual).  Inputs are resident in HBM before the
+timed region; the token batches and hidden states rotate over several
+buffers so gathered rows and activations are not served from the 256 MB
+Infinity Cache of a previous step.
+
+Prints one JSON line: whole-job tokens/s, the roofline of the dominant
+kernel (timed live with HIP events recorded by the library around each of
+its launches on the launch stream), gather bandwidth, per-kernel times and
+the CPU oracle's tokens/s on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+DEFAULT_WORKLOAD = "small"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--rotate", type=int, default=8, help="distinct token/h buffers cycled per step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
+    return ap.parse_args()
+
+
+def src_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "hashed_gram_embedding_vocab_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, kernel_src: str):
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3
+    counter runs, if they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("src_sha") != src_digest(kernel_src):
+        return None
+    return t
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The oracle, as it stands, on a contiguous block of sequence 0."""
+    import numpy as np
+
+    import oracle
+    from synthetic import workloads as W
+
+    dt = oracle.BF16 if wl.dtype == "bf16" else oracle.F32
+    seqlen = wl.seqlen
+    li = W.make_layer_inputs(wl, 0, batch=1, seqlen=seqlen)
+    comp = W.compression_map(wl.vocab, wl.vocab_comp, wl.seed(1))
+    toks = W.make_tokens(wl, batch=1, seqlen=seqlen)
+
+    def run(n):
+        t = time.perf_counter()
+        idx, _, _ = oracle.hash_tokens(toks[:, :n], comp, wl.vocab, wl.vocab_comp, wl.heads,
+                                       wl.primes(), li.hash_seed, orders=wl.orders)
+        emb = oracle.gather_synth(idx, wl.head_dim, li.table_seed, dt)
+        h = li.h[:, :n]
+        L = oracle.Layer(emb, h, li.w_k, li.w_v, li.gamma_h, li.gamma_k, li.conv_w, 1, n, dt)
+        L.forward_range(0, 0, n)
+        return time.perf_counter() - t
+
+    n0 = min(32, seqlen)
+    t0 = run(n0)
+    n = int(min(seqlen, max(n0, n0 * budget_s / max(t0, 1e-6))))
+    el = run(n)
+    layers = len(wl.layers)
+    tok_s = n / el / layers  # a step runs every layer over each token
+    return {"value": tok_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "positions 0..%d of sequence 0 (%d tokens, %d layer(s) of %d per step; "
+                      "single-threaded C, fp64), %.1f s" % (n - 1, n, 1, layers, el)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the Engram path here is single-GPU (tables fit one "
+              "MI355X's 288 GB); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from hashed_gram_embedding_vocab_amd import binding as B
+    from synthetic import workloads as W
+    from synthetic.device import make_device_layer, to_device
+
+    B.lib()
+    torch.cuda.set_device(0)
+    wl = W.workload(args.workload)
+    n_tok = wl.n_tokens
+    R = max(1, args.rotate)
+
+    layers = []
+    for slot in range(len(wl.layers)):
+        dl = make_device_layer(wl, layer_slot=slot)
+        hs = [dl.h] + [torch.randn_like(dl.h) for _ in range(R - 1)]
+        out = torch.empty_like(dl.h)
+        ws = dl.plan.workspace(wl.batch, wl.seqlen)
+        ctx = conv = None
+        if wl.decode:
+            ctx = to_device(dl.li.prev_ctx, torch.int32, "cuda")
+            conv = to_device(dl.li.conv_state, torch.float32, "cuda")
+        layers.append((dl, hs, out, ws, ctx, conv))
+    toks = [to_device(W.make_tokens(wl, seed=wl.seed(2) + 17 * r), torch.int32, "cuda") for r in range(R)]
+    torch.cuda.synchronize()
+
+    def step(i):
+        r = i % R
+        for dl, hs, out, ws, ctx, conv in layers:
+            dl.plan.engram_forward(toks[r], dl.comp_map, dl.tables, hs[r], dl.weights, out, ws,
+                                   prev_ctx=ctx, conv_state=conv)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    for dl, *_ in layers:
+        dl.plan.engram_profile_begin(8 * args.steps + 64)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if torch.distributed.is_available() and torch.distributed.is_initialized():
+        torch.distributed.barrier()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    if torch.distributed.is_available() and torch.distributed.is_initialized():
+        torch.distributed.barrier()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    profs = [dl.plan.engram_profile_end() for dl, *_ in layers]
+
+    def kern(name):
+        tot = sum(p[name]["total_ms"] for p in profs)
+        n = sum(p[name]["launches"] for p in profs)
+        return tot / max(n, 1), n
+
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_step = n_tok
+    value = tokens_per_step * args.steps / wall
+
+    # dominant kernel: the projections (MFMA), algorithmic flops per launch
+    De, d, Br = wl.emb_dim, wl.d_model, wl.n_branches
+    flops = 2.0 * n_tok * De * (Br + 1) * d
+    gemm_ms, gemm_n = kern("gemm")
+    achieved = flops / (gemm_ms * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[wl.dtype]
+    traffic = load_traffic(wl.name, "proj_bf16.hip")
+    roofline = {"kernel": "proj_bf16_kernel" if wl.dtype == "bf16" else "proj_f32_kernel",
+                "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4),
+                "traffic": None if traffic is None else traffic["bytes_per_launch"],
+                "avg_launch_us": round(gemm_ms * 1e3, 2), "launches": gemm_n,
+                "flops_per_launch": flops}
+
+    eb = 2 if wl.dtype == "bf16" else 4
+    g_bytes = n_tok * (wl.n_tables * 4 + 2 * De * eb)
+    g_ms, g_n = kern("gather")
+    gather = {"achieved_GBs": round(g_bytes / (g_ms * 1e-3) / 1e9, 1), "peak_GBs": HBM_PEAK_GBS,
+              "frac": round(g_bytes / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+              "bytes_per_launch": g_bytes, "avg_launch_us": round(g_ms * 1e3, 2)}
+    f_ms, _ = kern("fuse")
+    f_bytes = n_tok * (d * eb + Br * 2 * d * eb) + Br * (d // 128 if wl.dtype == "bf16" else 1) * 3 * 4 * n_tok
+    fuse = {"achieved_GBs": round(f_bytes / (f_ms * 1e-3) / 1e9, 1), "frac": round(
+        f_bytes / (f_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "avg_launch_us": round(f_ms * 1e3, 2)}
+    kernels_us = {k: round(kern(k)[0] * 1e3, 2) for k in ("hash", "gather", "gemm", "fuse", "aux")}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    line = {
+        "metric": "Engram fwd tokens/sec",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "gpu_event_ms_per_step": round(gpu_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic: Zipf(%s) token ids over V=%d, seeded Philox tables, N(0,1) hidden states"
+                % (wl.zipf_s, wl.vocab),
+        "config": {"workload": wl.name, "batch": wl.batch, "seq_len": wl.seqlen,
+                   "tokens_per_step": tokens_per_step, "layers": list(wl.layers),
+                   "n_branches": Br, "d_model": d, "heads_per_order": wl.heads,
+                   "head_dim": wl.head_dim, "emb_dim": De, "table_params": sum(wl.primes()) * wl.head_dim,
+                   "rotated_buffers": R, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "gather": gather,
+        "fuse": fuse,
+        "kernel_avg_us": kernels_us,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

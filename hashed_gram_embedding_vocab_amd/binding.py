@@ -1,0 +1,246 @@
+"""Thin Python binding of libengram.so (argument marshalling only).
+
+Every entry point mirrors a C function of ``include/engram.h`` /
+``include/engram_synth.h`` with the same name.  Tensors are torch tensors on
+the GPU; only their device pointers cross the boundary, together with the
+current HIP stream.  All computation happens in the HIP kernels of the
+library.  If the library is not built this module raises: there is no CPU
+fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+import threading
+from typing import Dict, Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libengram.so")
+
+OK, E_INVALID_ARG, E_UNSUPPORTED, E_DEVICE, E_NOMEM = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+CONV_LINEAR, CONV_SILU_SKIP = 0, 1
+OUT_DELTA = 1
+MAX_TABLES, MAX_BRANCHES = 32, 4
+KERNEL_NAMES = ("hash", "gather", "gemm", "fuse", "aux")
+
+
+class EngramError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__("%s failed: %s (status %d)" % (fn, msg, status))
+        self.status = status
+
+
+class Config(C.Structure):
+    _fields_ = [
+        ("vocab", C.c_int32), ("vocab_comp", C.c_int32), ("n_orders", C.c_int32),
+        ("orders", C.c_int32 * 4), ("heads", C.c_int32), ("head_dim", C.c_int32),
+        ("table_rows", C.c_uint32 * MAX_TABLES), ("hash_seed", C.c_uint64),
+        ("d_model", C.c_int32), ("n_branches", C.c_int32), ("conv_kernel", C.c_int32),
+        ("conv_mode", C.c_int32), ("rms_eps", C.c_float), ("dtype", C.c_int32),
+    ]
+
+
+class WeightsC(C.Structure):
+    _fields_ = [
+        ("w_k", C.c_void_p * MAX_BRANCHES), ("w_v", C.c_void_p),
+        ("gamma_h", C.c_void_p * MAX_BRANCHES), ("gamma_k", C.c_void_p * MAX_BRANCHES),
+        ("conv_w", C.c_void_p),
+    ]
+
+
+class ProfileC(C.Structure):
+    _fields_ = [("total_ms", C.c_double * 5), ("launches", C.c_int64 * 5), ("dropped", C.c_int64)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib() -> C.CDLL:
+    """Load libengram.so; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libengram.so not built at %s: run "
+                              "`python -m hashed_gram_embedding_vocab_amd.build`" % LIB_PATH)
+        L = C.CDLL(LIB_PATH)
+        P, i32, i64, u32, u64 = C.c_void_p, C.c_int32, C.c_int64, C.c_uint32, C.c_uint64
+        L.engram_status_string.restype = C.c_char_p
+        L.engram_status_string.argtypes = [C.c_int]
+        L.engram_plan_create.restype = C.c_int
+        L.engram_plan_create.argtypes = [C.POINTER(Config), C.POINTER(C.c_void_p)]
+        L.engram_plan_destroy.restype = C.c_int
+        L.engram_plan_destroy.argtypes = [P]
+        L.engram_workspace_size.restype = C.c_size_t
+        L.engram_workspace_size.argtypes = [P, i32, i32]
+        L.engram_hash.restype = C.c_int
+        L.engram_hash.argtypes = [P, P, i32, i32, P, P, P, P, P]
+        L.engram_gather.restype = C.c_int
+        L.engram_gather.argtypes = [P, P, i64, P, P, P]
+        L.engram_gate_fuse.restype = C.c_int
+        L.engram_gate_fuse.argtypes = [P, P, P, i32, i32, C.POINTER(WeightsC), P, P, P, u32, P,
+                                       C.c_size_t, P]
+        L.engram_forward.restype = C.c_int
+        L.engram_forward.argtypes = [P, P, i32, i32, P, P, P, P, C.POINTER(WeightsC), P, P, P, u32,
+                                     P, C.c_size_t, P, P]
+        L.engram_profile_begin.restype = C.c_int
+        L.engram_profile_begin.argtypes = [P, i32]
+        L.engram_profile_end.restype = C.c_int
+        L.engram_profile_end.argtypes = [P, C.POINTER(ProfileC)]
+        L.engram_synth_fill_table.restype = C.c_int
+        L.engram_synth_fill_table.argtypes = [i32, u64, i32, i64, i32, P, P]
+        _lib = L
+        return L
+
+
+def _check(fn: str, status: int):
+    if status != OK:
+        raise EngramError(fn, status, lib().engram_status_string(status).decode())
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a CUDA (HIP) tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> C.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _torch_dtype(dt: int):
+    return torch.bfloat16 if dt == BF16 else torch.float32
+
+
+class Weights:
+    """Device tensors of one layer's weights, plus their C struct."""
+
+    def __init__(self, w_k: Sequence[torch.Tensor], w_v: torch.Tensor, gamma_h: Sequence[torch.Tensor],
+                 gamma_k: Sequence[torch.Tensor], conv_w: torch.Tensor):
+        self.w_k, self.w_v = list(w_k), w_v
+        self.gamma_h, self.gamma_k, self.conv_w = list(gamma_h), list(gamma_k), conv_w
+        s = WeightsC()
+        for m, t in enumerate(self.w_k):
+            s.w_k[m] = _ptr(t, "w_k[%d]" % m).value
+        for m, t in enumerate(self.gamma_h):
+            s.gamma_h[m] = _ptr(t, "gamma_h[%d]" % m, torch.float32).value
+        for m, t in enumerate(self.gamma_k):
+            s.gamma_k[m] = _ptr(t, "gamma_k[%d]" % m, torch.float32).value
+        s.w_v = _ptr(w_v, "w_v").value
+        s.conv_w = _ptr(conv_w, "conv_w", torch.float32).value
+        self.c = s
+
+
+class Plan:
+    """An engram_plan: immutable hashing and shape constants of one Engram layer."""
+
+    def __init__(self, vocab: int, vocab_comp: int, heads: int, head_dim: int,
+                 table_rows: Sequence[int], hash_seed: int, d_model: int, n_branches: int = 1,
+                 conv_kernel: int = 4, conv_mode: int = CONV_LINEAR, rms_eps: float = 1e-6,
+                 dtype: int = BF16, orders: Sequence[int] = (2, 3)):
+        cfg = Config()
+        cfg.vocab, cfg.vocab_comp = vocab, vocab_comp
+        cfg.n_orders = len(orders)
+        for i, o in enumerate(orders):
+            cfg.orders[i] = o
+        cfg.heads, cfg.head_dim = heads, head_dim
+        if len(table_rows) > MAX_TABLES:
+            raise ValueError("too many tables")
+        for i, r in enumerate(table_rows):
+            cfg.table_rows[i] = r
+        cfg.hash_seed = hash_seed & 0xFFFFFFFFFFFFFFFF
+        cfg.d_model, cfg.n_branches = d_model, n_branches
+        cfg.conv_kernel, cfg.conv_mode, cfg.rms_eps, cfg.dtype = conv_kernel, conv_mode, rms_eps, dtype
+        self.cfg = cfg
+        self.n_tables = len(orders) * heads
+        self.emb_dim = self.n_tables * head_dim
+        self.dtype = dtype
+        self.torch_dtype = _torch_dtype(dtype)
+        h = C.c_void_p()
+        _check("engram_plan_create", lib().engram_plan_create(C.byref(cfg), C.byref(h)))
+        self._h = h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.engram_plan_destroy(h)
+            self._h = None
+
+    # ------------------------------------------------------------------ ABI calls
+    def engram_workspace_size(self, batch: int, seqlen: int) -> int:
+        return int(lib().engram_workspace_size(self._h, batch, seqlen))
+
+    def engram_hash(self, tokens, comp_map, idx, prev_ctx=None, bad_tokens=None, stream=None):
+        batch, seqlen = tokens.shape
+        _check("engram_hash", lib().engram_hash(
+            self._h, _ptr(tokens, "tokens", torch.int32), batch, seqlen,
+            _ptr(comp_map, "comp_map", torch.int32), _ptr(prev_ctx, "prev_ctx", torch.int32),
+            _ptr(idx, "idx", (torch.int32, torch.uint32)), _ptr(bad_tokens, "bad_tokens", (torch.int32, torch.uint32)),
+            _stream(stream)))
+
+    def engram_gather(self, idx, tables: Sequence[torch.Tensor], emb, stream=None):
+        n_tok = idx.shape[0]
+        ptrs = (C.c_void_p * len(tables))(*[_ptr(t, "table").value for t in tables])
+        _check("engram_gather", lib().engram_gather(
+            self._h, _ptr(idx, "idx", (torch.int32, torch.uint32)), n_tok, ptrs,
+            _ptr(emb, "emb", self.torch_dtype), _stream(stream)))
+
+    def engram_gate_fuse(self, emb, h, weights: Weights, out, workspace, batch: int, seqlen: int,
+                         conv_state=None, alpha=None, flags: int = 0, stream=None):
+        _check("engram_gate_fuse", lib().engram_gate_fuse(
+            self._h, _ptr(emb, "emb", self.torch_dtype), _ptr(h, "h", self.torch_dtype), batch, seqlen,
+            C.byref(weights.c), _ptr(conv_state, "conv_state", torch.float32),
+            _ptr(out, "out", self.torch_dtype), _ptr(alpha, "alpha", torch.float32), flags,
+            _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+            _stream(stream)))
+
+    def engram_forward(self, tokens, comp_map, tables: Sequence[torch.Tensor], h, weights: Weights,
+                       out, workspace, prev_ctx=None, conv_state=None, alpha=None, flags: int = 0,
+                       bad_tokens=None, stream=None):
+        batch, seqlen = tokens.shape
+        ptrs = (C.c_void_p * len(tables))(*[_ptr(t, "table").value for t in tables])
+        _check("engram_forward", lib().engram_forward(
+            self._h, _ptr(tokens, "tokens", torch.int32), batch, seqlen,
+            _ptr(comp_map, "comp_map", torch.int32), _ptr(prev_ctx, "prev_ctx", torch.int32), ptrs,
+            _ptr(h, "h", self.torch_dtype), C.byref(weights.c),
+            _ptr(conv_state, "conv_state", torch.float32), _ptr(out, "out", self.torch_dtype),
+            _ptr(alpha, "alpha", torch.float32), flags, _ptr(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(),
+            _ptr(bad_tokens, "bad_tokens", (torch.int32, torch.uint32)), _stream(stream)))
+
+    def engram_profile_begin(self, max_launches: int = 4096):
+        _check("engram_profile_begin", lib().engram_profile_begin(self._h, max_launches))
+
+    def engram_profile_end(self) -> Dict[str, Dict[str, float]]:
+        p = ProfileC()
+        _check("engram_profile_end", lib().engram_profile_end(self._h, C.byref(p)))
+        out = {n: {"total_ms": p.total_ms[i], "launches": int(p.launches[i])}
+               for i, n in enumerate(KERNEL_NAMES)}
+        out["dropped"] = int(p.dropped)
+        return out
+
+    # ------------------------------------------------------------------ helpers
+    def workspace(self, batch: int, seqlen: int, device="cuda") -> torch.Tensor:
+        """A caller-owned workspace tensor of the required size (256-byte aligned by torch)."""
+        return torch.empty(self.engram_workspace_size(batch, seqlen), dtype=torch.uint8, device=device)
+
+
+def engram_synth_fill_table(table: torch.Tensor, seed: int, tau: int, dtype: int, stream=None):
+    rows, head_dim = table.shape
+    _check("engram_synth_fill_table", lib().engram_synth_fill_table(
+        dtype, seed & 0xFFFFFFFFFFFFFFFF, tau, rows, head_dim,
+        _ptr(table, "table", _torch_dtype(dtype)), _stream(stream)))

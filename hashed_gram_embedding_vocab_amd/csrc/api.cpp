@@ -1,0 +1,424 @@
+// api.cpp -- host side of the C ABI declared in include/engram.h: plans,
+// argument validation, workspace layout and launch sequencing on the
+// caller's stream.  No entry point allocates device memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "engram.h"
+#include "engram_internal.h"
+#include "engram_synth.h"
+
+using namespace engram;
+
+struct engram_plan_s {
+    engram_config cfg;
+    int32_t n_tables = 0;
+    int32_t emb_dim = 0;    // D_e
+    int32_t elem = 0;       // bytes per element of the plan dtype
+    HashConsts hc{};
+    // profiling
+    bool prof_on = false;
+    int32_t prof_max = 0;
+    int32_t prof_used = 0;
+    int64_t prof_dropped = 0;
+    std::vector<hipEvent_t> prof_ev;
+    std::vector<int32_t> prof_kind;
+};
+
+namespace {
+
+// SplitMix64 output function, used to derive the per-table hash seeds.
+uint64_t host_mix64(uint64_t z) {
+    z ^= z >> 30;
+    z *= 0xBF58476D1CE4E5B9ull;
+    z ^= z >> 27;
+    z *= 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return z;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Layout {
+    size_t idx, emb, partials, v, kbuf, stage, total;
+};
+
+int32_t n_parts_of(const engram_plan_s &p) {
+    return p.cfg.dtype == ENGRAM_BF16 ? p.cfg.d_model / kPartCols : 1;
+}
+
+bool layout_of(const engram_plan_s &p, int64_t batch, int64_t seqlen, Layout &L) {
+    if (batch <= 0 || seqlen <= 0) return false;
+    const int64_t n_tok = batch * seqlen;
+    const int64_t d = p.cfg.d_model, Br = p.cfg.n_branches;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = round_up(off + bytes, 256);
+        return o;
+    };
+    L.idx = take((size_t)n_tok * p.n_tables * 4);
+    L.emb = take((size_t)n_tok * p.emb_dim * p.elem);
+    L.partials = take((size_t)Br * n_parts_of(p) * 3 * n_tok * 4);
+    L.v = take((size_t)n_tok * d * p.elem);
+    L.kbuf = p.cfg.dtype == ENGRAM_F32 ? take((size_t)Br * n_tok * d * 4) : off;
+    L.stage = take((size_t)Br * batch * (p.cfg.conv_kernel - 1) * d * 4);
+    L.total = off;
+    return true;
+}
+
+struct Launch {
+    engram_plan_s &p;
+    hipStream_t s;
+    int32_t kind;
+    int32_t slot = -1;
+    Launch(engram_plan_s &pl, int32_t k, hipStream_t st) : p(pl), s(st), kind(k) {
+        if (!p.prof_on) return;
+        if (p.prof_used < p.prof_max) {
+            slot = p.prof_used++;
+            p.prof_kind[slot] = kind;
+            hipEventRecord(p.prof_ev[2 * slot], s);
+        } else {
+            ++p.prof_dropped;
+        }
+    }
+    ~Launch() {
+        if (slot >= 0) hipEventRecord(p.prof_ev[2 * slot + 1], s);
+    }
+};
+
+engram_status last_launch_status() {
+    return hipGetLastError() == hipSuccess ? ENGRAM_OK : ENGRAM_E_DEVICE;
+}
+
+engram_status check_hash_args(const engram_plan_s *p, const int32_t *tokens, int32_t batch,
+                              int32_t seqlen, const int32_t *comp_map, uint32_t *idx) {
+    if (!p || !tokens || !comp_map || !idx) return ENGRAM_E_INVALID_ARG;
+    if (batch <= 0 || seqlen <= 0) return ENGRAM_E_INVALID_ARG;
+    if ((int64_t)batch * seqlen > (int64_t)INT32_MAX) return ENGRAM_E_UNSUPPORTED;
+    if (!aligned16(tokens) || !aligned16(comp_map) || !aligned16(idx)) return ENGRAM_E_INVALID_ARG;
+    return ENGRAM_OK;
+}
+
+engram_status do_hash(engram_plan_s &p, const int32_t *tokens, int32_t batch, int32_t seqlen,
+                      const int32_t *comp_map, const int32_t *prev_ctx, uint32_t *idx, uint32_t *bad,
+                      hipStream_t s) {
+    {
+        Launch l(p, ENGRAM_K_HASH, s);
+        launch_hash(p.hc, tokens, batch, seqlen, comp_map, prev_ctx, idx, bad, s);
+    }
+    return last_launch_status();
+}
+
+engram_status check_gather_args(const engram_plan_s *p, const uint32_t *idx, int64_t n_tok,
+                                const void *const *tables, const void *emb) {
+    if (!p || !idx || !tables || !emb) return ENGRAM_E_INVALID_ARG;
+    if (n_tok <= 0) return ENGRAM_E_INVALID_ARG;
+    if (!aligned16(idx) || !aligned16(emb)) return ENGRAM_E_INVALID_ARG;
+    const int64_t chunks = (int64_t)p->emb_dim * p->elem / 16;
+    if (n_tok > ((int64_t)1 << 40) / chunks) return ENGRAM_E_UNSUPPORTED;
+    for (int t = 0; t < p->n_tables; ++t)
+        if (!tables[t] || !aligned16(tables[t])) return ENGRAM_E_INVALID_ARG;
+    return ENGRAM_OK;
+}
+
+engram_status do_gather(engram_plan_s &p, const uint32_t *idx, int64_t n_tok,
+                        const void *const *tables, void *emb, hipStream_t s) {
+    GatherConsts gc{};
+    gc.n_tables = p.n_tables;
+    gc.row_chunks = p.cfg.head_dim * p.elem / 16;
+    gc.tok_chunks = gc.row_chunks * p.n_tables;
+    for (int t = 0; t < p.n_tables; ++t) {
+        gc.table[t] = static_cast<const char *>(tables[t]);
+        gc.last_row[t] = p.cfg.table_rows[t] - 1;
+    }
+    auto magic = [](int32_t dv) -> uint64_t {
+        return dv <= 1 ? 0 : (uint64_t)(((unsigned __int128)1 << 64) / (unsigned)dv) + 1;
+    };
+    gc.magic_tok = magic(gc.tok_chunks);
+    gc.magic_row = magic(gc.row_chunks);
+    {
+        Launch l(p, ENGRAM_K_GATHER, s);
+        launch_gather(gc, idx, n_tok, emb, s);
+    }
+    return last_launch_status();
+}
+
+engram_status check_fuse_args(const engram_plan_s *p, const void *emb, const void *h, int32_t batch,
+                              int32_t seqlen, const engram_weights *w, const void *out,
+                              const float *alpha, const float *conv_state, uint32_t flags,
+                              const void *ws, size_t ws_bytes) {
+    if (!p || !emb || !h || !w || !out || !ws) return ENGRAM_E_INVALID_ARG;
+    if (batch <= 0 || seqlen <= 0) return ENGRAM_E_INVALID_ARG;
+    if ((int64_t)batch * seqlen > (int64_t)INT32_MAX) return ENGRAM_E_UNSUPPORTED;
+    if (batch > 65535) return ENGRAM_E_UNSUPPORTED;  // one grid row per sequence in the fusion kernel
+    if (flags & ~(uint32_t)ENGRAM_OUT_DELTA) return ENGRAM_E_INVALID_ARG;
+    if (!aligned16(emb) || !aligned16(h) || !aligned16(out)) return ENGRAM_E_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return ENGRAM_E_INVALID_ARG;
+    if ((alpha && !aligned16(alpha)) || (conv_state && !aligned16(conv_state))) return ENGRAM_E_INVALID_ARG;
+    for (int m = 0; m < p->cfg.n_branches; ++m) {
+        if (!w->w_k[m] || !w->gamma_h[m] || !w->gamma_k[m]) return ENGRAM_E_INVALID_ARG;
+        if (!aligned16(w->w_k[m]) || !aligned16(w->gamma_h[m]) || !aligned16(w->gamma_k[m]))
+            return ENGRAM_E_INVALID_ARG;
+    }
+    if (!w->w_v || !w->conv_w || !aligned16(w->w_v)) return ENGRAM_E_INVALID_ARG;
+    Layout L;
+    if (!layout_of(*p, batch, seqlen, L) || ws_bytes < L.total) return ENGRAM_E_INVALID_ARG;
+    if (p->cfg.dtype == ENGRAM_BF16 && (p->cfg.d_model % kPartCols != 0 || p->emb_dim % 64 != 0))
+        return ENGRAM_E_UNSUPPORTED;
+    return ENGRAM_OK;
+}
+
+engram_status do_fuse(engram_plan_s &p, const void *emb, const void *h, int32_t batch, int32_t seqlen,
+                      const engram_weights *w, float *conv_state, void *out, float *alpha,
+                      uint32_t flags, void *ws, hipStream_t s) {
+    Layout L;
+    layout_of(p, batch, seqlen, L);
+    char *base = static_cast<char *>(ws);
+    const int64_t n_tok = (int64_t)batch * seqlen;
+    const int Br = p.cfg.n_branches;
+
+    ProjArgs pa{};
+    pa.emb = emb;
+    for (int m = 0; m < Br; ++m) {
+        pa.w[m] = w->w_k[m];
+        pa.gamma_h[m] = w->gamma_h[m];
+        pa.gamma_k[m] = w->gamma_k[m];
+    }
+    for (int m = Br; m < kMaxBranches; ++m) {  // unused slots: any valid pointer
+        pa.gamma_h[m] = w->gamma_h[0];
+        pa.gamma_k[m] = w->gamma_k[0];
+    }
+    pa.w[Br] = w->w_v;
+    for (int m = Br + 1; m <= kMaxBranches; ++m) pa.w[m] = w->w_v;
+    pa.h = h;
+    pa.partials = reinterpret_cast<float *>(base + L.partials);
+    pa.v = base + L.v;
+    pa.kbuf = p.cfg.dtype == ENGRAM_F32 ? reinterpret_cast<float *>(base + L.kbuf) : nullptr;
+    pa.n_tok = n_tok;
+    pa.K = p.emb_dim;
+    pa.d = p.cfg.d_model;
+    pa.n_branches = Br;
+    pa.n_parts = n_parts_of(p);
+    {
+        Launch l(p, ENGRAM_K_GEMM, s);
+        if (p.cfg.dtype == ENGRAM_BF16)
+            launch_proj_bf16(pa, s);
+        else
+            launch_proj_f32(pa, s);
+    }
+    if (last_launch_status() != ENGRAM_OK) return ENGRAM_E_DEVICE;
+
+    FuseArgs fa{};
+    fa.v = pa.v;
+    fa.partials = pa.partials;
+    fa.h = h;
+    fa.out = out;
+    fa.conv_w = w->conv_w;
+    fa.conv_state = conv_state;
+    fa.state_stage = (conv_state && p.cfg.conv_kernel > 1) ? reinterpret_cast<float *>(base + L.stage) : nullptr;
+    fa.alpha = alpha;
+    fa.batch = batch;
+    fa.seqlen = seqlen;
+    fa.d = p.cfg.d_model;
+    fa.n_branches = Br;
+    fa.n_parts = pa.n_parts;
+    fa.conv_k = p.cfg.conv_kernel;
+    fa.conv_mode = p.cfg.conv_mode;
+    fa.eps = p.cfg.rms_eps;
+    fa.flags = flags;
+    {
+        Launch l(p, ENGRAM_K_FUSE, s);
+        launch_fuse(fa, p.cfg.dtype, s);
+    }
+    if (last_launch_status() != ENGRAM_OK) return ENGRAM_E_DEVICE;
+    if (fa.state_stage) {
+        Launch l(p, ENGRAM_K_AUX, s);
+        const size_t bytes = (size_t)Br * batch * (p.cfg.conv_kernel - 1) * p.cfg.d_model * 4;
+        if (hipMemcpyAsync(conv_state, fa.state_stage, bytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
+            return ENGRAM_E_DEVICE;
+    }
+    return ENGRAM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *engram_status_string(engram_status s) {
+    switch (s) {
+        case ENGRAM_OK: return "ok";
+        case ENGRAM_E_INVALID_ARG: return "invalid argument";
+        case ENGRAM_E_UNSUPPORTED: return "unsupported shape";
+        case ENGRAM_E_DEVICE: return "device error";
+        case ENGRAM_E_NOMEM: return "out of host memory";
+    }
+    return "unknown status";
+}
+
+engram_status engram_plan_create(const engram_config *cfg, engram_plan *out) {
+    if (!cfg || !out) return ENGRAM_E_INVALID_ARG;
+    *out = nullptr;
+    const engram_config &c = *cfg;
+    if (c.vocab <= 0 || c.vocab_comp <= 0 || c.vocab_comp >= (1 << 21)) return ENGRAM_E_INVALID_ARG;
+    if (c.n_orders < 1 || c.n_orders > 2 || c.heads < 1) return ENGRAM_E_INVALID_ARG;
+    for (int o = 0; o < c.n_orders; ++o)
+        if (c.orders[o] != 2 && c.orders[o] != 3) return ENGRAM_E_INVALID_ARG;
+    if (c.n_orders == 2 && c.orders[0] == c.orders[1]) return ENGRAM_E_INVALID_ARG;
+    const int n_tables = c.n_orders * c.heads;
+    if (n_tables > ENGRAM_MAX_TABLES) return ENGRAM_E_INVALID_ARG;
+    if (c.dtype != ENGRAM_F32 && c.dtype != ENGRAM_BF16) return ENGRAM_E_INVALID_ARG;
+    const int elem = c.dtype == ENGRAM_BF16 ? 2 : 4;
+    if (c.head_dim <= 0 || (c.head_dim * elem) % 16 != 0 || c.head_dim % 4 != 0) return ENGRAM_E_INVALID_ARG;
+    for (int t = 0; t < n_tables; ++t)
+        if (c.table_rows[t] < 1 || c.table_rows[t] >= 0x80000000u) return ENGRAM_E_INVALID_ARG;
+    if (c.d_model <= 0 || c.d_model % 8 != 0) return ENGRAM_E_INVALID_ARG;
+    if (c.n_branches < 1 || c.n_branches > ENGRAM_MAX_BRANCHES) return ENGRAM_E_INVALID_ARG;
+    if (c.conv_kernel < 1 || c.conv_kernel > 4) return ENGRAM_E_INVALID_ARG;
+    if (c.conv_mode != ENGRAM_CONV_LINEAR && c.conv_mode != ENGRAM_CONV_SILU_SKIP) return ENGRAM_E_INVALID_ARG;
+    if (!(c.rms_eps >= 0.f)) return ENGRAM_E_INVALID_ARG;
+
+    engram_plan_s *p = new (std::nothrow) engram_plan_s();
+    if (!p) return ENGRAM_E_NOMEM;
+    p->cfg = c;
+    p->n_tables = n_tables;
+    p->emb_dim = n_tables * c.head_dim;
+    p->elem = elem;
+    p->hc.n_tables = n_tables;
+    p->hc.vocab = c.vocab;
+    p->hc.vocab_comp = c.vocab_comp;
+    for (int t = 0; t < n_tables; ++t) {
+        p->hc.seed[t] = host_mix64(c.hash_seed + (uint64_t)(t + 1) * 0x9E3779B97F4A7C15ull);
+        p->hc.rows[t] = c.table_rows[t];
+        p->hc.magic[t] = UINT64_MAX / c.table_rows[t];
+        p->hc.order_of[t] = c.orders[t / c.heads];
+    }
+    *out = p;
+    return ENGRAM_OK;
+}
+
+engram_status engram_plan_destroy(engram_plan p) {
+    if (!p) return ENGRAM_E_INVALID_ARG;
+    for (hipEvent_t e : p->prof_ev) hipEventDestroy(e);
+    delete p;
+    return ENGRAM_OK;
+}
+
+size_t engram_workspace_size(engram_plan p, int32_t batch, int32_t seqlen) {
+    Layout L;
+    if (!p || !layout_of(*p, batch, seqlen, L)) return 0;
+    return L.total;
+}
+
+engram_status engram_hash(engram_plan p, const int32_t *d_tokens, int32_t batch, int32_t seqlen,
+                          const int32_t *d_comp_map, const int32_t *d_prev_ctx, uint32_t *d_idx,
+                          uint32_t *d_bad_tokens, hipStream_t stream) {
+    engram_status st = check_hash_args(p, d_tokens, batch, seqlen, d_comp_map, d_idx);
+    if (st != ENGRAM_OK) return st;
+    return do_hash(*p, d_tokens, batch, seqlen, d_comp_map, d_prev_ctx, d_idx, d_bad_tokens, stream);
+}
+
+engram_status engram_gather(engram_plan p, const uint32_t *d_idx, int64_t n_tokens,
+                            const void *const *table_ptrs, void *d_emb, hipStream_t stream) {
+    engram_status st = check_gather_args(p, d_idx, n_tokens, table_ptrs, d_emb);
+    if (st != ENGRAM_OK) return st;
+    return do_gather(*p, d_idx, n_tokens, table_ptrs, d_emb, stream);
+}
+
+engram_status engram_gate_fuse(engram_plan p, const void *d_emb, const void *d_h, int32_t batch,
+                               int32_t seqlen, const engram_weights *w, float *d_conv_state,
+                               void *d_out, float *d_alpha, uint32_t flags, void *d_workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+    engram_status st = check_fuse_args(p, d_emb, d_h, batch, seqlen, w, d_out, d_alpha, d_conv_state,
+                                       flags, d_workspace, workspace_bytes);
+    if (st != ENGRAM_OK) return st;
+    return do_fuse(*p, d_emb, d_h, batch, seqlen, w, d_conv_state, d_out, d_alpha, flags, d_workspace,
+                   stream);
+}
+
+engram_status engram_forward(engram_plan p, const int32_t *d_tokens, int32_t batch, int32_t seqlen,
+                             const int32_t *d_comp_map, int32_t *d_prev_ctx,
+                             const void *const *table_ptrs, const void *d_h,
+                             const engram_weights *w, float *d_conv_state, void *d_out,
+                             float *d_alpha, uint32_t flags, void *d_workspace,
+                             size_t workspace_bytes, uint32_t *d_bad_tokens, hipStream_t stream) {
+    if (!p || !d_workspace) return ENGRAM_E_INVALID_ARG;
+    Layout L;
+    if (!layout_of(*p, batch, seqlen, L)) return ENGRAM_E_INVALID_ARG;
+    char *base = static_cast<char *>(d_workspace);
+    uint32_t *idx = reinterpret_cast<uint32_t *>(base + L.idx);
+    void *emb = base + L.emb;
+    engram_status st = check_hash_args(p, d_tokens, batch, seqlen, d_comp_map, idx);
+    if (st == ENGRAM_OK) st = check_gather_args(p, idx, (int64_t)batch * seqlen, table_ptrs, emb);
+    if (st == ENGRAM_OK)
+        st = check_fuse_args(p, emb, d_h, batch, seqlen, w, d_out, d_alpha, d_conv_state, flags,
+                             d_workspace, workspace_bytes);
+    if (st != ENGRAM_OK) return st;
+    st = do_hash(*p, d_tokens, batch, seqlen, d_comp_map, d_prev_ctx, idx, d_bad_tokens, stream);
+    if (st != ENGRAM_OK) return st;
+    if (d_prev_ctx) {
+        {
+            Launch l(*p, ENGRAM_K_AUX, stream);
+            launch_ctx_update(d_tokens, batch, seqlen, d_comp_map, p->cfg.vocab, p->cfg.vocab_comp,
+                              d_prev_ctx, stream);
+        }
+        if (last_launch_status() != ENGRAM_OK) return ENGRAM_E_DEVICE;
+    }
+    st = do_gather(*p, idx, (int64_t)batch * seqlen, table_ptrs, emb, stream);
+    if (st != ENGRAM_OK) return st;
+    return do_fuse(*p, emb, d_h, batch, seqlen, w, d_conv_state, d_out, d_alpha, flags, d_workspace,
+                   stream);
+}
+
+engram_status engram_profile_begin(engram_plan p, int32_t max_launches) {
+    if (!p || max_launches <= 0) return ENGRAM_E_INVALID_ARG;
+    if ((int32_t)p->prof_ev.size() < 2 * max_launches) {
+        for (hipEvent_t e : p->prof_ev) hipEventDestroy(e);
+        p->prof_ev.assign(2 * max_launches, nullptr);
+        for (auto &e : p->prof_ev)
+            if (hipEventCreate(&e) != hipSuccess) return ENGRAM_E_DEVICE;
+    }
+    p->prof_kind.assign(max_launches, 0);
+    p->prof_max = max_launches;
+    p->prof_used = 0;
+    p->prof_dropped = 0;
+    p->prof_on = true;
+    return ENGRAM_OK;
+}
+
+engram_status engram_profile_end(engram_plan p, engram_profile *out) {
+    if (!p || !out) return ENGRAM_E_INVALID_ARG;
+    std::memset(out, 0, sizeof(*out));
+    p->prof_on = false;
+    engram_status st = ENGRAM_OK;
+    for (int32_t i = 0; i < p->prof_used; ++i) {
+        float ms = 0.f;
+        if (hipEventSynchronize(p->prof_ev[2 * i + 1]) != hipSuccess ||
+            hipEventElapsedTime(&ms, p->prof_ev[2 * i], p->prof_ev[2 * i + 1]) != hipSuccess) {
+            st = ENGRAM_E_DEVICE;
+            continue;
+        }
+        out->total_ms[p->prof_kind[i]] += ms;
+        out->launches[p->prof_kind[i]] += 1;
+    }
+    out->dropped = p->prof_dropped;
+    p->prof_used = 0;
+    return st;
+}
+
+engram_status engram_synth_fill_table(int32_t dtype, uint64_t seed, int32_t tau, int64_t rows,
+                                      int32_t head_dim, void *d_table, hipStream_t stream) {
+    if (!d_table || rows <= 0 || head_dim <= 0 || head_dim % 4 != 0 || tau < 0) return ENGRAM_E_INVALID_ARG;
+    if (dtype != ENGRAM_F32 && dtype != ENGRAM_BF16) return ENGRAM_E_INVALID_ARG;
+    if (!aligned16(d_table)) return ENGRAM_E_INVALID_ARG;
+    launch_synth_fill((engram_dtype)dtype, seed, tau, rows, head_dim, d_table, stream);
+    return last_launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+// engram_internal.h -- shared declarations of the gfx950 kernels and their
+// host-side launchers.  Not part of the public ABI (see include/engram.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "engram.h"
+
+namespace engram {
+
+constexpr int kMaxTables = ENGRAM_MAX_TABLES;
+constexpr int kMaxBranches = ENGRAM_MAX_BRANCHES;
+
+// Clang vector types (HIP's uint4/float4 are unions that defeat scalar
+// replacement when kept in arrays, which then land in scratch or LDS).
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- bf16 bits
+// bf16 values travel as raw 16-bit patterns; widening is a shift, narrowing
+// rounds to nearest even (finite values only: every value on the path is).
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+__device__ __forceinline__ uint32_t f32_to_bf16(float x) {
+    uint32_t u = __float_as_uint(x);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// ---------------------------------------------------------------- hashing
+struct HashConsts {
+    uint64_t seed[kMaxTables];   // per-table 64-bit seed s_tau
+    uint64_t magic[kMaxTables];  // floor((2^64-1) / rows_tau), for the Barrett reduction
+    uint32_t rows[kMaxTables];   // prime row counts
+    int32_t order_of[kMaxTables];// n-gram order of table tau (2 or 3)
+    int32_t n_tables;
+    int32_t vocab;
+    int32_t vocab_comp;
+};
+
+void launch_hash(const HashConsts &hc, const int32_t *tokens, int32_t batch, int32_t seqlen,
+                 const int32_t *comp_map, const int32_t *prev_ctx, uint32_t *idx,
+                 uint32_t *bad, hipStream_t s);
+void launch_ctx_update(const int32_t *tokens, int32_t batch, int32_t seqlen,
+                       const int32_t *comp_map, int32_t vocab, int32_t vocab_comp,
+                       int32_t *prev_ctx, hipStream_t s);
+
+// ---------------------------------------------------------------- gather
+struct GatherConsts {
+    const char *table[kMaxTables];
+    uint32_t last_row[kMaxTables];
+    int32_t n_tables;
+    int32_t row_chunks;   // 16-byte chunks per table row
+    int32_t tok_chunks;   // 16-byte chunks per token (n_tables * row_chunks)
+    uint64_t magic_tok;   // division by tok_chunks (0 when tok_chunks == 1)
+    uint64_t magic_row;   // division by row_chunks (0 when row_chunks == 1)
+};
+
+void launch_gather(const GatherConsts &gc, const uint32_t *idx, int64_t n_tok, void *emb,
+                   hipStream_t s);
+
+// ---------------------------------------------------------------- projections
+struct ProjArgs {
+    const void *emb;                       // [n_tok][K]
+    const void *w[kMaxBranches + 1];       // w_k[0..B_r-1], then w_v; each [d][K]
+    const void *h;                         // [B_r][n_tok][d]
+    const float *gamma_h[kMaxBranches];
+    const float *gamma_k[kMaxBranches];
+    float *partials;                       // [B_r][n_parts][3][n_tok]
+    void *v;                               // [n_tok][d]
+    float *kbuf;                           // f32 path only: [B_r][n_tok][d]
+    int64_t n_tok;
+    int32_t K;                             // D_e
+    int32_t d;
+    int32_t n_branches;
+    int32_t n_parts;
+};
+
+constexpr int kPartCols = 128;  // columns of d summed into one gate partial (bf16 path)
+
+void launch_proj_bf16(const ProjArgs &a, hipStream_t s);
+void launch_proj_f32(const ProjArgs &a, hipStream_t s);  // k into kbuf, v, then partials
+
+// ---------------------------------------------------------------- fusion
+struct FuseArgs {
+    const void *v;             // [n_tok][d] (dtype)
+    const float *partials;     // [B_r][n_parts][3][n_tok]
+    const void *h;             // [B_r][n_tok][d]
+    void *out;                 // [B_r][n_tok][d]
+    const float *conv_w;       // [d][K_c]
+    const float *conv_state;   // [B_r][batch][K_c-1][d] or null
+    float *state_stage;        // [B_r][batch][K_c-1][d] or null
+    float *alpha;              // [B_r][n_tok] or null
+    int32_t batch, seqlen, d, n_branches, n_parts, conv_k, conv_mode;
+    float eps;
+    uint32_t flags;
+};
+
+void launch_fuse(const FuseArgs &a, engram_dtype dt, hipStream_t s);
+
+// ---------------------------------------------------------------- synthetic tables
+void launch_synth_fill(engram_dtype dt, uint64_t seed, int32_t tau, int64_t rows, int32_t head_dim,
+                       void *table, hipStream_t s);
+
+}  // namespace engram

@@ -1,0 +1,109 @@
+// proj_f32.hip -- fp32 path of the fusion projections (tiny-configuration
+// precision path): k^(m) = W_k^(m) e, v = W_v e in fp32 on the vector ALUs
+// (MI355X's fp32 matrix and vector peaks are equal, so MFMA buys nothing
+// here), followed by the per-token gate sums over all d channels.
+#include "engram_internal.h"
+
+namespace engram {
+namespace {
+
+constexpr int TN = 64, TT = 64, TK = 16;
+
+template <typename T, int N>
+__device__ __forceinline__ T pick(const T (&arr)[N], int i) {
+    T p = arr[0];
+#pragma unroll
+    for (int j = 1; j < N; ++j)
+        if (i == j) p = arr[j];
+    return p;
+}
+
+// C^T[n][t] = sum_k W[n][k] E[t][k] over the stacked rows of every W_k^(m)
+// and W_v; k goes to kbuf[m][t][n'], v to v[t][n'].
+__global__ __launch_bounds__(256) void proj_f32_kernel(ProjArgs a) {
+    __shared__ float ws[TN][TK + 1];
+    __shared__ float es[TT][TK + 1];
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    const int d = a.d, K = a.K;
+    const int n_total = (a.n_branches + 1) * d;
+    const int n0 = blockIdx.x * TN;
+    const int64_t t0 = (int64_t)blockIdx.y * TT;
+    const float *emb = reinterpret_cast<const float *>(a.emb);
+    float acc[4][4] = {};
+    for (int k0 = 0; k0 < K; k0 += TK) {
+        for (int x = threadIdx.x; x < TN * TK; x += 256) {
+            const int r = x / TK, c = x % TK;
+            const int n = n0 + r, k = k0 + c;
+            float w = 0.f;
+            if (n < n_total && k < K) {
+                const int mat = n / d;
+                w = reinterpret_cast<const float *>(pick(a.w, mat))[(int64_t)(n - mat * d) * K + k];
+            }
+            ws[r][c] = w;
+            const int64_t t = t0 + r;
+            es[r][c] = (t < a.n_tok && k < K) ? emb[t * K + k] : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < TK; ++kk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(ws[tx + 16 * i][kk], es[ty + 16 * j][kk], acc[i][j]);
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int n = n0 + tx + 16 * i;
+        if (n >= n_total) continue;
+        const int mat = n / d, nl = n - mat * d;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t t = t0 + ty + 16 * j;
+            if (t >= a.n_tok) continue;
+            if (mat < a.n_branches)
+                a.kbuf[((int64_t)mat * a.n_tok + t) * d + nl] = acc[i][j];
+            else
+                reinterpret_cast<float *>(a.v)[t * d + nl] = acc[i][j];
+        }
+    }
+}
+
+// Gate sums of one token and branch over all d channels (n_parts == 1).
+__global__ __launch_bounds__(256) void gate_sums_f32_kernel(ProjArgs a) {
+    __shared__ float red[3][256];
+    const int64_t t = blockIdx.x;
+    const int m = blockIdx.y;
+    const int d = a.d;
+    const float *k = a.kbuf + ((int64_t)m * a.n_tok + t) * d;
+    const float *h = reinterpret_cast<const float *>(a.h) + ((int64_t)m * a.n_tok + t) * d;
+    const float *gh = pick(a.gamma_h, m), *gk = pick(a.gamma_k, m);
+    float s_hk = 0.f, s_kk = 0.f, s_hh = 0.f;
+    for (int n = threadIdx.x; n < d; n += 256) {
+        const float kv = k[n], hv = h[n];
+        s_hk += hv * gh[n] * gk[n] * kv;
+        s_kk += kv * kv;
+        s_hh += hv * hv;
+    }
+    red[0][threadIdx.x] = s_hk;
+    red[1][threadIdx.x] = s_kk;
+    red[2][threadIdx.x] = s_hh;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (threadIdx.x < w)
+            for (int q = 0; q < 3; ++q) red[q][threadIdx.x] += red[q][threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x < 3) a.partials[((int64_t)m * 3 + threadIdx.x) * a.n_tok + t] = red[threadIdx.x][0];
+}
+
+}  // namespace
+
+void launch_proj_f32(const ProjArgs &a, hipStream_t s) {
+    const int n_total = (a.n_branches + 1) * a.d;
+    dim3 grid((n_total + TN - 1) / TN, (unsigned)((a.n_tok + TT - 1) / TT));
+    hipLaunchKernelGGL(proj_f32_kernel, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(gate_sums_f32_kernel, dim3((unsigned)a.n_tok, a.n_branches), dim3(256), 0, s, a);
+}
+
+}  // namespace engram

@@ -1,0 +1,215 @@
+/*
+ * engram.h -- C ABI of the MI355X (gfx950) Engram conditional-memory forward
+ * pass: hashed suffix n-gram embeddings fused into a hidden state by a
+ * context-aware gate, a short depthwise causal convolution and a residual.
+ *
+ * Source pages (summaries of "Conditional Memory via Scalable Lookup: A New
+ * Axis of Sparsity for Large Language Models"):
+ *   [club]  discuss.deepseek.club/t/topic/717, section 二 核心创新:
+ *           1.(1) 基于 N-gram 的稀疏哈希检索 (retrieval),
+ *           1.(2) 上下文感知的门控机制 (fusion), 2. 工程优化 (multi-branch,
+ *           prefetch), 三.4 系统效率 (throughput context)
+ *   [csdn]  gitcode.csdn.net "DeepSeek又搞了个大动作，这次是真的狠",
+ *           section Engram 到底怎么工作的 (four steps; layers 2 and 6)
+ *   [rep]   reportify.cn tag page 条件记忆, summaries 技术方案：Engram架构,
+ *           技术创新与架构 / 系统效率与扩展性 (retrieval depends only on tokens)
+ *
+ * Conventions (every entry point):
+ *   - Pointers named d_* are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or retains caller memory; a plan owns only a
+ *     small host struct.
+ *   - Arguments are validated synchronously.  On any failure a non-zero
+ *     engram_status is returned and nothing is enqueued.  Kernel launch
+ *     failures return ENGRAM_E_DEVICE.  No C++ exception crosses the ABI.
+ *   - Work is enqueued on the caller's stream in order; no call synchronises
+ *     the stream or the device.  Calls on different streams with disjoint
+ *     outputs may run concurrently; plans are immutable after creation.
+ *   - Device pointers must be 16-byte aligned.
+ *   - Data errors inside kernels are defined, not trapped: raw token ids
+ *     outside [0, vocab) are treated as the PAD id and counted.
+ */
+#ifndef ENGRAM_H
+#define ENGRAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define ENGRAM_API __attribute__((visibility("default")))
+#else
+#define ENGRAM_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ENGRAM_OK = 0,
+    ENGRAM_E_INVALID_ARG = 1, /* null pointer, bad size, misalignment, short workspace */
+    ENGRAM_E_UNSUPPORTED = 2, /* a shape this build's kernels do not cover */
+    ENGRAM_E_DEVICE = 3,      /* a HIP runtime call or kernel launch failed */
+    ENGRAM_E_NOMEM = 4        /* host allocation of the plan failed */
+} engram_status;
+
+typedef enum { ENGRAM_F32 = 0, ENGRAM_BF16 = 1 } engram_dtype;
+
+/* Conv output mode.  LINEAR: y = conv(u).  SILU_SKIP: y = u + silu(conv(u)),
+ * the "adds nonlinearity" reading of [club] 1.(2). */
+enum { ENGRAM_CONV_LINEAR = 0, ENGRAM_CONV_SILU_SKIP = 1 };
+
+/* engram_gate_fuse / engram_forward flag: write y instead of h + y. */
+enum { ENGRAM_OUT_DELTA = 1u << 0 };
+
+#define ENGRAM_MAX_TABLES 32
+#define ENGRAM_MAX_BRANCHES 4
+
+typedef struct engram_plan_s *engram_plan;
+
+typedef struct {
+    int32_t vocab;       /* raw vocabulary size V                                */
+    int32_t vocab_comp;  /* compressed vocabulary V' (< 2^21); PAD id = V'      */
+    int32_t n_orders;    /* 1 or 2                                              */
+    int32_t orders[4];   /* n-gram orders, each 2 or 3 ([csdn]: last 2 and 3)   */
+    int32_t heads;       /* K hash heads per order ([club] 1.(1))               */
+    int32_t head_dim;    /* d_e: row width of every table                       */
+    uint32_t table_rows[ENGRAM_MAX_TABLES]; /* rows of table tau = o*K + k (primes) */
+    uint64_t hash_seed;  /* seed of the per-table hash seeds                    */
+    int32_t d_model;     /* hidden size d                                       */
+    int32_t n_branches;  /* residual branches B_r sharing tables and W_v (1..4) */
+    int32_t conv_kernel; /* depthwise causal conv taps K_c (1..4)               */
+    int32_t conv_mode;   /* ENGRAM_CONV_LINEAR or ENGRAM_CONV_SILU_SKIP         */
+    float rms_eps;       /* epsilon inside both RMSNorms (e.g. 1e-6)            */
+    engram_dtype dtype;  /* dtype of tables, E, h, W_k, W_v and out             */
+} engram_config;
+
+/* Device pointers to one layer's weights; all caller-owned and read-only.
+ * Multi-branch integration ([club] 2. 工程优化): branches share the tables and
+ * W_v, each has its own W_k.  Conv taps are shared by all branches. */
+typedef struct {
+    const void *w_k[ENGRAM_MAX_BRANCHES];       /* [d][D_e] per branch, dtype; row n gives channel n */
+    const void *w_v;                            /* [d][D_e], dtype                          */
+    const float *gamma_h[ENGRAM_MAX_BRANCHES];  /* [d] RMSNorm weight of h, per branch      */
+    const float *gamma_k[ENGRAM_MAX_BRANCHES];  /* [d] RMSNorm weight of k, per branch      */
+    const float *conv_w;                        /* [d][K_c]; tap K_c-1 multiplies the current token */
+} engram_weights;
+
+/* Per-kernel timing gathered while profiling is on (see engram_profile_*). */
+enum {
+    ENGRAM_K_HASH = 0,
+    ENGRAM_K_GATHER = 1,
+    ENGRAM_K_GEMM = 2,   /* projections W_k e (all branches) and W_v e, gate partials fused */
+    ENGRAM_K_FUSE = 3,   /* gate, gated value, depthwise conv, residual, state */
+    ENGRAM_K_AUX = 4,    /* context / state bookkeeping                        */
+    ENGRAM_K_COUNT = 5
+};
+
+typedef struct {
+    double total_ms[ENGRAM_K_COUNT];
+    int64_t launches[ENGRAM_K_COUNT];
+    int64_t dropped; /* launches not timed because the event pool ran out */
+} engram_profile;
+
+/* Create a plan from a config (host only, no device work).  Validates the
+ * config: V' < 2^21 so n-gram keys stay injective in 64 bits, n_tables =
+ * n_orders*heads <= 32, every table_rows in [1, 2^31), head_dim*elem_bytes a
+ * multiple of 16, 1 <= n_branches <= 4, 1 <= conv_kernel <= 4. */
+ENGRAM_API engram_status engram_plan_create(const engram_config *cfg, engram_plan *out);
+ENGRAM_API engram_status engram_plan_destroy(engram_plan p);
+
+/* Bytes of device workspace engram_forward needs for batch*seqlen tokens
+ * (also enough for engram_gate_fuse).  0 on invalid arguments. */
+ENGRAM_API size_t engram_workspace_size(engram_plan p, int32_t batch, int32_t seqlen);
+
+ENGRAM_API const char *engram_status_string(engram_status s);
+
+/*
+ * Retrieval, steps 1-3 ([club] 1.(1); [csdn] first two steps; [rep]
+ * 技术创新与架构): compress every raw id through the vocabulary projection,
+ * form the suffix n-grams of each order at every position (oldest id first;
+ * positions before the sequence start take d_prev_ctx, else PAD = V'), and
+ * hash each n-gram with each head into its prime-sized table.
+ *   d_tokens     [batch][seqlen] int32 raw ids
+ *   d_comp_map   [V] int32, values in [0, V')
+ *   d_prev_ctx   [batch][2] int32 compressed ids preceding token 0 (oldest
+ *                first), or NULL for a sequence start.  Not modified.
+ *   d_idx        [batch*seqlen][n_tables] uint32 output slots
+ *   d_bad_tokens optional uint32 counter, incremented (atomically) once per
+ *                raw id outside [0, V); such ids hash as PAD.
+ * The slot of an n-gram g = (g_0..g_{n-1}) in table tau is
+ *   mix64(key(g) XOR s_tau) mod rows_tau,  key(g) = sum_i g_i (V'+1)^(n-1-i),
+ * mix64 the SplitMix64 output function, s_tau = mix64(hash_seed +
+ * (tau+1)*0x9E3779B97F4A7C15) (the pages only say the hashing is
+ * deterministic and multi-headed; these constants are this library's).
+ */
+ENGRAM_API engram_status engram_hash(engram_plan p, const int32_t *d_tokens, int32_t batch, int32_t seqlen,
+                          const int32_t *d_comp_map, const int32_t *d_prev_ctx, uint32_t *d_idx,
+                          uint32_t *d_bad_tokens, hipStream_t stream);
+
+/*
+ * Retrieval, step 4 ([club] 1.(1): concatenate the heads' lookups): for every
+ * token t and table tau, copy row d_idx[t][tau] of table tau into
+ * E[t][tau*d_e : (tau+1)*d_e].  Bit-exact copy.
+ *   d_idx       [n_tokens][n_tables] uint32, each < table_rows[tau]
+ *               (larger values are clamped to the last row, never read out of bounds)
+ *   table_ptrs  HOST array of n_tables DEVICE pointers, table tau is
+ *               [table_rows[tau]][d_e] row-major in the plan dtype
+ *   d_emb       [n_tokens][n_tables*d_e] plan dtype
+ */
+ENGRAM_API engram_status engram_gather(engram_plan p, const uint32_t *d_idx, int64_t n_tokens,
+                            const void *const *table_ptrs, void *d_emb, hipStream_t stream);
+
+/*
+ * Fusion ([club] 1.(2); [csdn] third and fourth steps), per branch m and token t:
+ *   k = W_k^(m) e_t, v = W_v e_t                      (fp32 accumulation)
+ *   alpha = sigmoid( <RMSNorm_{gamma_h}(h_t), RMSNorm_{gamma_k}(k)> / sqrt(d) )
+ *   u_t = alpha * v
+ *   conv_t[i] = sum_j conv_w[i][K_c-1-j] * u_{t-j}[i]   (depthwise, causal)
+ *   y = conv (LINEAR) or u + conv*sigmoid(conv) (SILU_SKIP)
+ *   out_t = h_t + y   (or y with ENGRAM_OUT_DELTA)
+ * with RMSNorm_g(x) = g * x / sqrt(mean(x^2) + eps).
+ *   d_emb        [batch*seqlen][D_e], D_e = n_tables*d_e
+ *   d_h, d_out   [n_branches][batch*seqlen][d]; d_out may alias d_h
+ *   d_conv_state [n_branches][batch][K_c-1][d] fp32 gated values preceding
+ *                position 0 (oldest first), or NULL for zeros.  When given it
+ *                is replaced by the last K_c-1 gated values of the sequence
+ *                extended by this chunk, so chunked prefill and decode equal
+ *                one full prefill.
+ *   d_alpha      optional [n_branches][batch*seqlen] fp32 gate values
+ *   d_workspace  >= engram_workspace_size(p, batch, seqlen) bytes, 256-byte aligned
+ * Supported: bf16 with d % 128 == 0 and D_e % 64 == 0; f32 any d, D_e.
+ */
+ENGRAM_API engram_status engram_gate_fuse(engram_plan p, const void *d_emb, const void *d_h, int32_t batch,
+                               int32_t seqlen, const engram_weights *w, float *d_conv_state,
+                               void *d_out, float *d_alpha, uint32_t flags, void *d_workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The whole forward pass: engram_hash, engram_gather and engram_gate_fuse in
+ * one call (indices and E live in the workspace).  If d_prev_ctx is non-NULL
+ * it is read as in engram_hash and then replaced by the last two compressed
+ * ids of the sequence extended by this chunk.
+ */
+ENGRAM_API engram_status engram_forward(engram_plan p, const int32_t *d_tokens, int32_t batch, int32_t seqlen,
+                             const int32_t *d_comp_map, int32_t *d_prev_ctx,
+                             const void *const *table_ptrs, const void *d_h,
+                             const engram_weights *w, float *d_conv_state, void *d_out,
+                             float *d_alpha, uint32_t flags, void *d_workspace,
+                             size_t workspace_bytes, uint32_t *d_bad_tokens, hipStream_t stream);
+
+/*
+ * Profiling: while on, every kernel the plan launches is bracketed by HIP
+ * events recorded on the launch stream (at most max_launches launches are
+ * timed).  engram_profile_end synchronises on those events, fills *out with
+ * per-kernel totals and turns profiling off.  Not thread-safe per plan.
+ */
+ENGRAM_API engram_status engram_profile_begin(engram_plan p, int32_t max_launches);
+ENGRAM_API engram_status engram_profile_end(engram_plan p, engram_profile *out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ENGRAM_H */

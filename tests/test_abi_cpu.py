@@ -1,0 +1,162 @@
+"""The C-ABI library on the CPU: it loads, exports every declared entry point,
+and its host-side validation rejects bad arguments without touching a GPU."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def B():
+    from hashed_gram_embedding_vocab_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from hashed_gram_embedding_vocab_amd import build
+        build.build()
+    binding.lib()
+    return binding
+
+
+def declared_symbols():
+    names = []
+    inc = os.path.join(ROOT, "include")
+    for f in sorted(os.listdir(inc)):
+        if f.endswith(".h"):
+            text = open(os.path.join(inc, f)).read()
+            names += re.findall(r"ENGRAM_API\s+[\w\s\*]+?\b(engram_\w+)\s*\(", text)
+    return names
+
+
+def test_library_exports_every_declared_symbol(B):
+    names = declared_symbols()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(B.lib(), n), n
+
+
+def _cfg(B, **kw):
+    c = B.Config()
+    c.vocab, c.vocab_comp, c.n_orders = 1000, 770, 2
+    c.orders[0], c.orders[1] = 2, 3
+    c.heads, c.head_dim = 4, 32
+    for i in range(8):
+        c.table_rows[i] = 10007
+    c.hash_seed = 1
+    c.d_model, c.n_branches, c.conv_kernel, c.conv_mode = 256, 1, 4, 0
+    c.rms_eps, c.dtype = 1e-6, B.F32
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def _create(B, c):
+    h = C.c_void_p()
+    st = B.lib().engram_plan_create(C.byref(c), C.byref(h))
+    if st == 0:
+        B.lib().engram_plan_destroy(h)
+    return st
+
+
+def test_plan_validation(B):
+    assert _create(B, _cfg(B)) == B.OK
+    bad = [dict(vocab_comp=1 << 21), dict(heads=0), dict(heads=17), dict(head_dim=30),
+           dict(head_dim=0), dict(d_model=100), dict(n_branches=5), dict(n_branches=0),
+           dict(conv_kernel=5), dict(conv_kernel=0), dict(conv_mode=7), dict(n_orders=3),
+           dict(dtype=5), dict(rms_eps=-1.0)]
+    for kw in bad:
+        assert _create(B, _cfg(B, **kw)) == B.E_INVALID_ARG, kw
+    c = _cfg(B)
+    c.table_rows[3] = 0
+    assert _create(B, c) == B.E_INVALID_ARG
+    c = _cfg(B)
+    c.orders[1] = 4
+    assert _create(B, c) == B.E_INVALID_ARG
+    # bf16 rows of 32 dims are 64 bytes: fine; 4 dims are 8 bytes: rejected
+    assert _create(B, _cfg(B, dtype=B.BF16)) == B.OK
+    assert _create(B, _cfg(B, dtype=B.BF16, head_dim=4)) == B.E_INVALID_ARG
+
+
+def test_workspace_size(B):
+    p = B.Plan(vocab=1000, vocab_comp=770, heads=4, head_dim=32, table_rows=[10007] * 8, hash_seed=1,
+               d_model=256, dtype=B.F32)
+    a = p.engram_workspace_size(2, 128)
+    b = p.engram_workspace_size(2, 256)
+    assert 0 < a < b and a % 256 == 0
+    n_tok = 256
+    # idx + E + partials + v + k + conv stage, all fp32 here
+    assert a >= n_tok * 8 * 4 + n_tok * 256 * 4 + 3 * n_tok * 4 + n_tok * 256 * 4 * 2
+    assert p.engram_workspace_size(0, 5) == 0
+    assert p.engram_workspace_size(2, -1) == 0
+
+
+def test_status_strings(B):
+    for s in range(5):
+        assert B.lib().engram_status_string(s)
+    assert B.lib().engram_status_string(99) == b"unknown status"
+
+
+def _no_gpu():
+    # These calls hand the library fake device pointers that only host-side
+    # validation stands between and a launch; keep them off machines with a GPU.
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("fake-pointer validation tests run only where no GPU exists")
+
+
+def test_entry_points_reject_bad_arguments_before_launching(B):
+    _no_gpu()
+    L = B.lib()
+    p = B.Plan(vocab=1000, vocab_comp=770, heads=4, head_dim=32, table_rows=[10007] * 8, hash_seed=1,
+               d_model=256, dtype=B.F32)
+    h = p._h
+    fake = C.c_void_p(0x10000)       # never dereferenced: validation fails first
+    odd = C.c_void_p(0x10004)        # not 16-byte aligned
+    assert L.engram_hash(None, fake, 1, 1, fake, None, fake, None, None) == B.E_INVALID_ARG
+    assert L.engram_hash(h, None, 1, 1, fake, None, fake, None, None) == B.E_INVALID_ARG
+    assert L.engram_hash(h, fake, 0, 1, fake, None, fake, None, None) == B.E_INVALID_ARG
+    assert L.engram_hash(h, fake, 1, -3, fake, None, fake, None, None) == B.E_INVALID_ARG
+    assert L.engram_hash(h, odd, 1, 1, fake, None, fake, None, None) == B.E_INVALID_ARG
+    tabs = (C.c_void_p * 8)(*([0x10000] * 8))
+    assert L.engram_gather(h, fake, 0, tabs, fake, None) == B.E_INVALID_ARG
+    assert L.engram_gather(h, fake, 4, None, fake, None) == B.E_INVALID_ARG
+    tabs_bad = (C.c_void_p * 8)(*([0x10000] * 7 + [0]))
+    assert L.engram_gather(h, fake, 4, tabs_bad, fake, None) == B.E_INVALID_ARG
+    tabs_odd = (C.c_void_p * 8)(*([0x10000] * 7 + [0x10008]))
+    assert L.engram_gather(h, fake, 4, tabs_odd, fake, None) == B.E_INVALID_ARG
+    w = B.WeightsC()
+    w.w_k[0] = w.w_v = w.gamma_h[0] = w.gamma_k[0] = w.conv_w = 0x10000
+    ws_ok = p.engram_workspace_size(1, 4)
+    args = [h, fake, fake, 1, 4, C.byref(w), None, fake, None, 0, fake, ws_ok, None]
+    # workspace too small, bad flags, missing weight, misaligned workspace
+    a = list(args); a[11] = ws_ok - 1
+    assert L.engram_gate_fuse(*a) == B.E_INVALID_ARG
+    a = list(args); a[9] = 0x8
+    assert L.engram_gate_fuse(*a) == B.E_INVALID_ARG
+    a = list(args); a[10] = C.c_void_p(0x10010)
+    assert L.engram_gate_fuse(*a) == B.E_INVALID_ARG
+    w2 = B.WeightsC()
+    w2.w_v = w2.gamma_h[0] = w2.gamma_k[0] = w2.conv_w = 0x10000
+    a = list(args); a[5] = C.byref(w2)
+    assert L.engram_gate_fuse(*a) == B.E_INVALID_ARG
+    assert L.engram_forward(h, fake, 1, 4, fake, None, tabs, fake, C.byref(w), None, fake, None, 0,
+                            None, 0, None, None) == B.E_INVALID_ARG
+    assert L.engram_synth_fill_table(7, 1, 0, 10, 32, fake, None) == B.E_INVALID_ARG
+    assert L.engram_synth_fill_table(0, 1, 0, 10, 30, fake, None) == B.E_INVALID_ARG
+    assert L.engram_synth_fill_table(0, 1, 0, 10, 32, odd, None) == B.E_INVALID_ARG
+
+
+def test_bf16_shape_support_is_checked(B):
+    _no_gpu()
+    L = B.lib()
+    # d = 200 is a multiple of 8 but not of 128: the bf16 MFMA path reports UNSUPPORTED
+    p = B.Plan(vocab=1000, vocab_comp=770, heads=4, head_dim=32, table_rows=[10007] * 8, hash_seed=1,
+               d_model=200, dtype=B.BF16)
+    fake = C.c_void_p(0x10000)
+    w = B.WeightsC()
+    w.w_k[0] = w.w_v = w.gamma_h[0] = w.gamma_k[0] = w.conv_w = 0x10000
+    ws = p.engram_workspace_size(1, 4)
+    assert L.engram_gate_fuse(p._h, fake, fake, 1, 4, C.byref(w), None, fake, None, 0,
+                              C.c_void_p(0x100000), ws, None) == B.E_UNSUPPORTED

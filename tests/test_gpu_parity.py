@@ -1,0 +1,423 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Indices and gathered rows must match bit for bit; floating-point outputs
+within the tolerances of ``engram_harness`` (fp32: 1e-5 relative to the
+larger of |ref| and the row's rms; bf16 storage with fp32 accumulation:
+1e-2 absolute + 2e-2 relative).  Expected values come only from ``oracle/``
+on the same seeded inputs.
+"""
+
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from engram_harness import (alpha_tol, assert_within, oracle_dtype, oracle_indices, oracle_layer,
+                            rows_needed, sample_positions)
+from synthetic import workloads as W
+from synthetic.device import make_device_layer, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B(gpu):
+    from hashed_gram_embedding_vocab_amd import binding
+    binding.lib()  # raises if the library is not built: no fallback
+    return binding
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_i32(x):
+    return to_device(np.asarray(x, np.int32), torch.int32, "cuda")
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy()
+    return t.cpu().numpy()
+
+
+def forward(dl, tokens, prev_ctx=None, conv_state=None, flags=0, h=None, out=None, stream=None):
+    batch, seqlen = tokens.shape
+    h = dl.h if h is None else h
+    out = torch.empty_like(h) if out is None else out
+    alpha = torch.full((dl.wl.n_branches, batch * seqlen), -1.0, dtype=torch.float32, device="cuda")
+    ws = dl.plan.workspace(batch, seqlen)
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dl.plan.engram_forward(dev_i32(tokens), dl.comp_map, dl.tables, h, dl.weights, out, ws,
+                           prev_ctx=prev_ctx, conv_state=conv_state, alpha=alpha, flags=flags,
+                           bad_tokens=bad, stream=stream)
+    torch.cuda.synchronize()
+    return out, alpha, int(bad.item())
+
+
+def small_wl(n_branches=1, batch=3, seqlen=77, d_model=256, heads=2, head_dim=32, conv_kernel=4,
+             dtype="bf16", name="small_custom"):
+    return dataclasses.replace(W.workload("small"), name=name, index=40 + n_branches, batch=batch,
+                               seqlen=seqlen, d_model=d_model, heads=heads, head_dim=head_dim,
+                               table_target=10007, same_prime=False, n_branches=n_branches,
+                               conv_kernel=conv_kernel, dtype=dtype)
+
+
+# ----------------------------------------------------------------------------
+# synthetic tables: the device generator equals the oracle's generator
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt,rows,hd", [("f32", 10007, 32), ("bf16", 4099, 80)])
+def test_synth_fill_bit_exact(B, dt, rows, hd):
+    say("synth fill", dt, rows, hd)
+    code = B.BF16 if dt == "bf16" else B.F32
+    t = torch.empty((rows, hd), dtype=torch.bfloat16 if dt == "bf16" else torch.float32, device="cuda")
+    B.engram_synth_fill_table(t, 3, 5, code)
+    torch.cuda.synchronize()
+    if dt == "bf16":
+        got = t.view(torch.int16).cpu().numpy().view(np.uint16)
+    else:
+        got = t.cpu().numpy()
+    rng = np.random.default_rng(1)
+    sample = sorted({0, 1, rows - 1, *rng.integers(0, rows, 40).tolist()})
+    for r in sample:
+        for c in range(hd):
+            v = oracle.synth_value(3, 5, r, c)
+            if dt == "bf16":
+                assert got[r, c] == oracle.bf16_rne(v), (r, c)
+            else:
+                assert got[r, c] == np.float32(v), (r, c)
+
+
+# ----------------------------------------------------------------------------
+# hashing: bit-exact slots
+# ----------------------------------------------------------------------------
+
+def _hash_gpu(B, plan, tokens, comp_dev, n_tables, prev_ctx=None):
+    batch, seqlen = tokens.shape
+    idx = torch.zeros((batch * seqlen, n_tables), dtype=torch.int32, device="cuda")
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    plan.engram_hash(dev_i32(tokens), comp_dev, idx,
+                     prev_ctx=None if prev_ctx is None else dev_i32(prev_ctx), bad_tokens=bad)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy().view(np.uint32), int(bad.item())
+
+
+def test_hash_tiny_vocab_exhaustive(B):
+    say("hash tiny vocab")
+    V, Vc, heads = 7, 5, 2
+    comp = W.compression_map(V, Vc, 99)
+    pre = {int(c): int(np.nonzero(comp == c)[0][0]) for c in range(Vc)}
+    seqs = [(a, b, c) for a in range(Vc) for b in range(Vc) for c in range(Vc)]
+    toks = np.array([[pre[a], pre[b], pre[c]] for a, b, c in seqs], np.int32)
+    primes = [13, 11, 7, 5]
+    plan = B.Plan(vocab=V, vocab_comp=Vc, heads=heads, head_dim=32, table_rows=primes, hash_seed=0x1234,
+                  d_model=256, dtype=B.F32)
+    comp_dev = dev_i32(comp)
+    got, bad = _hash_gpu(B, plan, toks, comp_dev, 4)
+    ref, rbad, _ = oracle.hash_tokens(toks, comp, V, Vc, heads, primes, 0x1234)
+    assert bad == rbad == 0
+    assert np.array_equal(got, ref)
+    ctx = np.random.default_rng(2).integers(0, Vc + 1, (len(seqs), 2)).astype(np.int32)
+    got, _ = _hash_gpu(B, plan, toks, comp_dev, 4, prev_ctx=ctx)
+    ref, _, _ = oracle.hash_tokens(toks, comp, V, Vc, heads, primes, 0x1234, prev_ctx=ctx)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("name,batch,seqlen", [
+    ("tiny", 1, 1), ("tiny", 1, 2), ("tiny", 1, 3), ("tiny", 3, 63), ("tiny", 2, 64), ("tiny", 2, 65),
+    ("tiny", 5, 200), ("layer27b", 2, 1000), ("maxtable_uniform", 1, 300), ("multibranch_prefill", 1, 129),
+])
+@pytest.mark.parametrize("with_ctx", [False, True])
+def test_hash_shapes(B, name, batch, seqlen, with_ctx):
+    say("hash", name, batch, seqlen, with_ctx)
+    wl = W.workload(name)
+    li = W.make_layer_inputs(wl, batch=1, seqlen=1)
+    comp = W.compression_map(wl.vocab, wl.vocab_comp, wl.seed(1))
+    toks = W.make_tokens(wl, batch=batch, seqlen=seqlen)
+    ctx = None
+    if with_ctx:
+        ctx = np.random.default_rng(3).integers(0, wl.vocab_comp + 1, (batch, 2)).astype(np.int32)
+    plan = B.Plan(vocab=wl.vocab, vocab_comp=wl.vocab_comp, heads=wl.heads, head_dim=wl.head_dim,
+                  table_rows=wl.primes(), hash_seed=li.hash_seed, d_model=wl.d_model,
+                  n_branches=wl.n_branches, dtype=B.BF16 if wl.dtype == "bf16" else B.F32)
+    got, bad = _hash_gpu(B, plan, toks, dev_i32(comp), wl.n_tables, prev_ctx=ctx)
+    ref, rbad, _ = oracle_indices(wl, li, toks, comp, prev_ctx=ctx)
+    assert bad == rbad == 0
+    assert np.array_equal(got, ref)
+
+
+def test_hash_out_of_range_tokens(B):
+    say("hash bad tokens")
+    wl = W.workload("tiny")
+    li = W.make_layer_inputs(wl, batch=1, seqlen=1)
+    comp = W.compression_map(wl.vocab, wl.vocab_comp, wl.seed(1))
+    toks = W.make_tokens(wl, batch=2, seqlen=130)
+    for b, t, v in [(0, 0, -1), (0, 1, wl.vocab), (0, 63, 2**31 - 1), (0, 64, -2**31), (1, 129, 5000),
+                    (1, 65, -7)]:
+        toks[b, t] = v
+    plan = B.Plan(vocab=wl.vocab, vocab_comp=wl.vocab_comp, heads=wl.heads, head_dim=wl.head_dim,
+                  table_rows=wl.primes(), hash_seed=li.hash_seed, d_model=wl.d_model, dtype=B.F32)
+    got, bad = _hash_gpu(B, plan, toks, dev_i32(comp), wl.n_tables)
+    ref, rbad, _ = oracle_indices(wl, li, toks, comp)
+    assert bad == rbad == 6
+    assert np.array_equal(got, ref)
+
+
+# ----------------------------------------------------------------------------
+# gather: bit-exact rows
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt,head_dim,primes", [
+    ("f32", 32, [10007] * 8),
+    ("bf16", 80, W.largest_primes_at_most(5000, 16)),
+    ("bf16", 64, W.largest_primes_at_most(3001, 4)),
+])
+@pytest.mark.parametrize("n_tok", [1, 1000, 4099])
+def test_gather_bit_exact(B, dt, head_dim, primes, n_tok):
+    say("gather", dt, head_dim, len(primes), n_tok)
+    code = B.BF16 if dt == "bf16" else B.F32
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    n_tables = len(primes)
+    plan = B.Plan(vocab=1000, vocab_comp=770, heads=n_tables // 2, head_dim=head_dim, table_rows=primes,
+                  hash_seed=1, d_model=256, dtype=code)
+    seed = 17
+    tables = []
+    for tau, p in enumerate(primes):
+        t = torch.empty((p, head_dim), dtype=tdt, device="cuda")
+        B.engram_synth_fill_table(t, seed, tau, code)
+        tables.append(t)
+    rng = np.random.default_rng(n_tok)
+    idx = np.stack([rng.integers(0, p, n_tok) for p in primes], 1).astype(np.uint32)
+    idx[0] = 0
+    idx[-1] = np.array(primes) - 1
+    emb = torch.empty((n_tok, n_tables * head_dim), dtype=tdt, device="cuda")
+    plan.engram_gather(dev_i32(idx.view(np.int32)), tables, emb)
+    torch.cuda.synchronize()
+    got = emb.view(torch.int16).cpu().numpy().view(np.uint16) if dt == "bf16" else emb.cpu().numpy()
+    ref = oracle.gather_synth(idx, head_dim, seed, oracle.BF16 if dt == "bf16" else oracle.F32)
+    assert np.array_equal(got.view(np.uint8), ref.view(np.uint8))
+
+
+# ----------------------------------------------------------------------------
+# whole forward pass
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode,flags", [(oracle.CONV_LINEAR, 0), (oracle.CONV_SILU_SKIP, 0),
+                                        (oracle.CONV_LINEAR, oracle.OUT_DELTA)])
+def test_forward_tiny_all_positions(B, mode, flags):
+    say("forward tiny", mode, flags)
+    wl = W.workload("tiny")
+    dl = make_device_layer(wl, conv_mode=mode)
+    toks = W.make_tokens(wl)
+    out, alpha, bad = forward(dl, toks, flags=flags)
+    idx, _, _ = oracle_indices(wl, dl.li, toks, dl.comp_map_host)
+    L = oracle_layer(wl, dl.li, idx, wl.batch, wl.seqlen, conv_mode=mode, flags=flags)
+    ref, ref_alpha, _ = L.forward_all()
+    assert bad == 0
+    assert_within(host(out), ref, "f32", "tiny out")
+    assert np.abs(host(alpha) - ref_alpha).max() <= alpha_tol("f32")
+
+
+@pytest.mark.parametrize("n_branches", [1, 2, 4])
+@pytest.mark.parametrize("batch,seqlen", [(3, 77), (1, 1), (2, 130)])
+def test_forward_bf16_small_shapes_all_positions(B, n_branches, batch, seqlen):
+    say("forward bf16 small", n_branches, batch, seqlen)
+    wl = small_wl(n_branches=n_branches, batch=batch, seqlen=seqlen)
+    dl = make_device_layer(wl)
+    toks = W.make_tokens(wl)
+    out, alpha, _ = forward(dl, toks)
+    idx, _, _ = oracle_indices(wl, dl.li, toks, dl.comp_map_host)
+    L = oracle_layer(wl, dl.li, idx, batch, seqlen)
+    ref, ref_alpha, _ = L.forward_all()
+    assert_within(host(out), ref, "bf16", "bf16 small out")
+    assert np.abs(host(alpha) - ref_alpha).max() <= alpha_tol("bf16")
+    # y alone, so an error in y cannot hide next to h
+    dl2 = make_device_layer(wl, conv_mode=oracle.CONV_SILU_SKIP)
+    y, _, _ = forward(dl2, toks, flags=oracle.OUT_DELTA)
+    L2 = oracle_layer(wl, dl2.li, idx, batch, seqlen, conv_mode=oracle.CONV_SILU_SKIP,
+                      flags=oracle.OUT_DELTA)
+    ref_y, _, _ = L2.forward_all()
+    assert_within(host(y), ref_y, "bf16", "bf16 small y (silu skip)")
+
+
+def _sampled_check(wl, dl, toks, n_pos, what, prev_ctx=None, conv_state=None, seed=0):
+    batch, seqlen = toks.shape
+    out, alpha, bad = forward(dl, toks, prev_ctx=None if prev_ctx is None else dev_i32(prev_ctx),
+                              conv_state=None if conv_state is None else to_device(conv_state, torch.float32, "cuda"))
+    assert bad == 0
+    pos = sample_positions(batch, seqlen, n_pos, seed)
+    idx, _, _ = oracle_indices(wl, dl.li, toks, dl.comp_map_host, prev_ctx=prev_ctx)
+    L = oracle_layer(wl, dl.li, idx, batch, seqlen, rows=rows_needed(pos, seqlen, wl.conv_kernel),
+                     conv_state=conv_state)
+    ref, ref_alpha = L.forward_positions(pos)
+    got = host(out)[:, pos]
+    assert_within(got, ref, wl.dtype, what)
+    assert np.abs(host(alpha)[:, pos] - ref_alpha).max() <= alpha_tol(wl.dtype)
+    return out
+
+
+@pytest.mark.parametrize("name", ["small", "layer27b"])
+def test_forward_full_size_sampled(B, name):
+    say("forward full size", name)
+    wl = W.workload(name)
+    dl = make_device_layer(wl)
+    toks = W.make_tokens(wl)
+    _sampled_check(wl, dl, toks, 48, name)
+    del dl
+    torch.cuda.empty_cache()
+
+
+def test_forward_multibranch_prefill_two_layers_sampled(B):
+    wl = W.workload("multibranch_prefill")
+    toks = W.make_tokens(wl)
+    for slot in range(len(wl.layers)):
+        say("forward multibranch prefill layer", wl.layers[slot])
+        dl = make_device_layer(wl, layer_slot=slot)
+        _sampled_check(wl, dl, toks, 20, "multibranch layer %d" % wl.layers[slot], seed=slot)
+        del dl
+        torch.cuda.empty_cache()
+
+
+def test_forward_multibranch_decode_with_state(B):
+    wl = W.workload("multibranch_decode")
+    toks = W.make_tokens(wl)
+    for slot in range(len(wl.layers)):
+        say("forward multibranch decode layer", wl.layers[slot])
+        dl = make_device_layer(wl, layer_slot=slot)
+        ctx = dev_i32(dl.li.prev_ctx)
+        state = to_device(dl.li.conv_state, torch.float32, "cuda")
+        out, alpha, bad = forward(dl, toks, prev_ctx=ctx, conv_state=state)
+        assert bad == 0
+        rows = np.arange(0, wl.batch, 7)
+        idx, _, new_ctx = oracle_indices(wl, dl.li, toks, dl.comp_map_host, prev_ctx=dl.li.prev_ctx)
+        L = oracle_layer(wl, dl.li, idx, wl.batch, 1, rows=rows, conv_state=dl.li.conv_state)
+        ref, ref_alpha = L.forward_positions(rows)
+        assert_within(host(out)[:, rows], ref, "bf16", "decode out")
+        assert np.abs(host(alpha)[:, rows] - ref_alpha).max() <= alpha_tol("bf16")
+        assert np.array_equal(ctx.cpu().numpy(), new_ctx)
+        # new conv state = [old rows 1, 2, u_0]
+        st = state.cpu().numpy()
+        assert np.array_equal(st[:, :, :2], dl.li.conv_state[:, :, 1:])
+        for r in rows[:8]:
+            _, _, u = L.forward_range(int(r), 0, 1, want_u=True)
+            np.testing.assert_allclose(st[:, r, 2], u[:, 0], rtol=2e-2, atol=1e-2)
+        del dl
+        torch.cuda.empty_cache()
+
+
+@pytest.fixture(scope="module")
+def maxtable_layer(B):
+    wl = W.workload("maxtable_zipf")
+    say("allocating max-table layer (%.1f GB of tables)" % (wl.table_bytes() / 1e9))
+    dl = make_device_layer(wl)
+    yield dl
+    dl.free_tables()
+    del dl
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["maxtable_zipf", "maxtable_uniform"])
+def test_forward_maxtable_sampled(B, maxtable_layer, name):
+    say("forward", name)
+    wl = W.workload(name)
+    toks = W.make_tokens(wl)
+    _sampled_check(wl, maxtable_layer, toks, 24, name)
+
+
+# ----------------------------------------------------------------------------
+# invariants on the GPU path
+# ----------------------------------------------------------------------------
+
+def _split(x, n_branches, batch, seqlen, a, b):
+    d = x.shape[-1]
+    return x.view(n_branches, batch, seqlen, d)[:, :, a:b].contiguous().view(n_branches, batch * (b - a), d)
+
+
+def test_chunked_prefill_and_decode_equal_full_prefill_bitwise(B):
+    say("chunk invariance")
+    wl = small_wl(n_branches=4, batch=3, seqlen=40)
+    dl = make_device_layer(wl)
+    toks = W.make_tokens(wl)
+    Br, d = wl.n_branches, wl.d_model
+    pad = np.full((wl.batch, 2), wl.vocab_comp, np.int32)
+    ctx_full = dev_i32(pad)
+    st_full = torch.zeros((Br, wl.batch, 3, d), dtype=torch.float32, device="cuda")
+    full, alpha_full, _ = forward(dl, toks, prev_ctx=ctx_full, conv_state=st_full)
+    ctx = dev_i32(pad)
+    st = torch.zeros_like(st_full)
+    parts, alphas = [], []
+    for a, b in [(0, 1), (1, 2), (2, 5), (5, 37), (37, 38), (38, 40)]:
+        h = _split(dl.h, Br, wl.batch, wl.seqlen, a, b)
+        o, al, _ = forward(dl, np.ascontiguousarray(toks[:, a:b]), prev_ctx=ctx, conv_state=st, h=h)
+        parts.append(o.view(Br, wl.batch, b - a, d))
+        alphas.append(al.view(Br, wl.batch, b - a))
+    chunked = torch.cat(parts, 2).view(Br, -1, d)
+    assert torch.equal(chunked, full)
+    assert torch.equal(torch.cat(alphas, 2).view(Br, -1), alpha_full)
+    assert torch.equal(ctx, ctx_full)
+    assert torch.equal(st, st_full)
+    # and the carried context is the last two compressed ids
+    assert np.array_equal(ctx.cpu().numpy(), dl.comp_map_host[toks[:, -2:]])
+
+
+def test_determinism_streams_and_in_place(B):
+    say("determinism")
+    wl = W.workload("small")
+    dl = make_device_layer(wl, batch=2, seqlen=1024)
+    toks = W.make_tokens(wl, batch=2, seqlen=1024)
+    o1, a1, _ = forward(dl, toks)
+    o2, a2, _ = forward(dl, toks)
+    assert torch.equal(o1, o2) and torch.equal(a1, a2)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o3, a3, _ = forward(dl, toks, stream=s)
+    assert torch.equal(o1, o3) and torch.equal(a1, a3)
+    h_copy = dl.h.clone()
+    o4, _, _ = forward(dl, toks, h=h_copy, out=h_copy)  # out aliases h
+    assert torch.equal(o1, o4)
+
+
+def test_causality_on_gpu(B):
+    say("causality")
+    wl = small_wl(n_branches=2, batch=2, seqlen=100)
+    dl = make_device_layer(wl)
+    toks = W.make_tokens(wl)
+    base, _, _ = forward(dl, toks)
+    t0 = 60
+    toks2 = toks.copy()
+    toks2[0, t0 + 1:] = np.random.default_rng(5).integers(0, wl.vocab, wl.seqlen - t0 - 1)
+    h2 = dl.h.clone().view(2, 2, 100, -1)
+    h2[:, 0, t0 + 1:] += 1.0
+    pert, _, _ = forward(dl, toks2, h=h2.view(2, 200, -1))
+    b4 = base.view(2, 2, 100, -1)
+    p4 = pert.view(2, 2, 100, -1)
+    assert torch.equal(p4[:, 0, :t0 + 1], b4[:, 0, :t0 + 1])
+    assert not torch.equal(p4[:, 0, t0 + 1:], b4[:, 0, t0 + 1:])
+    assert torch.equal(p4[:, 1], b4[:, 1])
+
+
+def test_profiling_counts_launches(B):
+    wl = W.workload("tiny")
+    dl = make_device_layer(wl)
+    toks = W.make_tokens(wl)
+    dl.plan.engram_profile_begin(64)
+    forward(dl, toks)
+    forward(dl, toks)
+    prof = dl.plan.engram_profile_end()
+    for k in ("hash", "gather", "gemm", "fuse"):
+        assert prof[k]["launches"] == 2, (k, prof)
+        assert prof[k]["total_ms"] > 0
+    assert prof["dropped"] == 0
+
+
+def test_unsupported_bf16_shape_is_rejected(B):
+    wl = small_wl(d_model=200, batch=1, seqlen=8)
+    with pytest.raises(B.EngramError) as e:
+        dl = make_device_layer(wl)
+        forward(dl, W.make_tokens(wl))
+    assert e.value.status == B.E_UNSUPPORTED
