@@ -66,7 +66,7 @@ bool layout_of(const engram_plan_s &p, int64_t batch, int64_t seqlen, Layout &L)
     L.idx = take((size_t)n_tok * p.n_tables * 4);
     L.emb = take((size_t)n_tok * p.emb_dim * p.elem);
     L.partials = take((size_t)Br * n_parts_of(p) * 3 * n_tok * 4);
-    L.v = take((size_t)n_tok * d * p.elem);
+    L.v = take((size_t)n_tok * d * 4);
     L.kbuf = p.cfg.dtype == ENGRAM_F32 ? take((size_t)Br * n_tok * d * 4) : off;
     L.stage = take((size_t)Br * batch * (p.cfg.conv_kernel - 1) * d * 4);
     L.total = off;
@@ -170,7 +170,13 @@ engram_status check_fuse_args(const engram_plan_s *p, const void *emb, const voi
     if (!w->w_v || !w->conv_w || !aligned16(w->w_v)) return ENGRAM_E_INVALID_ARG;
     Layout L;
     if (!layout_of(*p, batch, seqlen, L) || ws_bytes < L.total) return ENGRAM_E_INVALID_ARG;
-    if (p->cfg.dtype == ENGRAM_BF16 && (p->cfg.d_model % kPartCols != 0 || p->emb_dim % 64 != 0))
+    // bf16 MFMA tiles: 256 weight rows never straddle two matrices, and the
+    // K loop runs an even number of 64-wide stages
+    if (p->cfg.dtype == ENGRAM_BF16 && (p->cfg.d_model % 256 != 0 || p->emb_dim % 128 != 0))
+        return ENGRAM_E_UNSUPPORTED;
+    // the projection kernel addresses E and each weight matrix with 32-bit offsets
+    if ((int64_t)batch * seqlen * p->emb_dim * p->elem >= ((int64_t)1 << 31) ||
+        (int64_t)p->cfg.d_model * p->emb_dim * p->elem >= ((int64_t)1 << 31))
         return ENGRAM_E_UNSUPPORTED;
     return ENGRAM_OK;
 }
@@ -199,7 +205,7 @@ engram_status do_fuse(engram_plan_s &p, const void *emb, const void *h, int32_t 
     for (int m = Br + 1; m <= kMaxBranches; ++m) pa.w[m] = w->w_v;
     pa.h = h;
     pa.partials = reinterpret_cast<float *>(base + L.partials);
-    pa.v = base + L.v;
+    pa.v = reinterpret_cast<float *>(base + L.v);
     pa.kbuf = p.cfg.dtype == ENGRAM_F32 ? reinterpret_cast<float *>(base + L.kbuf) : nullptr;
     pa.n_tok = n_tok;
     pa.K = p.emb_dim;

@@ -73,7 +73,7 @@ struct ProjArgs {
     const float *gamma_h[kMaxBranches];
     const float *gamma_k[kMaxBranches];
     float *partials;                       // [B_r][n_parts][3][n_tok]
-    void *v;                               // [n_tok][d]
+    float *v;                              // [n_tok][d] fp32
     float *kbuf;                           // f32 path only: [B_r][n_tok][d]
     int64_t n_tok;
     int32_t K;                             // D_e
@@ -89,7 +89,7 @@ void launch_proj_f32(const ProjArgs &a, hipStream_t s);  // k into kbuf, v, then
 
 // ---------------------------------------------------------------- fusion
 struct FuseArgs {
-    const void *v;             // [n_tok][d] (dtype)
+    const float *v;            // [n_tok][d] fp32
     const float *partials;     // [B_r][n_parts][3][n_tok]
     const void *h;             // [B_r][n_tok][d]
     void *out;                 // [B_r][n_tok][d]

@@ -4,8 +4,8 @@
 // sums the projection kernel left behind, the gated value u = alpha * v, the
 // short depthwise causal convolution and the residual into the hidden state.
 //
-// HBM-bound: it reads v once, h once per branch and writes out once per
-// branch.  A block owns kPos consecutive positions of one sequence and a
+// HBM-bound: it reads v (fp32) once, h once per branch and writes out once
+// per branch.  A block owns kPos consecutive positions of one sequence and a
 // stripe of channels; each thread owns 8 channels (one 16-byte bf16 vector)
 // and walks the positions in order, keeping the last three gated values of
 // every branch in registers, so no gated value is ever written to memory.
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(512) void fuse_kernel(FuseArgs a) {
             const int p = t0 - s;
             float vv[kVec];
             if (p >= 0) {
-                Vec8<BF16>::load(a.v, (row0 + p) * d + c0, vv);
+                Vec8<false>::load(a.v, (row0 + p) * d + c0, vv);
                 const float al = alpha_s[m][3 - s];
 #pragma unroll
                 for (int c = 0; c < kVec; ++c) win[m][s - 1][c] = al * vv[c];
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(512) void fuse_kernel(FuseArgs a) {
     for (int t = t0; t < t1; ++t) {
         const int64_t row = row0 + t;
         float vv[kVec];
-        Vec8<BF16>::load(a.v, row * d + c0, vv);
+        Vec8<false>::load(a.v, row * d + c0, vv);
 #pragma unroll
         for (int m = 0; m < kMaxBranches; ++m) {
             if (m >= a.n_branches) break;

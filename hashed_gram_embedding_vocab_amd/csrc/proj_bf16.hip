@@ -13,36 +13,47 @@
 //   W_k tiles never store k; they store per-token partial sums over their
 //     128 channels of  h*gamma_h*gamma_k*k,  k^2  and  h^2  (the RMSNorm dot
 //     product decomposes into these three sums).
-//   W_v tiles store v (bf16) for the fusion kernel.
+//   W_v tiles store v (fp32) for the fusion kernel.
 //
-// Tile: 256 weight rows x 128 tokens x 64 K per stage, 4 waves as 2 x 2, each
-// wave 128 x 64 (8 x 4 MFMA blocks, 128 fp32 accumulators per lane).  Both
-// operand tiles are staged through LDS (rows padded by 16 bytes so the
-// 16-byte fragment reads of 16 consecutive rows hit distinct banks), double
-// buffered with the next stage's global loads held in registers.
+// Tile: 256 weight rows x 256 tokens (d % 256 == 0, so a weight tile never
+// straddles two matrices), 64 K per stage (D_e % 128 == 0), 8 waves (two per SIMD) as 2 x 4,
+// each wave 128 x 64 (8 x 4 MFMA blocks, 128 fp32 accumulators per lane).
+// Operands go from global memory straight into LDS (buffer_load_dwordx4 ...
+// lds: no register staging, one 32-bit offset register per load, and reads
+// past a buffer's end return zeros instead of faulting), two stages deep: stage s+1 is in flight while stage s
+// is multiplied.  LDS holds each operand as 1 KB blocks of 16 rows x 32 K
+// (one MFMA fragment); inside a block the four 16-byte chunks of a row are
+// XOR-swizzled by ((r>>1) ^ (r>>2)) & 3 so the fragment reads of 8 or 16
+// consecutive rows fall in distinct banks.
 #include "engram_internal.h"
 
 namespace engram {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int BN = 256;           // weight rows per block
-constexpr int BT = 128;           // tokens per block
-constexpr int BK = 64;            // K per stage
-constexpr int LDK = BK + 8;       // padded LDS row (bf16 elements)
-constexpr int kThreads = 256;
-constexpr int WN = 128, WT = 64;  // wave tile
+constexpr int BN = 256;            // weight rows per block
+constexpr int BT = 256;            // tokens per block
+constexpr int BK = 64;             // K per stage (two 32-wide slabs)
+constexpr int kThreads = 512;      // 8 waves: two per SIMD
+constexpr int kWaves = kThreads / 64;
+constexpr int WN = 128, WT = 64;   // wave tile; waves form a 2 (n) x 4 (t) grid
 constexpr int FN = WN / 16, FT = WT / 16;
-constexpr int kLoadsW = BN * (BK / 8) / kThreads;  // 16-byte chunks per thread per stage
-constexpr int kLoadsE = BT * (BK / 8) / kThreads;
+constexpr int kBlockBytes = 1024;                           // 16 rows x 32 bf16
+constexpr int kOperandBytes = (BN / 16) * 2 * kBlockBytes;  // 32 KB per operand per stage
+constexpr int kBlocksPerWave = (BN / 16) / kWaves;          // row blocks each wave fills, per operand and stage
 constexpr int kXcds = 8;
-constexpr int kGroupT = 4;        // token tiles interleaved per weight tile in the launch order
+constexpr int kGroupT = 4;  // token tiles sharing each weight tile in the launch order
 
-struct __attribute__((aligned(16))) Smem {
-    uint16_t w[2][BN * LDK];
-    uint16_t e[2][BT * LDK];
+static_assert(BN == BT, "one block-load pattern serves both operands");
+
+struct __attribute__((aligned(1024))) Stage {
+    unsigned char w[kOperandBytes];
+    unsigned char e[kOperandBytes];
 };
+
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
 // Hardware hands consecutive block ids to the 8 XCDs round-robin.  Remap so
 // every XCD walks one contiguous range of the logical tile order (its own
@@ -73,12 +84,37 @@ __device__ __forceinline__ T pick(const T (&arr)[N], int i) {
     return p;
 }
 
+// Raw buffer resource over [base, base + bytes): dword 3 selects 32-bit data
+// format with no swizzling, as every gfx9 raw buffer access expects.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier without a memory fence.  __syncthreads() would also
+// wait for every outstanding load, including the next stage's LDS fills this
+// kernel deliberately leaves in flight; visibility of a stage is instead
+// established by each wave's own vmcnt wait before the barrier.  The empty
+// asm statements keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __global__ __launch_bounds__(kThreads, 1) void proj_bf16_kernel(ProjArgs a) {
-    __shared__ Smem sm;
+    __shared__ Stage st0, st1;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
     const int K = a.K;
     const int d = a.d;
     const int n_total = (a.n_branches + 1) * d;
@@ -89,40 +125,47 @@ __global__ __launch_bounds__(kThreads, 1) void proj_bf16_kernel(ProjArgs a) {
     const int n0 = tile_n * BN;
     const int64_t t0 = (int64_t)tile_t * BT;
 
-    // ---- per-thread global source rows (fixed over the K loop).  Rows past
-    //      the end are clamped to the last valid row: their products only
-    //      reach outputs that are never written (n_total and the token count
-    //      are checked in the epilogue), so no load ever leaves the buffers.
-    const uint16_t *wsrc[kLoadsW];
-    const uint16_t *esrc[kLoadsE];
-    const int kc = (tid & 7) * 8;  // K offset of this thread's chunk within a stage
+    // ---- this lane's share of the block loads.  Wave w fills row blocks
+    //      2w and 2w+1 of each operand, both 32-wide K slabs.
+    //      Lane l fills row l>>2 of the block, LDS chunk l&3, which holds
+    //      global K chunk (l&3) ^ swz(row).  Rows past the end are clamped to
+    //      the last valid row: their products only reach outputs that the
+    //      epilogue never writes, so no load leaves the buffers.
+    const int lr = lane >> 2;
+    const int lchunk = (lane & 3) ^ swz(lr);
+    // d % 256 == 0, so a 256-row weight tile lies inside one matrix
+    const int mat0 = min(n0, n_total - 1) / d;
+    const char *wmat = reinterpret_cast<const char *>(pick(a.w, mat0));
+    const __amdgpu_buffer_rsrc_t wres = make_rsrc(wmat, (uint32_t)d * K * 2u);
+    const __amdgpu_buffer_rsrc_t eres = make_rsrc(a.emb, (uint32_t)(a.n_tok * K * 2));
+    const int rows_left_t = (int)min<int64_t>(a.n_tok - t0, BT) - 1;  // last valid token row in the tile
+    uint32_t woff[kBlocksPerWave], eoff[kBlocksPerWave];
 #pragma unroll
-    for (int i = 0; i < kLoadsW; ++i) {
-        const int n = min(n0 + (tid >> 3) + 32 * i, n_total - 1);
-        const int mat = n / d;
-        wsrc[i] = reinterpret_cast<const uint16_t *>(pick(a.w, mat)) + (int64_t)(n - mat * d) * K + kc;
-    }
-#pragma unroll
-    for (int i = 0; i < kLoadsE; ++i) {
-        const int64_t t = min(t0 + (tid >> 3) + 32 * i, a.n_tok - 1);
-        esrc[i] = reinterpret_cast<const uint16_t *>(a.emb) + t * K + kc;
+    for (int i = 0; i < kBlocksPerWave; ++i) {
+        const int row = (wave * kBlocksPerWave + i) * 16 + lr;
+        woff[i] = (uint32_t)((n0 - mat0 * d + row) * K + lchunk * 8) * 2u;
+        eoff[i] = (uint32_t)((t0 + min(row, rows_left_t)) * K + lchunk * 8) * 2u;
     }
 
-    u32x4_t rw[kLoadsW], re[kLoadsE];
-#define ENGRAM_LOAD_STAGE(k0)                                                                  \
-    do {                                                                                       \
-        _Pragma("unroll") for (int i = 0; i < kLoadsW; ++i)                                    \
-            rw[i] = *reinterpret_cast<const u32x4_t *>(wsrc[i] + (k0));                          \
-        _Pragma("unroll") for (int i = 0; i < kLoadsE; ++i)                                    \
-            re[i] = *reinterpret_cast<const u32x4_t *>(esrc[i] + (k0));                          \
+// The immediate offset of a buffer load with an LDS destination moves the LDS
+// address as well, so the K position (including the second slab's 64 bytes)
+// travels in the scalar offset, which only moves the global address.
+#define ENGRAM_ISSUE(STG, k0)                                                                    \
+    do {                                                                                         \
+        const int kbytes = (k0) * 2;                                                             \
+        _Pragma("unroll") for (int i = 0; i < kBlocksPerWave; ++i) {                             \
+            const int blk = wave * kBlocksPerWave + i; /* slab 0; slab 1 is BN/16 later */       \
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void_t *)&STG.w[blk * kBlockBytes], \
+                                                     16, woff[i], kbytes, 0, 0);                 \
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(eres, (lds_void_t *)&STG.e[blk * kBlockBytes], \
+                                                     16, eoff[i], kbytes, 0, 0);                 \
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(                                            \
+                wres, (lds_void_t *)&STG.w[(blk + BN / 16) * kBlockBytes], 16, woff[i], kbytes + 64, 0, 0); \
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(                                            \
+                eres, (lds_void_t *)&STG.e[(blk + BN / 16) * kBlockBytes], 16, eoff[i], kbytes + 64, 0, 0); \
+        }                                                                                        \
     } while (0)
-#define ENGRAM_STORE_STAGE(buf)                                                                \
-    do {                                                                                       \
-        _Pragma("unroll") for (int i = 0; i < kLoadsW; ++i)                                    \
-            *reinterpret_cast<u32x4_t *>(&sm.w[buf][((tid >> 3) + 32 * i) * LDK + kc]) = rw[i];  \
-        _Pragma("unroll") for (int i = 0; i < kLoadsE; ++i)                                    \
-            *reinterpret_cast<u32x4_t *>(&sm.e[buf][((tid >> 3) + 32 * i) * LDK + kc]) = re[i];  \
-    } while (0)
+    constexpr int kLoadsInFlight = 4 * kBlocksPerWave;  // per wave per stage
 
     f32x4_t acc[FN][FT];
 #pragma unroll
@@ -130,79 +173,106 @@ __global__ __launch_bounds__(kThreads, 1) void proj_bf16_kernel(ProjArgs a) {
 #pragma unroll
         for (int j = 0; j < FT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const int wn = (wave & 1) * WN;   // wave's weight-row offset in the tile
-    const int wt = (wave >> 1) * WT;  // wave's token offset in the tile
-    const int frag_row = lane & 15;
-    const int frag_k = (lane >> 4) * 8;
+    const int wn_blk = (wave & 1) * (WN / 16);   // wave's first weight row block
+    const int wt_blk = (wave >> 1) * (WT / 16);  // wave's first token row block (4 t-groups)
+    const int fr = lane & 15;                    // fragment row
+    const int fpos = fr * 64 + ((lane >> 4) ^ swz(fr)) * 16;  // byte offset inside a 1 KB block
 
+#define ENGRAM_COMPUTE(STG)                                                                      \
+    do {                                                                                         \
+        _Pragma("unroll") for (int slab = 0; slab < 2; ++slab) {                                 \
+            bf16x8_t fa[FN], fb[FT];                                                             \
+            _Pragma("unroll") for (int i = 0; i < FN; ++i) fa[i] =                               \
+                *reinterpret_cast<const bf16x8_t *>(                                             \
+                    &STG.w[(slab * (BN / 16) + wn_blk + i) * kBlockBytes + fpos]);               \
+            _Pragma("unroll") for (int j = 0; j < FT; ++j) fb[j] =                               \
+                *reinterpret_cast<const bf16x8_t *>(                                             \
+                    &STG.e[(slab * (BT / 16) + wt_blk + j) * kBlockBytes + fpos]);               \
+            _Pragma("unroll") for (int i = 0; i < FN; ++i)                                       \
+                _Pragma("unroll") for (int j = 0; j < FT; ++j)                                   \
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], \
+                                                                        0, 0, 0);                \
+        }                                                                                        \
+    } while (0)
+
+    // Stage s lives in st0 when s is even, st1 when odd (K % 128 == 0, so the
+    // number of stages is even).  Each step: start filling the other buffer
+    // with stage s+1, wait for this wave's loads of stage s, barrier (every
+    // wave's stage s has landed), multiply, barrier (nobody reads stage s any
+    // more, so stage s+2 may overwrite it).  The loop body has no branches, so
+    // the compiler can tell which buffer the in-flight fills target and adds
+    // no waits of its own.
     const int k_steps = K / BK;
-    ENGRAM_LOAD_STAGE(0);
-    ENGRAM_STORE_STAGE(0);
-    __syncthreads();
-    for (int ks = 0; ks < k_steps; ++ks) {
-        const int buf = ks & 1;
-        if (ks + 1 < k_steps) ENGRAM_LOAD_STAGE((ks + 1) * BK);
-        const uint16_t *lw = sm.w[buf];
-        const uint16_t *le = sm.e[buf];
-#pragma unroll
-        for (int kk = 0; kk < BK; kk += 32) {
-            bf16x8_t fa[FN], fb[FT];
-#pragma unroll
-            for (int i = 0; i < FN; ++i)
-                fa[i] = *reinterpret_cast<const bf16x8_t *>(&lw[(wn + 16 * i + frag_row) * LDK + kk + frag_k]);
-#pragma unroll
-            for (int j = 0; j < FT; ++j)
-                fb[j] = *reinterpret_cast<const bf16x8_t *>(&le[(wt + 16 * j + frag_row) * LDK + kk + frag_k]);
-#pragma unroll
-            for (int i = 0; i < FN; ++i)
-#pragma unroll
-                for (int j = 0; j < FT; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-        }
-        if (ks + 1 < k_steps) ENGRAM_STORE_STAGE(buf ^ 1);
-        __syncthreads();
+    ENGRAM_ISSUE(st0, 0);
+    for (int ks = 0; ks + 2 < k_steps; ks += 2) {
+        ENGRAM_ISSUE(st1, (ks + 1) * BK);
+        wait_vmcnt<kLoadsInFlight>();
+        block_barrier();
+        ENGRAM_COMPUTE(st0);
+        block_barrier();
+        ENGRAM_ISSUE(st0, (ks + 2) * BK);
+        wait_vmcnt<kLoadsInFlight>();
+        block_barrier();
+        ENGRAM_COMPUTE(st1);
+        block_barrier();
     }
-
-#undef ENGRAM_LOAD_STAGE
-#undef ENGRAM_STORE_STAGE
+    ENGRAM_ISSUE(st1, (k_steps - 1) * BK);
+    wait_vmcnt<kLoadsInFlight>();
+    block_barrier();
+    ENGRAM_COMPUTE(st0);
+    wait_vmcnt<0>();
+    block_barrier();
+    ENGRAM_COMPUTE(st1);
+#undef ENGRAM_COMPUTE
+#undef ENGRAM_ISSUE
 
     // ---- epilogue.  acc[i][j][r] is output channel n = nw + 16i + 4*(lane/16) + r
-    //      of token t = t0 + wt + 16j + lane%16.
-    const int nw = n0 + wn;
+    //      of token t = tw + 16j + lane%16.
+    const int nw = n0 + wn_blk * 16;
     if (nw >= n_total) return;
-    const int mat = nw / d;              // the wave's 128 rows lie in one matrix (d % 128 == 0)
-    const int nl = nw - mat * d;         // first channel within that matrix
+    const int mat = nw / d;       // the wave's 128 rows lie in one matrix (d % 128 == 0)
+    const int nl = nw - mat * d;  // first channel within that matrix
     const int sub = 4 * (lane >> 4);
+    const int64_t tw = t0 + wt_blk * 16;
 
     if (mat < a.n_branches) {
-        // gate partials of branch `mat` over channels [nl, nl+128)
-        const float *gh = pick(a.gamma_h, mat);
-        const float *gk = pick(a.gamma_k, mat);
-        float g[FN][4];
-#pragma unroll
-        for (int i = 0; i < FN; ++i) {
-            const float4 x = *reinterpret_cast<const float4 *>(gh + nl + 16 * i + sub);
-            const float4 y = *reinterpret_cast<const float4 *>(gk + nl + 16 * i + sub);
-            g[i][0] = x.x * y.x; g[i][1] = x.y * y.y; g[i][2] = x.z * y.z; g[i][3] = x.w * y.w;
+        // gate partials of branch `mat` over channels [nl, nl+128).
+        // gamma_h * gamma_k for the wave's channels goes through the now idle
+        // st0 (its last reader finished before the final barrier), so it costs
+        // no registers; each wave writes and reads only its own 512 bytes.
+        float *gsm = reinterpret_cast<float *>(st0.w) + wave * WN;
+        {
+            const float *gh = pick(a.gamma_h, mat);
+            const float *gk = pick(a.gamma_k, mat);
+            for (int c = lane; c < WN; c += 64) gsm[c] = gh[nl + c] * gk[nl + c];
         }
         const uint16_t *hm = reinterpret_cast<const uint16_t *>(a.h) + (int64_t)mat * a.n_tok * d;
         const int part = nl / kPartCols;
         float *pbase = a.partials + ((int64_t)mat * a.n_parts + part) * 3 * a.n_tok;
+        // h for token block j+1 is in flight while block j is reduced
+        u32x2_t hv[2][FN];
+        auto load_h = [&](int j, u32x2_t(&dst)[FN]) {
+            const int64_t t = min(tw + 16 * j + (lane & 15), a.n_tok - 1);
+            const uint16_t *hrow = hm + t * d + nl + sub;
+#pragma unroll
+            for (int i = 0; i < FN; ++i) dst[i] = *reinterpret_cast<const u32x2_t *>(hrow + 16 * i);
+        };
+        load_h(0, hv[0]);
 #pragma unroll
         for (int j = 0; j < FT; ++j) {
-            const int64_t t = t0 + wt + 16 * j + (lane & 15);
-            const bool live = t < a.n_tok;
+            if (j + 1 < FT) load_h(j + 1, hv[(j + 1) & 1]);
+            const int64_t t = tw + 16 * j + (lane & 15);
             float s_hk = 0.f, s_kk = 0.f, s_hh = 0.f;
-            const uint16_t *hrow = hm + (live ? t : 0) * d + nl + sub;
 #pragma unroll
             for (int i = 0; i < FN; ++i) {
-                uint2 hv = live ? *reinterpret_cast<const uint2 *>(hrow + 16 * i) : make_uint2(0, 0);
-                const float h4[4] = {bf16_to_f32(hv.x & 0xFFFFu), bf16_to_f32(hv.x >> 16),
-                                     bf16_to_f32(hv.y & 0xFFFFu), bf16_to_f32(hv.y >> 16)};
+                const u32x2_t x = hv[j & 1][i];
+                const f32x4_t g = *reinterpret_cast<const f32x4_t *>(gsm + 16 * i + sub);
+                const float h4[4] = {bf16_to_f32(x[0] & 0xFFFFu), bf16_to_f32(x[0] >> 16),
+                                     bf16_to_f32(x[1] & 0xFFFFu), bf16_to_f32(x[1] >> 16)};
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float kv = acc[i][j][r];
-                    s_hk += h4[r] * g[i][r] * kv;
+                    s_hk += h4[r] * g[r] * kv;
                     s_kk += kv * kv;
                     s_hh += h4[r] * h4[r];
                 }
@@ -211,26 +281,22 @@ __global__ __launch_bounds__(kThreads, 1) void proj_bf16_kernel(ProjArgs a) {
             s_hk += __shfl_xor(s_hk, 16); s_hk += __shfl_xor(s_hk, 32);
             s_kk += __shfl_xor(s_kk, 16); s_kk += __shfl_xor(s_kk, 32);
             s_hh += __shfl_xor(s_hh, 16); s_hh += __shfl_xor(s_hh, 32);
-            if (lane < 16 && live) {
+            if (lane < 16 && t < a.n_tok) {
                 pbase[t] = s_hk;
                 pbase[a.n_tok + t] = s_kk;
                 pbase[2 * a.n_tok + t] = s_hh;
             }
         }
     } else {
-        // v = W_v e, stored bf16 [n_tok][d]
-        uint16_t *vout = reinterpret_cast<uint16_t *>(a.v);
+        // v = W_v e, kept fp32 [n_tok][d]: rounding it to bf16 here would add
+        // up to half a bf16 ulp of |v| to every gated value the conv sums.
 #pragma unroll
         for (int j = 0; j < FT; ++j) {
-            const int64_t t = t0 + wt + 16 * j + (lane & 15);
+            const int64_t t = tw + 16 * j + (lane & 15);
             if (t >= a.n_tok) continue;
 #pragma unroll
-            for (int i = 0; i < FN; ++i) {
-                uint2 pk;
-                pk.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
-                pk.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
-                *reinterpret_cast<uint2 *>(vout + t * d + nl + 16 * i + sub) = pk;
-            }
+            for (int i = 0; i < FN; ++i)
+                *reinterpret_cast<f32x4_t *>(a.v + t * d + nl + 16 * i + sub) = acc[i][j];
         }
     }
 }

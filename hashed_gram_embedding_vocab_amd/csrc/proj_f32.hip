@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) void proj_f32_kernel(ProjArgs a) {
             if (mat < a.n_branches)
                 a.kbuf[((int64_t)mat * a.n_tok + t) * d + nl] = acc[i][j];
             else
-                reinterpret_cast<float *>(a.v)[t * d + nl] = acc[i][j];
+                a.v[t * d + nl] = acc[i][j];
         }
     }
 }
