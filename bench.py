@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--rotate", type=int, default=8, help="distinct token/h buffers cycled per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB 5 times (counter calibration)")
     return ap.parse_args()
 
 
@@ -108,6 +110,19 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_probe_mib:
+        # A plain copy of known size: FETCH_SIZE / WRITE_SIZE of these
+        # dispatches calibrate the counters against bytes actually moved.
+        n = args.copy_probe_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 5}))
+        return
 
     from hashed_gram_embedding_vocab_amd import binding as B
     from synthetic import workloads as W
@@ -185,13 +200,18 @@ def main():
                 "flops_per_launch": flops}
 
     eb = 2 if wl.dtype == "bf16" else 4
-    g_bytes = n_tok * (wl.n_tables * 4 + 2 * De * eb)
     g_ms, g_n = kern("gather")
-    gather = {"achieved_GBs": round(g_bytes / (g_ms * 1e-3) / 1e9, 1), "peak_GBs": HBM_PEAK_GBS,
+    # engram_forward retrieves in one kernel (hash + gather): it reads each raw
+    # token id, every slot row, and writes E; no index buffer round trip
+    fused_retrieval = kern("hash")[1] == 0
+    g_bytes = n_tok * ((4 if fused_retrieval else wl.n_tables * 4) + 2 * De * eb)
+    gather = {"kernel": "hash_gather_kernel" if fused_retrieval else "gather_kernel",
+              "achieved_GBs": round(g_bytes / (g_ms * 1e-3) / 1e9, 1), "peak_GBs": HBM_PEAK_GBS,
               "frac": round(g_bytes / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
               "bytes_per_launch": g_bytes, "avg_launch_us": round(g_ms * 1e3, 2)}
     f_ms, _ = kern("fuse")
-    f_bytes = n_tok * (d * eb + Br * 2 * d * eb) + Br * (d // 128 if wl.dtype == "bf16" else 1) * 3 * 4 * n_tok
+    # fusion kernel: reads v (fp32) once, h once per branch, the gate partials; writes out per branch
+    f_bytes = n_tok * (4 * d + Br * 2 * d * eb) + Br * (d // 128 if wl.dtype == "bf16" else 1) * 3 * 4 * n_tok
     fuse = {"achieved_GBs": round(f_bytes / (f_ms * 1e-3) / 1e9, 1), "frac": round(
         f_bytes / (f_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "avg_launch_us": round(f_ms * 1e3, 2)}
     kernels_us = {k: round(kern(k)[0] * 1e3, 2) for k in ("hash", "gather", "gemm", "fuse", "aux")}

@@ -128,8 +128,7 @@ engram_status check_gather_args(const engram_plan_s *p, const uint32_t *idx, int
     return ENGRAM_OK;
 }
 
-engram_status do_gather(engram_plan_s &p, const uint32_t *idx, int64_t n_tok,
-                        const void *const *tables, void *emb, hipStream_t s) {
+GatherConsts gather_consts(const engram_plan_s &p, const void *const *tables) {
     GatherConsts gc{};
     gc.n_tables = p.n_tables;
     gc.row_chunks = p.cfg.head_dim * p.elem / 16;
@@ -143,9 +142,26 @@ engram_status do_gather(engram_plan_s &p, const uint32_t *idx, int64_t n_tok,
     };
     gc.magic_tok = magic(gc.tok_chunks);
     gc.magic_row = magic(gc.row_chunks);
+    return gc;
+}
+
+engram_status do_gather(engram_plan_s &p, const uint32_t *idx, int64_t n_tok,
+                        const void *const *tables, void *emb, hipStream_t s) {
+    const GatherConsts gc = gather_consts(p, tables);
     {
         Launch l(p, ENGRAM_K_GATHER, s);
         launch_gather(gc, idx, n_tok, emb, s);
+    }
+    return last_launch_status();
+}
+
+engram_status do_hash_gather(engram_plan_s &p, const int32_t *tokens, int32_t batch, int32_t seqlen,
+                             const int32_t *comp_map, const int32_t *prev_ctx, uint32_t *bad,
+                             const void *const *tables, void *emb, hipStream_t s) {
+    const GatherConsts gc = gather_consts(p, tables);
+    {
+        Launch l(p, ENGRAM_K_GATHER, s);
+        launch_hash_gather(p.hc, gc, tokens, batch, seqlen, comp_map, prev_ctx, bad, emb, s);
     }
     return last_launch_status();
 }
@@ -366,9 +382,11 @@ engram_status engram_forward(engram_plan p, const int32_t *d_tokens, int32_t bat
         st = check_fuse_args(p, emb, d_h, batch, seqlen, w, d_out, d_alpha, d_conv_state, flags,
                              d_workspace, workspace_bytes);
     if (st != ENGRAM_OK) return st;
-    st = do_hash(*p, d_tokens, batch, seqlen, d_comp_map, d_prev_ctx, idx, d_bad_tokens, stream);
+    // retrieval in one kernel: hash every (token, table) pair and copy its row
+    st = do_hash_gather(*p, d_tokens, batch, seqlen, d_comp_map, d_prev_ctx, d_bad_tokens, table_ptrs,
+                        emb, stream);
     if (st != ENGRAM_OK) return st;
-    if (d_prev_ctx) {
+    if (d_prev_ctx) {  // after the retrieval kernel has read the old context
         {
             Launch l(*p, ENGRAM_K_AUX, stream);
             launch_ctx_update(d_tokens, batch, seqlen, d_comp_map, p->cfg.vocab, p->cfg.vocab_comp,
@@ -376,8 +394,6 @@ engram_status engram_forward(engram_plan p, const int32_t *d_tokens, int32_t bat
         }
         if (last_launch_status() != ENGRAM_OK) return ENGRAM_E_DEVICE;
     }
-    st = do_gather(*p, idx, (int64_t)batch * seqlen, table_ptrs, emb, stream);
-    if (st != ENGRAM_OK) return st;
     return do_fuse(*p, emb, d_h, batch, seqlen, w, d_conv_state, d_out, d_alpha, flags, d_workspace,
                    stream);
 }

@@ -34,6 +34,34 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // ---------------------------------------------------------------- hashing
+// SplitMix64 output function (Steele, Lea & Flood 2014; Mix13 constants):
+// the deterministic mixer of the multi-head n-gram hash.
+__device__ __forceinline__ uint64_t mix64(uint64_t z) {
+    z ^= z >> 30;
+    z *= 0xBF58476D1CE4E5B9ull;
+    z ^= z >> 27;
+    z *= 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return z;
+}
+
+// z mod p for a 64-bit z and 32-bit p without a hardware divide.  With
+// m = floor((2^64-1)/p) the estimate q = floor(z*m / 2^64) satisfies
+// floor(z/p) - 2 <= q <= floor(z/p), so two conditional subtractions finish it.
+__device__ __forceinline__ uint32_t mod_prime(uint64_t z, uint32_t p, uint64_t m) {
+    const uint64_t q = __umul64hi(z, m);
+    uint64_t r = z - q * (uint64_t)p;
+    if (r >= p) r -= p;
+    if (r >= p) r -= p;
+    return (uint32_t)r;
+}
+
+// Vocabulary projection of one raw id; ids outside [0, vocab) become PAD.
+__device__ __forceinline__ int32_t compress_id(int32_t x, const int32_t *__restrict__ comp_map,
+                                               int32_t vocab, int32_t pad) {
+    return (x >= 0 && x < vocab) ? __ldg(comp_map + x) : pad;
+}
+
 struct HashConsts {
     uint64_t seed[kMaxTables];   // per-table 64-bit seed s_tau
     uint64_t magic[kMaxTables];  // floor((2^64-1) / rows_tau), for the Barrett reduction
@@ -64,6 +92,11 @@ struct GatherConsts {
 
 void launch_gather(const GatherConsts &gc, const uint32_t *idx, int64_t n_tok, void *emb,
                    hipStream_t s);
+// Retrieval in one pass (engram_forward): every lane hashes the n-gram of its
+// own (token, table) pair and copies its 16-byte chunk of that row.
+void launch_hash_gather(const HashConsts &hc, const GatherConsts &gc, const int32_t *tokens,
+                        int32_t batch, int32_t seqlen, const int32_t *comp_map,
+                        const int32_t *prev_ctx, uint32_t *bad, void *emb, hipStream_t s);
 
 // ---------------------------------------------------------------- projections
 struct ProjArgs {

@@ -6,9 +6,10 @@
 //
 // HBM-bound: it reads v (fp32) once, h once per branch and writes out once
 // per branch.  A block owns kPos consecutive positions of one sequence and a
-// stripe of channels; each thread owns 8 channels (one 16-byte bf16 vector)
-// and walks the positions in order, keeping the last three gated values of
+// stripe of channels; each thread owns 4 channels (one 16-byte fp32 vector of
+// v) and walks the positions in order, keeping the last three gated values of
 // every branch in registers, so no gated value is ever written to memory.
+// Loads for a group of positions are issued before any of their arithmetic.
 // The three values before the block's first position are recomputed from v
 // (or taken from the carried conv state at the sequence start).
 #include "engram_internal.h"
@@ -17,47 +18,44 @@ namespace engram {
 namespace {
 
 constexpr int kPos = 32;
-constexpr int kVec = 8;
+constexpr int kVec = 4;
 
+// Four values in their stored form: 8 bytes for bf16, 16 for fp32.
 template <bool BF16>
-struct Vec8 {
-    static __device__ __forceinline__ void load(const void *base, int64_t off, float (&x)[kVec]) {
+struct Raw4 {
+    u32x4_t w;
+    __device__ __forceinline__ void load(const void *base, int64_t off) {
         if constexpr (BF16) {
-            const u32x4_t p = *reinterpret_cast<const u32x4_t *>(reinterpret_cast<const uint16_t *>(base) + off);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x[2 * i] = bf16_to_f32(p[i] & 0xFFFFu);
-                x[2 * i + 1] = bf16_to_f32(p[i] >> 16);
-            }
+            const u32x2_t x = *reinterpret_cast<const u32x2_t *>(reinterpret_cast<const uint16_t *>(base) + off);
+            w[0] = x[0];
+            w[1] = x[1];
         } else {
-            const f32x4_t *p = reinterpret_cast<const f32x4_t *>(reinterpret_cast<const float *>(base) + off);
-            const f32x4_t lo = p[0], hi = p[1];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x[i] = lo[i];
-                x[4 + i] = hi[i];
-            }
+            w = *reinterpret_cast<const u32x4_t *>(reinterpret_cast<const float *>(base) + off);
+        }
+    }
+    __device__ __forceinline__ float get(int c) const {
+        if constexpr (BF16) {
+            const uint32_t x = w[c >> 1];
+            return bf16_to_f32((c & 1) ? (x >> 16) : (x & 0xFFFFu));
+        } else {
+            return __uint_as_float(w[c]);
         }
     }
     static __device__ __forceinline__ void store(void *base, int64_t off, const float (&x)[kVec]) {
         if constexpr (BF16) {
-            u32x4_t p;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) p[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
-            *reinterpret_cast<u32x4_t *>(reinterpret_cast<uint16_t *>(base) + off) = p;
+            *reinterpret_cast<u32x2_t *>(reinterpret_cast<uint16_t *>(base) + off) =
+                u32x2_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
         } else {
-            f32x4_t *p = reinterpret_cast<f32x4_t *>(reinterpret_cast<float *>(base) + off);
-            p[0] = f32x4_t{x[0], x[1], x[2], x[3]};
-            p[1] = f32x4_t{x[4], x[5], x[6], x[7]};
+            *reinterpret_cast<f32x4_t *>(reinterpret_cast<float *>(base) + off) = f32x4_t{x[0], x[1], x[2], x[3]};
         }
     }
 };
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + expf(-x)); }
 
-template <bool BF16>
-__global__ __launch_bounds__(512) void fuse_kernel(FuseArgs a) {
-    __shared__ float alpha_s[kMaxBranches][kPos + 3];
+template <bool BF16, int BR>
+__global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
+    __shared__ float alpha_s[BR][kPos + 3];
     const int b = blockIdx.y;
     const int t0 = blockIdx.x * kPos;
     const int t1 = min(t0 + kPos, a.seqlen);
@@ -68,7 +66,7 @@ __global__ __launch_bounds__(512) void fuse_kernel(FuseArgs a) {
     const float inv_sqrt_d = rsqrtf((float)d);
 
     // gate values for positions t0-3 .. t1-1 (zero where unused)
-    for (int x = threadIdx.x; x < a.n_branches * (kPos + 3); x += blockDim.x) {
+    for (int x = threadIdx.x; x < BR * (kPos + 3); x += blockDim.x) {
         const int m = x / (kPos + 3), j = x - m * (kPos + 3);
         const int p = t0 - 3 + j;
         float al = 0.f;
@@ -92,6 +90,8 @@ __global__ __launch_bounds__(512) void fuse_kernel(FuseArgs a) {
     const int c0 = (blockIdx.z * blockDim.x + threadIdx.x) * kVec;
     if (c0 >= d) return;
     const int kc = a.conv_k;
+    const bool silu = a.conv_mode == ENGRAM_CONV_SILU_SKIP;
+    const bool delta = (a.flags & ENGRAM_OUT_DELTA) != 0;
 
     float wt[4][kVec];  // wt[j][c] multiplies u_{t-j}
 #pragma unroll
@@ -101,16 +101,14 @@ __global__ __launch_bounds__(512) void fuse_kernel(FuseArgs a) {
             wt[j][c] = j < kc ? a.conv_w[(int64_t)(c0 + c) * kc + (kc - 1 - j)] : 0.f;
 
     // win[m][s-1][c] = u_{t-s}
-    float win[kMaxBranches][3][kVec];
+    float win[BR][3][kVec];
 #pragma unroll
-    for (int m = 0; m < kMaxBranches; ++m) {
-        if (m >= a.n_branches) break;
+    for (int m = 0; m < BR; ++m) {
 #pragma unroll
         for (int s = 1; s <= 3; ++s) {
             const int p = t0 - s;
-            float vv[kVec];
             if (p >= 0) {
-                Vec8<false>::load(a.v, (row0 + p) * d + c0, vv);
+                const f32x4_t vv = *reinterpret_cast<const f32x4_t *>(a.v + (row0 + p) * d + c0);
                 const float al = alpha_s[m][3 - s];
 #pragma unroll
                 for (int c = 0; c < kVec; ++c) win[m][s - 1][c] = al * vv[c];
@@ -125,37 +123,46 @@ __global__ __launch_bounds__(512) void fuse_kernel(FuseArgs a) {
         }
     }
 
-    for (int t = t0; t < t1; ++t) {
-        const int64_t row = row0 + t;
-        float vv[kVec];
-        Vec8<false>::load(a.v, row * d + c0, vv);
+    constexpr int kGroup = BR == 1 ? 8 : (BR == 2 ? 4 : 2);
+    for (int tg = t0; tg < t1; tg += kGroup) {
+        const int n = min(kGroup, t1 - tg);
+        f32x4_t vv[kGroup];
+        Raw4<BF16> hv[kGroup][BR];
 #pragma unroll
-        for (int m = 0; m < kMaxBranches; ++m) {
-            if (m >= a.n_branches) break;
-            const float al = alpha_s[m][t - t0 + 3];
-            const int64_t off = ((int64_t)m * n_tok + row) * d + c0;
-            float hv[kVec], o[kVec];
-            Vec8<BF16>::load(a.h, off, hv);
+        for (int q = 0; q < kGroup; ++q) {
+            const int64_t row = row0 + tg + min(q, n - 1);
+            vv[q] = *reinterpret_cast<const f32x4_t *>(a.v + row * d + c0);
 #pragma unroll
-            for (int c = 0; c < kVec; ++c) {
-                const float u = al * vv[c];
-                const float conv = wt[0][c] * u + wt[1][c] * win[m][0][c] + wt[2][c] * win[m][1][c] +
-                                   wt[3][c] * win[m][2][c];
-                const float y = a.conv_mode == ENGRAM_CONV_SILU_SKIP ? u + conv * sigmoidf_(conv) : conv;
-                o[c] = (a.flags & ENGRAM_OUT_DELTA) ? y : hv[c] + y;
-                win[m][2][c] = win[m][1][c];
-                win[m][1][c] = win[m][0][c];
-                win[m][0][c] = u;
+            for (int m = 0; m < BR; ++m) hv[q][m].load(a.h, ((int64_t)m * n_tok + row) * d + c0);
+        }
+#pragma unroll
+        for (int q = 0; q < kGroup; ++q) {
+            if (q >= n) break;
+            const int64_t row = row0 + tg + q;
+#pragma unroll
+            for (int m = 0; m < BR; ++m) {
+                const float al = alpha_s[m][tg + q - t0 + 3];
+                float o[kVec];
+#pragma unroll
+                for (int c = 0; c < kVec; ++c) {
+                    const float u = al * vv[q][c];
+                    const float conv = wt[0][c] * u + wt[1][c] * win[m][0][c] + wt[2][c] * win[m][1][c] +
+                                       wt[3][c] * win[m][2][c];
+                    const float y = silu ? u + conv * sigmoidf_(conv) : conv;
+                    o[c] = delta ? y : hv[q][m].get(c) + y;
+                    win[m][2][c] = win[m][1][c];
+                    win[m][1][c] = win[m][0][c];
+                    win[m][0][c] = u;
+                }
+                Raw4<BF16>::store(a.out, ((int64_t)m * n_tok + row) * d + c0, o);
             }
-            Vec8<BF16>::store(a.out, off, o);
         }
     }
 
     // new conv state: the last K_c-1 gated values of the extended sequence
     if (a.state_stage && t1 == a.seqlen) {
 #pragma unroll
-        for (int m = 0; m < kMaxBranches; ++m) {
-            if (m >= a.n_branches) break;
+        for (int m = 0; m < BR; ++m) {
             for (int j = 0; j < kc - 1; ++j) {
                 float *st = a.state_stage + (((int64_t)m * a.batch + b) * (kc - 1) + j) * d + c0;
                 const int s = kc - 1 - j;  // u_{T-s}
@@ -171,13 +178,23 @@ __global__ __launch_bounds__(512) void fuse_kernel(FuseArgs a) {
 void launch_fuse(const FuseArgs &a, engram_dtype dt, hipStream_t s) {
     const int need = (a.d + kVec - 1) / kVec;
     int threads = ((need + 63) / 64) * 64;
-    if (threads > 512) threads = 512;
+    if (threads > 256) threads = 256;
     const int gz = (need + threads - 1) / threads;
     dim3 grid((a.seqlen + kPos - 1) / kPos, a.batch, gz);
-    if (dt == ENGRAM_BF16)
-        hipLaunchKernelGGL(fuse_kernel<true>, grid, dim3(threads), 0, s, a);
-    else
-        hipLaunchKernelGGL(fuse_kernel<false>, grid, dim3(threads), 0, s, a);
+#define ENGRAM_FUSE_LAUNCH(BR)                                                                   \
+    do {                                                                                         \
+        if (dt == ENGRAM_BF16)                                                                   \
+            hipLaunchKernelGGL((fuse_kernel<true, BR>), grid, dim3(threads), 0, s, a);            \
+        else                                                                                     \
+            hipLaunchKernelGGL((fuse_kernel<false, BR>), grid, dim3(threads), 0, s, a);           \
+    } while (0)
+    switch (a.n_branches) {
+        case 1: ENGRAM_FUSE_LAUNCH(1); break;
+        case 2: ENGRAM_FUSE_LAUNCH(2); break;
+        case 3: ENGRAM_FUSE_LAUNCH(3); break;
+        default: ENGRAM_FUSE_LAUNCH(4); break;
+    }
+#undef ENGRAM_FUSE_LAUNCH
 }
 
 }  // namespace engram

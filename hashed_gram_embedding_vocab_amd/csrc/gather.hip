@@ -15,7 +15,8 @@ namespace engram {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 8;
+constexpr int kUnroll = 8;    // chunks in flight per thread (index-driven gather)
+constexpr int kHGUnroll = 10; // row chunks in flight per thread in the fused kernel
 
 __device__ __forceinline__ uint64_t div_magic(uint64_t n, uint64_t magic, int32_t d) {
     // floor(n / d) for n < 2^40 with magic = floor(2^64 / d) + 1; d == 1 -> n
@@ -54,7 +55,81 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherConsts gc,
     }
 }
 
+// Fused retrieval (engram_forward): a block owns tpb = 256 / n_tables
+// consecutive tokens.  Phase 1: one thread per
+// (token, table) pair forms the token's suffix n-gram from the raw ids (ids
+// before a sequence's first token come from prev_ctx, else PAD), hashes it
+// with the table's seed and leaves the slot in LDS.  Phase 2: the block
+// copies the pairs' rows in 16-byte chunks, up to kHGUnroll loads in flight
+// per thread.  The slots never travel through HBM.
+__global__ __launch_bounds__(kThreads) void hash_gather_kernel(
+    HashConsts hc, GatherConsts gc, const int32_t *__restrict__ tokens, int64_t n_tok, int32_t seqlen,
+    uint64_t magic_seq, int32_t tpb, const int32_t *__restrict__ comp_map,
+    const int32_t *__restrict__ prev_ctx, uint32_t *__restrict__ bad, u32x4_t *__restrict__ emb) {
+    __shared__ uint32_t slot_s[kThreads];
+    const int64_t tok0 = (int64_t)blockIdx.x * tpb;
+    const int n_tables = gc.n_tables;
+    const int pairs = tpb * n_tables;
+    {
+        const int pr = threadIdx.x;
+        const int tl = pr / n_tables;
+        const int tau = pr - tl * n_tables;
+        const int64_t tok = tok0 + tl;
+        if (pr < pairs && tok < n_tok) {
+            const int32_t pad = hc.vocab_comp;
+            const uint64_t B = (uint64_t)hc.vocab_comp + 1u;
+            const int64_t b = (int64_t)div_magic((uint64_t)tok, magic_seq, seqlen);
+            const int32_t t = (int32_t)(tok - b * seqlen);
+            const int32_t x0 = tokens[tok];
+            const int32_t c0 = compress_id(x0, comp_map, hc.vocab, pad);
+            int32_t c1, c2;
+            if (t >= 1) c1 = compress_id(tokens[tok - 1], comp_map, hc.vocab, pad);
+            else c1 = prev_ctx ? prev_ctx[b * 2 + 1] : pad;
+            if (t >= 2) c2 = compress_id(tokens[tok - 2], comp_map, hc.vocab, pad);
+            else if (t == 1) c2 = prev_ctx ? prev_ctx[b * 2 + 1] : pad;
+            else c2 = prev_ctx ? prev_ctx[b * 2 + 0] : pad;
+            const uint64_t key = hc.order_of[tau] == 2 ? (uint64_t)c1 * B + (uint64_t)c0
+                                                       : ((uint64_t)c2 * B + (uint64_t)c1) * B + (uint64_t)c0;
+            slot_s[pr] = mod_prime(mix64(key ^ hc.seed[tau]), hc.rows[tau], hc.magic[tau]);
+            if (bad && tau == 0 && (x0 < 0 || x0 >= hc.vocab)) atomicAdd(bad, 1u);
+        }
+    }
+    __syncthreads();
+    const int64_t ntok_here = min<int64_t>(tpb, n_tok - tok0);
+    const int chunks = (int)ntok_here * gc.tok_chunks;
+    u32x4_t *dst = emb + tok0 * gc.tok_chunks;
+    for (int c0 = threadIdx.x; c0 < chunks; c0 += kThreads * kHGUnroll) {
+        u32x4_t val[kHGUnroll];
+#pragma unroll
+        for (int u = 0; u < kHGUnroll; ++u) {
+            const int c = min(c0 + u * kThreads, chunks - 1);
+            const int tl = (int)div_magic((uint64_t)c, gc.magic_tok, gc.tok_chunks);
+            const int rem = c - tl * gc.tok_chunks;
+            const int tau = (int)div_magic((uint64_t)rem, gc.magic_row, gc.row_chunks);
+            const int ch = rem - tau * gc.row_chunks;
+            const uint32_t r = slot_s[tl * n_tables + tau];
+            val[u] = reinterpret_cast<const u32x4_t *>(gc.table[tau])[(int64_t)r * gc.row_chunks + ch];
+        }
+#pragma unroll
+        for (int u = 0; u < kHGUnroll; ++u) {
+            const int c = c0 + u * kThreads;
+            if (c < chunks) dst[c] = val[u];
+        }
+    }
+}
+
 }  // namespace
+
+void launch_hash_gather(const HashConsts &hc, const GatherConsts &gc, const int32_t *tokens,
+                        int32_t batch, int32_t seqlen, const int32_t *comp_map,
+                        const int32_t *prev_ctx, uint32_t *bad, void *emb, hipStream_t s) {
+    const int64_t n_tok = (int64_t)batch * seqlen;
+    const int tpb = kThreads / gc.n_tables;
+    const int64_t blocks = (n_tok + tpb - 1) / tpb;
+    const uint64_t magic_seq = seqlen <= 1 ? 0 : (uint64_t)(((unsigned __int128)1 << 64) / (unsigned)seqlen) + 1;
+    hipLaunchKernelGGL(hash_gather_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, hc, gc, tokens, n_tok,
+                       seqlen, magic_seq, tpb, comp_map, prev_ctx, bad, reinterpret_cast<u32x4_t *>(emb));
+}
 
 void launch_gather(const GatherConsts &gc, const uint32_t *idx, int64_t n_tok, void *emb,
                    hipStream_t s) {

@@ -16,12 +16,14 @@
 //   W_v tiles store v (fp32) for the fusion kernel.
 //
 // Tile: 256 weight rows x 256 tokens (d % 256 == 0, so a weight tile never
-// straddles two matrices), 64 K per stage (D_e % 128 == 0), 8 waves (two per SIMD) as 2 x 4,
-// each wave 128 x 64 (8 x 4 MFMA blocks, 128 fp32 accumulators per lane).
-// Operands go from global memory straight into LDS (buffer_load_dwordx4 ...
-// lds: no register staging, one 32-bit offset register per load, and reads
-// past a buffer's end return zeros instead of faulting), two stages deep: stage s+1 is in flight while stage s
-// is multiplied.  LDS holds each operand as 1 KB blocks of 16 rows x 32 K
+// straddles two matrices), 32 K per stage (D_e % 128 == 0), 8 waves (two per
+// SIMD) as 2 x 4, each wave 128 x 64 (8 x 4 MFMA blocks, 128 fp32
+// accumulators per lane).  Operands go from global memory straight into LDS
+// (buffer_load_dwordx4 ... lds: no register staging, one 32-bit offset
+// register per load, and reads past a buffer's end return zeros instead of
+// faulting) through a ring of four 32 KB stages: while one stage is
+// multiplied the next three are in flight, which covers the latency of
+// operands that miss L2.  LDS holds each operand as 1 KB blocks of 16 rows x 32 K
 // (one MFMA fragment); inside a block the four 16-byte chunks of a row are
 // XOR-swizzled by ((r>>1) ^ (r>>2)) & 3 so the fragment reads of 8 or 16
 // consecutive rows fall in distinct banks.
@@ -35,16 +37,20 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int BN = 256;            // weight rows per block
 constexpr int BT = 256;            // tokens per block
-constexpr int BK = 64;             // K per stage (two 32-wide slabs)
+constexpr int BK = 32;             // K per stage (one MFMA K slab)
+constexpr int kStages = 4;         // LDS ring: one stage multiplied, three in flight
 constexpr int kThreads = 512;      // 8 waves: two per SIMD
 constexpr int kWaves = kThreads / 64;
 constexpr int WN = 128, WT = 64;   // wave tile; waves form a 2 (n) x 4 (t) grid
 constexpr int FN = WN / 16, FT = WT / 16;
-constexpr int kBlockBytes = 1024;                           // 16 rows x 32 bf16
-constexpr int kOperandBytes = (BN / 16) * 2 * kBlockBytes;  // 32 KB per operand per stage
+constexpr int kBlockBytes = 1024;                       // 16 rows x 32 bf16
+constexpr int kOperandBytes = (BN / 16) * kBlockBytes;  // 16 KB per operand per stage
 constexpr int kBlocksPerWave = (BN / 16) / kWaves;          // row blocks each wave fills, per operand and stage
 constexpr int kXcds = 8;
-constexpr int kGroupT = 4;  // token tiles sharing each weight tile in the launch order
+#ifndef ENGRAM_PROJ_GROUP_T
+#define ENGRAM_PROJ_GROUP_T 4
+#endif
+constexpr int kGroupT = ENGRAM_PROJ_GROUP_T;  // token tiles sharing each weight tile in the launch order
 
 static_assert(BN == BT, "one block-load pattern serves both operands");
 
@@ -110,7 +116,7 @@ __device__ __forceinline__ void block_barrier() {
 }
 
 __global__ __launch_bounds__(kThreads, 1) void proj_bf16_kernel(ProjArgs a) {
-    __shared__ Stage st0, st1;
+    __shared__ Stage st0, st1, st2, st3;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -126,7 +132,7 @@ __global__ __launch_bounds__(kThreads, 1) void proj_bf16_kernel(ProjArgs a) {
     const int64_t t0 = (int64_t)tile_t * BT;
 
     // ---- this lane's share of the block loads.  Wave w fills row blocks
-    //      2w and 2w+1 of each operand, both 32-wide K slabs.
+    //      2w and 2w+1 of each operand.
     //      Lane l fills row l>>2 of the block, LDS chunk l&3, which holds
     //      global K chunk (l&3) ^ swz(row).  Rows past the end are clamped to
     //      the last valid row: their products only reach outputs that the
@@ -148,24 +154,20 @@ __global__ __launch_bounds__(kThreads, 1) void proj_bf16_kernel(ProjArgs a) {
     }
 
 // The immediate offset of a buffer load with an LDS destination moves the LDS
-// address as well, so the K position (including the second slab's 64 bytes)
-// travels in the scalar offset, which only moves the global address.
+// address as well, so the K position travels in the scalar offset, which only
+// moves the global address.
 #define ENGRAM_ISSUE(STG, k0)                                                                    \
     do {                                                                                         \
         const int kbytes = (k0) * 2;                                                             \
         _Pragma("unroll") for (int i = 0; i < kBlocksPerWave; ++i) {                             \
-            const int blk = wave * kBlocksPerWave + i; /* slab 0; slab 1 is BN/16 later */       \
+            const int blk = wave * kBlocksPerWave + i;                                           \
             __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void_t *)&STG.w[blk * kBlockBytes], \
                                                      16, woff[i], kbytes, 0, 0);                 \
             __builtin_amdgcn_raw_ptr_buffer_load_lds(eres, (lds_void_t *)&STG.e[blk * kBlockBytes], \
                                                      16, eoff[i], kbytes, 0, 0);                 \
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(                                            \
-                wres, (lds_void_t *)&STG.w[(blk + BN / 16) * kBlockBytes], 16, woff[i], kbytes + 64, 0, 0); \
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(                                            \
-                eres, (lds_void_t *)&STG.e[(blk + BN / 16) * kBlockBytes], 16, eoff[i], kbytes + 64, 0, 0); \
         }                                                                                        \
     } while (0)
-    constexpr int kLoadsInFlight = 4 * kBlocksPerWave;  // per wave per stage
+    constexpr int kLoadsPerStage = 2 * kBlocksPerWave;  // per wave
 
     f32x4_t acc[FN][FT];
 #pragma unroll
@@ -180,49 +182,61 @@ __global__ __launch_bounds__(kThreads, 1) void proj_bf16_kernel(ProjArgs a) {
 
 #define ENGRAM_COMPUTE(STG)                                                                      \
     do {                                                                                         \
-        _Pragma("unroll") for (int slab = 0; slab < 2; ++slab) {                                 \
-            bf16x8_t fa[FN], fb[FT];                                                             \
-            _Pragma("unroll") for (int i = 0; i < FN; ++i) fa[i] =                               \
-                *reinterpret_cast<const bf16x8_t *>(                                             \
-                    &STG.w[(slab * (BN / 16) + wn_blk + i) * kBlockBytes + fpos]);               \
-            _Pragma("unroll") for (int j = 0; j < FT; ++j) fb[j] =                               \
-                *reinterpret_cast<const bf16x8_t *>(                                             \
-                    &STG.e[(slab * (BT / 16) + wt_blk + j) * kBlockBytes + fpos]);               \
-            _Pragma("unroll") for (int i = 0; i < FN; ++i)                                       \
-                _Pragma("unroll") for (int j = 0; j < FT; ++j)                                   \
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], \
-                                                                        0, 0, 0);                \
-        }                                                                                        \
+        bf16x8_t fa[FN], fb[FT];                                                                 \
+        _Pragma("unroll") for (int i = 0; i < FN; ++i) fa[i] =                                   \
+            *reinterpret_cast<const bf16x8_t *>(&STG.w[(wn_blk + i) * kBlockBytes + fpos]);      \
+        _Pragma("unroll") for (int j = 0; j < FT; ++j) fb[j] =                                   \
+            *reinterpret_cast<const bf16x8_t *>(&STG.e[(wt_blk + j) * kBlockBytes + fpos]);      \
+        _Pragma("unroll") for (int i = 0; i < FN; ++i)                                           \
+            _Pragma("unroll") for (int j = 0; j < FT; ++j)                                       \
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0); \
     } while (0)
 
-    // Stage s lives in st0 when s is even, st1 when odd (K % 128 == 0, so the
-    // number of stages is even).  Each step: start filling the other buffer
-    // with stage s+1, wait for this wave's loads of stage s, barrier (every
-    // wave's stage s has landed), multiply, barrier (nobody reads stage s any
-    // more, so stage s+2 may overwrite it).  The loop body has no branches, so
-    // the compiler can tell which buffer the in-flight fills target and adds
-    // no waits of its own.
+    // Stage s lives in buffer s % 4 (D_e % 128 == 0, so the number of stages
+    // is a multiple of four and the unrolled loop below names every buffer
+    // statically).  Step s: wait until this wave's loads of stage s landed
+    // (stages s+1 and s+2 may still be in flight), barrier (every wave's stage
+    // s has landed, and every wave finished multiplying stage s-1), refill the
+    // buffer of stage s-1 with stage s+3, multiply stage s.  The loop body has
+    // no branches, so the compiler can tell which buffer each in-flight fill
+    // targets and adds no waits of its own.
     const int k_steps = K / BK;
-    ENGRAM_ISSUE(st0, 0);
-    for (int ks = 0; ks + 2 < k_steps; ks += 2) {
-        ENGRAM_ISSUE(st1, (ks + 1) * BK);
-        wait_vmcnt<kLoadsInFlight>();
+    ENGRAM_ISSUE(st0, 0 * BK);
+    ENGRAM_ISSUE(st1, 1 * BK);
+    ENGRAM_ISSUE(st2, 2 * BK);
+    int ks = 0;
+    for (; ks + 4 < k_steps; ks += 4) {  // every stage but the last four: s + 3 < k_steps
+        wait_vmcnt<2 * kLoadsPerStage>();
         block_barrier();
+        ENGRAM_ISSUE(st3, (ks + 3) * BK);
         ENGRAM_COMPUTE(st0);
+        wait_vmcnt<2 * kLoadsPerStage>();
         block_barrier();
-        ENGRAM_ISSUE(st0, (ks + 2) * BK);
-        wait_vmcnt<kLoadsInFlight>();
-        block_barrier();
+        ENGRAM_ISSUE(st0, (ks + 4) * BK);
         ENGRAM_COMPUTE(st1);
+        wait_vmcnt<2 * kLoadsPerStage>();
         block_barrier();
+        ENGRAM_ISSUE(st1, (ks + 5) * BK);
+        ENGRAM_COMPUTE(st2);
+        wait_vmcnt<2 * kLoadsPerStage>();
+        block_barrier();
+        ENGRAM_ISSUE(st2, (ks + 6) * BK);
+        ENGRAM_COMPUTE(st3);
     }
-    ENGRAM_ISSUE(st1, (k_steps - 1) * BK);
-    wait_vmcnt<kLoadsInFlight>();
+    // the last four stages: ks = k_steps - 4; stages ks..ks+2 are in flight
+    wait_vmcnt<2 * kLoadsPerStage>();
     block_barrier();
+    ENGRAM_ISSUE(st3, (ks + 3) * BK);
     ENGRAM_COMPUTE(st0);
-    wait_vmcnt<0>();
+    wait_vmcnt<2 * kLoadsPerStage>();
     block_barrier();
     ENGRAM_COMPUTE(st1);
+    wait_vmcnt<kLoadsPerStage>();
+    block_barrier();
+    ENGRAM_COMPUTE(st2);
+    wait_vmcnt<0>();
+    block_barrier();
+    ENGRAM_COMPUTE(st3);
 #undef ENGRAM_COMPUTE
 #undef ENGRAM_ISSUE
 
