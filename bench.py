@@ -2,16 +2,18 @@
 """Benchmark of the Engram forward pass on one MI355X.
 
 One step = one engram_forward call per Engram layer of the workload over one
-batch of synthetic tokens (hash, gather, projections with the fused gate
-partials, gate + conv + residual).  Inputs are resident in HBM before the
+batch of synthetic tokens (fused hash + gather, the W_k projections with the
+gate partials fused, the W_v projection with gate, gated value, causal conv,
+residual and conv state fused into its epilogue).  Inputs are resident in HBM before the
 timed region; the token batches and hidden states rotate over several
 buffers so gathered rows and activations are not served from the 256 MB
 Infinity Cache of a previous step.
 
 Prints one JSON line: whole-job tokens/s, the roofline of the dominant
-kernel (timed live with HIP events recorded by the library around each of
-its launches on the launch stream), gather bandwidth, per-kernel times and
-the CPU oracle's tokens/s on a bounded sample of the same workload.
+kernel (the one with the most time per step, timed live with HIP events
+recorded by the library around each of its launches on the launch stream),
+every kernel's roofline figures and the CPU oracle's tokens/s on a bounded
+sample of the same workload.
 """
 
 from __future__ import annotations
@@ -185,36 +187,64 @@ def main():
     tokens_per_step = n_tok
     value = tokens_per_step * args.steps / wall
 
-    # dominant kernel: the projections (MFMA), algorithmic flops per launch
+    # Per-kernel algorithmic work per launch.  Projections are MFMA-bound
+    # (flops); retrieval and the fusion kernel are HBM-bound (bytes).
     De, d, Br = wl.emb_dim, wl.d_model, wl.n_branches
-    flops = 2.0 * n_tok * De * (Br + 1) * d
-    gemm_ms, gemm_n = kern("gemm")
-    achieved = flops / (gemm_ms * 1e-3) / 1e12
-    peak = MFMA_PEAK_TFLOPS[wl.dtype]
-    traffic = load_traffic(wl.name, "proj_bf16.hip")
-    roofline = {"kernel": "proj_bf16_kernel" if wl.dtype == "bf16" else "proj_f32_kernel",
-                "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4),
-                "traffic": None if traffic is None else traffic["bytes_per_launch"],
-                "avg_launch_us": round(gemm_ms * 1e3, 2), "launches": gemm_n,
-                "flops_per_launch": flops}
-
     eb = 2 if wl.dtype == "bf16" else 4
-    g_ms, g_n = kern("gather")
+    two_launch = kern("gemm_v")[1] > 0
+    n_parts = d // 128 if wl.dtype == "bf16" else 1
     # engram_forward retrieves in one kernel (hash + gather): it reads each raw
     # token id, every slot row, and writes E; no index buffer round trip
     fused_retrieval = kern("hash")[1] == 0
-    g_bytes = n_tok * ((4 if fused_retrieval else wl.n_tables * 4) + 2 * De * eb)
-    gather = {"kernel": "hash_gather_kernel" if fused_retrieval else "gather_kernel",
-              "achieved_GBs": round(g_bytes / (g_ms * 1e-3) / 1e9, 1), "peak_GBs": HBM_PEAK_GBS,
-              "frac": round(g_bytes / (g_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-              "bytes_per_launch": g_bytes, "avg_launch_us": round(g_ms * 1e3, 2)}
-    f_ms, _ = kern("fuse")
-    # fusion kernel: reads v (fp32) once, h once per branch, the gate partials; writes out per branch
-    f_bytes = n_tok * (4 * d + Br * 2 * d * eb) + Br * (d // 128 if wl.dtype == "bf16" else 1) * 3 * 4 * n_tok
-    fuse = {"achieved_GBs": round(f_bytes / (f_ms * 1e-3) / 1e9, 1), "frac": round(
-        f_bytes / (f_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "avg_launch_us": round(f_ms * 1e3, 2)}
-    kernels_us = {k: round(kern(k)[0] * 1e3, 2) for k in ("hash", "gather", "gemm", "fuse", "aux")}
+    n_w = Br if two_launch else Br + 1
+    part_bytes = Br * n_parts * 3 * 4 * n_tok
+    models = {
+        # W_k e of every branch (and W_v e on the one-launch path)
+        "gemm": ("mfma", 2.0 * n_tok * De * n_w * d),
+        # W_v e with gate, gated value, conv, residual, state in the epilogue
+        "gemm_v": ("mfma", 2.0 * n_tok * De * d),
+        "gather": ("hbm", n_tok * ((4 if fused_retrieval else wl.n_tables * 4) + 2 * De * eb)),
+        # reads the partial sums, writes one gate per token and branch
+        "gate": ("hbm", part_bytes + Br * 4 * n_tok),
+        # reads v (fp32) once, h once per branch, the gates; writes out per branch
+        "fuse": ("hbm", n_tok * (4 * d + Br * 2 * d * eb) + Br * 4 * n_tok),
+    }
+    # HBM bytes of the projection launches as well (E, weights, h, partials,
+    # and v or out): the W_v launch sits close to both roofs
+    mem_bytes = {
+        "gemm": n_tok * De * eb + n_w * d * De * eb + Br * n_tok * d * eb + part_bytes
+                + (0 if two_launch else n_tok * d * 4),
+        "gemm_v": n_tok * De * eb + d * De * eb + Br * 4 * n_tok + 2 * Br * n_tok * d * eb,
+    }
+    kernel_src = {"gemm": "proj_bf16_kernel<0,1>" if wl.dtype == "bf16" else "proj_f32_kernel",
+                  "gemm_v": "proj_bf16_kernel<1,%d>" % Br,
+                  "gather": "hash_gather_kernel" if fused_retrieval else "gather_kernel",
+                  "gate": "gate_kernel",
+                  "fuse": "fuse_kernel<%s,%d>" % ("true" if wl.dtype == "bf16" else "false", Br)}
+    per_kernel = {}
+    for k, (bound, work) in models.items():
+        ms, n = kern(k)
+        if n == 0:
+            continue
+        if bound == "mfma":
+            ach, peak, unit = work / (ms * 1e-3) / 1e12, MFMA_PEAK_TFLOPS[wl.dtype], "TFLOP/s"
+        else:
+            ach, peak, unit = work / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
+        per_kernel[k] = {"kernel": kernel_src[k], "bound": bound, "achieved": round(ach, 2), "peak": peak,
+                         "unit": unit, "frac": round(ach / peak, 4), "avg_launch_us": round(ms * 1e3, 2),
+                         "launches": n, ("flops_per_launch" if bound == "mfma" else "bytes_per_launch"): work,
+                         "ms_per_step": round(ms * n / args.steps, 4)}
+        if k in mem_bytes:
+            gbs = mem_bytes[k] / (ms * 1e-3) / 1e9
+            per_kernel[k].update({"hbm_bytes_per_launch": mem_bytes[k], "hbm_GBs": round(gbs, 1),
+                                  "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+    dom = max(per_kernel, key=lambda k: per_kernel[k]["ms_per_step"])
+    traffic = load_traffic(wl.name, "proj_bf16.hip")
+    roofline = dict(per_kernel[dom])
+    tk = None if traffic is None else traffic.get("kernels", {}).get(dom)
+    roofline["traffic"] = None if tk is None else tk["bytes_per_launch"]
+    roofline["traffic_unit"] = "bytes"
+    kernels_us = {k: round(kern(k)[0] * 1e3, 2) for k in B.KERNEL_NAMES}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -241,8 +271,7 @@ def main():
                    "head_dim": wl.head_dim, "emb_dim": De, "table_params": sum(wl.primes()) * wl.head_dim,
                    "rotated_buffers": R, "parallelism": "single GPU"},
         "roofline": roofline,
-        "gather": gather,
-        "fuse": fuse,
+        "kernels": per_kernel,
         "kernel_avg_us": kernels_us,
         "cpu_baseline": cpu,
     }

@@ -25,7 +25,7 @@ F32, BF16 = 0, 1
 CONV_LINEAR, CONV_SILU_SKIP = 0, 1
 OUT_DELTA = 1
 MAX_TABLES, MAX_BRANCHES = 32, 4
-KERNEL_NAMES = ("hash", "gather", "gemm", "fuse", "aux")
+KERNEL_NAMES = ("hash", "gather", "gemm", "fuse", "aux", "gemm_v", "gate")
 
 
 class EngramError(RuntimeError):
@@ -53,7 +53,7 @@ class WeightsC(C.Structure):
 
 
 class ProfileC(C.Structure):
-    _fields_ = [("total_ms", C.c_double * 5), ("launches", C.c_int64 * 5), ("dropped", C.c_int64)]
+    _fields_ = [("total_ms", C.c_double * 7), ("launches", C.c_int64 * 7), ("dropped", C.c_int64)]
 
 
 _lib = None

@@ -46,11 +46,25 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Layout {
-    size_t idx, emb, partials, v, kbuf, stage, total;
+    size_t idx, emb, partials, alpha, v, kbuf, stage, total;
 };
 
 int32_t n_parts_of(const engram_plan_s &p) {
     return p.cfg.dtype == ENGRAM_BF16 ? p.cfg.d_model / kPartCols : 1;
+}
+
+// Whether the W_v projection carries the rest of the fusion step in its
+// epilogue (v never stored).  Its epilogue addresses h and out of all
+// branches through one buffer resource each, with rows it must not write
+// sent 2^31 bytes past the start (so h and out of all branches stay below
+// 2^31 bytes), and the conv state through 32-bit offsets; it writes only the
+// state rows of its own positions, so a chunk shorter than K_c - 1 (which
+// also keeps rows of the old state) takes the fusion kernel.
+bool fused_value_path(const engram_plan_s &p, int64_t batch, int64_t seqlen) {
+    const int64_t Br = p.cfg.n_branches, d = p.cfg.d_model, kc = p.cfg.conv_kernel;
+    return p.cfg.dtype == ENGRAM_BF16 && seqlen >= kc - 1 &&
+           Br * batch * seqlen * d * 2 < ((int64_t)1 << 31) &&
+           Br * batch * (kc - 1) * d * 4 < ((int64_t)1 << 32);
 }
 
 bool layout_of(const engram_plan_s &p, int64_t batch, int64_t seqlen, Layout &L) {
@@ -66,7 +80,8 @@ bool layout_of(const engram_plan_s &p, int64_t batch, int64_t seqlen, Layout &L)
     L.idx = take((size_t)n_tok * p.n_tables * 4);
     L.emb = take((size_t)n_tok * p.emb_dim * p.elem);
     L.partials = take((size_t)Br * n_parts_of(p) * 3 * n_tok * 4);
-    L.v = take((size_t)n_tok * d * 4);
+    L.alpha = take((size_t)Br * n_tok * 4);
+    L.v = fused_value_path(p, batch, seqlen) ? off : take((size_t)n_tok * d * 4);
     L.kbuf = p.cfg.dtype == ENGRAM_F32 ? take((size_t)Br * n_tok * d * 4) : off;
     L.stage = take((size_t)Br * batch * (p.cfg.conv_kernel - 1) * d * 4);
     L.total = off;
@@ -228,6 +243,13 @@ engram_status do_fuse(engram_plan_s &p, const void *emb, const void *h, int32_t 
     pa.d = p.cfg.d_model;
     pa.n_branches = Br;
     pa.n_parts = n_parts_of(p);
+    float *stage = (conv_state && p.cfg.conv_kernel > 1) ? reinterpret_cast<float *>(base + L.stage) : nullptr;
+    // the gate goes straight into the caller's alpha when one is given
+    float *gate = alpha ? alpha : reinterpret_cast<float *>(base + L.alpha);
+    const bool fused_v = fused_value_path(p, batch, seqlen);
+
+    // W_k of every branch (gate partials); on the fusion-kernel path W_v too
+    pa.n_mats = fused_v ? Br : Br + 1;
     {
         Launch l(p, ENGRAM_K_GEMM, s);
         if (p.cfg.dtype == ENGRAM_BF16)
@@ -237,33 +259,61 @@ engram_status do_fuse(engram_plan_s &p, const void *emb, const void *h, int32_t 
     }
     if (last_launch_status() != ENGRAM_OK) return ENGRAM_E_DEVICE;
 
-    FuseArgs fa{};
-    fa.v = pa.v;
-    fa.partials = pa.partials;
-    fa.h = h;
-    fa.out = out;
-    fa.conv_w = w->conv_w;
-    fa.conv_state = conv_state;
-    fa.state_stage = (conv_state && p.cfg.conv_kernel > 1) ? reinterpret_cast<float *>(base + L.stage) : nullptr;
-    fa.alpha = alpha;
-    fa.batch = batch;
-    fa.seqlen = seqlen;
-    fa.d = p.cfg.d_model;
-    fa.n_branches = Br;
-    fa.n_parts = pa.n_parts;
-    fa.conv_k = p.cfg.conv_kernel;
-    fa.conv_mode = p.cfg.conv_mode;
-    fa.eps = p.cfg.rms_eps;
-    fa.flags = flags;
+    GateArgs ga{};
+    ga.partials = pa.partials;
+    ga.alpha = gate;
+    ga.n_tok = n_tok;
+    ga.d = p.cfg.d_model;
+    ga.n_branches = Br;
+    ga.n_parts = pa.n_parts;
+    ga.eps = p.cfg.rms_eps;
     {
+        Launch l(p, ENGRAM_K_GATE, s);
+        launch_gate(ga, s);
+    }
+    if (last_launch_status() != ENGRAM_OK) return ENGRAM_E_DEVICE;
+
+    if (fused_v) {
+        // W_v with gated value, conv, residual and state in its epilogue
+        ProjArgs pv = pa;
+        pv.w[0] = w->w_v;
+        pv.n_mats = 1;
+        pv.out = out;
+        pv.conv_w = w->conv_w;
+        pv.conv_state = conv_state;
+        pv.state_stage = stage;
+        pv.alpha = gate;
+        pv.batch = batch;
+        pv.seqlen = seqlen;
+        pv.conv_k = p.cfg.conv_kernel;
+        pv.conv_mode = p.cfg.conv_mode;
+        pv.flags = flags;
+        Launch l(p, ENGRAM_K_GEMM_V, s);
+        launch_proj_v_fused_bf16(pv, s);
+    } else {
+        FuseArgs fa{};
+        fa.v = pa.v;
+        fa.alpha = gate;
+        fa.h = h;
+        fa.out = out;
+        fa.conv_w = w->conv_w;
+        fa.conv_state = conv_state;
+        fa.state_stage = stage;
+        fa.batch = batch;
+        fa.seqlen = seqlen;
+        fa.d = p.cfg.d_model;
+        fa.n_branches = Br;
+        fa.conv_k = p.cfg.conv_kernel;
+        fa.conv_mode = p.cfg.conv_mode;
+        fa.flags = flags;
         Launch l(p, ENGRAM_K_FUSE, s);
         launch_fuse(fa, p.cfg.dtype, s);
     }
     if (last_launch_status() != ENGRAM_OK) return ENGRAM_E_DEVICE;
-    if (fa.state_stage) {
+    if (stage) {
         Launch l(p, ENGRAM_K_AUX, s);
         const size_t bytes = (size_t)Br * batch * (p.cfg.conv_kernel - 1) * p.cfg.d_model * 4;
-        if (hipMemcpyAsync(conv_state, fa.state_stage, bytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
+        if (hipMemcpyAsync(conv_state, stage, bytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
             return ENGRAM_E_DEVICE;
     }
     return ENGRAM_OK;

@@ -29,8 +29,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float x) {
     u += 0x7FFFu + ((u >> 16) & 1u);
     return u >> 16;
 }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+    const bf16x2_t p = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, p);
 }
 
 // ---------------------------------------------------------------- hashing
@@ -101,7 +104,7 @@ void launch_hash_gather(const HashConsts &hc, const GatherConsts &gc, const int3
 // ---------------------------------------------------------------- projections
 struct ProjArgs {
     const void *emb;                       // [n_tok][K]
-    const void *w[kMaxBranches + 1];       // w_k[0..B_r-1], then w_v; each [d][K]
+    const void *w[kMaxBranches + 1];       // the launch's weight matrices stacked along N, each [d][K]
     const void *h;                         // [B_r][n_tok][d]
     const float *gamma_h[kMaxBranches];
     const float *gamma_k[kMaxBranches];
@@ -113,25 +116,49 @@ struct ProjArgs {
     int32_t d;
     int32_t n_branches;
     int32_t n_parts;
+    int32_t n_mats;                        // matrices in w[]: mat < n_branches is W_k^(mat), else W_v
+    // fused value launch only (gate, gated value, conv, residual in the epilogue)
+    void *out;                             // [B_r][n_tok][d]
+    const float *conv_w;                   // [d][K_c]
+    const float *conv_state;               // [B_r][batch][K_c-1][d] or null
+    float *state_stage;                    // [B_r][batch][K_c-1][d] or null
+    const float *alpha;                    // [B_r][n_tok], from the gate kernel
+    int32_t batch, seqlen, conv_k, conv_mode;
+    uint32_t flags;
 };
 
 constexpr int kPartCols = 128;  // columns of d summed into one gate partial (bf16 path)
 
+// W_k^(m) (and, when n_mats == n_branches + 1, W_v) projections: gate
+// partials from W_k tiles, fp32 v from W_v tiles.
 void launch_proj_bf16(const ProjArgs &a, hipStream_t s);
+// W_v projection with the gate, gated value, depthwise causal conv, residual
+// and conv-state update fused into the epilogue (needs seqlen >= K_c - 1).
+void launch_proj_v_fused_bf16(const ProjArgs &a, hipStream_t s);
 void launch_proj_f32(const ProjArgs &a, hipStream_t s);  // k into kbuf, v, then partials
 
 // ---------------------------------------------------------------- fusion
+// Gate per branch and token, alpha = sigmoid(<RMSNorm(h), RMSNorm(k)> / sqrt(d)),
+// from the partial sums of the W_k projection (summed in a fixed order).
+struct GateArgs {
+    const float *partials;     // [B_r][n_parts][3][n_tok]
+    float *alpha;              // [B_r][n_tok]
+    int64_t n_tok;
+    int32_t d, n_branches, n_parts;
+    float eps;
+};
+
+void launch_gate(const GateArgs &a, hipStream_t s);
+
 struct FuseArgs {
     const float *v;            // [n_tok][d] fp32
-    const float *partials;     // [B_r][n_parts][3][n_tok]
+    const float *alpha;        // [B_r][n_tok], from the gate kernel
     const void *h;             // [B_r][n_tok][d]
     void *out;                 // [B_r][n_tok][d]
     const float *conv_w;       // [d][K_c]
     const float *conv_state;   // [B_r][batch][K_c-1][d] or null
     float *state_stage;        // [B_r][batch][K_c-1][d] or null
-    float *alpha;              // [B_r][n_tok] or null
-    int32_t batch, seqlen, d, n_branches, n_parts, conv_k, conv_mode;
-    float eps;
+    int32_t batch, seqlen, d, n_branches, conv_k, conv_mode;
     uint32_t flags;
 };
 

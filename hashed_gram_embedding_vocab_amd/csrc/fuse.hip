@@ -1,17 +1,21 @@
-// fuse.hip -- the rest of Engram's fusion step on gfx950 ([club] 1.(2)
-// 上下文感知的门控机制, last two bullets; [csdn] Engram 到底怎么工作的, third
-// and fourth steps): the scalar gate per token and branch from the partial
-// sums the projection kernel left behind, the gated value u = alpha * v, the
-// short depthwise causal convolution and the residual into the hidden state.
+// fuse.hip -- the gate and, for short chunks and the fp32 path, the rest of
+// Engram's fusion step on gfx950 ([club] 1.(2) 上下文感知的门控机制, last two
+// bullets; [csdn] Engram 到底怎么工作的, third and fourth steps).
 //
-// HBM-bound: it reads v (fp32) once, h once per branch and writes out once
-// per branch.  A block owns kPos consecutive positions of one sequence and a
-// stripe of channels; each thread owns 4 channels (one 16-byte fp32 vector of
-// v) and walks the positions in order, keeping the last three gated values of
-// every branch in registers, so no gated value is ever written to memory.
-// Loads for a group of positions are issued before any of their arithmetic.
-// The three values before the block's first position are recomputed from v
-// (or taken from the carried conv state at the sequence start).
+// gate_kernel: the scalar gate per token and branch from the partial sums the
+// projection kernel left behind (one thread per token, the partial index
+// summed in a fixed order, so every path gets the same bits).
+//
+// fuse_kernel: the gated value u = alpha * v, the short depthwise causal
+// convolution and the residual into the hidden state.  HBM-bound: it reads v
+// (fp32) once, h once per branch and writes out once per branch.  A block
+// owns kPos consecutive positions of one sequence and a stripe of channels;
+// each thread owns 4 channels (one 16-byte fp32 vector of v) and walks the
+// positions in order, keeping the last three gated values of every branch in
+// registers, so no gated value is ever written to memory.  Loads for a group
+// of positions are issued before any of their arithmetic.  The three values
+// before the block's first position are recomputed from v (or taken from the
+// carried conv state at the sequence start).
 #include "engram_internal.h"
 
 namespace engram {
@@ -53,6 +57,24 @@ struct Raw4 {
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + expf(-x)); }
 
+__global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int m = blockIdx.y;
+    if (t >= a.n_tok) return;
+    const float *pp = a.partials + (int64_t)m * a.n_parts * 3 * a.n_tok + t;
+    float s_hk = 0.f, s_kk = 0.f, s_hh = 0.f;
+#pragma unroll 8
+    for (int q = 0; q < a.n_parts; ++q) {
+        s_hk += pp[(3 * q + 0) * a.n_tok];
+        s_kk += pp[(3 * q + 1) * a.n_tok];
+        s_hh += pp[(3 * q + 2) * a.n_tok];
+    }
+    const float inv_d = 1.f / (float)a.d;
+    const float rh = sqrtf(s_hh * inv_d + a.eps);
+    const float rk = sqrtf(s_kk * inv_d + a.eps);
+    a.alpha[m * a.n_tok + t] = sigmoidf_(s_hk / (rh * rk) * rsqrtf((float)a.d));
+}
+
 template <bool BF16, int BR>
 __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
     __shared__ float alpha_s[BR][kPos + 3];
@@ -62,28 +84,12 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
     const int64_t n_tok = (int64_t)a.batch * a.seqlen;
     const int64_t row0 = (int64_t)b * a.seqlen;
     const int d = a.d;
-    const float inv_d = 1.f / (float)d;
-    const float inv_sqrt_d = rsqrtf((float)d);
 
     // gate values for positions t0-3 .. t1-1 (zero where unused)
     for (int x = threadIdx.x; x < BR * (kPos + 3); x += blockDim.x) {
         const int m = x / (kPos + 3), j = x - m * (kPos + 3);
         const int p = t0 - 3 + j;
-        float al = 0.f;
-        if (p >= 0 && p < t1) {
-            const float *pp = a.partials + (int64_t)m * a.n_parts * 3 * n_tok + row0 + p;
-            float s_hk = 0.f, s_kk = 0.f, s_hh = 0.f;
-            for (int q = 0; q < a.n_parts; ++q) {  // fixed order: bit-reproducible
-                s_hk += pp[(3 * q + 0) * n_tok];
-                s_kk += pp[(3 * q + 1) * n_tok];
-                s_hh += pp[(3 * q + 2) * n_tok];
-            }
-            const float rh = sqrtf(s_hh * inv_d + a.eps);
-            const float rk = sqrtf(s_kk * inv_d + a.eps);
-            al = sigmoidf_(s_hk / (rh * rk) * inv_sqrt_d);
-            if (a.alpha && p >= t0 && blockIdx.z == 0) a.alpha[m * n_tok + row0 + p] = al;
-        }
-        alpha_s[m][j] = al;
+        alpha_s[m][j] = (p >= 0 && p < t1) ? a.alpha[m * n_tok + row0 + p] : 0.f;
     }
     __syncthreads();
 
@@ -174,6 +180,11 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
 }
 
 }  // namespace
+
+void launch_gate(const GateArgs &a, hipStream_t s) {
+    const dim3 grid((unsigned)((a.n_tok + 255) / 256), (unsigned)a.n_branches);
+    hipLaunchKernelGGL(gate_kernel, grid, dim3(256), 0, s, a);
+}
 
 void launch_fuse(const FuseArgs &a, engram_dtype dt, hipStream_t s) {
     const int need = (a.d + kVec - 1) / kVec;

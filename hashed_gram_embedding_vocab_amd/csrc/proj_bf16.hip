@@ -2,8 +2,14 @@
 // MFMA: k^(m) = W_k^(m) e and v = W_v e for every token ([club] 1.(2): the
 // hidden state is the query, the retrieved embedding is key and value through
 // projection matrices; [club] 2. 工程优化: branches share W_v, each has its
-// own W_k).  One launch covers every projection: the weight rows of all
-// W_k^(m) followed by W_v form the N dimension.
+// own W_k).  Two modes share one main loop:
+//   mode 0: the weight rows of the launch's matrices (all W_k^(m), optionally
+//     followed by W_v) form the N dimension; W_k tiles leave gate partials,
+//     W_v tiles store v.
+//   mode 1: W_v only, with the rest of the fusion step in the epilogue:
+//     alpha from the gate partials of a preceding mode-0 launch, u = alpha v,
+//     the short depthwise causal conv over tokens, the residual into h and
+//     the conv-state update ([club] 1.(2) last bullet).  v never reaches HBM.
 //
 // Roles: the MFMA A operand is a tile of weight rows (n) and the B operand a
 // tile of tokens (t), both K-contiguous ([d][D_e] weights, [n_tok][D_e] E), so
@@ -14,6 +20,11 @@
 //     128 channels of  h*gamma_h*gamma_k*k,  k^2  and  h^2  (the RMSNorm dot
 //     product decomposes into these three sums).
 //   W_v tiles store v (fp32) for the fusion kernel.
+// In mode 1 each lane holds four channels of one token per MFMA block and the
+// 16 lanes of a row hold 16 consecutive tokens, so the conv's neighbours
+// u_{t-1..t-3} come from DPP row rotations across lanes (plus the previous
+// block's registers); token tiles overlap by three rows so no tile needs
+// another tile's values, and neighbouring waves pass three rows via LDS.
 //
 // Tile: 256 weight rows x 256 tokens (d % 256 == 0, so a weight tile never
 // straddles two matrices), 32 K per stage (D_e % 128 == 0), 8 waves (two per
@@ -27,6 +38,8 @@
 // (one MFMA fragment); inside a block the four 16-byte chunks of a row are
 // XOR-swizzled by ((r>>1) ^ (r>>2)) & 3 so the fragment reads of 8 or 16
 // consecutive rows fall in distinct banks.
+#include <type_traits>
+
 #include "engram_internal.h"
 
 namespace engram {
@@ -46,6 +59,8 @@ constexpr int FN = WN / 16, FT = WT / 16;
 constexpr int kBlockBytes = 1024;                       // 16 rows x 32 bf16
 constexpr int kOperandBytes = (BN / 16) * kBlockBytes;  // 16 KB per operand per stage
 constexpr int kBlocksPerWave = (BN / 16) / kWaves;          // row blocks each wave fills, per operand and stage
+constexpr int kHalo = 3;              // rows of conv history a mode-1 token tile recomputes
+constexpr int kStrideV = BT - kHalo;  // token tile stride in mode 1
 constexpr int kXcds = 8;
 #ifndef ENGRAM_PROJ_GROUP_T
 #define ENGRAM_PROJ_GROUP_T 4
@@ -115,27 +130,288 @@ __device__ __forceinline__ void block_barrier() {
     asm volatile("" ::: "memory");
 }
 
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }
+
+// x from lane (l - s) of the same 16-lane row (rotating), s in 1..3
+template <int S>
+__device__ __forceinline__ float row_ror(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + S, 0xF, 0xF, false));
+}
+
+// s_waitcnt lgkmcnt(0) alone: every LDS access of this wave has completed.
+__device__ __forceinline__ void wait_lgkm0() {
+    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
+}
+
+// Mode-1 epilogue.  The tile's E rows were loaded so that in each wave's
+// group of 64 tokens, lane row l (l = lane % 16) holds tokens 4l + j in its
+// accumulator blocks j = 0..3: acc[i][j][r] is v of channel
+// nl + 16i + 4*(lane/16) + r and token t0 + 64g + 4l + j.  For the conv,
+// u_{t-s} then lies in the same lane (block j - s) when s <= j, else in lane
+// row l - 1 (block j - s + 4, one DPP row shift), or for lane row 0 among the
+// previous group's last three tokens, which pass through LDS.
+//
+// h arrives in LDS by DMA, one 8 KB chunk (64 tokens x 64 channels of one
+// branch) per wave at a time, two chunks in flight, so the loads need no
+// registers and overlap the arithmetic of the previous chunk.  Chunk c holds
+// branch c/2, channels nl + 64(c%2) .. +63, in buffer hA (c even) or hB
+// (c odd); LDS row p is token 64g + p, its eight 16-byte pieces XOR-swizzled
+// by (p/4) % 8.  out is stored straight from registers; every store is
+// issued (rows outside the tile's own tokens get an offset past the buffer,
+// which the hardware drops), so the number of memory operations between two
+// chunk loads is known and the waits below are exact.
+template <int BR, bool SILU>
+__device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t (&acc)[FN][FT],
+                                                     float (&alpha_s)[BR][BT], float *halo, float *taps,
+                                                     unsigned char *hA, unsigned char *hB, int wave,
+                                                     int lane, int nl, int n0, int64_t t0) {
+    const int d = a.d;
+    const int l16 = lane & 15;
+    const int sub = 4 * (lane >> 4);
+    const int g = wave >> 1;
+    const int rowbase = 64 * g;
+    const int64_t n_tok = a.n_tok;
+    const int kc = a.conv_k;
+    const bool delta = (a.flags & ENGRAM_OUT_DELTA) != 0;
+
+    // the block's 256 channels of conv taps, as taps[c][s] multiplying
+    // u_{t-s} (zero beyond K_c)
+    for (int x = threadIdx.x; x < BN; x += kThreads) {
+        f32x4_t w4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (q < kc) w4[q] = a.conv_w[(int64_t)(n0 + x) * kc + (kc - 1 - q)];
+        *reinterpret_cast<f32x4_t *>(&taps[4 * x]) = w4;
+    }
+    // the group's last three tokens (lane row 15, blocks 1..3) for the wave
+    // holding the next 64 tokens of the same channels: halo row j-1 is token 60+j
+    if (l16 == 15) {
+#pragma unroll
+        for (int j = 1; j < FT; ++j)
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+                *reinterpret_cast<f32x4_t *>(&halo[(wave * kHalo + (j - 1)) * WN + 16 * i + sub]) = acc[i][j];
+    }
+    __syncthreads();  // taps and halo written; every wave is done with the stage buffers
+    // the first group's leading tokens are the tile's recomputed history
+    // (never stored), so it needs nothing from a neighbour
+    // (it reads its own halo rows, finite, times a zero gate: no branch)
+    const bool has_prev = g > 0;
+    const float *prev = halo + (has_prev ? wave - 2 : wave) * kHalo * WN;
+
+    const uint32_t branch_bytes = (uint32_t)(n_tok * d * 2);
+    const uint32_t state_branch_bytes = (uint32_t)a.batch * (uint32_t)(kc - 1) * (uint32_t)d * 4u;
+    const uint32_t state_row_bytes = (uint32_t)d * 4u;
+    const __amdgpu_buffer_rsrc_t hres = make_rsrc(a.h, branch_bytes * BR);
+    const __amdgpu_buffer_rsrc_t ores = make_rsrc(a.out, branch_bytes * BR);
+    const __amdgpu_buffer_rsrc_t cres = make_rsrc(a.conv_state, state_branch_bytes * BR);
+    const __amdgpu_buffer_rsrc_t sres = make_rsrc(a.state_stage, state_branch_bytes * BR);
+    // the new state's rows are the gated values of the last K_c-1 positions
+    const uint32_t stage_shift = (uint32_t)(a.seqlen - (kc - 1)) * state_row_bytes;
+
+    int pos[FT];
+    bool edge[FT], to_state[FT];
+    uint32_t stoff[FT], srow[FT], stagerow[FT];
+#pragma unroll
+    for (int j = 0; j < FT; ++j) {
+        const int row = rowbase + 4 * l16 + j;
+        const int64_t tt = t0 + row;
+        const bool valid = tt >= 0 && tt < n_tok;
+        const int tc = valid ? (int)tt : 0;
+        const int bseq = tc / a.seqlen;
+        pos[j] = tc - bseq * a.seqlen;
+        const bool store = valid && row >= kHalo;
+        to_state[j] = store && pos[j] >= a.seqlen - (kc - 1);
+        // rows that need carried state (sequence start) or write it (sequence end)
+        edge[j] = __ballot(store && (pos[j] < kHalo || to_state[j])) != 0;
+        stoff[j] = store ? (uint32_t)((tc * (int64_t)d + nl + sub) * 2) : 0x80000000u;
+        // byte offset of state row pos of sequence bseq, modulo 2^32: exact
+        // (in range) for the rows that read or write the state
+        srow[j] = ((uint32_t)bseq * (uint32_t)(kc - 1) + (uint32_t)pos[j]) * state_row_bytes +
+                  (uint32_t)(nl + sub) * 4u;
+        stagerow[j] = srow[j] - stage_shift;
+    }
+
+    const bool any_edge = edge[0] || edge[1] || edge[2] || edge[3];
+
+    // chunk DMA: instruction k fills LDS rows 8k .. 8k+7 (lane -> row
+    // 8k + lane/8, piece lane%8), so lane reads global piece
+    // (lane%8) ^ swizzle(row) of its token's 64 channels
+    uint32_t hoff[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int p = 8 * k + (lane >> 3);
+        const int64_t tok = min(max(t0 + rowbase + p, (int64_t)0), n_tok - 1);
+        hoff[k] = (uint32_t)((tok * d + nl) * 2) + (uint32_t)(((lane & 7) ^ ((p >> 2) & 7)) << 4);
+    }
+    auto issue = [&](unsigned char *buf, int c) {
+        wait_lgkm0();  // this wave's reads of the buffer's previous chunk are done
+        asm volatile("" ::: "memory");
+        const int soff = (int)(branch_bytes * (uint32_t)(c >> 1)) + 128 * (c & 1);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(hres, (lds_void_t *)(buf + k * 1024), 16, hoff[k], soff, 0, 0);
+    };
+    // LDS byte offset of this lane's 4 channels of block i' of a chunk, token
+    // row 4*l16 (+ 128 bytes per block j): piece 2i' + sub/8, swizzled by l16 % 8
+    uint32_t ldo[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+        ldo[ii] = (uint32_t)(l16 * 512 + (((2 * ii + (sub >> 3)) ^ (l16 & 7)) << 4) + (sub & 4) * 2);
+
+    // EDGE: some token block of the wave holds a sequence's first or last
+    // positions.  Without it the body is straight-line code.
+    auto chunk = [&](auto qc, auto ec, const unsigned char *buf, int m, int moff, int smoff,
+                     const float (&al)[FT], const float (&alh)[3]) {
+        constexpr int q = decltype(qc)::value;
+        constexpr bool EDGE = decltype(ec)::value;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            asm volatile("" ::: "memory");  // one channel group at a time: bounds register use
+            const int i = 4 * q + ii;
+            const int c0 = nl + 16 * i + sub;
+            f32x4_t tap[4];  // tap[r][s] multiplies u_{t-s} of channel c0 + r
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tap[r] = *reinterpret_cast<const f32x4_t *>(&taps[4 * (c0 + r - n0)]);
+            float u[FT][4];
+#pragma unroll
+            for (int j = 0; j < FT; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) u[j][r] = al[j] * acc[i][j][r];
+            // pr[s-1][r] = u_{4l-s}: block 4-s of lane row l-1; for lane row 0
+            // the previous group's token 64-s (DPP row shift keeps `old` there)
+            float pr[3][4];
+#pragma unroll
+            for (int s = 1; s <= 3; ++s) {
+                const f32x4_t hp = *reinterpret_cast<const f32x4_t *>(&prev[(3 - s) * WN + 16 * i + sub]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    pr[s - 1][r] = __int_as_float(__builtin_amdgcn_update_dpp(
+                        __float_as_int(alh[s - 1] * hp[r]), __float_as_int(u[4 - s][r]), 0x111, 0xF, 0xF, false));
+            }
+#pragma unroll
+            for (int j = 0; j < FT; ++j) {
+                f32x4_t sh[3];  // sh[s-1][r] = u_{t-s} of channel c0 + r
+#pragma unroll
+                for (int s = 1; s <= 3; ++s)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sh[s - 1][r] = j >= s ? u[j - s][r] : pr[s - j - 1][r];
+                if (EDGE && edge[j]) {  // wave-uniform: a sequence starts or ends among these rows
+                    // u before a sequence's first position is its carried state
+                    // (state row K_c-1-s of the sequence for u_{-s}), or zero
+                    // beyond it.  Lanes that do not need it read offset 0 of
+                    // the branch's state, so every lane stays inside the buffer.
+                    // (The empty asm makes sr opaque here, so the offsets
+                    // derived from it are not hoisted out of the branch loop.)
+                    uint32_t sr = srow[j];
+                    asm volatile("" : "+v"(sr));
+#pragma unroll
+                    for (int s = 1; s <= 3; ++s) {
+                        f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+                        if (a.conv_state && s <= kc - 1) {
+                            const uint32_t off = pos[j] < s ? sr + 64u * i : 0u;
+                            c = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                cres, off, smoff + (kc - 1 - s) * (int)state_row_bytes, 0));
+                        }
+                        if (pos[j] < s) sh[s - 1] = c;
+                    }
+                    // drain here: left pending, the compiler would wait for
+                    // them (and everything before) after the branch, on every path
+                    wait_vmcnt<0>();
+                    asm volatile("" ::: "memory");
+                }
+                const u32x2_t h2 = *reinterpret_cast<const u32x2_t *>(buf + ldo[ii] + 128 * j);
+                float o[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float conv =
+                        tap[r][0] * u[j][r] + tap[r][1] * sh[0][r] + tap[r][2] * sh[1][r] + tap[r][3] * sh[2][r];
+                    const float y = SILU ? u[j][r] + conv * sigmoid_f(conv) : conv;
+                    const uint32_t hw = h2[r >> 1];
+                    const float hval = bf16_to_f32((r & 1) ? (hw >> 16) : (hw & 0xFFFFu));
+                    o[r] = delta ? y : hval + y;
+                }
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])},
+                                                      ores, stoff[j] + 32 * i, moff, 0);
+                if (EDGE && edge[j] && a.state_stage && to_state[j])
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        __builtin_bit_cast(u32x4_t, f32x4_t{u[j][0], u[j][1], u[j][2], u[j][3]}), sres,
+                        stagerow[j] + 64 * i, smoff, 0);
+            }
+        }
+    };
+
+    // Issue order: load(0), load(1), chunk 0's 16 stores, load(2), chunk 1's
+    // stores, load(3), ...  Before chunk c, the operations issued after
+    // load(c) are chunk c-1's stores (16, for c >= 1) and load(c+1) (8, if
+    // there is one).  Vector memory operations complete in issue order, so
+    // waiting until no more than those are outstanding means chunk c has
+    // landed.  State stores and carried-state loads near sequence edges only
+    // add operations, which makes these waits stricter, never looser.
+    issue(hA, 0);
+    issue(hB, 1);
+#pragma unroll 1
+    for (int m = 0; m < BR; ++m) {
+        const int moff = (int)(branch_bytes * (uint32_t)m);
+        const int smoff = (int)(state_branch_bytes * (uint32_t)m);
+        float al[FT], alh[3];
+#pragma unroll
+        for (int j = 0; j < FT; ++j) al[j] = alpha_s[m][rowbase + 4 * l16 + j];
+#pragma unroll
+        for (int s = 1; s <= 3; ++s) alh[s - 1] = has_prev ? alpha_s[m][rowbase - s] : 0.f;
+        if (m == 0)
+            wait_vmcnt<8>();
+        else
+            wait_vmcnt<24>();
+        asm volatile("" ::: "memory");
+        if (any_edge)
+            chunk(std::integral_constant<int, 0>{}, std::true_type{}, hA, m, moff, smoff, al, alh);
+        else
+            chunk(std::integral_constant<int, 0>{}, std::false_type{}, hA, m, moff, smoff, al, alh);
+        if (m + 1 < BR) issue(hA, 2 * m + 2);
+        if (m + 1 < BR)
+            wait_vmcnt<24>();
+        else
+            wait_vmcnt<16>();
+        asm volatile("" ::: "memory");
+        if (any_edge)
+            chunk(std::integral_constant<int, 1>{}, std::true_type{}, hB, m, moff, smoff, al, alh);
+        else
+            chunk(std::integral_constant<int, 1>{}, std::false_type{}, hB, m, moff, smoff, al, alh);
+        if (m + 1 < BR) issue(hB, 2 * m + 3);
+    }
+}
+
+// MODE 0, or MODE 1 with BR branches and the conv output passed through
+// SiLU plus the skip term (SILU) or not.
+template <int MODE, int BR, bool SILU>
 __global__ __launch_bounds__(kThreads, 1) void proj_bf16_kernel(ProjArgs a) {
     __shared__ Stage st0, st1, st2, st3;
+    __shared__ float alpha_s[MODE == 1 ? BR : 1][BT];
+    __shared__ __attribute__((aligned(16))) float taps_s[MODE == 1 ? 4 * BN : 4];
+    __shared__ __attribute__((aligned(16))) float halo_s[MODE == 1 ? kWaves * kHalo * WN : 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
     const int K = a.K;
     const int d = a.d;
-    const int n_total = (a.n_branches + 1) * d;
+    const int n_total = a.n_mats * d;
+    const int stride_t = MODE == 1 ? kStrideV : BT;
     const int n_tiles_n = (n_total + BN - 1) / BN;
-    const int n_tiles_t = (int)((a.n_tok + BT - 1) / BT);
+    const int n_tiles_t = (int)((a.n_tok + stride_t - 1) / stride_t);
     int tile_n, tile_t;
     tile_of(blockIdx.x, gridDim.x, n_tiles_n, n_tiles_t, tile_n, tile_t);
     const int n0 = tile_n * BN;
-    const int64_t t0 = (int64_t)tile_t * BT;
+    // first token row of the tile; in mode 1 the first kHalo rows are the
+    // previous tile's last tokens (negative for the first tile: never stored)
+    const int64_t t0 = (int64_t)tile_t * stride_t - (MODE == 1 ? kHalo : 0);
 
     // ---- this lane's share of the block loads.  Wave w fills row blocks
     //      2w and 2w+1 of each operand.
     //      Lane l fills row l>>2 of the block, LDS chunk l&3, which holds
-    //      global K chunk (l&3) ^ swz(row).  Rows past the end are clamped to
-    //      the last valid row: their products only reach outputs that the
+    //      global K chunk (l&3) ^ swz(row).  Token rows outside [0, n_tok) are
+    //      clamped to a valid row: their products only reach outputs that the
     //      epilogue never writes, so no load leaves the buffers.
     const int lr = lane >> 2;
     const int lchunk = (lane & 3) ^ swz(lr);
@@ -144,13 +420,17 @@ __global__ __launch_bounds__(kThreads, 1) void proj_bf16_kernel(ProjArgs a) {
     const char *wmat = reinterpret_cast<const char *>(pick(a.w, mat0));
     const __amdgpu_buffer_rsrc_t wres = make_rsrc(wmat, (uint32_t)d * K * 2u);
     const __amdgpu_buffer_rsrc_t eres = make_rsrc(a.emb, (uint32_t)(a.n_tok * K * 2));
-    const int rows_left_t = (int)min<int64_t>(a.n_tok - t0, BT) - 1;  // last valid token row in the tile
     uint32_t woff[kBlocksPerWave], eoff[kBlocksPerWave];
 #pragma unroll
     for (int i = 0; i < kBlocksPerWave; ++i) {
-        const int row = (wave * kBlocksPerWave + i) * 16 + lr;
+        const int blk = wave * kBlocksPerWave + i;
+        const int row = blk * 16 + lr;
+        // mode 1 takes the tokens of each group of four row blocks in the
+        // order 4 * row + block (see the mode-1 epilogue)
+        const int trow = MODE == 1 ? 64 * (blk >> 2) + 4 * lr + (blk & 3) : row;
+        const int64_t t = min(max(t0 + trow, (int64_t)0), a.n_tok - 1);
         woff[i] = (uint32_t)((n0 - mat0 * d + row) * K + lchunk * 8) * 2u;
-        eoff[i] = (uint32_t)((t0 + min(row, rows_left_t)) * K + lchunk * 8) * 2u;
+        eoff[i] = (uint32_t)(t * K + lchunk * 8) * 2u;
     }
 
 // The immediate offset of a buffer load with an LDS destination moves the LDS
@@ -204,6 +484,16 @@ __global__ __launch_bounds__(kThreads, 1) void proj_bf16_kernel(ProjArgs a) {
     ENGRAM_ISSUE(st0, 0 * BK);
     ENGRAM_ISSUE(st1, 1 * BK);
     ENGRAM_ISSUE(st2, 2 * BK);
+
+    if constexpr (MODE == 1) {
+        // gate of every row of the tile and branch (zero outside the tokens),
+        // while the first stages are in flight
+        for (int x = tid; x < BR * BT; x += kThreads) {
+            const int m = x / BT, r = x - m * BT;
+            const int64_t t = t0 + r;
+            alpha_s[m][r] = (t >= 0 && t < a.n_tok) ? a.alpha[m * a.n_tok + t] : 0.f;
+        }
+    }
     int ks = 0;
     for (; ks + 4 < k_steps; ks += 4) {  // every stage but the last four: s + 3 < k_steps
         wait_vmcnt<2 * kLoadsPerStage>();
@@ -249,6 +539,7 @@ __global__ __launch_bounds__(kThreads, 1) void proj_bf16_kernel(ProjArgs a) {
     const int sub = 4 * (lane >> 4);
     const int64_t tw = t0 + wt_blk * 16;
 
+    if constexpr (MODE == 0) {
     if (mat < a.n_branches) {
         // gate partials of branch `mat` over channels [nl, nl+128).
         // gamma_h * gamma_k for the wave's channels goes through the now idle
@@ -263,23 +554,23 @@ __global__ __launch_bounds__(kThreads, 1) void proj_bf16_kernel(ProjArgs a) {
         const uint16_t *hm = reinterpret_cast<const uint16_t *>(a.h) + (int64_t)mat * a.n_tok * d;
         const int part = nl / kPartCols;
         float *pbase = a.partials + ((int64_t)mat * a.n_parts + part) * 3 * a.n_tok;
-        // h for token block j+1 is in flight while block j is reduced
-        u32x2_t hv[2][FN];
-        auto load_h = [&](int j, u32x2_t(&dst)[FN]) {
+        // every h value the wave needs is requested before any is used: one
+        // memory round trip for the whole epilogue
+        u32x2_t hv[FT][FN];
+#pragma unroll
+        for (int j = 0; j < FT; ++j) {
             const int64_t t = min(tw + 16 * j + (lane & 15), a.n_tok - 1);
             const uint16_t *hrow = hm + t * d + nl + sub;
 #pragma unroll
-            for (int i = 0; i < FN; ++i) dst[i] = *reinterpret_cast<const u32x2_t *>(hrow + 16 * i);
-        };
-        load_h(0, hv[0]);
+            for (int i = 0; i < FN; ++i) hv[j][i] = *reinterpret_cast<const u32x2_t *>(hrow + 16 * i);
+        }
 #pragma unroll
         for (int j = 0; j < FT; ++j) {
-            if (j + 1 < FT) load_h(j + 1, hv[(j + 1) & 1]);
             const int64_t t = tw + 16 * j + (lane & 15);
             float s_hk = 0.f, s_kk = 0.f, s_hh = 0.f;
 #pragma unroll
             for (int i = 0; i < FN; ++i) {
-                const u32x2_t x = hv[j & 1][i];
+                const u32x2_t x = hv[j][i];
                 const f32x4_t g = *reinterpret_cast<const f32x4_t *>(gsm + 16 * i + sub);
                 const float h4[4] = {bf16_to_f32(x[0] & 0xFFFFu), bf16_to_f32(x[0] >> 16),
                                      bf16_to_f32(x[1] & 0xFFFFu), bf16_to_f32(x[1] >> 16)};
@@ -313,16 +604,42 @@ __global__ __launch_bounds__(kThreads, 1) void proj_bf16_kernel(ProjArgs a) {
                 *reinterpret_cast<f32x4_t *>(a.v + t * d + nl + 16 * i + sub) = acc[i][j];
         }
     }
+    } else {
+        // each wave's two chunk buffers: 8 KB of st0/st1 (A) and of st2/st3 (B)
+        unsigned char *hA = reinterpret_cast<unsigned char *>(wave < 4 ? &st0 : &st1) + (wave & 3) * 8192;
+        unsigned char *hB = reinterpret_cast<unsigned char *>(wave < 4 ? &st2 : &st3) + (wave & 3) * 8192;
+        fused_value_epilogue<BR, SILU>(a, acc, alpha_s, halo_s, taps_s, hA, hB, wave, lane, nl, n0, t0);
+    }
 }
 
 }  // namespace
 
 void launch_proj_bf16(const ProjArgs &a, hipStream_t s) {
-    const int n_total = (a.n_branches + 1) * a.d;
+    const int n_total = a.n_mats * a.d;
     const int n_tiles_n = (n_total + BN - 1) / BN;
     const int64_t n_tiles_t = (a.n_tok + BT - 1) / BT;
     const int64_t blocks = (int64_t)n_tiles_n * n_tiles_t;
-    hipLaunchKernelGGL(proj_bf16_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((proj_bf16_kernel<0, 1, false>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+}
+
+void launch_proj_v_fused_bf16(const ProjArgs &a, hipStream_t s) {
+    const int n_tiles_n = (a.d + BN - 1) / BN;
+    const int64_t n_tiles_t = (a.n_tok + kStrideV - 1) / kStrideV;
+    const dim3 grid((unsigned)((int64_t)n_tiles_n * n_tiles_t));
+#define ENGRAM_PROJ_V_LAUNCH(BR)                                                                      \
+    do {                                                                                              \
+        if (a.conv_mode == ENGRAM_CONV_SILU_SKIP)                                                     \
+            hipLaunchKernelGGL((proj_bf16_kernel<1, BR, true>), grid, dim3(kThreads), 0, s, a);        \
+        else                                                                                          \
+            hipLaunchKernelGGL((proj_bf16_kernel<1, BR, false>), grid, dim3(kThreads), 0, s, a);       \
+    } while (0)
+    switch (a.n_branches) {
+        case 1: ENGRAM_PROJ_V_LAUNCH(1); break;
+        case 2: ENGRAM_PROJ_V_LAUNCH(2); break;
+        case 3: ENGRAM_PROJ_V_LAUNCH(3); break;
+        default: ENGRAM_PROJ_V_LAUNCH(4); break;
+    }
+#undef ENGRAM_PROJ_V_LAUNCH
 }
 
 }  // namespace engram

@@ -50,7 +50,8 @@ __global__ __launch_bounds__(256) void synth_fill_kernel(uint64_t seed, int32_t 
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = ih4_value(c[i]);
         if constexpr (BF16) {
-            u32x2_t p = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            // integer round-to-nearest-even: bit-exact whatever the FP mode register says
+            u32x2_t p = {f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16), f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16)};
             reinterpret_cast<u32x2_t *>(table)[g] = p;
         } else {
             reinterpret_cast<f32x4_t *>(table)[g] = f32x4_t{v[0], v[1], v[2], v[3]};

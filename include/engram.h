@@ -98,12 +98,16 @@ typedef struct {
 
 /* Per-kernel timing gathered while profiling is on (see engram_profile_*). */
 enum {
-    ENGRAM_K_HASH = 0,
-    ENGRAM_K_GATHER = 1,
-    ENGRAM_K_GEMM = 2,   /* projections W_k e (all branches) and W_v e, gate partials fused */
-    ENGRAM_K_FUSE = 3,   /* gate, gated value, depthwise conv, residual, state */
-    ENGRAM_K_AUX = 4,    /* context / state bookkeeping                        */
-    ENGRAM_K_COUNT = 5
+    ENGRAM_K_HASH = 0,    /* engram_hash                                                     */
+    ENGRAM_K_GATHER = 1,  /* engram_gather, or the fused hash + gather of engram_forward      */
+    ENGRAM_K_GEMM = 2,    /* projections W_k e of every branch with the gate partials fused
+                             (and W_v e on the fusion-kernel path)                           */
+    ENGRAM_K_FUSE = 3,    /* fusion-kernel path (short chunks, fp32): gated value, conv,
+                             residual, state                                                 */
+    ENGRAM_K_AUX = 4,     /* context / state bookkeeping                                      */
+    ENGRAM_K_GEMM_V = 5,  /* W_v e with gated value, conv, residual, state fused (prefill)     */
+    ENGRAM_K_GATE = 6,    /* gate per token and branch from the partial sums                  */
+    ENGRAM_K_COUNT = 7
 };
 
 typedef struct {

@@ -223,7 +223,7 @@ def test_forward_tiny_all_positions(B, mode, flags):
     assert np.abs(host(alpha) - ref_alpha).max() <= alpha_tol("f32")
 
 
-@pytest.mark.parametrize("n_branches", [1, 2, 4])
+@pytest.mark.parametrize("n_branches", [1, 2, 3, 4])
 @pytest.mark.parametrize("batch,seqlen", [(3, 77), (1, 1), (2, 130)])
 def test_forward_bf16_small_shapes_all_positions(B, n_branches, batch, seqlen):
     say("forward bf16 small", n_branches, batch, seqlen)
@@ -413,10 +413,22 @@ def test_profiling_counts_launches(B):
     dl.plan.engram_hash(dev_i32(toks), dl.comp_map, idx)
     torch.cuda.synchronize()
     prof = dl.plan.engram_profile_end()
-    for k, n in (("hash", 1), ("gather", 2), ("gemm", 2), ("fuse", 2)):
+    for k, n in (("hash", 1), ("gather", 2), ("gemm", 2), ("gate", 2), ("fuse", 2), ("gemm_v", 0)):
         assert prof[k]["launches"] == n, (k, prof)
-        assert prof[k]["total_ms"] > 0
+        assert (prof[k]["total_ms"] > 0) == (n > 0)
     assert prof["dropped"] == 0
+    # bf16 prefill: the W_k launch, then the W_v launch with the fusion
+    # step in its epilogue; chunks shorter than K_c - 1 use the fusion kernel
+    wl = small_wl(n_branches=2, batch=2, seqlen=50)
+    dl = make_device_layer(wl)
+    toks = W.make_tokens(wl)
+    dl.plan.engram_profile_begin(64)
+    forward(dl, toks)
+    forward(dl, np.ascontiguousarray(toks[:, :2]), h=_split(dl.h, 2, 2, 50, 0, 2))
+    torch.cuda.synchronize()
+    prof = dl.plan.engram_profile_end()
+    for k, n in (("hash", 0), ("gather", 2), ("gemm", 2), ("gate", 2), ("fuse", 1), ("gemm_v", 1)):
+        assert prof[k]["launches"] == n, (k, prof)
 
 
 def test_unsupported_bf16_shape_is_rejected(B):
