@@ -25,7 +25,7 @@ F32, BF16 = 0, 1
 CONV_LINEAR, CONV_SILU_SKIP = 0, 1
 OUT_DELTA = 1
 MAX_TABLES, MAX_BRANCHES = 32, 4
-KERNEL_NAMES = ("hash", "gather", "gemm", "fuse", "aux", "gemm_v", "gate")
+KERNEL_NAMES = ("hash", "gather", "gemm", "fuse", "aux", "gemm_v", "gate", "seam")
 
 
 class EngramError(RuntimeError):
@@ -53,7 +53,7 @@ class WeightsC(C.Structure):
 
 
 class ProfileC(C.Structure):
-    _fields_ = [("total_ms", C.c_double * 7), ("launches", C.c_int64 * 7), ("dropped", C.c_int64)]
+    _fields_ = [("total_ms", C.c_double * 8), ("launches", C.c_int64 * 8), ("dropped", C.c_int64)]
 
 
 _lib = None
@@ -90,7 +90,7 @@ def lib() -> C.CDLL:
         L.engram_forward.argtypes = [P, P, i32, i32, P, P, P, P, C.POINTER(WeightsC), P, P, P, u32,
                                      P, C.c_size_t, P, P]
         L.engram_profile_begin.restype = C.c_int
-        L.engram_profile_begin.argtypes = [P, i32]
+        L.engram_profile_begin.argtypes = [P, i32, u32]
         L.engram_profile_end.restype = C.c_int
         L.engram_profile_end.argtypes = [P, C.POINTER(ProfileC)]
         L.engram_synth_fill_table.restype = C.c_int
@@ -222,8 +222,10 @@ class Plan:
             workspace.numel() * workspace.element_size(),
             _ptr(bad_tokens, "bad_tokens", (torch.int32, torch.uint32)), _stream(stream)))
 
-    def engram_profile_begin(self, max_launches: int = 4096):
-        _check("engram_profile_begin", lib().engram_profile_begin(self._h, max_launches))
+    def engram_profile_begin(self, max_launches: int = 4096, kinds: Optional[Sequence[str]] = None):
+        """Time launches of the named kinds (KERNEL_NAMES; None: all)."""
+        mask = 0 if kinds is None else sum(1 << KERNEL_NAMES.index(k) for k in kinds)
+        _check("engram_profile_begin", lib().engram_profile_begin(self._h, max_launches, mask))
 
     def engram_profile_end(self) -> Dict[str, Dict[str, float]]:
         p = ProfileC()

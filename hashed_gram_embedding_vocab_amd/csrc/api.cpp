@@ -22,6 +22,7 @@ struct engram_plan_s {
     HashConsts hc{};
     // profiling
     bool prof_on = false;
+    uint32_t prof_mask = 0;
     int32_t prof_max = 0;
     int32_t prof_used = 0;
     int64_t prof_dropped = 0;
@@ -46,7 +47,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Layout {
-    size_t idx, emb, partials, alpha, v, kbuf, stage, total;
+    size_t idx, emb, partials, alpha, v, seam, kbuf, stage, total;
 };
 
 int32_t n_parts_of(const engram_plan_s &p) {
@@ -81,30 +82,34 @@ bool layout_of(const engram_plan_s &p, int64_t batch, int64_t seqlen, Layout &L)
     L.emb = take((size_t)n_tok * p.emb_dim * p.elem);
     L.partials = take((size_t)Br * n_parts_of(p) * 3 * n_tok * 4);
     L.alpha = take((size_t)Br * n_tok * 4);
-    L.v = fused_value_path(p, batch, seqlen) ? off : take((size_t)n_tok * d * 4);
+    const bool fused_v = fused_value_path(p, batch, seqlen);
+    L.v = fused_v ? off : take((size_t)n_tok * d * 4);
+    L.seam = fused_v ? take((size_t)((n_tok + kTokTile - 1) / kTokTile) * 6 * d * 4) : off;
     L.kbuf = p.cfg.dtype == ENGRAM_F32 ? take((size_t)Br * n_tok * d * 4) : off;
     L.stage = take((size_t)Br * batch * (p.cfg.conv_kernel - 1) * d * 4);
     L.total = off;
     return true;
 }
 
+// One timed library launch while profiling is on: hands a pair of the
+// plan's events to the kernel launches in its scope (see launch_kernel).
 struct Launch {
     engram_plan_s &p;
-    hipStream_t s;
-    int32_t kind;
     int32_t slot = -1;
-    Launch(engram_plan_s &pl, int32_t k, hipStream_t st) : p(pl), s(st), kind(k) {
-        if (!p.prof_on) return;
+    Launch(engram_plan_s &pl, int32_t kind, hipStream_t) : p(pl) {
+        if (!p.prof_on || !((p.prof_mask >> kind) & 1u)) return;
         if (p.prof_used < p.prof_max) {
             slot = p.prof_used++;
             p.prof_kind[slot] = kind;
-            hipEventRecord(p.prof_ev[2 * slot], s);
+            launch_events() = LaunchEvents{p.prof_ev[2 * slot], p.prof_ev[2 * slot + 1]};
         } else {
             ++p.prof_dropped;
         }
     }
     ~Launch() {
-        if (slot >= 0) hipEventRecord(p.prof_ev[2 * slot + 1], s);
+        if (slot < 0) return;
+        if (launch_events().start != nullptr) p.prof_kind[slot] = -1;  // nothing was launched
+        launch_events() = LaunchEvents{};
     }
 };
 
@@ -283,13 +288,38 @@ engram_status do_fuse(engram_plan_s &p, const void *emb, const void *h, int32_t 
         pv.conv_state = conv_state;
         pv.state_stage = stage;
         pv.alpha = gate;
+        pv.seam_v = reinterpret_cast<float *>(base + L.seam);
         pv.batch = batch;
         pv.seqlen = seqlen;
         pv.conv_k = p.cfg.conv_kernel;
         pv.conv_mode = p.cfg.conv_mode;
         pv.flags = flags;
-        Launch l(p, ENGRAM_K_GEMM_V, s);
-        launch_proj_v_fused_bf16(pv, s);
+        {
+            Launch l(p, ENGRAM_K_GEMM_V, s);
+            launch_proj_v_fused_bf16(pv, s);
+        }
+        const int32_t n_tiles = (int32_t)((n_tok + kTokTile - 1) / kTokTile);
+        if (n_tiles > 1) {
+            if (last_launch_status() != ENGRAM_OK) return ENGRAM_E_DEVICE;
+            SeamArgs sa{};
+            sa.seam_v = pv.seam_v;
+            sa.alpha = gate;
+            sa.h = h;
+            sa.out = out;
+            sa.conv_w = w->conv_w;
+            sa.conv_state = conv_state;
+            sa.n_tok = n_tok;
+            sa.n_tiles = n_tiles;
+            sa.batch = batch;
+            sa.seqlen = seqlen;
+            sa.d = p.cfg.d_model;
+            sa.n_branches = Br;
+            sa.conv_k = p.cfg.conv_kernel;
+            sa.conv_mode = p.cfg.conv_mode;
+            sa.flags = flags;
+            Launch l(p, ENGRAM_K_SEAM, s);
+            launch_seam(sa, s);
+        }
     } else {
         FuseArgs fa{};
         fa.v = pa.v;
@@ -313,13 +343,17 @@ engram_status do_fuse(engram_plan_s &p, const void *emb, const void *h, int32_t 
     if (stage) {
         Launch l(p, ENGRAM_K_AUX, s);
         const size_t bytes = (size_t)Br * batch * (p.cfg.conv_kernel - 1) * p.cfg.d_model * 4;
-        if (hipMemcpyAsync(conv_state, stage, bytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
-            return ENGRAM_E_DEVICE;
+        launch_copy_f32(stage, conv_state, (int64_t)(bytes / 4), s);
     }
     return ENGRAM_OK;
 }
 
 }  // namespace
+
+LaunchEvents &engram::launch_events() {
+    static thread_local LaunchEvents ev;
+    return ev;
+}
 
 extern "C" {
 
@@ -448,8 +482,10 @@ engram_status engram_forward(engram_plan p, const int32_t *d_tokens, int32_t bat
                    stream);
 }
 
-engram_status engram_profile_begin(engram_plan p, int32_t max_launches) {
+engram_status engram_profile_begin(engram_plan p, int32_t max_launches, uint32_t kind_mask) {
     if (!p || max_launches <= 0) return ENGRAM_E_INVALID_ARG;
+    if (kind_mask >> ENGRAM_K_COUNT) return ENGRAM_E_INVALID_ARG;
+    p->prof_mask = kind_mask ? kind_mask : (1u << ENGRAM_K_COUNT) - 1u;
     if ((int32_t)p->prof_ev.size() < 2 * max_launches) {
         for (hipEvent_t e : p->prof_ev) hipEventDestroy(e);
         p->prof_ev.assign(2 * max_launches, nullptr);
@@ -470,6 +506,7 @@ engram_status engram_profile_end(engram_plan p, engram_profile *out) {
     p->prof_on = false;
     engram_status st = ENGRAM_OK;
     for (int32_t i = 0; i < p->prof_used; ++i) {
+        if (p->prof_kind[i] < 0) continue;
         float ms = 0.f;
         if (hipEventSynchronize(p->prof_ev[2 * i + 1]) != hipSuccess ||
             hipEventElapsedTime(&ms, p->prof_ev[2 * i], p->prof_ev[2 * i + 1]) != hipSuccess) {

@@ -2,12 +2,32 @@
 // host-side launchers.  Not part of the public ABI (see include/engram.h).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "engram.h"
 
 namespace engram {
+
+// ---------------------------------------------------------------- launches
+// Events of the launch being timed (profiling on), else null.  Every kernel
+// of the library is launched through launch_kernel, which hands them to
+// hipExtLaunchKernel: the dispatch packet itself takes the timestamps, so
+// timing adds no packets to the stream.  The start event goes to the first
+// kernel of a timed launch, the stop event to every kernel (the last wins).
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents &launch_events();  // this thread's
+
+template <typename F, typename... Args>
+inline void launch_kernel(F kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+    LaunchEvents &ev = launch_events();
+    hipEvent_t start = ev.start;
+    ev.start = nullptr;
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, start, ev.stop, 0, args...);
+}
 
 constexpr int kMaxTables = ENGRAM_MAX_TABLES;
 constexpr int kMaxBranches = ENGRAM_MAX_BRANCHES;
@@ -123,6 +143,7 @@ struct ProjArgs {
     const float *conv_state;               // [B_r][batch][K_c-1][d] or null
     float *state_stage;                    // [B_r][batch][K_c-1][d] or null
     const float *alpha;                    // [B_r][n_tok], from the gate kernel
+    float *seam_v;                         // [token tiles][6][d] fp32 v of each tile's first and last 3 rows
     int32_t batch, seqlen, conv_k, conv_mode;
     uint32_t flags;
 };
@@ -134,6 +155,9 @@ constexpr int kPartCols = 128;  // columns of d summed into one gate partial (bf
 void launch_proj_bf16(const ProjArgs &a, hipStream_t s);
 // W_v projection with the gate, gated value, depthwise causal conv, residual
 // and conv-state update fused into the epilogue (needs seqlen >= K_c - 1).
+// Rows 0..2 of each 256-token tile whose conv history lies in the previous
+// tile are left to launch_seam.
+constexpr int kTokTile = 256;
 void launch_proj_v_fused_bf16(const ProjArgs &a, hipStream_t s);
 void launch_proj_f32(const ProjArgs &a, hipStream_t s);  // k into kbuf, v, then partials
 
@@ -150,6 +174,22 @@ struct GateArgs {
 
 void launch_gate(const GateArgs &a, hipStream_t s);
 
+// The rows launch_proj_v_fused_bf16 leaves: tile rows 0..2 (tile > 0) whose
+// conv history reaches into the previous tile, from both tiles' saved v.
+struct SeamArgs {
+    const float *seam_v;       // [n_tiles][6][d]
+    const float *alpha;        // [B_r][n_tok]
+    const void *h;             // [B_r][n_tok][d] bf16
+    void *out;                 // [B_r][n_tok][d] bf16
+    const float *conv_w;       // [d][K_c]
+    const float *conv_state;   // [B_r][batch][K_c-1][d] or null
+    int64_t n_tok;
+    int32_t n_tiles, batch, seqlen, d, n_branches, conv_k, conv_mode;
+    uint32_t flags;
+};
+
+void launch_seam(const SeamArgs &a, hipStream_t s);
+
 struct FuseArgs {
     const float *v;            // [n_tok][d] fp32
     const float *alpha;        // [B_r][n_tok], from the gate kernel
@@ -165,6 +205,9 @@ struct FuseArgs {
 void launch_fuse(const FuseArgs &a, engram_dtype dt, hipStream_t s);
 
 // ---------------------------------------------------------------- synthetic tables
+// ---------------------------------------------------------------- copies
+void launch_copy_f32(const float *src, float *dst, int64_t n, hipStream_t s);  // n % 4 == 0
+
 void launch_synth_fill(engram_dtype dt, uint64_t seed, int32_t tau, int64_t rows, int32_t head_dim,
                        void *table, hipStream_t s);
 

@@ -1,5 +1,5 @@
-// fuse.hip -- the gate and, for short chunks and the fp32 path, the rest of
-// Engram's fusion step on gfx950 ([club] 1.(2) 上下文感知的门控机制, last two
+// fuse.hip -- the gate, the seam rows of the fused value projection and, for
+// short chunks and the fp32 path, the rest of Engram's fusion step on gfx950 ([club] 1.(2) 上下文感知的门控机制, last two
 // bullets; [csdn] Engram 到底怎么工作的, third and fourth steps).
 //
 // gate_kernel: the scalar gate per token and branch from the partial sums the
@@ -181,9 +181,128 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
 
 }  // namespace
 
+// One thread per (seam row, 4 channels), branches in a loop.  Tile T > 0,
+// row rho < 3 (token t = 256 T + rho) belongs here when its sequence started
+// before the tile (position > rho): u_{t-s} for s > rho then comes from the
+// previous tile's last rows.  Same expressions, in the same order, as the
+// projection kernel's epilogue, so the bits match the unsplit computation.
+template <int BR, bool SILU>
+__global__ __launch_bounds__(256) void seam_kernel(SeamArgs a) {
+    const int d = a.d;
+    const int quads = d / 4;
+    const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (x >= (int64_t)(a.n_tiles - 1) * 3 * quads) return;
+    const int c0 = 4 * (int)(x % quads);
+    const int64_t rt = x / quads;
+    const int rho = (int)(rt % 3);
+    const int T = 1 + (int)(rt / 3);
+    const int64_t t = (int64_t)T * kTokTile + rho;
+    if (t >= a.n_tok) return;
+    const int b = (int)(t / a.seqlen);
+    const int pos = (int)(t - (int64_t)b * a.seqlen);
+    if (pos <= rho) return;  // the projection kernel finished this row
+    const int kc = a.conv_k;
+    const int64_t n_tok = a.n_tok;
+
+    // Every load below is issued unconditionally from an index that is
+    // always valid (t - s >= 253 here), then selected: one memory round trip.
+    // v of tokens t - s (s = 0..3): seam row rho - s of tile T, or row
+    // 6 + rho - s of tile T-1 (its last three rows)
+    f32x4_t vs[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int k = rho - s;
+        const int64_t row = k >= 0 ? (int64_t)T * 6 + k : (int64_t)(T - 1) * 6 + 6 + k;
+        vs[s] = *reinterpret_cast<const f32x4_t *>(a.seam_v + row * d + c0);
+    }
+    f32x4_t tap[4];  // tap[r][s] multiplies u_{t-s} of channel c0 + r
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const float w = a.conv_w[(int64_t)(c0 + r) * kc + max(kc - 1 - s, 0)];
+            tap[r][s] = s < kc ? w : 0.f;
+        }
+    const bool delta = (a.flags & ENGRAM_OUT_DELTA) != 0;
+    float al[BR][4];
+    u32x2_t h2[BR];
+#pragma unroll
+    for (int m = 0; m < BR; ++m) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) al[m][s] = a.alpha[m * n_tok + t - s];
+        h2[m] = *reinterpret_cast<const u32x2_t *>(reinterpret_cast<const uint16_t *>(a.h) +
+                                                   ((int64_t)m * n_tok + t) * d + c0);
+    }
+
+#pragma unroll
+    for (int m = 0; m < BR; ++m) {
+        float u[4][4];  // u[s][r] = u_{t-s} of channel c0 + r
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            if (pos - s >= 0) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) u[s][r] = al[m][s] * vs[s][r];
+            } else if (a.conv_state && s <= kc - 1) {
+                const float *st = a.conv_state + (((int64_t)m * a.batch + b) * (kc - 1) + (kc - 1) + pos - s) * d + c0;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) u[s][r] = st[r];
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) u[s][r] = 0.f;
+            }
+        }
+        float o[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float conv = tap[r][0] * u[0][r] + tap[r][1] * u[1][r] + tap[r][2] * u[2][r] + tap[r][3] * u[3][r];
+            const float y = SILU ? u[0][r] + conv * sigmoidf_(conv) : conv;
+            const uint32_t hw = h2[m][r >> 1];
+            const float hval = bf16_to_f32((r & 1) ? (hw >> 16) : (hw & 0xFFFFu));
+            o[r] = delta ? y : hval + y;
+        }
+        *reinterpret_cast<u32x2_t *>(reinterpret_cast<uint16_t *>(a.out) + ((int64_t)m * n_tok + t) * d + c0) =
+            u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    }
+}
+
+void launch_seam(const SeamArgs &a, hipStream_t s) {
+    const int64_t items = (int64_t)(a.n_tiles - 1) * 3 * (a.d / 4);
+    if (items <= 0) return;
+    const dim3 grid((unsigned)((items + 255) / 256));
+    const bool silu = a.conv_mode == ENGRAM_CONV_SILU_SKIP;
+#define ENGRAM_SEAM_LAUNCH(BR)                                                                    \
+    do {                                                                                          \
+        if (silu)                                                                                 \
+            launch_kernel((seam_kernel<BR, true>), grid, dim3(256), s, a);                 \
+        else                                                                                      \
+            launch_kernel((seam_kernel<BR, false>), grid, dim3(256), s, a);                \
+    } while (0)
+    switch (a.n_branches) {
+        case 1: ENGRAM_SEAM_LAUNCH(1); break;
+        case 2: ENGRAM_SEAM_LAUNCH(2); break;
+        case 3: ENGRAM_SEAM_LAUNCH(3); break;
+        default: ENGRAM_SEAM_LAUNCH(4); break;
+    }
+#undef ENGRAM_SEAM_LAUNCH
+}
+
+__global__ __launch_bounds__(256) void copy_f32_kernel(const f32x4_t *src, f32x4_t *dst, int64_t n4) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x)
+        dst[i] = src[i];
+}
+
+void launch_copy_f32(const float *src, float *dst, int64_t n, hipStream_t s) {
+    const int64_t n4 = n / 4;
+    int64_t blocks = (n4 + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks < 1) blocks = 1;
+    launch_kernel(copy_f32_kernel, dim3((unsigned)blocks), dim3(256), s, reinterpret_cast<const f32x4_t *>(src),
+                  reinterpret_cast<f32x4_t *>(dst), n4);
+}
+
 void launch_gate(const GateArgs &a, hipStream_t s) {
     const dim3 grid((unsigned)((a.n_tok + 255) / 256), (unsigned)a.n_branches);
-    hipLaunchKernelGGL(gate_kernel, grid, dim3(256), 0, s, a);
+    launch_kernel(gate_kernel, grid, dim3(256), s, a);
 }
 
 void launch_fuse(const FuseArgs &a, engram_dtype dt, hipStream_t s) {
@@ -195,9 +314,9 @@ void launch_fuse(const FuseArgs &a, engram_dtype dt, hipStream_t s) {
 #define ENGRAM_FUSE_LAUNCH(BR)                                                                   \
     do {                                                                                         \
         if (dt == ENGRAM_BF16)                                                                   \
-            hipLaunchKernelGGL((fuse_kernel<true, BR>), grid, dim3(threads), 0, s, a);            \
+            launch_kernel((fuse_kernel<true, BR>), grid, dim3(threads), s, a);            \
         else                                                                                     \
-            hipLaunchKernelGGL((fuse_kernel<false, BR>), grid, dim3(threads), 0, s, a);           \
+            launch_kernel((fuse_kernel<false, BR>), grid, dim3(threads), s, a);           \
     } while (0)
     switch (a.n_branches) {
         case 1: ENGRAM_FUSE_LAUNCH(1); break;

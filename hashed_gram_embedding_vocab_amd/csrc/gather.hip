@@ -127,7 +127,7 @@ void launch_hash_gather(const HashConsts &hc, const GatherConsts &gc, const int3
     const int tpb = kThreads / gc.n_tables;
     const int64_t blocks = (n_tok + tpb - 1) / tpb;
     const uint64_t magic_seq = seqlen <= 1 ? 0 : (uint64_t)(((unsigned __int128)1 << 64) / (unsigned)seqlen) + 1;
-    hipLaunchKernelGGL(hash_gather_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, hc, gc, tokens, n_tok,
+    launch_kernel(hash_gather_kernel, dim3((unsigned)blocks), dim3(kThreads), s, hc, gc, tokens, n_tok,
                        seqlen, magic_seq, tpb, comp_map, prev_ctx, bad, reinterpret_cast<u32x4_t *>(emb));
 }
 
@@ -136,7 +136,7 @@ void launch_gather(const GatherConsts &gc, const uint32_t *idx, int64_t n_tok, v
     const int64_t total = n_tok * gc.tok_chunks;
     const int64_t per_block = (int64_t)kThreads * kUnroll;
     const int64_t blocks = (total + per_block - 1) / per_block;
-    hipLaunchKernelGGL(gather_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, gc, idx, total,
+    launch_kernel(gather_kernel, dim3((unsigned)blocks), dim3(kThreads), s, gc, idx, total,
                        reinterpret_cast<u32x4_t *>(emb));
 }
 

@@ -108,13 +108,13 @@ void launch_hash(const HashConsts &hc, const int32_t *tokens, int32_t batch, int
                  hipStream_t s) {
     const int64_t waves = (int64_t)batch * ((seqlen + kWave - 1) / kWave);
     const int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL(hash_kernel, dim3((unsigned)blocks), dim3(kWave * kWavesPerBlock), 0, s, hc,
+    launch_kernel(hash_kernel, dim3((unsigned)blocks), dim3(kWave * kWavesPerBlock), s, hc,
                        tokens, batch, seqlen, comp_map, prev_ctx, idx, bad);
 }
 
 void launch_ctx_update(const int32_t *tokens, int32_t batch, int32_t seqlen, const int32_t *comp_map,
                        int32_t vocab, int32_t vocab_comp, int32_t *prev_ctx, hipStream_t s) {
-    hipLaunchKernelGGL(ctx_update_kernel, dim3((batch + 255) / 256), dim3(256), 0, s, tokens, batch,
+    launch_kernel(ctx_update_kernel, dim3((batch + 255) / 256), dim3(256), s, tokens, batch,
                        seqlen, comp_map, vocab, vocab_comp, prev_ctx);
 }
 

@@ -59,8 +59,7 @@ constexpr int FN = WN / 16, FT = WT / 16;
 constexpr int kBlockBytes = 1024;                       // 16 rows x 32 bf16
 constexpr int kOperandBytes = (BN / 16) * kBlockBytes;  // 16 KB per operand per stage
 constexpr int kBlocksPerWave = (BN / 16) / kWaves;          // row blocks each wave fills, per operand and stage
-constexpr int kHalo = 3;              // rows of conv history a mode-1 token tile recomputes
-constexpr int kStrideV = BT - kHalo;  // token tile stride in mode 1
+constexpr int kHalo = 3;              // rows of conv history (K_c - 1 at most)
 constexpr int kXcds = 8;
 #ifndef ENGRAM_PROJ_GROUP_T
 #define ENGRAM_PROJ_GROUP_T 4
@@ -68,6 +67,7 @@ constexpr int kXcds = 8;
 constexpr int kGroupT = ENGRAM_PROJ_GROUP_T;  // token tiles sharing each weight tile in the launch order
 
 static_assert(BN == BT, "one block-load pattern serves both operands");
+static_assert(BT == kTokTile, "the seam kernel assumes this token tile");
 
 struct __attribute__((aligned(1024))) Stage {
     unsigned char w[kOperandBytes];
@@ -149,7 +149,11 @@ __device__ __forceinline__ void wait_lgkm0() {
 // nl + 16i + 4*(lane/16) + r and token t0 + 64g + 4l + j.  For the conv,
 // u_{t-s} then lies in the same lane (block j - s) when s <= j, else in lane
 // row l - 1 (block j - s + 4, one DPP row shift), or for lane row 0 among the
-// previous group's last three tokens, which pass through LDS.
+// previous group's last three tokens, which pass through LDS.  The first
+// group's first three rows need the previous tile's last three tokens unless a
+// sequence starts close enough (position <= row); those rows are left to
+// the seam kernel, which finishes them from the fp32 v of both tiles' edge
+// rows that every block saves (seam_v).
 //
 // h arrives in LDS by DMA, one 8 KB chunk (64 tokens x 64 channels of one
 // branch) per wave at a time, two chunks in flight, so the loads need no
@@ -164,7 +168,7 @@ template <int BR, bool SILU>
 __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t (&acc)[FN][FT],
                                                      float (&alpha_s)[BR][BT], float *halo, float *taps,
                                                      unsigned char *hA, unsigned char *hB, int wave,
-                                                     int lane, int nl, int n0, int64_t t0) {
+                                                     int lane, int nl, int n0, int tile_t, int64_t t0) {
     const int d = a.d;
     const int l16 = lane & 15;
     const int sub = 4 * (lane >> 4);
@@ -192,9 +196,27 @@ __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t 
             for (int i = 0; i < FN; ++i)
                 *reinterpret_cast<f32x4_t *>(&halo[(wave * kHalo + (j - 1)) * WN + 16 * i + sub]) = acc[i][j];
     }
+    // v of the tile's first and last three rows, for the seam kernel (issued
+    // before the chunk loads below, so they do not enter the waits there)
+    // (seam row k of tile T is at seam_v[(6T + k) * d]: rows 0..2 are tile
+    // rows 0..2, blocks 0..2 of lane row 0 of the first group; rows 3..5 are
+    // tile rows BT-3..BT-1, blocks 1..3 of lane row 15 of the last group)
+    float *sv = a.seam_v + (int64_t)tile_t * 6 * d + nl + sub;
+    if (g == 0 && l16 == 0) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+#pragma unroll
+            for (int i = 0; i < FN; ++i) *reinterpret_cast<f32x4_t *>(sv + (int64_t)j * d + 16 * i) = acc[i][j];
+    }
+    if (g == kWaves / 2 - 1 && l16 == 15) {
+#pragma unroll
+        for (int j = 1; j < FT; ++j)
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+                *reinterpret_cast<f32x4_t *>(sv + (int64_t)(2 + j) * d + 16 * i) = acc[i][j];
+    }
     __syncthreads();  // taps and halo written; every wave is done with the stage buffers
-    // the first group's leading tokens are the tile's recomputed history
-    // (never stored), so it needs nothing from a neighbour
+    // the first group's rows before its own take no values from a neighbour
     // (it reads its own halo rows, finite, times a zero gate: no branch)
     const bool has_prev = g > 0;
     const float *prev = halo + (has_prev ? wave - 2 : wave) * kHalo * WN;
@@ -220,10 +242,12 @@ __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t 
         const int tc = valid ? (int)tt : 0;
         const int bseq = tc / a.seqlen;
         pos[j] = tc - bseq * a.seqlen;
-        const bool store = valid && row >= kHalo;
-        to_state[j] = store && pos[j] >= a.seqlen - (kc - 1);
+        // rows whose conv history reaches into the previous tile are the
+        // seam kernel's (their state rows, plain gated values, are written here)
+        const bool store = valid && !(row < kHalo && pos[j] > row);
+        to_state[j] = valid && pos[j] >= a.seqlen - (kc - 1);
         // rows that need carried state (sequence start) or write it (sequence end)
-        edge[j] = __ballot(store && (pos[j] < kHalo || to_state[j])) != 0;
+        edge[j] = __ballot(valid && (pos[j] < kHalo || to_state[j])) != 0;
         stoff[j] = store ? (uint32_t)((tc * (int64_t)d + nl + sub) * 2) : 0x80000000u;
         // byte offset of state row pos of sequence bseq, modulo 2^32: exact
         // (in range) for the rows that read or write the state
@@ -397,15 +421,14 @@ __global__ __launch_bounds__(kThreads, 1) void proj_bf16_kernel(ProjArgs a) {
     const int K = a.K;
     const int d = a.d;
     const int n_total = a.n_mats * d;
-    const int stride_t = MODE == 1 ? kStrideV : BT;
     const int n_tiles_n = (n_total + BN - 1) / BN;
-    const int n_tiles_t = (int)((a.n_tok + stride_t - 1) / stride_t);
+    const int n_tiles_t = (int)((a.n_tok + BT - 1) / BT);
     int tile_n, tile_t;
     tile_of(blockIdx.x, gridDim.x, n_tiles_n, n_tiles_t, tile_n, tile_t);
     const int n0 = tile_n * BN;
-    // first token row of the tile; in mode 1 the first kHalo rows are the
+    // first token row of the tile
     // previous tile's last tokens (negative for the first tile: never stored)
-    const int64_t t0 = (int64_t)tile_t * stride_t - (MODE == 1 ? kHalo : 0);
+    const int64_t t0 = (int64_t)tile_t * BT;
 
     // ---- this lane's share of the block loads.  Wave w fills row blocks
     //      2w and 2w+1 of each operand.
@@ -608,7 +631,7 @@ __global__ __launch_bounds__(kThreads, 1) void proj_bf16_kernel(ProjArgs a) {
         // each wave's two chunk buffers: 8 KB of st0/st1 (A) and of st2/st3 (B)
         unsigned char *hA = reinterpret_cast<unsigned char *>(wave < 4 ? &st0 : &st1) + (wave & 3) * 8192;
         unsigned char *hB = reinterpret_cast<unsigned char *>(wave < 4 ? &st2 : &st3) + (wave & 3) * 8192;
-        fused_value_epilogue<BR, SILU>(a, acc, alpha_s, halo_s, taps_s, hA, hB, wave, lane, nl, n0, t0);
+        fused_value_epilogue<BR, SILU>(a, acc, alpha_s, halo_s, taps_s, hA, hB, wave, lane, nl, n0, tile_t, t0);
     }
 }
 
@@ -619,19 +642,19 @@ void launch_proj_bf16(const ProjArgs &a, hipStream_t s) {
     const int n_tiles_n = (n_total + BN - 1) / BN;
     const int64_t n_tiles_t = (a.n_tok + BT - 1) / BT;
     const int64_t blocks = (int64_t)n_tiles_n * n_tiles_t;
-    hipLaunchKernelGGL((proj_bf16_kernel<0, 1, false>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    launch_kernel((proj_bf16_kernel<0, 1, false>), dim3((unsigned)blocks), dim3(kThreads), s, a);
 }
 
 void launch_proj_v_fused_bf16(const ProjArgs &a, hipStream_t s) {
     const int n_tiles_n = (a.d + BN - 1) / BN;
-    const int64_t n_tiles_t = (a.n_tok + kStrideV - 1) / kStrideV;
+    const int64_t n_tiles_t = (a.n_tok + BT - 1) / BT;
     const dim3 grid((unsigned)((int64_t)n_tiles_n * n_tiles_t));
 #define ENGRAM_PROJ_V_LAUNCH(BR)                                                                      \
     do {                                                                                              \
         if (a.conv_mode == ENGRAM_CONV_SILU_SKIP)                                                     \
-            hipLaunchKernelGGL((proj_bf16_kernel<1, BR, true>), grid, dim3(kThreads), 0, s, a);        \
+            launch_kernel((proj_bf16_kernel<1, BR, true>), grid, dim3(kThreads), s, a);        \
         else                                                                                          \
-            hipLaunchKernelGGL((proj_bf16_kernel<1, BR, false>), grid, dim3(kThreads), 0, s, a);       \
+            launch_kernel((proj_bf16_kernel<1, BR, false>), grid, dim3(kThreads), s, a);       \
     } while (0)
     switch (a.n_branches) {
         case 1: ENGRAM_PROJ_V_LAUNCH(1); break;

@@ -102,8 +102,8 @@ __global__ __launch_bounds__(256) void gate_sums_f32_kernel(ProjArgs a) {
 void launch_proj_f32(const ProjArgs &a, hipStream_t s) {
     const int n_total = (a.n_branches + 1) * a.d;
     dim3 grid((n_total + TN - 1) / TN, (unsigned)((a.n_tok + TT - 1) / TT));
-    hipLaunchKernelGGL(proj_f32_kernel, grid, dim3(256), 0, s, a);
-    hipLaunchKernelGGL(gate_sums_f32_kernel, dim3((unsigned)a.n_tok, a.n_branches), dim3(256), 0, s, a);
+    launch_kernel(proj_f32_kernel, grid, dim3(256), s, a);
+    launch_kernel(gate_sums_f32_kernel, dim3((unsigned)a.n_tok, a.n_branches), dim3(256), s, a);
 }
 
 }  // namespace engram

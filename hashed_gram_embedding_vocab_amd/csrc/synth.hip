@@ -68,10 +68,10 @@ void launch_synth_fill(engram_dtype dt, uint64_t seed, int32_t tau, int64_t rows
     int64_t blocks = (total + 255) / 256;
     if (blocks > 256 * 1024) blocks = 256 * 1024;
     if (dt == ENGRAM_BF16)
-        hipLaunchKernelGGL(synth_fill_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, seed, tau,
+        launch_kernel(synth_fill_kernel<true>, dim3((unsigned)blocks), dim3(256), s, seed, tau,
                            rows, groups, table);
     else
-        hipLaunchKernelGGL(synth_fill_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, seed, tau,
+        launch_kernel(synth_fill_kernel<false>, dim3((unsigned)blocks), dim3(256), s, seed, tau,
                            rows, groups, table);
 }
 

@@ -107,7 +107,8 @@ enum {
     ENGRAM_K_AUX = 4,     /* context / state bookkeeping                                      */
     ENGRAM_K_GEMM_V = 5,  /* W_v e with gated value, conv, residual, state fused (prefill)     */
     ENGRAM_K_GATE = 6,    /* gate per token and branch from the partial sums                  */
-    ENGRAM_K_COUNT = 7
+    ENGRAM_K_SEAM = 7,    /* rows at 256-token tile seams left by ENGRAM_K_GEMM_V             */
+    ENGRAM_K_COUNT = 8
 };
 
 typedef struct {
@@ -204,12 +205,14 @@ ENGRAM_API engram_status engram_forward(engram_plan p, const int32_t *d_tokens, 
                              size_t workspace_bytes, uint32_t *d_bad_tokens, hipStream_t stream);
 
 /*
- * Profiling: while on, every kernel the plan launches is bracketed by HIP
- * events recorded on the launch stream (at most max_launches launches are
- * timed).  engram_profile_end synchronises on those events, fills *out with
- * per-kernel totals and turns profiling off.  Not thread-safe per plan.
+ * Profiling: while on, each launch of a kind selected by kind_mask (bit k
+ * selects ENGRAM_K_* value k; 0 selects every kind) is timed by a pair of HIP
+ * events that the kernel's own dispatch records (hipExtLaunchKernel), on the
+ * launch stream, at most max_launches launches.  Launches of other kinds run
+ * untimed.  engram_profile_end synchronises on those events, fills *out with
+ * per-kind totals and turns profiling off.  Not thread-safe per plan.
  */
-ENGRAM_API engram_status engram_profile_begin(engram_plan p, int32_t max_launches);
+ENGRAM_API engram_status engram_profile_begin(engram_plan p, int32_t max_launches, uint32_t kind_mask);
 ENGRAM_API engram_status engram_profile_end(engram_plan p, engram_profile *out);
 
 #ifdef __cplusplus

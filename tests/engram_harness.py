@@ -52,13 +52,24 @@ def oracle_layer(wl: W.Workload, li: W.LayerInputs, idx: np.ndarray, batch: int,
 
 
 def sample_positions(batch: int, seqlen: int, n: int, seed: int = 0) -> np.ndarray:
-    """Edge positions (sequence starts, tile and block seams, ends) plus random ones."""
+    """Edge positions (sequence starts, tile and block seams, ends) plus random ones.
+
+    Seams are sequence-relative (positions around 32 and 128) and global:
+    the tokens around multiples of 256, where one token tile of the
+    projection kernels ends and the next begins."""
     rng = np.random.default_rng(seed)
     cand = set()
     for b in {0, batch - 1}:
         for t in (0, 1, 2, 3, 31, 32, 33, 127, 128, 129, seqlen - 2, seqlen - 1):
             if 0 <= t < seqlen:
                 cand.add(b * seqlen + t)
+    n_tok = batch * seqlen
+    n_seams = (n_tok - 1) // 256
+    for k in sorted({1, 2, (n_seams + 1) // 2, n_seams}):
+        for dt in (-1, 0, 1, 2, 3):
+            g = 256 * k + dt
+            if 1 <= k <= n_seams and 0 <= g < n_tok:
+                cand.add(g)
     while len(cand) < n:
         cand.add(int(rng.integers(0, batch * seqlen)))
     return np.array(sorted(cand), np.int64)

@@ -224,7 +224,7 @@ def test_forward_tiny_all_positions(B, mode, flags):
 
 
 @pytest.mark.parametrize("n_branches", [1, 2, 3, 4])
-@pytest.mark.parametrize("batch,seqlen", [(3, 77), (1, 1), (2, 130)])
+@pytest.mark.parametrize("batch,seqlen", [(3, 77), (1, 1), (2, 130), (3, 300), (3, 127)])
 def test_forward_bf16_small_shapes_all_positions(B, n_branches, batch, seqlen):
     say("forward bf16 small", n_branches, batch, seqlen)
     wl = small_wl(n_branches=n_branches, batch=batch, seqlen=seqlen)
@@ -417,18 +417,21 @@ def test_profiling_counts_launches(B):
         assert prof[k]["launches"] == n, (k, prof)
         assert (prof[k]["total_ms"] > 0) == (n > 0)
     assert prof["dropped"] == 0
-    # bf16 prefill: the W_k launch, then the W_v launch with the fusion
-    # step in its epilogue; chunks shorter than K_c - 1 use the fusion kernel
-    wl = small_wl(n_branches=2, batch=2, seqlen=50)
-    dl = make_device_layer(wl)
-    toks = W.make_tokens(wl)
-    dl.plan.engram_profile_begin(64)
-    forward(dl, toks)
-    forward(dl, np.ascontiguousarray(toks[:, :2]), h=_split(dl.h, 2, 2, 50, 0, 2))
-    torch.cuda.synchronize()
-    prof = dl.plan.engram_profile_end()
-    for k, n in (("hash", 0), ("gather", 2), ("gemm", 2), ("gate", 2), ("fuse", 1), ("gemm_v", 1)):
-        assert prof[k]["launches"] == n, (k, prof)
+    # bf16 prefill: the W_k launch, the gate, then the W_v launch with the
+    # fusion step in its epilogue and, past one 256-token tile, the seam
+    # rows; chunks shorter than K_c - 1 use the fusion kernel
+    for seqlen, seams in ((50, 0), (300, 1)):
+        wl = small_wl(n_branches=2, batch=2, seqlen=seqlen)
+        dl = make_device_layer(wl)
+        toks = W.make_tokens(wl)
+        dl.plan.engram_profile_begin(64)
+        forward(dl, toks)
+        forward(dl, np.ascontiguousarray(toks[:, :2]), h=_split(dl.h, 2, 2, seqlen, 0, 2))
+        torch.cuda.synchronize()
+        prof = dl.plan.engram_profile_end()
+        for k, n in (("hash", 0), ("gather", 2), ("gemm", 2), ("gate", 2), ("fuse", 1), ("gemm_v", 1),
+                     ("seam", seams)):
+            assert prof[k]["launches"] == n, (seqlen, k, prof)
 
 
 def test_unsupported_bf16_shape_is_rejected(B):
