@@ -60,21 +60,28 @@ def src_digest(*names):
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str, kernel_src: str):
-    """HBM bytes per launch of the dominant kernel from committed rocprofv3
-    counter runs, if they were taken on the current kernel source."""
+KERNEL_SRC = {"gemm": "proj_bf16.hip", "gemm_v": "proj_bf16.hip", "gather": "gather.hip",
+              "gate": "fuse.hip", "seam": "fuse.hip", "fuse": "fuse.hip"}
+
+
+def load_traffic(workload: str, kind: str):
+    """HBM bytes per launch of one kernel from committed rocprofv3 counter
+    runs (FETCH_SIZE, WRITE_SIZE scaled by a plain-copy calibration), if they
+    were taken on the kernel's current source."""
     path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        t = json.load(f)
-    if t.get("src_sha") != src_digest(kernel_src):
+        t = json.load(f).get("kernels", {}).get(kind)
+    if t is None or t.get("src_sha") != src_digest(KERNEL_SRC[kind]):
         return None
     return t
 
 
 def cpu_baseline(wl, budget_s: float):
-    """The oracle, as it stands, on a contiguous block of sequence 0."""
+    """The oracle, as it stands, on whole sequences of the workload (as many
+    as about budget_s of single-threaded CPU work takes, at least one
+    32-token slice), timed end to end: hash, gather, projections, gate, conv."""
     import numpy as np
 
     import oracle
@@ -82,29 +89,37 @@ def cpu_baseline(wl, budget_s: float):
 
     dt = oracle.BF16 if wl.dtype == "bf16" else oracle.F32
     seqlen = wl.seqlen
-    li = W.make_layer_inputs(wl, 0, batch=1, seqlen=seqlen)
     comp = W.compression_map(wl.vocab, wl.vocab_comp, wl.seed(1))
-    toks = W.make_tokens(wl, batch=1, seqlen=seqlen)
 
-    def run(n):
+    def run(n_seq, n_pos):
+        """n_seq sequences, the first n_pos positions of each."""
+        li = W.make_layer_inputs(wl, 0, batch=n_seq, seqlen=seqlen)
+        toks = W.make_tokens(wl, batch=n_seq, seqlen=seqlen)[:, :n_pos]
+        h = li.h.reshape(wl.n_branches, n_seq, seqlen, -1)[:, :, :n_pos].reshape(wl.n_branches, n_seq * n_pos, -1)
         t = time.perf_counter()
-        idx, _, _ = oracle.hash_tokens(toks[:, :n], comp, wl.vocab, wl.vocab_comp, wl.heads,
+        idx, _, _ = oracle.hash_tokens(np.ascontiguousarray(toks), comp, wl.vocab, wl.vocab_comp, wl.heads,
                                        wl.primes(), li.hash_seed, orders=wl.orders)
         emb = oracle.gather_synth(idx, wl.head_dim, li.table_seed, dt)
-        h = li.h[:, :n]
-        L = oracle.Layer(emb, h, li.w_k, li.w_v, li.gamma_h, li.gamma_k, li.conv_w, 1, n, dt)
-        L.forward_range(0, 0, n)
+        L = oracle.Layer(emb, np.ascontiguousarray(h), li.w_k, li.w_v, li.gamma_h, li.gamma_k, li.conv_w, n_seq,
+                         n_pos, dt)
+        for b in range(n_seq):
+            L.forward_range(b, 0, n_pos)
         return time.perf_counter() - t
 
     n0 = min(32, seqlen)
-    t0 = run(n0)
-    n = int(min(seqlen, max(n0, n0 * budget_s / max(t0, 1e-6))))
-    el = run(n)
+    t0 = run(1, n0)
+    want = max(n0, int(n0 * budget_s / max(t0, 1e-6)))  # tokens for about budget_s
+    if want <= seqlen:
+        n_seq, n_pos = 1, want
+    else:
+        n_seq, n_pos = min(wl.batch, -(-want // seqlen)), seqlen
+    el = run(n_seq, n_pos)
+    n = n_seq * n_pos
     layers = len(wl.layers)
     tok_s = n / el / layers  # a step runs every layer over each token
     return {"value": tok_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": "positions 0..%d of sequence 0 (%d tokens, %d layer(s) of %d per step; "
-                      "single-threaded C, fp64), %.1f s" % (n - 1, n, 1, layers, el)}
+            "sample": "positions 0..%d of %d sequence(s) (%d tokens, 1 layer of the %d per step; "
+                      "single-threaded C, fp64), %.1f s" % (n_pos - 1, n_seq, n, layers, el)}
 
 
 def main():
@@ -268,7 +283,6 @@ def main():
             per_kernel[k].update({"hbm_bytes_per_launch": mem_bytes[k], "hbm_GBs": round(gbs, 1),
                                   "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
     dom = dominant
-    traffic = load_traffic(wl.name, "proj_bf16.hip")
     roofline = dict(per_kernel[dom])
     # the dominant kernel's figures as measured inside the timed run
     ms, n = kern_dom(dom)
@@ -283,10 +297,22 @@ def main():
     if dom in mem_bytes:
         gbs = mem_bytes[dom] / (ms * 1e-3) / 1e9
         roofline.update({"hbm_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
-    tk = None if traffic is None else traffic.get("kernels", {}).get(dom)
+    tk = load_traffic(wl.name, dom) if wl.dtype == "bf16" or dom not in ("gemm", "gemm_v") else None
     roofline["traffic"] = None if tk is None else tk["bytes_per_launch"]
     roofline["traffic_unit"] = "bytes"
     kernels_us = {k: round(kern(k)[0] * 1e3, 2) for k in B.KERNEL_NAMES}
+    # the gate GEMMs together: W_k and W_v flops over the time of every
+    # projection launch (breakdown pass)
+    proj_ms = sum(kern(k)[0] * kern(k)[1] for k in ("gemm", "gemm_v")) / args.breakdown_steps
+    proj_flops = 2.0 * n_tok * De * (Br + 1) * d * len(wl.layers)
+    gemm_tf = proj_flops / (proj_ms * 1e-3) / 1e12
+    gate_gemm = {"achieved": round(gemm_tf, 2), "peak": MFMA_PEAK_TFLOPS[wl.dtype], "unit": "TFLOP/s",
+                 "frac": round(gemm_tf / MFMA_PEAK_TFLOPS[wl.dtype], 4), "ms_per_step": round(proj_ms, 4),
+                 "flops_per_step": proj_flops}
+    g = per_kernel.get("gather")
+    gather = None if g is None else {"kernel": g["kernel"], "achieved_GBs": g["achieved"], "peak_GBs": HBM_PEAK_GBS,
+                                     "frac": g["frac"], "bytes_per_launch": g["bytes_per_launch"],
+                                     "avg_launch_us": g["avg_launch_us"]}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -313,6 +339,8 @@ def main():
                    "head_dim": wl.head_dim, "emb_dim": De, "table_params": sum(wl.primes()) * wl.head_dim,
                    "rotated_buffers": R, "parallelism": "single GPU"},
         "roofline": roofline,
+        "gather": gather,
+        "gate_gemm": gate_gemm,
         "kernels": per_kernel,
         "kernel_avg_us": kernels_us,
         "cpu_baseline": cpu,
