@@ -210,9 +210,11 @@ engram_status check_fuse_args(const engram_plan_s *p, const void *emb, const voi
     // K loop runs an even number of 64-wide stages
     if (p->cfg.dtype == ENGRAM_BF16 && (p->cfg.d_model % 256 != 0 || p->emb_dim % 128 != 0))
         return ENGRAM_E_UNSUPPORTED;
-    // the projection kernel addresses E and each weight matrix with 32-bit offsets
+    // the projection kernel addresses E, each weight matrix and each
+    // branch of h with 32-bit offsets
     if ((int64_t)batch * seqlen * p->emb_dim * p->elem >= ((int64_t)1 << 31) ||
-        (int64_t)p->cfg.d_model * p->emb_dim * p->elem >= ((int64_t)1 << 31))
+        (int64_t)p->cfg.d_model * p->emb_dim * p->elem >= ((int64_t)1 << 31) ||
+        (p->cfg.dtype == ENGRAM_BF16 && (int64_t)batch * seqlen * p->cfg.d_model * 2 >= ((int64_t)1 << 32)))
         return ENGRAM_E_UNSUPPORTED;
     return ENGRAM_OK;
 }
@@ -411,7 +413,7 @@ engram_status engram_plan_create(const engram_config *cfg, engram_plan *out) {
 
 engram_status engram_plan_destroy(engram_plan p) {
     if (!p) return ENGRAM_E_INVALID_ARG;
-    for (hipEvent_t e : p->prof_ev) hipEventDestroy(e);
+    for (hipEvent_t e : p->prof_ev) (void)hipEventDestroy(e);
     delete p;
     return ENGRAM_OK;
 }
@@ -487,7 +489,7 @@ engram_status engram_profile_begin(engram_plan p, int32_t max_launches, uint32_t
     if (kind_mask >> ENGRAM_K_COUNT) return ENGRAM_E_INVALID_ARG;
     p->prof_mask = kind_mask ? kind_mask : (1u << ENGRAM_K_COUNT) - 1u;
     if ((int32_t)p->prof_ev.size() < 2 * max_launches) {
-        for (hipEvent_t e : p->prof_ev) hipEventDestroy(e);
+        for (hipEvent_t e : p->prof_ev) (void)hipEventDestroy(e);
         p->prof_ev.assign(2 * max_launches, nullptr);
         for (auto &e : p->prof_ev)
             if (hipEventCreate(&e) != hipSuccess) return ENGRAM_E_DEVICE;

@@ -160,10 +160,11 @@ __device__ __forceinline__ void wait_lgkm0() {
 // registers and overlap the arithmetic of the previous chunk.  Chunk c holds
 // branch c/2, channels nl + 64(c%2) .. +63, in buffer hA (c even) or hB
 // (c odd); LDS row p is token 64g + p, its eight 16-byte pieces XOR-swizzled
-// by (p/4) % 8.  out is stored straight from registers; every store is
-// issued (rows outside the tile's own tokens get an offset past the buffer,
-// which the hardware drops), so the number of memory operations between two
-// chunk loads is known and the waits below are exact.
+// by (p/4) % 8.  Each lane overwrites the h values it read with out, and the
+// chunk goes back to memory the way it came, eight whole 128-byte rows per
+// store.  Every store is issued (rows the tile must not write get an offset
+// past the buffer, which the hardware drops), so the number of memory
+// operations between two chunk loads is known and the waits below are exact.
 template <int BR, bool SILU>
 __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t (&acc)[FN][FT],
                                                      float (&alpha_s)[BR][BT], float *halo, float *taps,
@@ -233,7 +234,7 @@ __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t 
 
     int pos[FT];
     bool edge[FT], to_state[FT];
-    uint32_t stoff[FT], srow[FT], stagerow[FT];
+    uint32_t srow[FT], stagerow[FT];
 #pragma unroll
     for (int j = 0; j < FT; ++j) {
         const int row = rowbase + 4 * l16 + j;
@@ -242,13 +243,9 @@ __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t 
         const int tc = valid ? (int)tt : 0;
         const int bseq = tc / a.seqlen;
         pos[j] = tc - bseq * a.seqlen;
-        // rows whose conv history reaches into the previous tile are the
-        // seam kernel's (their state rows, plain gated values, are written here)
-        const bool store = valid && !(row < kHalo && pos[j] > row);
         to_state[j] = valid && pos[j] >= a.seqlen - (kc - 1);
         // rows that need carried state (sequence start) or write it (sequence end)
         edge[j] = __ballot(valid && (pos[j] < kHalo || to_state[j])) != 0;
-        stoff[j] = store ? (uint32_t)((tc * (int64_t)d + nl + sub) * 2) : 0x80000000u;
         // byte offset of state row pos of sequence bseq, modulo 2^32: exact
         // (in range) for the rows that read or write the state
         srow[j] = ((uint32_t)bseq * (uint32_t)(kc - 1) + (uint32_t)pos[j]) * state_row_bytes +
@@ -260,13 +257,23 @@ __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t 
 
     // chunk DMA: instruction k fills LDS rows 8k .. 8k+7 (lane -> row
     // 8k + lane/8, piece lane%8), so lane reads global piece
-    // (lane%8) ^ swizzle(row) of its token's 64 channels
+    // (lane%8) ^ swizzle(row) of its token's 64 channels.  out goes back
+    // the same way (same offsets), for the rows the tile writes: bit k of
+    // store_rows.  Rows whose conv history reaches into the previous tile
+    // are the seam kernel's (their state rows, plain gated values, are
+    // written here).
     uint32_t hoff[8];
+    uint32_t store_rows = 0;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         const int p = 8 * k + (lane >> 3);
-        const int64_t tok = min(max(t0 + rowbase + p, (int64_t)0), n_tok - 1);
+        const int row = rowbase + p;
+        const int64_t tt = t0 + row;
+        const int64_t tok = min(max(tt, (int64_t)0), n_tok - 1);
         hoff[k] = (uint32_t)((tok * d + nl) * 2) + (uint32_t)(((lane & 7) ^ ((p >> 2) & 7)) << 4);
+        bool store = tt < n_tok;
+        if (row < kHalo) store = store && (int)(tok % a.seqlen) <= row;
+        if (store) store_rows |= 1u << k;
     }
     auto issue = [&](unsigned char *buf, int c) {
         wait_lgkm0();  // this wave's reads of the buffer's previous chunk are done
@@ -285,7 +292,7 @@ __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t 
 
     // EDGE: some token block of the wave holds a sequence's first or last
     // positions.  Without it the body is straight-line code.
-    auto chunk = [&](auto qc, auto ec, const unsigned char *buf, int m, int moff, int smoff,
+    auto chunk = [&](auto qc, auto ec, unsigned char *buf, int m, int moff, int smoff,
                      const float (&al)[FT], const float (&alh)[3]) {
         constexpr int q = decltype(qc)::value;
         constexpr bool EDGE = decltype(ec)::value;
@@ -355,19 +362,31 @@ __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t 
                     const float hval = bf16_to_f32((r & 1) ? (hw >> 16) : (hw & 0xFFFFu));
                     o[r] = delta ? y : hval + y;
                 }
-                __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])},
-                                                      ores, stoff[j] + 32 * i, moff, 0);
+                // out replaces h in the chunk buffer (same place, same lane)
+                *reinterpret_cast<u32x2_t *>(buf + ldo[ii] + 128 * j) =
+                    u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
                 if (EDGE && edge[j] && a.state_stage && to_state[j])
                     __builtin_amdgcn_raw_buffer_store_b128(
                         __builtin_bit_cast(u32x4_t, f32x4_t{u[j][0], u[j][1], u[j][2], u[j][3]}), sres,
                         stagerow[j] + 64 * i, smoff, 0);
             }
         }
+        // out leaves in the layout h arrived in: each store writes eight whole
+        // 128-byte rows (storing straight from the MFMA layout would write 16
+        // rows x 32 bytes per instruction, a quarter line each).  Every store
+        // is issued; rows the tile does not write go past the buffer's end.
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(buf + k * 1024 + lane * 16);
+            __builtin_amdgcn_raw_buffer_store_b128(v, ores, ((store_rows >> k) & 1u) ? hoff[k] : 0x80000000u,
+                                                   moff + 128 * q, 0);
+        }
     };
 
-    // Issue order: load(0), load(1), chunk 0's 16 stores, load(2), chunk 1's
+    // Issue order: load(0), load(1), chunk 0's 8 stores, load(2), chunk 1's
     // stores, load(3), ...  Before chunk c, the operations issued after
-    // load(c) are chunk c-1's stores (16, for c >= 1) and load(c+1) (8, if
+    // load(c) are chunk c-1's stores (8, for c >= 1) and load(c+1) (8, if
     // there is one).  Vector memory operations complete in issue order, so
     // waiting until no more than those are outstanding means chunk c has
     // landed.  State stores and carried-state loads near sequence edges only
@@ -386,7 +405,7 @@ __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t 
         if (m == 0)
             wait_vmcnt<8>();
         else
-            wait_vmcnt<24>();
+            wait_vmcnt<16>();
         asm volatile("" ::: "memory");
         if (any_edge)
             chunk(std::integral_constant<int, 0>{}, std::true_type{}, hA, m, moff, smoff, al, alh);
@@ -394,9 +413,9 @@ __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t 
             chunk(std::integral_constant<int, 0>{}, std::false_type{}, hA, m, moff, smoff, al, alh);
         if (m + 1 < BR) issue(hA, 2 * m + 2);
         if (m + 1 < BR)
-            wait_vmcnt<24>();
-        else
             wait_vmcnt<16>();
+        else
+            wait_vmcnt<8>();
         asm volatile("" ::: "memory");
         if (any_edge)
             chunk(std::integral_constant<int, 1>{}, std::true_type{}, hB, m, moff, smoff, al, alh);
@@ -412,6 +431,7 @@ template <int MODE, int BR, bool SILU>
 __global__ __launch_bounds__(kThreads, 1) void proj_bf16_kernel(ProjArgs a) {
     __shared__ Stage st0, st1, st2, st3;
     __shared__ float alpha_s[MODE == 1 ? BR : 1][BT];
+    __shared__ __attribute__((aligned(16))) float gsm_s[MODE == 0 ? kWaves * WN : 4];
     __shared__ __attribute__((aligned(16))) float taps_s[MODE == 1 ? 4 * BN : 4];
     __shared__ __attribute__((aligned(16))) float halo_s[MODE == 1 ? kWaves * kHalo * WN : 4];
 
@@ -565,35 +585,51 @@ __global__ __launch_bounds__(kThreads, 1) void proj_bf16_kernel(ProjArgs a) {
     if constexpr (MODE == 0) {
     if (mat < a.n_branches) {
         // gate partials of branch `mat` over channels [nl, nl+128).
-        // gamma_h * gamma_k for the wave's channels goes through the now idle
-        // st0 (its last reader finished before the final barrier), so it costs
-        // no registers; each wave writes and reads only its own 512 bytes.
-        float *gsm = reinterpret_cast<float *>(st0.w) + wave * WN;
+        // gamma_h * gamma_k for the wave's channels goes through LDS, so it
+        // costs no registers; each wave writes and reads only its own 512 bytes.
+        float *gsm = gsm_s + wave * WN;
         {
             const float *gh = pick(a.gamma_h, mat);
             const float *gk = pick(a.gamma_k, mat);
             for (int c = lane; c < WN; c += 64) gsm[c] = gh[nl + c] * gk[nl + c];
         }
-        const uint16_t *hm = reinterpret_cast<const uint16_t *>(a.h) + (int64_t)mat * a.n_tok * d;
         const int part = nl / kPartCols;
         float *pbase = a.partials + ((int64_t)mat * a.n_parts + part) * 3 * a.n_tok;
-        // every h value the wave needs is requested before any is used: one
-        // memory round trip for the whole epilogue
-        u32x2_t hv[FT][FN];
+        // h of the wave's 64 tokens x 128 channels arrives in LDS by DMA, in
+        // whole 128-byte rows (loading it straight into the MFMA layout would
+        // read 16 rows x 32 bytes per instruction): 16 KB per wave in the now
+        // idle stage buffers, two 8 KB halves for channels nl + 64q, row p =
+        // token tw + p, its eight 16-byte pieces XOR-swizzled by hswz(p).
+        // All of it is requested at once: one memory round trip.
+        block_barrier();  // every wave is done reading the stage buffers
+        unsigned char *hbuf = reinterpret_cast<unsigned char *>(
+                                  wave < 2 ? &st0 : (wave < 4 ? &st1 : (wave < 6 ? &st2 : &st3))) +
+                              (wave & 1) * 16384;
+        auto hswz = [](int p) { return (p ^ (p >> 3)) & 7; };
+        {
+            const __amdgpu_buffer_rsrc_t hres = make_rsrc(
+                reinterpret_cast<const uint16_t *>(a.h) + (int64_t)mat * a.n_tok * d, (uint32_t)(a.n_tok * d * 2));
 #pragma unroll
-        for (int j = 0; j < FT; ++j) {
-            const int64_t t = min(tw + 16 * j + (lane & 15), a.n_tok - 1);
-            const uint16_t *hrow = hm + t * d + nl + sub;
-#pragma unroll
-            for (int i = 0; i < FN; ++i) hv[j][i] = *reinterpret_cast<const u32x2_t *>(hrow + 16 * i);
+            for (int k = 0; k < 8; ++k) {
+                const int p = 8 * k + (lane >> 3);
+                const int64_t tok = min(tw + p, a.n_tok - 1);
+                const uint32_t off = (uint32_t)((tok * d + nl) * 2) + (uint32_t)(((lane & 7) ^ hswz(p)) << 4);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(hres, (lds_void_t *)(hbuf + k * 1024), 16, off, 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(hres, (lds_void_t *)(hbuf + 8192 + k * 1024), 16, off, 128,
+                                                         0, 0);
+            }
         }
+        wait_vmcnt<0>();
+        asm volatile("" ::: "memory");
 #pragma unroll
         for (int j = 0; j < FT; ++j) {
             const int64_t t = tw + 16 * j + (lane & 15);
+            const int p = 16 * j + (lane & 15);
             float s_hk = 0.f, s_kk = 0.f, s_hh = 0.f;
 #pragma unroll
             for (int i = 0; i < FN; ++i) {
-                const u32x2_t x = hv[j][i];
+                const u32x2_t x = *reinterpret_cast<const u32x2_t *>(
+                    hbuf + (i >> 2) * 8192 + p * 128 + (((2 * (i & 3) + (sub >> 3)) ^ hswz(p)) << 4) + (sub & 4) * 2);
                 const f32x4_t g = *reinterpret_cast<const f32x4_t *>(gsm + 16 * i + sub);
                 const float h4[4] = {bf16_to_f32(x[0] & 0xFFFFu), bf16_to_f32(x[0] >> 16),
                                      bf16_to_f32(x[1] & 0xFFFFu), bf16_to_f32(x[1] >> 16)};

@@ -184,7 +184,10 @@ ENGRAM_API engram_status engram_gather(engram_plan p, const uint32_t *d_idx, int
  *                one full prefill.
  *   d_alpha      optional [n_branches][batch*seqlen] fp32 gate values
  *   d_workspace  >= engram_workspace_size(p, batch, seqlen) bytes, 256-byte aligned
- * Supported: bf16 with d % 256 == 0 and D_e % 128 == 0; f32 any d, D_e.
+ * Supported: bf16 with d % 256 == 0, D_e % 128 == 0 and one branch of h
+ * (batch*seqlen*d*2 bytes) under 4 GiB; f32 any d, D_e.  batch*seqlen*D_e and
+ * d*D_e elements must stay under 2^31 bytes.  Anything else returns
+ * ENGRAM_E_UNSUPPORTED and launches nothing.
  */
 ENGRAM_API engram_status engram_gate_fuse(engram_plan p, const void *d_emb, const void *d_h, int32_t batch,
                                int32_t seqlen, const engram_weights *w, float *d_conv_state,
