@@ -80,9 +80,9 @@ bool layout_of(const engram_plan_s &p, int64_t batch, int64_t seqlen, Layout &L)
     };
     L.idx = take((size_t)n_tok * p.n_tables * 4);
     L.emb = take((size_t)n_tok * p.emb_dim * p.elem);
-    L.partials = take((size_t)Br * n_parts_of(p) * 3 * n_tok * 4);
-    L.alpha = take((size_t)Br * n_tok * 4);
     const bool fused_v = fused_value_path(p, batch, seqlen);
+    L.partials = take((size_t)Br * n_parts_of(p) * 3 * n_tok * 4);
+    L.alpha = fused_v ? take((size_t)Br * n_tok * 4) : off;
     L.v = fused_v ? off : take((size_t)n_tok * d * 4);
     L.seam = fused_v ? take((size_t)((n_tok + kTokTile - 1) / kTokTile) * 6 * d * 4) : off;
     L.kbuf = p.cfg.dtype == ENGRAM_F32 ? take((size_t)Br * n_tok * d * 4) : off;
@@ -221,7 +221,8 @@ engram_status check_fuse_args(const engram_plan_s *p, const void *emb, const voi
 
 engram_status do_fuse(engram_plan_s &p, const void *emb, const void *h, int32_t batch, int32_t seqlen,
                       const engram_weights *w, float *conv_state, void *out, float *alpha,
-                      uint32_t flags, void *ws, hipStream_t s) {
+                      uint32_t flags, void *ws, hipStream_t s,
+                      const CtxUpdate &ctx = CtxUpdate{}) {
     Layout L;
     layout_of(p, batch, seqlen, L);
     char *base = static_cast<char *>(ws);
@@ -266,21 +267,26 @@ engram_status do_fuse(engram_plan_s &p, const void *emb, const void *h, int32_t 
     }
     if (last_launch_status() != ENGRAM_OK) return ENGRAM_E_DEVICE;
 
-    GateArgs ga{};
-    ga.partials = pa.partials;
-    ga.alpha = gate;
-    ga.n_tok = n_tok;
-    ga.d = p.cfg.d_model;
-    ga.n_branches = Br;
-    ga.n_parts = pa.n_parts;
-    ga.eps = p.cfg.rms_eps;
-    {
-        Launch l(p, ENGRAM_K_GATE, s);
-        launch_gate(ga, s);
-    }
-    if (last_launch_status() != ENGRAM_OK) return ENGRAM_E_DEVICE;
-
     if (fused_v) {
+        // the gate of every token, which the W_v launch's epilogue reads
+        // (plus the carried context, if any)
+        GateArgs ga{};
+        ga.partials = pa.partials;
+        ga.alpha = gate;
+        ga.n_tok = n_tok;
+        ga.d = p.cfg.d_model;
+        ga.n_branches = Br;
+        ga.n_parts = pa.n_parts;
+        ga.eps = p.cfg.rms_eps;
+        ga.ctx = ctx;
+        ga.batch = batch;
+        ga.seqlen = seqlen;
+        {
+            Launch l(p, ENGRAM_K_GATE, s);
+            launch_gate(ga, s);
+        }
+        if (last_launch_status() != ENGRAM_OK) return ENGRAM_E_DEVICE;
+
         // W_v with gated value, conv, residual and state in its epilogue
         ProjArgs pv = pa;
         pv.w[0] = w->w_v;
@@ -323,9 +329,19 @@ engram_status do_fuse(engram_plan_s &p, const void *emb, const void *h, int32_t 
             launch_seam(sa, s);
         }
     } else {
+        // a chunk of at most kFusePositions positions is one fusion-kernel
+        // workgroup per sequence and channel stripe, which reads a state row
+        // before it writes it: the state is updated in place
+        if (stage && seqlen <= kFusePositions) stage = conv_state;
+        // the fusion kernel computes the gate itself (the same function as
+        // the gate kernel), and the carried context
         FuseArgs fa{};
         fa.v = pa.v;
-        fa.alpha = gate;
+        fa.partials = pa.partials;
+        fa.n_parts = pa.n_parts;
+        fa.eps = p.cfg.rms_eps;
+        fa.alpha = alpha;
+        fa.ctx = ctx;
         fa.h = h;
         fa.out = out;
         fa.conv_w = w->conv_w;
@@ -342,7 +358,7 @@ engram_status do_fuse(engram_plan_s &p, const void *emb, const void *h, int32_t 
         launch_fuse(fa, p.cfg.dtype, s);
     }
     if (last_launch_status() != ENGRAM_OK) return ENGRAM_E_DEVICE;
-    if (stage) {
+    if (stage && stage != conv_state) {
         Launch l(p, ENGRAM_K_AUX, s);
         const size_t bytes = (size_t)Br * batch * (p.cfg.conv_kernel - 1) * p.cfg.d_model * 4;
         launch_copy_f32(stage, conv_state, (int64_t)(bytes / 4), s);
@@ -472,16 +488,16 @@ engram_status engram_forward(engram_plan p, const int32_t *d_tokens, int32_t bat
     st = do_hash_gather(*p, d_tokens, batch, seqlen, d_comp_map, d_prev_ctx, d_bad_tokens, table_ptrs,
                         emb, stream);
     if (st != ENGRAM_OK) return st;
-    if (d_prev_ctx) {  // after the retrieval kernel has read the old context
-        {
-            Launch l(*p, ENGRAM_K_AUX, stream);
-            launch_ctx_update(d_tokens, batch, seqlen, d_comp_map, p->cfg.vocab, p->cfg.vocab_comp,
-                              d_prev_ctx, stream);
-        }
-        if (last_launch_status() != ENGRAM_OK) return ENGRAM_E_DEVICE;
-    }
+    // the carried context is updated by a later kernel of this call, after
+    // the retrieval kernel has read the old one
+    CtxUpdate ctx{};
+    ctx.tokens = d_tokens;
+    ctx.comp_map = d_comp_map;
+    ctx.prev_ctx = d_prev_ctx;
+    ctx.vocab = p->cfg.vocab;
+    ctx.vocab_comp = p->cfg.vocab_comp;
     return do_fuse(*p, emb, d_h, batch, seqlen, w, d_conv_state, d_out, d_alpha, flags, d_workspace,
-                   stream);
+                   stream, ctx);
 }
 
 engram_status engram_profile_begin(engram_plan p, int32_t max_launches, uint32_t kind_mask) {

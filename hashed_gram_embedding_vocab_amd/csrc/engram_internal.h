@@ -98,9 +98,7 @@ struct HashConsts {
 void launch_hash(const HashConsts &hc, const int32_t *tokens, int32_t batch, int32_t seqlen,
                  const int32_t *comp_map, const int32_t *prev_ctx, uint32_t *idx,
                  uint32_t *bad, hipStream_t s);
-void launch_ctx_update(const int32_t *tokens, int32_t batch, int32_t seqlen,
-                       const int32_t *comp_map, int32_t vocab, int32_t vocab_comp,
-                       int32_t *prev_ctx, hipStream_t s);
+
 
 // ---------------------------------------------------------------- gather
 struct GatherConsts {
@@ -162,6 +160,25 @@ void launch_proj_v_fused_bf16(const ProjArgs &a, hipStream_t s);
 void launch_proj_f32(const ProjArgs &a, hipStream_t s);  // k into kbuf, v, then partials
 
 // ---------------------------------------------------------------- fusion
+// The carried context of the next chunk: the last two compressed ids of
+// (prev_ctx followed by this chunk's tokens), per sequence.  engram_forward
+// hands it to a kernel that runs after retrieval has read prev_ctx.
+struct CtxUpdate {
+    const int32_t *tokens;     // [batch][seqlen] raw ids
+    const int32_t *comp_map;   // [vocab]
+    int32_t *prev_ctx;         // [batch][2], or null: nothing to update
+    int32_t vocab, vocab_comp;
+};
+
+__device__ __forceinline__ void ctx_update_one(const CtxUpdate &c, int32_t b, int32_t seqlen) {
+    const int32_t *seq = c.tokens + (int64_t)b * seqlen;
+    const int32_t n1 = compress_id(seq[seqlen - 1], c.comp_map, c.vocab, c.vocab_comp);
+    const int32_t n0 =
+        seqlen >= 2 ? compress_id(seq[seqlen - 2], c.comp_map, c.vocab, c.vocab_comp) : c.prev_ctx[b * 2 + 1];
+    c.prev_ctx[b * 2 + 0] = n0;
+    c.prev_ctx[b * 2 + 1] = n1;
+}
+
 // Gate per branch and token, alpha = sigmoid(<RMSNorm(h), RMSNorm(k)> / sqrt(d)),
 // from the partial sums of the W_k projection (summed in a fixed order).
 struct GateArgs {
@@ -170,6 +187,8 @@ struct GateArgs {
     int64_t n_tok;
     int32_t d, n_branches, n_parts;
     float eps;
+    CtxUpdate ctx;             // done by the first batch threads of branch 0
+    int32_t batch, seqlen;
 };
 
 void launch_gate(const GateArgs &a, hipStream_t s);
@@ -190,16 +209,21 @@ struct SeamArgs {
 
 void launch_seam(const SeamArgs &a, hipStream_t s);
 
+constexpr int kFusePositions = 32;  // positions of one sequence per fusion-kernel workgroup
+
 struct FuseArgs {
     const float *v;            // [n_tok][d] fp32
-    const float *alpha;        // [B_r][n_tok], from the gate kernel
+    const float *partials;     // [B_r][n_parts][3][n_tok]: the gate is computed here
+    float *alpha;              // [B_r][n_tok] gate output, or null
     const void *h;             // [B_r][n_tok][d]
     void *out;                 // [B_r][n_tok][d]
     const float *conv_w;       // [d][K_c]
     const float *conv_state;   // [B_r][batch][K_c-1][d] or null
     float *state_stage;        // [B_r][batch][K_c-1][d] or null
-    int32_t batch, seqlen, d, n_branches, conv_k, conv_mode;
+    int32_t batch, seqlen, d, n_branches, n_parts, conv_k, conv_mode;
+    float eps;
     uint32_t flags;
+    CtxUpdate ctx;             // done by the first workgroup of each sequence
 };
 
 void launch_fuse(const FuseArgs &a, engram_dtype dt, hipStream_t s);

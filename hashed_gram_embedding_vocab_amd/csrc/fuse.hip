@@ -21,7 +21,7 @@
 namespace engram {
 namespace {
 
-constexpr int kPos = 32;
+constexpr int kPos = kFusePositions;
 constexpr int kVec = 4;
 
 // Four values in their stored form: 8 bytes for bf16, 16 for fp32.
@@ -57,22 +57,31 @@ struct Raw4 {
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + expf(-x)); }
 
+// The gate of token t, branch m, from the n_parts partial sums, in a fixed
+// order.  The one definition both kernels below use, so every path gets the
+// same bits.
+__device__ __forceinline__ float gate_value(const float *partials, int m, int n_parts, int64_t n_tok, int64_t t,
+                                            int d, float eps) {
+    const float *pp = partials + (int64_t)m * n_parts * 3 * n_tok + t;
+    float s_hk = 0.f, s_kk = 0.f, s_hh = 0.f;
+#pragma unroll 8
+    for (int q = 0; q < n_parts; ++q) {
+        s_hk += pp[(3 * q + 0) * n_tok];
+        s_kk += pp[(3 * q + 1) * n_tok];
+        s_hh += pp[(3 * q + 2) * n_tok];
+    }
+    const float inv_d = 1.f / (float)d;
+    const float rh = sqrtf(s_hh * inv_d + eps);
+    const float rk = sqrtf(s_kk * inv_d + eps);
+    return sigmoidf_(s_hk / (rh * rk) * rsqrtf((float)d));
+}
+
 __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int m = blockIdx.y;
+    if (a.ctx.prev_ctx && m == 0 && t < a.batch) ctx_update_one(a.ctx, (int32_t)t, a.seqlen);
     if (t >= a.n_tok) return;
-    const float *pp = a.partials + (int64_t)m * a.n_parts * 3 * a.n_tok + t;
-    float s_hk = 0.f, s_kk = 0.f, s_hh = 0.f;
-#pragma unroll 8
-    for (int q = 0; q < a.n_parts; ++q) {
-        s_hk += pp[(3 * q + 0) * a.n_tok];
-        s_kk += pp[(3 * q + 1) * a.n_tok];
-        s_hh += pp[(3 * q + 2) * a.n_tok];
-    }
-    const float inv_d = 1.f / (float)a.d;
-    const float rh = sqrtf(s_hh * inv_d + a.eps);
-    const float rk = sqrtf(s_kk * inv_d + a.eps);
-    a.alpha[m * a.n_tok + t] = sigmoidf_(s_hk / (rh * rk) * rsqrtf((float)a.d));
+    a.alpha[m * a.n_tok + t] = gate_value(a.partials, m, a.n_parts, a.n_tok, t, a.d, a.eps);
 }
 
 template <bool BF16, int BR>
@@ -85,11 +94,17 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
     const int64_t row0 = (int64_t)b * a.seqlen;
     const int d = a.d;
 
+    if (a.ctx.prev_ctx && blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x == 0) ctx_update_one(a.ctx, b, a.seqlen);
     // gate values for positions t0-3 .. t1-1 (zero where unused)
     for (int x = threadIdx.x; x < BR * (kPos + 3); x += blockDim.x) {
         const int m = x / (kPos + 3), j = x - m * (kPos + 3);
         const int p = t0 - 3 + j;
-        alpha_s[m][j] = (p >= 0 && p < t1) ? a.alpha[m * n_tok + row0 + p] : 0.f;
+        float al = 0.f;
+        if (p >= 0 && p < t1) {
+            al = gate_value(a.partials, m, a.n_parts, n_tok, row0 + p, d, a.eps);
+            if (a.alpha && p >= t0 && blockIdx.z == 0) a.alpha[m * n_tok + row0 + p] = al;
+        }
+        alpha_s[m][j] = al;
     }
     __syncthreads();
 

@@ -82,25 +82,6 @@ __global__ __launch_bounds__(kWave *kWavesPerBlock) void hash_kernel(
     }
 }
 
-// The last two compressed ids of (prev_ctx followed by this chunk), per sequence.
-__global__ void ctx_update_kernel(const int32_t *__restrict__ tokens, int32_t batch, int32_t seqlen,
-                                  const int32_t *__restrict__ comp_map, int32_t vocab,
-                                  int32_t vocab_comp, int32_t *prev_ctx) {
-    const int32_t b = blockIdx.x * blockDim.x + threadIdx.x;
-    if (b >= batch) return;
-    const int32_t *seq = tokens + (int64_t)b * seqlen;
-    int32_t n0, n1;
-    if (seqlen >= 2) {
-        n0 = compress(seq[seqlen - 2], comp_map, vocab, vocab_comp);
-        n1 = compress(seq[seqlen - 1], comp_map, vocab, vocab_comp);
-    } else {
-        n0 = prev_ctx[b * 2 + 1];
-        n1 = compress(seq[0], comp_map, vocab, vocab_comp);
-    }
-    prev_ctx[b * 2 + 0] = n0;
-    prev_ctx[b * 2 + 1] = n1;
-}
-
 }  // namespace
 
 void launch_hash(const HashConsts &hc, const int32_t *tokens, int32_t batch, int32_t seqlen,
@@ -112,10 +93,5 @@ void launch_hash(const HashConsts &hc, const int32_t *tokens, int32_t batch, int
                        tokens, batch, seqlen, comp_map, prev_ctx, idx, bad);
 }
 
-void launch_ctx_update(const int32_t *tokens, int32_t batch, int32_t seqlen, const int32_t *comp_map,
-                       int32_t vocab, int32_t vocab_comp, int32_t *prev_ctx, hipStream_t s) {
-    launch_kernel(ctx_update_kernel, dim3((batch + 255) / 256), dim3(256), s, tokens, batch,
-                       seqlen, comp_map, vocab, vocab_comp, prev_ctx);
-}
 
 }  // namespace engram

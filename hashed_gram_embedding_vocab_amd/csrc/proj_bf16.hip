@@ -69,10 +69,28 @@ constexpr int kGroupT = ENGRAM_PROJ_GROUP_T;  // token tiles sharing each weight
 static_assert(BN == BT, "one block-load pattern serves both operands");
 static_assert(BT == kTokTile, "the seam kernel assumes this token tile");
 
-struct __attribute__((aligned(1024))) Stage {
-    unsigned char w[kOperandBytes];
-    unsigned char e[kOperandBytes];
+// Tile shapes of proj_bf16_kernel: wide (256 x 256, 8 waves as 2 x 4) and
+// narrow (128 x 128, 4 waves as 1 x 4).
+template <bool NARROW>
+struct TileCfg {
+    static constexpr int BN = NARROW ? 128 : 256;                 // weight rows per block
+    static constexpr int BT = NARROW ? 128 : 256;                 // tokens per block
+    static constexpr int kThreads = NARROW ? 256 : 512;
+    static constexpr int kWaves = kThreads / 64;
+    static constexpr int kWavesN = NARROW ? 1 : 2;                // waves along n
+    static constexpr int WT = BT / (kWaves / kWavesN);            // tokens per wave
+    static constexpr int FT = WT / 16;
+    static constexpr int kOperandBytes = (BN / 16) * kBlockBytes; // per operand and stage
+    static constexpr int kBlocksPerWave = (BN / 16) / kWaves;     // row blocks each wave fills
+    static_assert(BN == BT && kBlocksPerWave >= 1 && FN * 16 * kWavesN == BN, "tile shape");
 };
+
+template <int OPB>
+struct __attribute__((aligned(1024))) StageT {
+    unsigned char w[OPB];
+    unsigned char e[OPB];
+};
+typedef StageT<kOperandBytes> Stage;
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
@@ -426,14 +444,22 @@ __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t 
 }
 
 // MODE 0, or MODE 1 with BR branches and the conv output passed through
-// SiLU plus the skip term (SILU) or not.
-template <int MODE, int BR, bool SILU>
-__global__ __launch_bounds__(kThreads, 1) void proj_bf16_kernel(ProjArgs a) {
-    __shared__ Stage st0, st1, st2, st3;
-    __shared__ float alpha_s[MODE == 1 ? BR : 1][BT];
-    __shared__ __attribute__((aligned(16))) float gsm_s[MODE == 0 ? kWaves * WN : 4];
-    __shared__ __attribute__((aligned(16))) float taps_s[MODE == 1 ? 4 * BN : 4];
-    __shared__ __attribute__((aligned(16))) float halo_s[MODE == 1 ? kWaves * kHalo * WN : 4];
+// SiLU plus the skip term (SILU) or not.  NARROW (mode 0 only): tiles of 128
+// weight rows x 128 tokens and 4 waves of 128 x 32, for launches with too few
+// 256 x 256 tiles to fill the chip (decode).  A wave always owns 128 output
+// channels in the same MFMA layout, so the gate partial sums come out
+// bit-identical whichever tile computed them.
+template <int MODE, int BR, bool SILU, bool NARROW>
+__global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_bf16_kernel(ProjArgs a) {
+    static_assert(!(NARROW && MODE == 1), "the fused value epilogue is written for the wide tile");
+    typedef TileCfg<NARROW> C;
+    constexpr int TBN = C::BN, TBT = C::BT, TTHREADS = C::kThreads, TWAVES = C::kWaves, TWGN = C::kWavesN;
+    constexpr int TWT = C::WT, TFT = C::FT, TOPB = C::kOperandBytes, TBPW = C::kBlocksPerWave;
+    __shared__ StageT<TOPB> st0, st1, st2, st3;
+    __shared__ float alpha_s[MODE == 1 ? BR : 1][TBT];
+    __shared__ __attribute__((aligned(16))) float gsm_s[MODE == 0 ? TWAVES * WN : 4];
+    __shared__ __attribute__((aligned(16))) float taps_s[MODE == 1 ? 4 * TBN : 4];
+    __shared__ __attribute__((aligned(16))) float halo_s[MODE == 1 ? TWAVES * kHalo * WN : 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -441,14 +467,14 @@ __global__ __launch_bounds__(kThreads, 1) void proj_bf16_kernel(ProjArgs a) {
     const int K = a.K;
     const int d = a.d;
     const int n_total = a.n_mats * d;
-    const int n_tiles_n = (n_total + BN - 1) / BN;
-    const int n_tiles_t = (int)((a.n_tok + BT - 1) / BT);
+    const int n_tiles_n = (n_total + TBN - 1) / TBN;
+    const int n_tiles_t = (int)((a.n_tok + TBT - 1) / TBT);
     int tile_n, tile_t;
     tile_of(blockIdx.x, gridDim.x, n_tiles_n, n_tiles_t, tile_n, tile_t);
-    const int n0 = tile_n * BN;
+    const int n0 = tile_n * TBN;
     // first token row of the tile
     // previous tile's last tokens (negative for the first tile: never stored)
-    const int64_t t0 = (int64_t)tile_t * BT;
+    const int64_t t0 = (int64_t)tile_t * TBT;
 
     // ---- this lane's share of the block loads.  Wave w fills row blocks
     //      2w and 2w+1 of each operand.
@@ -463,10 +489,13 @@ __global__ __launch_bounds__(kThreads, 1) void proj_bf16_kernel(ProjArgs a) {
     const char *wmat = reinterpret_cast<const char *>(pick(a.w, mat0));
     const __amdgpu_buffer_rsrc_t wres = make_rsrc(wmat, (uint32_t)d * K * 2u);
     const __amdgpu_buffer_rsrc_t eres = make_rsrc(a.emb, (uint32_t)(a.n_tok * K * 2));
+    // (a template-dependent bound here keeps the host pass from emitting the
+    // kernel's launch stub, so the bound is the namespace constant both tiles share)
+    static_assert(TBPW == kBlocksPerWave, "two row blocks per wave and operand in both tiles");
     uint32_t woff[kBlocksPerWave], eoff[kBlocksPerWave];
 #pragma unroll
-    for (int i = 0; i < kBlocksPerWave; ++i) {
-        const int blk = wave * kBlocksPerWave + i;
+    for (int i = 0; i < TBPW; ++i) {
+        const int blk = wave * TBPW + i;
         const int row = blk * 16 + lr;
         // mode 1 takes the tokens of each group of four row blocks in the
         // order 4 * row + block (see the mode-1 epilogue)
@@ -482,36 +511,36 @@ __global__ __launch_bounds__(kThreads, 1) void proj_bf16_kernel(ProjArgs a) {
 #define ENGRAM_ISSUE(STG, k0)                                                                    \
     do {                                                                                         \
         const int kbytes = (k0) * 2;                                                             \
-        _Pragma("unroll") for (int i = 0; i < kBlocksPerWave; ++i) {                             \
-            const int blk = wave * kBlocksPerWave + i;                                           \
+        _Pragma("unroll") for (int i = 0; i < TBPW; ++i) {                             \
+            const int blk = wave * TBPW + i;                                           \
             __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void_t *)&STG.w[blk * kBlockBytes], \
                                                      16, woff[i], kbytes, 0, 0);                 \
             __builtin_amdgcn_raw_ptr_buffer_load_lds(eres, (lds_void_t *)&STG.e[blk * kBlockBytes], \
                                                      16, eoff[i], kbytes, 0, 0);                 \
         }                                                                                        \
     } while (0)
-    constexpr int kLoadsPerStage = 2 * kBlocksPerWave;  // per wave
+    constexpr int kLoadsPerStage = 2 * TBPW;  // per wave
 
-    f32x4_t acc[FN][FT];
+    f32x4_t acc[FN][TFT];
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll
-        for (int j = 0; j < FT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < TFT; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const int wn_blk = (wave & 1) * (WN / 16);   // wave's first weight row block
-    const int wt_blk = (wave >> 1) * (WT / 16);  // wave's first token row block (4 t-groups)
+    const int wn_blk = (wave % TWGN) * (WN / 16);  // wave's first weight row block
+    const int wt_blk = (wave / TWGN) * TFT;        // wave's first token row block
     const int fr = lane & 15;                    // fragment row
     const int fpos = fr * 64 + ((lane >> 4) ^ swz(fr)) * 16;  // byte offset inside a 1 KB block
 
 #define ENGRAM_COMPUTE(STG)                                                                      \
     do {                                                                                         \
-        bf16x8_t fa[FN], fb[FT];                                                                 \
+        bf16x8_t fa[FN], fb[TFT];                                                                 \
         _Pragma("unroll") for (int i = 0; i < FN; ++i) fa[i] =                                   \
             *reinterpret_cast<const bf16x8_t *>(&STG.w[(wn_blk + i) * kBlockBytes + fpos]);      \
-        _Pragma("unroll") for (int j = 0; j < FT; ++j) fb[j] =                                   \
+        _Pragma("unroll") for (int j = 0; j < TFT; ++j) fb[j] =                                   \
             *reinterpret_cast<const bf16x8_t *>(&STG.e[(wt_blk + j) * kBlockBytes + fpos]);      \
         _Pragma("unroll") for (int i = 0; i < FN; ++i)                                           \
-            _Pragma("unroll") for (int j = 0; j < FT; ++j)                                       \
+            _Pragma("unroll") for (int j = 0; j < TFT; ++j)                                       \
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0); \
     } while (0)
 
@@ -531,8 +560,8 @@ __global__ __launch_bounds__(kThreads, 1) void proj_bf16_kernel(ProjArgs a) {
     if constexpr (MODE == 1) {
         // gate of every row of the tile and branch (zero outside the tokens),
         // while the first stages are in flight
-        for (int x = tid; x < BR * BT; x += kThreads) {
-            const int m = x / BT, r = x - m * BT;
+        for (int x = tid; x < BR * TBT; x += TTHREADS) {
+            const int m = x / TBT, r = x - m * TBT;
             const int64_t t = t0 + r;
             alpha_s[m][r] = (t >= 0 && t < a.n_tok) ? a.alpha[m * a.n_tok + t] : 0.f;
         }
@@ -595,41 +624,44 @@ __global__ __launch_bounds__(kThreads, 1) void proj_bf16_kernel(ProjArgs a) {
         }
         const int part = nl / kPartCols;
         float *pbase = a.partials + ((int64_t)mat * a.n_parts + part) * 3 * a.n_tok;
-        // h of the wave's 64 tokens x 128 channels arrives in LDS by DMA, in
+        // h of the wave's TWT tokens x 128 channels arrives in LDS by DMA, in
         // whole 128-byte rows (loading it straight into the MFMA layout would
-        // read 16 rows x 32 bytes per instruction): 16 KB per wave in the now
-        // idle stage buffers, two 8 KB halves for channels nl + 64q, row p =
-        // token tw + p, its eight 16-byte pieces XOR-swizzled by hswz(p).
-        // All of it is requested at once: one memory round trip.
+        // read 16 rows x 32 bytes per instruction): TWT * 256 bytes per wave
+        // in the now idle stage buffers (two waves per stage), two halves for
+        // channels nl + 64q, row p = token tw + p, its eight 16-byte pieces
+        // XOR-swizzled by hswz(p).  All of it is requested at once: one
+        // memory round trip.
+        constexpr int kHalf = TWT * 128;
+        static_assert(4 * kHalf == 2 * TOPB, "two waves' h per stage buffer");
         block_barrier();  // every wave is done reading the stage buffers
         unsigned char *hbuf = reinterpret_cast<unsigned char *>(
                                   wave < 2 ? &st0 : (wave < 4 ? &st1 : (wave < 6 ? &st2 : &st3))) +
-                              (wave & 1) * 16384;
+                              (wave & 1) * 2 * kHalf;
         auto hswz = [](int p) { return (p ^ (p >> 3)) & 7; };
         {
             const __amdgpu_buffer_rsrc_t hres = make_rsrc(
                 reinterpret_cast<const uint16_t *>(a.h) + (int64_t)mat * a.n_tok * d, (uint32_t)(a.n_tok * d * 2));
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
+            for (int k = 0; k < TWT / 8; ++k) {
                 const int p = 8 * k + (lane >> 3);
                 const int64_t tok = min(tw + p, a.n_tok - 1);
                 const uint32_t off = (uint32_t)((tok * d + nl) * 2) + (uint32_t)(((lane & 7) ^ hswz(p)) << 4);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(hres, (lds_void_t *)(hbuf + k * 1024), 16, off, 0, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(hres, (lds_void_t *)(hbuf + 8192 + k * 1024), 16, off, 128,
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(hres, (lds_void_t *)(hbuf + kHalf + k * 1024), 16, off, 128,
                                                          0, 0);
             }
         }
         wait_vmcnt<0>();
         asm volatile("" ::: "memory");
 #pragma unroll
-        for (int j = 0; j < FT; ++j) {
+        for (int j = 0; j < TFT; ++j) {
             const int64_t t = tw + 16 * j + (lane & 15);
             const int p = 16 * j + (lane & 15);
             float s_hk = 0.f, s_kk = 0.f, s_hh = 0.f;
 #pragma unroll
             for (int i = 0; i < FN; ++i) {
                 const u32x2_t x = *reinterpret_cast<const u32x2_t *>(
-                    hbuf + (i >> 2) * 8192 + p * 128 + (((2 * (i & 3) + (sub >> 3)) ^ hswz(p)) << 4) + (sub & 4) * 2);
+                    hbuf + (i >> 2) * kHalf + p * 128 + (((2 * (i & 3) + (sub >> 3)) ^ hswz(p)) << 4) + (sub & 4) * 2);
                 const f32x4_t g = *reinterpret_cast<const f32x4_t *>(gsm + 16 * i + sub);
                 const float h4[4] = {bf16_to_f32(x[0] & 0xFFFFu), bf16_to_f32(x[0] >> 16),
                                      bf16_to_f32(x[1] & 0xFFFFu), bf16_to_f32(x[1] >> 16)};
@@ -655,7 +687,7 @@ __global__ __launch_bounds__(kThreads, 1) void proj_bf16_kernel(ProjArgs a) {
         // v = W_v e, kept fp32 [n_tok][d]: rounding it to bf16 here would add
         // up to half a bf16 ulp of |v| to every gated value the conv sums.
 #pragma unroll
-        for (int j = 0; j < FT; ++j) {
+        for (int j = 0; j < TFT; ++j) {
             const int64_t t = tw + 16 * j + (lane & 15);
             if (t >= a.n_tok) continue;
 #pragma unroll
@@ -675,10 +707,13 @@ __global__ __launch_bounds__(kThreads, 1) void proj_bf16_kernel(ProjArgs a) {
 
 void launch_proj_bf16(const ProjArgs &a, hipStream_t s) {
     const int n_total = a.n_mats * a.d;
-    const int n_tiles_n = (n_total + BN - 1) / BN;
-    const int64_t n_tiles_t = (a.n_tok + BT - 1) / BT;
-    const int64_t blocks = (int64_t)n_tiles_n * n_tiles_t;
-    launch_kernel((proj_bf16_kernel<0, 1, false>), dim3((unsigned)blocks), dim3(kThreads), s, a);
+    const int64_t wide = (int64_t)((n_total + BN - 1) / BN) * ((a.n_tok + BT - 1) / BT);
+    if (wide < 256) {  // fewer wide tiles than CUs: narrow tiles, up to two per CU
+        const int64_t blocks = (int64_t)((n_total + 127) / 128) * ((a.n_tok + 127) / 128);
+        launch_kernel((proj_bf16_kernel<0, 1, false, true>), dim3((unsigned)blocks), dim3(256), s, a);
+    } else {
+        launch_kernel((proj_bf16_kernel<0, 1, false, false>), dim3((unsigned)wide), dim3(kThreads), s, a);
+    }
 }
 
 void launch_proj_v_fused_bf16(const ProjArgs &a, hipStream_t s) {
@@ -688,9 +723,9 @@ void launch_proj_v_fused_bf16(const ProjArgs &a, hipStream_t s) {
 #define ENGRAM_PROJ_V_LAUNCH(BR)                                                                      \
     do {                                                                                              \
         if (a.conv_mode == ENGRAM_CONV_SILU_SKIP)                                                     \
-            launch_kernel((proj_bf16_kernel<1, BR, true>), grid, dim3(kThreads), s, a);        \
+            launch_kernel((proj_bf16_kernel<1, BR, true, false>), grid, dim3(kThreads), s, a);        \
         else                                                                                          \
-            launch_kernel((proj_bf16_kernel<1, BR, false>), grid, dim3(kThreads), s, a);       \
+            launch_kernel((proj_bf16_kernel<1, BR, false, false>), grid, dim3(kThreads), s, a);       \
     } while (0)
     switch (a.n_branches) {
         case 1: ENGRAM_PROJ_V_LAUNCH(1); break;
