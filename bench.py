@@ -249,8 +249,11 @@ def main():
         "gate": ("hbm", part_bytes + Br * 4 * n_tok),
         # tile-seam rows: v of 6 rows per tile, h and out of up to 3 rows per tile and branch
         "seam": ("hbm", (n_tok // 256) * (6 * d * 4 + 3 * Br * (2 * d * eb + 16))),
-        # reads v (fp32) once, h once per branch, the gates; writes out per branch
-        "fuse": ("hbm", n_tok * (4 * d + Br * 2 * d * eb) + Br * 4 * n_tok),
+        # reads v (fp32) once, h once per branch and the partial sums (the
+        # gate is computed there); writes out per branch; with a carried conv
+        # state, reads and rewrites its K_c-1 fp32 rows per sequence and branch
+        "fuse": ("hbm", n_tok * (4 * d + Br * 2 * d * eb) + part_bytes
+                 + (2 * Br * wl.batch * (wl.conv_kernel - 1) * d * 4 if wl.decode else 0)),
     }
     # HBM bytes of the projection launches as well (E, weights, h, partials,
     # and v or out): the W_v launch sits close to both roofs
