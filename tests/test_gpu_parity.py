@@ -330,6 +330,71 @@ def test_forward_maxtable_sampled(B, maxtable_layer, name):
 
 
 # ----------------------------------------------------------------------------
+# the split calls: engram_hash -> engram_gather -> engram_gate_fuse
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", ["tiny", "bf16_1x2x300", "bf16_4x3x2", "bf16_2x2x77"])
+def test_split_calls_equal_forward_and_oracle(B, case):
+    """Retrieval and fusion as separate calls, with a carried context, a conv
+    state and the caller's alpha buffer: indices and E bit-exact against the
+    oracle; out, alpha and the new state within tolerance of the oracle and
+    bit-identical to engram_forward on the same inputs."""
+    say("split calls", case)
+    if case == "tiny":
+        wl = W.workload("tiny")
+    else:
+        br, batch, seqlen = (int(x) for x in case.split("_")[1].split("x"))
+        wl = small_wl(n_branches=br, batch=batch, seqlen=seqlen)
+    dl = make_device_layer(wl)
+    toks = W.make_tokens(wl)
+    batch, seqlen = toks.shape
+    n_tok, Br, d, S = batch * seqlen, wl.n_branches, wl.d_model, wl.conv_kernel - 1
+    rng = np.random.default_rng(23)
+    ctx0 = rng.integers(0, wl.vocab_comp + 1, (batch, 2)).astype(np.int32)  # PAD = V' included
+    ctx0[0] = wl.vocab_comp
+    st0 = (0.05 * rng.standard_normal((Br, batch, S, d))).astype(np.float32)
+    tdt = dl.h.dtype
+
+    ctx_s = dev_i32(ctx0)
+    idx = torch.zeros((n_tok, wl.n_tables), dtype=torch.int32, device="cuda")
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dl.plan.engram_hash(dev_i32(toks), dl.comp_map, idx, prev_ctx=ctx_s, bad_tokens=bad)
+    emb = torch.empty((n_tok, wl.emb_dim), dtype=tdt, device="cuda")
+    dl.plan.engram_gather(idx, dl.tables, emb)
+    st_s = to_device(st0, torch.float32, "cuda")
+    out_s = torch.empty_like(dl.h)
+    alpha_s = torch.full((Br, n_tok), -1.0, dtype=torch.float32, device="cuda")
+    ws = dl.plan.workspace(batch, seqlen)
+    dl.plan.engram_gate_fuse(emb, dl.h, dl.weights, out_s, ws, batch, seqlen, conv_state=st_s, alpha=alpha_s)
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 0
+    assert np.array_equal(ctx_s.cpu().numpy(), ctx0)  # engram_hash leaves the context alone
+
+    ctx_f = dev_i32(ctx0)
+    st_f = to_device(st0, torch.float32, "cuda")
+    out_f, alpha_f, _ = forward(dl, toks, prev_ctx=ctx_f, conv_state=st_f)
+    assert torch.equal(out_s, out_f)
+    assert torch.equal(alpha_s, alpha_f)
+    assert torch.equal(st_s, st_f)
+
+    idx_ref, _, new_ctx = oracle_indices(wl, dl.li, toks, dl.comp_map_host, prev_ctx=ctx0)
+    assert np.array_equal(idx.cpu().numpy().view(np.uint32), idx_ref)
+    assert np.array_equal(ctx_f.cpu().numpy(), new_ctx)
+    dt = oracle_dtype(wl)
+    emb_ref = oracle.gather_synth(idx_ref, wl.head_dim, dl.li.table_seed, dt)
+    got_emb = emb.view(torch.int16).cpu().numpy().view(np.uint16) if wl.dtype == "bf16" else emb.cpu().numpy()
+    assert np.array_equal(got_emb.view(np.uint8), emb_ref.view(np.uint8))
+    L = oracle_layer(wl, dl.li, idx_ref, batch, seqlen, conv_state=st0)
+    ref, ref_alpha, u = L.forward_all(want_u=True)
+    assert_within(host(out_s), ref, wl.dtype, case + " out")
+    assert np.abs(host(alpha_s) - ref_alpha).max() <= alpha_tol(wl.dtype)
+    assert np.all((host(alpha_s) > 0) & (host(alpha_s) < 1))
+    assert_within(st_s.cpu().numpy(), L.new_conv_state(u), wl.dtype, case + " new conv state")
+    del dl
+    torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------
 # invariants on the GPU path
 # ----------------------------------------------------------------------------
 
