@@ -15,7 +15,10 @@
 // registers, so no gated value is ever written to memory.  Loads for a group
 // of positions are issued before any of their arithmetic.  The three values
 // before the block's first position are recomputed from v (or taken from the
-// carried conv state at the sequence start).
+// carried conv state at the sequence start).  Those values, the first
+// group's v and h and the gate partials (staged in LDS by the whole block)
+// are all requested before any of them is used: at decode the kernel makes
+// one round trip to memory before it stores.
 #include "engram_internal.h"
 
 namespace engram {
@@ -57,9 +60,17 @@ struct Raw4 {
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + expf(-x)); }
 
-// The gate of token t, branch m, from the n_parts partial sums, in a fixed
-// order.  The one definition both kernels below use, so every path gets the
-// same bits.
+// The gate from the three sums over d of h*gamma_h*gamma_k*k, k^2 and h^2.
+__device__ __forceinline__ float gate_finish(float s_hk, float s_kk, float s_hh, int d, float eps) {
+    const float inv_d = 1.f / (float)d;
+    const float rh = sqrtf(s_hh * inv_d + eps);
+    const float rk = sqrtf(s_kk * inv_d + eps);
+    return sigmoidf_(s_hk / (rh * rk) * rsqrtf((float)d));
+}
+
+// The gate of token t, branch m, from the n_parts partial sums, added in
+// part order.  Every path adds the parts in this order and finishes with
+// gate_finish, so every path gets the same bits.
 __device__ __forceinline__ float gate_value(const float *partials, int m, int n_parts, int64_t n_tok, int64_t t,
                                             int d, float eps) {
     const float *pp = partials + (int64_t)m * n_parts * 3 * n_tok + t;
@@ -70,10 +81,7 @@ __device__ __forceinline__ float gate_value(const float *partials, int m, int n_
         s_kk += pp[(3 * q + 1) * n_tok];
         s_hh += pp[(3 * q + 2) * n_tok];
     }
-    const float inv_d = 1.f / (float)d;
-    const float rh = sqrtf(s_hh * inv_d + eps);
-    const float rk = sqrtf(s_kk * inv_d + eps);
-    return sigmoidf_(s_hk / (rh * rk) * rsqrtf((float)d));
+    return gate_finish(s_hk, s_kk, s_hh, d, eps);
 }
 
 __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
@@ -84,36 +92,115 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
     a.alpha[m * a.n_tok + t] = gate_value(a.partials, m, a.n_parts, a.n_tok, t, a.d, a.eps);
 }
 
+constexpr int kPartCap = 4096;  // gate partials staged in LDS per round
+
 template <bool BF16, int BR>
 __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
     __shared__ float alpha_s[BR][kPos + 3];
+    __shared__ float sums_s[3][BR * (kPos + 3)];
+    __shared__ float part_s[kPartCap];
     const int b = blockIdx.y;
     const int t0 = blockIdx.x * kPos;
     const int t1 = min(t0 + kPos, a.seqlen);
     const int64_t n_tok = (int64_t)a.batch * a.seqlen;
     const int64_t row0 = (int64_t)b * a.seqlen;
     const int d = a.d;
+    const int tid = threadIdx.x;
+    const int c0 = (blockIdx.z * blockDim.x + tid) * kVec;
+    const bool live = c0 < d;
+    const int kc = a.conv_k;
 
-    if (a.ctx.prev_ctx && blockIdx.x == 0 && blockIdx.z == 0 && threadIdx.x == 0) ctx_update_one(a.ctx, b, a.seqlen);
-    // gate values for positions t0-3 .. t1-1 (zero where unused)
-    for (int x = threadIdx.x; x < BR * (kPos + 3); x += blockDim.x) {
+    if (a.ctx.prev_ctx && blockIdx.x == 0 && blockIdx.z == 0 && tid == 0) ctx_update_one(a.ctx, b, a.seqlen);
+
+    // Everything this thread reads that does not depend on the gate is
+    // requested first, so it arrives in the same round trip as the gate
+    // partials below: the three values before t0 (v of earlier positions,
+    // or the carried state at the sequence start) and the first group's v
+    // and h.
+    f32x4_t vprev[3];
+    f32x4_t sprev[BR][3];
+#pragma unroll
+    for (int s = 1; s <= 3; ++s) {
+        const int p = t0 - s;
+        vprev[s - 1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (live && p >= 0) vprev[s - 1] = *reinterpret_cast<const f32x4_t *>(a.v + (row0 + p) * d + c0);
+#pragma unroll
+        for (int m = 0; m < BR; ++m) {
+            sprev[m][s - 1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (live && p < 0 && a.conv_state && s <= kc - 1)
+                sprev[m][s - 1] = *reinterpret_cast<const f32x4_t *>(
+                    a.conv_state + (((int64_t)m * a.batch + b) * (kc - 1) + (kc - 1 - s)) * d + c0);
+        }
+    }
+    constexpr int kGroup = BR == 1 ? 8 : (BR == 2 ? 4 : 2);
+    f32x4_t vv[kGroup];
+    Raw4<BF16> hv[kGroup][BR];
+    auto load_group = [&](int tg) {
+        const int n = min(kGroup, t1 - tg);
+#pragma unroll
+        for (int q = 0; q < kGroup; ++q) {
+            const int64_t row = row0 + tg + min(q, n - 1);
+            vv[q] = *reinterpret_cast<const f32x4_t *>(a.v + row * d + c0);
+#pragma unroll
+            for (int m = 0; m < BR; ++m) hv[q][m].load(a.h, ((int64_t)m * n_tok + row) * d + c0);
+        }
+    };
+    if (live) load_group(t0);
+
+    // Gates of positions pa .. t1-1 (the block's and up to three before it).
+    // The whole block stages the partial sums in LDS, as many parts per
+    // round as fit (all of them at decode sizes); one thread per (branch,
+    // position) then adds them in part order, as gate_value does.
+    const int pa = max(t0 - 3, 0);
+    const int npos = t1 - pa;
+    const int n_sum = BR * npos;
+    const int per_part = 3 * n_sum;
+    const int q_round = max(1, kPartCap / per_part);
+    for (int w = tid; w < n_sum; w += blockDim.x) sums_s[0][w] = sums_s[1][w] = sums_s[2][w] = 0.f;
+    for (int q0 = 0; q0 < a.n_parts; q0 += q_round) {
+        const int qn = min(q_round, a.n_parts - q0);
+        // staged layout: x = ((qq * BR + m) * 3 + k) * npos + pi
+        for (int x = tid; x < qn * per_part; x += blockDim.x) {
+            const int pi = x % npos;
+            const int r = x / npos;
+            const int k = r % 3;
+            const int mq = r / 3;
+            const int m = mq % BR, qq = mq / BR;
+            part_s[x] = a.partials[(((int64_t)m * a.n_parts + q0 + qq) * 3 + k) * n_tok + row0 + pa + pi];
+        }
+        __syncthreads();
+        for (int w = tid; w < n_sum; w += blockDim.x) {
+            const int m = w / npos, pi = w - m * npos;
+            float s_hk = sums_s[0][w], s_kk = sums_s[1][w], s_hh = sums_s[2][w];
+            for (int qq = 0; qq < qn; ++qq) {
+                const int base = ((qq * BR + m) * 3) * npos + pi;
+                s_hk += part_s[base];
+                s_kk += part_s[base + npos];
+                s_hh += part_s[base + 2 * npos];
+            }
+            sums_s[0][w] = s_hk;
+            sums_s[1][w] = s_kk;
+            sums_s[2][w] = s_hh;
+        }
+        __syncthreads();
+    }
+    // alpha_s[m][j] is the gate of position t0 - 3 + j (zero where unused)
+    for (int x = tid; x < BR * (kPos + 3); x += blockDim.x) {
         const int m = x / (kPos + 3), j = x - m * (kPos + 3);
         const int p = t0 - 3 + j;
         float al = 0.f;
-        if (p >= 0 && p < t1) {
-            al = gate_value(a.partials, m, a.n_parts, n_tok, row0 + p, d, a.eps);
+        if (p >= pa && p < t1) {
+            const int w = m * npos + (p - pa);
+            al = gate_finish(sums_s[0][w], sums_s[1][w], sums_s[2][w], d, a.eps);
             if (a.alpha && p >= t0 && blockIdx.z == 0) a.alpha[m * n_tok + row0 + p] = al;
         }
         alpha_s[m][j] = al;
     }
     __syncthreads();
+    if (!live) return;
 
-    const int c0 = (blockIdx.z * blockDim.x + threadIdx.x) * kVec;
-    if (c0 >= d) return;
-    const int kc = a.conv_k;
     const bool silu = a.conv_mode == ENGRAM_CONV_SILU_SKIP;
     const bool delta = (a.flags & ENGRAM_OUT_DELTA) != 0;
-
     float wt[4][kVec];  // wt[j][c] multiplies u_{t-j}
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -124,38 +211,17 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
     // win[m][s-1][c] = u_{t-s}
     float win[BR][3][kVec];
 #pragma unroll
-    for (int m = 0; m < BR; ++m) {
+    for (int m = 0; m < BR; ++m)
 #pragma unroll
         for (int s = 1; s <= 3; ++s) {
-            const int p = t0 - s;
-            if (p >= 0) {
-                const f32x4_t vv = *reinterpret_cast<const f32x4_t *>(a.v + (row0 + p) * d + c0);
-                const float al = alpha_s[m][3 - s];
+            const bool from_v = t0 - s >= 0;
+            const float al = alpha_s[m][3 - s];
 #pragma unroll
-                for (int c = 0; c < kVec; ++c) win[m][s - 1][c] = al * vv[c];
-            } else if (a.conv_state && s <= kc - 1) {
-                const float *st = a.conv_state + (((int64_t)m * a.batch + b) * (kc - 1) + (kc - 1 - s)) * d + c0;
-#pragma unroll
-                for (int c = 0; c < kVec; ++c) win[m][s - 1][c] = st[c];
-            } else {
-#pragma unroll
-                for (int c = 0; c < kVec; ++c) win[m][s - 1][c] = 0.f;
-            }
+            for (int c = 0; c < kVec; ++c) win[m][s - 1][c] = from_v ? al * vprev[s - 1][c] : sprev[m][s - 1][c];
         }
-    }
 
-    constexpr int kGroup = BR == 1 ? 8 : (BR == 2 ? 4 : 2);
     for (int tg = t0; tg < t1; tg += kGroup) {
         const int n = min(kGroup, t1 - tg);
-        f32x4_t vv[kGroup];
-        Raw4<BF16> hv[kGroup][BR];
-#pragma unroll
-        for (int q = 0; q < kGroup; ++q) {
-            const int64_t row = row0 + tg + min(q, n - 1);
-            vv[q] = *reinterpret_cast<const f32x4_t *>(a.v + row * d + c0);
-#pragma unroll
-            for (int m = 0; m < BR; ++m) hv[q][m].load(a.h, ((int64_t)m * n_tok + row) * d + c0);
-        }
 #pragma unroll
         for (int q = 0; q < kGroup; ++q) {
             if (q >= n) break;
@@ -178,6 +244,7 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
                 Raw4<BF16>::store(a.out, ((int64_t)m * n_tok + row) * d + c0, o);
             }
         }
+        if (tg + kGroup < t1) load_group(tg + kGroup);
     }
 
     // new conv state: the last K_c-1 gated values of the extended sequence
