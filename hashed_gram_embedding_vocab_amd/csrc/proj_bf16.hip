@@ -161,6 +161,17 @@ __device__ __forceinline__ void wait_lgkm0() {
     __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
 }
 
+// Byte offset (in one branch of h or out) of the 16-byte piece that lane
+// moves with chunk instruction k of the mode-1 epilogue: LDS row p = 8k +
+// lane/8 of the wave's 64 tokens (token t0 + rowbase + p, clamped into the
+// tokens), piece lane%8 of the row, read from global piece (lane%8) ^ ((p/4) % 8).
+__device__ __forceinline__ uint32_t chunk_offset(int k, int lane, int rowbase, int64_t t0, int64_t n_tok, int d,
+                                                 int nl) {
+    const int p = 8 * k + (lane >> 3);
+    const int64_t tok = min(max(t0 + rowbase + p, (int64_t)0), n_tok - 1);
+    return (uint32_t)((tok * d + nl) * 2) + (uint32_t)(((lane & 7) ^ ((p >> 2) & 7)) << 4);
+}
+
 // Mode-1 epilogue.  The tile's E rows were loaded so that in each wave's
 // group of 64 tokens, lane row l (l = lane % 16) holds tokens 4l + j in its
 // accumulator blocks j = 0..3: acc[i][j][r] is v of channel
@@ -288,7 +299,7 @@ __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t 
         const int row = rowbase + p;
         const int64_t tt = t0 + row;
         const int64_t tok = min(max(tt, (int64_t)0), n_tok - 1);
-        hoff[k] = (uint32_t)((tok * d + nl) * 2) + (uint32_t)(((lane & 7) ^ ((p >> 2) & 7)) << 4);
+        hoff[k] = chunk_offset(k, lane, rowbase, t0, n_tok, d, nl);
         bool store = tt < n_tok;
         if (row < kHalo) store = store && (int)(tok % a.seqlen) <= row;
         if (store) store_rows |= 1u << k;
@@ -402,14 +413,15 @@ __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t 
         }
     };
 
-    // Issue order: load(0), load(1), chunk 0's 8 stores, load(2), chunk 1's
+    // Issue order: load(0) (by the main loop, into buffer A as soon as the
+    // ring released it), load(1), chunk 0's 8 stores, load(2), chunk 1's
     // stores, load(3), ...  Before chunk c, the operations issued after
     // load(c) are chunk c-1's stores (8, for c >= 1) and load(c+1) (8, if
     // there is one).  Vector memory operations complete in issue order, so
     // waiting until no more than those are outstanding means chunk c has
-    // landed.  State stores and carried-state loads near sequence edges only
-    // add operations, which makes these waits stricter, never looser.
-    issue(hA, 0);
+    // landed.  State stores and carried-state loads near sequence edges, and
+    // the seam rows stored above after load(0), only add operations, which
+    // makes these waits stricter, never looser.
     issue(hB, 1);
 #pragma unroll 1
     for (int m = 0; m < BR; ++m) {
@@ -585,6 +597,59 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
         ENGRAM_ISSUE(st2, (ks + 6) * BK);
         ENGRAM_COMPUTE(st3);
     }
+    // Mode 0 epilogue input: h of the wave's TWT tokens x 128 channels, in
+    // whole 128-byte rows (loading it straight into the MFMA layout would read
+    // 16 rows x 32 bytes per instruction), two halves of TWT * 128 bytes for
+    // channels nl + 64q.  Half 0 goes to buffers 0 and 1, half 1 to buffers 2
+    // and 3 (wave w at byte w * kHalf of the pair); LDS row p is token tw + p,
+    // its eight 16-byte pieces XOR-swizzled by hswz(p).  Half 0 is requested
+    // as soon as buffers 0 and 1 are free, two stages before the main loop
+    // ends.  Waves whose rows are not a W_k matrix send their requests past
+    // the buffer's end (dropped, no branch), so every wave issues the same
+    // number of loads.
+    constexpr int kHalf = TWT * 128;
+    constexpr int kStageBytes = 2 * TOPB;
+    static_assert(TWAVES * kHalf <= 2 * kStageBytes, "half of every wave's h in two stage buffers");
+    const int nw = n0 + wn_blk * 16;  // the wave's first output row (n_total % 128 == 0: inside the launch)
+    const int mat = nw / d;           // the wave's 128 rows lie in one matrix (d % 128 == 0)
+    const int nl = nw - mat * d;      // first channel within that matrix
+    const int64_t tw = t0 + wt_blk * 16;
+    auto hswz = [](int p) { return (p ^ (p >> 3)) & 7; };
+    auto h_half = [&](int q) -> unsigned char * {
+        const int off = wave * kHalf;
+        unsigned char *pair0 = reinterpret_cast<unsigned char *>(q == 0 ? &st0 : &st2);
+        unsigned char *pair1 = reinterpret_cast<unsigned char *>(q == 0 ? &st1 : &st3);
+        return (off < kStageBytes ? pair0 : pair1) + (off % kStageBytes);
+    };
+    auto h_issue = [&](int q) {
+        const bool is_k = mat < a.n_branches;
+        const int hm = is_k ? mat : 0;
+        const __amdgpu_buffer_rsrc_t hres = make_rsrc(
+            reinterpret_cast<const uint16_t *>(a.h) + (int64_t)hm * a.n_tok * d, (uint32_t)(a.n_tok * d * 2));
+        unsigned char *dst = h_half(q);
+#pragma unroll
+        for (int k = 0; k < TWT / 8; ++k) {
+            const int p = 8 * k + (lane >> 3);
+            const int64_t tok = min(tw + p, a.n_tok - 1);
+            const uint32_t off = (uint32_t)((tok * d + nl) * 2) + (uint32_t)(((lane & 7) ^ hswz(p)) << 4);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(hres, (lds_void_t *)(dst + k * 1024), 16,
+                                                     is_k ? off : 0x80000000u, 128 * q, 0, 0);
+        }
+    };
+    // Mode 1: chunk 0 of the epilogue (branch 0, the wave's first 64
+    // channels) into buffer A, likewise two stages early.
+    unsigned char *hA = reinterpret_cast<unsigned char *>(wave < 4 ? &st0 : &st1) + (wave & 3) * 8192;
+    unsigned char *hB = reinterpret_cast<unsigned char *>(wave < 4 ? &st2 : &st3) + (wave & 3) * 8192;
+    auto chunk0_issue = [&]() {
+        const __amdgpu_buffer_rsrc_t hres = make_rsrc(a.h, (uint32_t)(a.n_tok * d * 2) * (uint32_t)BR);
+        const int rowbase = 64 * (wave >> 1);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(hres, (lds_void_t *)(hA + k * 1024), 16,
+                                                     chunk_offset(k, lane, rowbase, t0, a.n_tok, d, nl), 0, 0, 0);
+    };
+    constexpr int kEarlyH = MODE == 0 ? TWT / 8 : 8;  // loads issued in the ring's tail
+
     // the last four stages: ks = k_steps - 4; stages ks..ks+2 are in flight
     wait_vmcnt<2 * kLoadsPerStage>();
     block_barrier();
@@ -594,9 +659,11 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
     block_barrier();
     ENGRAM_COMPUTE(st1);
     wait_vmcnt<kLoadsPerStage>();
-    block_barrier();
+    block_barrier();  // buffers 0 and 1 are done with
+    if constexpr (MODE == 0) h_issue(0);
+    if constexpr (MODE == 1) chunk0_issue();
     ENGRAM_COMPUTE(st2);
-    wait_vmcnt<0>();
+    wait_vmcnt<kEarlyH>();
     block_barrier();
     ENGRAM_COMPUTE(st3);
 #undef ENGRAM_COMPUTE
@@ -604,12 +671,7 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
 
     // ---- epilogue.  acc[i][j][r] is output channel n = nw + 16i + 4*(lane/16) + r
     //      of token t = tw + 16j + lane%16.
-    const int nw = n0 + wn_blk * 16;
-    if (nw >= n_total) return;
-    const int mat = nw / d;       // the wave's 128 rows lie in one matrix (d % 128 == 0)
-    const int nl = nw - mat * d;  // first channel within that matrix
     const int sub = 4 * (lane >> 4);
-    const int64_t tw = t0 + wt_blk * 16;
 
     if constexpr (MODE == 0) {
     if (mat < a.n_branches) {
@@ -624,33 +686,10 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
         }
         const int part = nl / kPartCols;
         float *pbase = a.partials + ((int64_t)mat * a.n_parts + part) * 3 * a.n_tok;
-        // h of the wave's TWT tokens x 128 channels arrives in LDS by DMA, in
-        // whole 128-byte rows (loading it straight into the MFMA layout would
-        // read 16 rows x 32 bytes per instruction): TWT * 256 bytes per wave
-        // in the now idle stage buffers (two waves per stage), two halves for
-        // channels nl + 64q, row p = token tw + p, its eight 16-byte pieces
-        // XOR-swizzled by hswz(p).  All of it is requested at once: one
-        // memory round trip.
-        constexpr int kHalf = TWT * 128;
-        static_assert(4 * kHalf == 2 * TOPB, "two waves' h per stage buffer");
+        // half 1 of h (half 0 is in flight since the ring's tail)
         block_barrier();  // every wave is done reading the stage buffers
-        unsigned char *hbuf = reinterpret_cast<unsigned char *>(
-                                  wave < 2 ? &st0 : (wave < 4 ? &st1 : (wave < 6 ? &st2 : &st3))) +
-                              (wave & 1) * 2 * kHalf;
-        auto hswz = [](int p) { return (p ^ (p >> 3)) & 7; };
-        {
-            const __amdgpu_buffer_rsrc_t hres = make_rsrc(
-                reinterpret_cast<const uint16_t *>(a.h) + (int64_t)mat * a.n_tok * d, (uint32_t)(a.n_tok * d * 2));
-#pragma unroll
-            for (int k = 0; k < TWT / 8; ++k) {
-                const int p = 8 * k + (lane >> 3);
-                const int64_t tok = min(tw + p, a.n_tok - 1);
-                const uint32_t off = (uint32_t)((tok * d + nl) * 2) + (uint32_t)(((lane & 7) ^ hswz(p)) << 4);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(hres, (lds_void_t *)(hbuf + k * 1024), 16, off, 0, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(hres, (lds_void_t *)(hbuf + kHalf + k * 1024), 16, off, 128,
-                                                         0, 0);
-            }
-        }
+        h_issue(1);
+        unsigned char *h0 = h_half(0), *h1 = h_half(1);
         wait_vmcnt<0>();
         asm volatile("" ::: "memory");
 #pragma unroll
@@ -661,7 +700,7 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
 #pragma unroll
             for (int i = 0; i < FN; ++i) {
                 const u32x2_t x = *reinterpret_cast<const u32x2_t *>(
-                    hbuf + (i >> 2) * kHalf + p * 128 + (((2 * (i & 3) + (sub >> 3)) ^ hswz(p)) << 4) + (sub & 4) * 2);
+                    ((i >> 2) ? h1 : h0) + p * 128 + (((2 * (i & 3) + (sub >> 3)) ^ hswz(p)) << 4) + (sub & 4) * 2);
                 const f32x4_t g = *reinterpret_cast<const f32x4_t *>(gsm + 16 * i + sub);
                 const float h4[4] = {bf16_to_f32(x[0] & 0xFFFFu), bf16_to_f32(x[0] >> 16),
                                      bf16_to_f32(x[1] & 0xFFFFu), bf16_to_f32(x[1] >> 16)};
@@ -697,8 +736,6 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
     }
     } else {
         // each wave's two chunk buffers: 8 KB of st0/st1 (A) and of st2/st3 (B)
-        unsigned char *hA = reinterpret_cast<unsigned char *>(wave < 4 ? &st0 : &st1) + (wave & 3) * 8192;
-        unsigned char *hB = reinterpret_cast<unsigned char *>(wave < 4 ? &st2 : &st3) + (wave & 3) * 8192;
         fused_value_epilogue<BR, SILU>(a, acc, alpha_s, halo_s, taps_s, hA, hB, wave, lane, nl, n0, tile_t, t0);
     }
 }
