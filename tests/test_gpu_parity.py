@@ -329,6 +329,44 @@ def test_forward_maxtable_sampled(B, maxtable_layer, name):
     _sampled_check(wl, maxtable_layer, toks, 24, name)
 
 
+@pytest.mark.parametrize("dtype,d,heads,head_dim,orders,kc,br,batch,seqlen", [
+    ("bf16", 256, 2, 32, (2, 3), 1, 2, 2, 300),   # no conv history
+    ("bf16", 256, 2, 32, (2, 3), 2, 1, 3, 77),
+    ("bf16", 512, 4, 32, (3,), 3, 3, 2, 130),     # trigrams only
+    ("bf16", 256, 4, 32, (2,), 4, 1, 1, 257),     # bigrams only, one token past a tile
+    ("bf16", 256, 2, 32, (2, 3), 2, 4, 4, 1),     # one-token chunks on the fused path (K_c - 1 = 1)
+    ("bf16", 256, 2, 32, (2, 3), 3, 2, 5, 1),     # one-token chunks on the fusion kernel, K_c = 3
+    ("f32", 200, 3, 4, (2, 3), 3, 2, 2, 45),      # d not a multiple of 64, D_e = 24
+    ("f32", 72, 1, 12, (2, 3), 2, 3, 3, 33),      # a sequence over two fusion workgroups
+])
+def test_forward_other_shapes_all_positions(B, dtype, d, heads, head_dim, orders, kc, br, batch, seqlen):
+    """Conv kernels shorter than 4, single-order n-grams and odd fp32 widths,
+    with a carried context and conv state: every position against the oracle,
+    and the new state and context."""
+    say("other shapes", dtype, d, heads, head_dim, orders, kc, br, batch, seqlen)
+    wl = dataclasses.replace(small_wl(n_branches=br, batch=batch, seqlen=seqlen, d_model=d, heads=heads,
+                                      head_dim=head_dim, conv_kernel=kc, dtype=dtype), orders=orders)
+    dl = make_device_layer(wl)
+    toks = W.make_tokens(wl)
+    rng = np.random.default_rng(d + kc)
+    ctx0 = rng.integers(0, wl.vocab_comp + 1, (batch, 2)).astype(np.int32)
+    st0 = (0.05 * rng.standard_normal((br, batch, max(kc - 1, 0), d))).astype(np.float32)
+    ctx = dev_i32(ctx0)
+    st = to_device(st0, torch.float32, "cuda") if kc > 1 else None
+    out, alpha, bad = forward(dl, toks, prev_ctx=ctx, conv_state=st)
+    assert bad == 0
+    idx, _, new_ctx = oracle_indices(wl, dl.li, toks, dl.comp_map_host, prev_ctx=ctx0)
+    L = oracle_layer(wl, dl.li, idx, batch, seqlen, conv_state=st0 if kc > 1 else None)
+    ref, ref_alpha, u = L.forward_all(want_u=True)
+    assert_within(host(out), ref, dtype, "out")
+    assert np.abs(host(alpha) - ref_alpha).max() <= alpha_tol(dtype)
+    assert np.array_equal(ctx.cpu().numpy(), new_ctx)
+    if kc > 1:
+        assert_within(st.cpu().numpy(), L.new_conv_state(u), dtype, "new conv state")
+    del dl
+    torch.cuda.empty_cache()
+
+
 # ----------------------------------------------------------------------------
 # the split calls: engram_hash -> engram_gather -> engram_gate_fuse
 # ----------------------------------------------------------------------------
