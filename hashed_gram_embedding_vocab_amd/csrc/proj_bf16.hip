@@ -137,13 +137,18 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Workgroup barrier without a memory fence.  __syncthreads() would also
-// wait for every outstanding load, including the next stage's LDS fills this
-// kernel deliberately leaves in flight; visibility of a stage is instead
-// established by each wave's own vmcnt wait before the barrier.  The empty
-// asm statements keep the compiler from moving LDS accesses across it.
+// Workgroup barrier without a vector-memory wait.  __syncthreads() would
+// also wait for every outstanding load, including the next stage's LDS fills
+// this kernel deliberately leaves in flight; visibility of a stage is instead
+// established by each wave's own vmcnt wait before the barrier.  The wave's
+// own LDS reads are drained first (lgkmcnt(0)): the compiler may otherwise
+// issue a stage's last fragment reads before the barrier and wait for them
+// after it, and the buffer they read is refilled by DMA right after the
+// barrier.  The empty asm statements keep the compiler from moving LDS
+// accesses across it.
 __device__ __forceinline__ void block_barrier() {
     asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0) only
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
