@@ -76,6 +76,11 @@ def lib():
                                             C.c_double, u32, i32, P, P, P, P, P, P, P, P, P, P, P]
             L.orc_conv_state_update.restype = None
             L.orc_conv_state_update.argtypes = [i64, i64, i32, i32, i32, P, P, P]
+            L.orc_backward.restype = i32
+            L.orc_backward.argtypes = [i64, i64, i32, i32, i32, i32, i32, C.c_double, u32, i32,
+                                       P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
+            L.orc_table_grad.restype = None
+            L.orc_table_grad.argtypes = [P, i64, i32, i32, P, P, P, P]
             _lib = L
         return _lib
 
@@ -247,6 +252,26 @@ class Layer:
         u = np.concatenate(us, 1) if want_u else None
         return out, alpha, u
 
+    def backward(self, dout) -> dict:
+        """Gradients of <dout, out> over whole sequences (no carried conv state):
+        dh [B_r][n_tok][d], demb [n_tok][De], dw_k [B_r][d][De], dw_v [d][De],
+        dgamma_h, dgamma_k [B_r][d], dconv_w [d][K_c], all float64."""
+        if self.conv_state is not None:
+            raise ValueError("the backward oracle covers whole sequences (no carried state)")
+        n_tok = self.batch * self.seqlen
+        Br, d, De, kc = self.n_branches, self.d, self.De, self.conv_k
+        g = {"dh": np.zeros((Br, n_tok, d)), "demb": np.zeros((n_tok, De)), "dw_k": np.zeros((Br, d, De)),
+             "dw_v": np.zeros((d, De)), "dgamma_h": np.zeros((Br, d)), "dgamma_k": np.zeros((Br, d)),
+             "dconv_w": np.zeros((d, kc))}
+        rc = lib().orc_backward(self.batch, self.seqlen, d, De, Br, kc, self.conv_mode, self.eps, self.flags,
+                                self.dtype, _p(self.emb), _p(self.h), _p(self.w_k), _p(self.w_v),
+                                _p(self.gamma_h), _p(self.gamma_k), _p(self.conv_w),
+                                _p(_stored(dout, self.dtype)), _p(g["dh"]), _p(g["demb"]), _p(g["dw_k"]),
+                                _p(g["dw_v"]), _p(g["dgamma_h"]), _p(g["dgamma_k"]), _p(g["dconv_w"]))
+        if rc != 0:
+            raise ValueError("orc_backward: bad arguments")
+        return g
+
     def new_conv_state(self, u_all: np.ndarray) -> np.ndarray:
         """State after this chunk, from the chunk's gated values u_all [B_r][n_tok][d]."""
         S = self.conv_k - 1
@@ -257,3 +282,17 @@ class Layer:
         lib().orc_conv_state_update(self.batch, self.seqlen, self.d, self.n_branches, self.conv_k,
                                     _p(u), _p(self.conv_state), _p(out))
         return out
+
+
+def table_grad(idx: np.ndarray, demb: np.ndarray, head_dim: int):
+    """Per table: distinct rows (ascending), their summed gradients and the
+    count: rows [n_tables][n_tok] uint32, grads [n_tables][n_tok][head_dim]
+    float64, counts [n_tables] (only the first counts[tau] entries are set)."""
+    idx = _c(idx, np.uint32)
+    n_tok, n_tables = idx.shape
+    demb = _c(demb, np.float64)
+    rows = np.zeros((n_tables, n_tok), np.uint32)
+    grads = np.zeros((n_tables, n_tok, head_dim), np.float64)
+    counts = np.zeros(n_tables, np.int64)
+    lib().orc_table_grad(_p(idx), n_tok, n_tables, head_dim, _p(demb), _p(rows), _p(grads), _p(counts))
+    return rows, grads, counts

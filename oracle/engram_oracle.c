@@ -414,3 +414,215 @@ void orc_conv_state_update(int64_t batch, int64_t seqlen, int32_t d, int32_t n_b
                 }
             }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Backward of O5-O10 (gradients for training)                               */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Gradients of L = <dout, out> for whole sequences (no carried conv state),
+ * every branch.  The pages say the table slots learn from the gradients that
+ * reach them ([csdn] 实际效果到底有多好); the derivative itself is the chain
+ * rule through the forward of orc_forward_range, written out step by step:
+ *   out = h + y (or y with ORC_OUT_DELTA)            dh += dout
+ *   y = conv (LINEAR) or u + conv*sigmoid(conv)      dconv, du (direct term)
+ *   conv_t = sum_j w[K-1-j] u_{t-j}                  du_t += sum_j w[K-1-j] dconv_{t+j},
+ *                                                    dw[K-1-j] += sum_t u_{t-j} dconv_t
+ *   u = alpha v                                      dalpha = <v, du>, dv += alpha du
+ *   alpha = sigmoid(s)                               ds = dalpha alpha (1 - alpha)
+ *   s = <a, b>/sqrt(d), a = gh*h/rh, b = gk*k/rk     da = ds b/sqrt(d), db = ds a/sqrt(d)
+ *   RMSNorm x -> g*x/r, r = sqrt(mean(x^2) + eps)    dgamma += dy x/r,
+ *                                                    dx = (g*dy - (x/r) <g*dy, x/r>/d) / r
+ *   k = W_k e, v = W_v e                             dW += d(k|v) e^T, de += W^T d(k|v)
+ * Inputs as orc_forward_range (dtype fp32 or bf16), dout [n_branches][n_tok][d].
+ * Outputs (double, overwritten):
+ *   dh [n_branches][n_tok][d], demb [n_tok][De], dw_k [n_branches][d][De],
+ *   dw_v [d][De], dgamma_h/dgamma_k [n_branches][d], dconv_w [d][conv_k].
+ */
+int32_t orc_backward(int64_t batch, int64_t seqlen, int32_t d, int32_t De, int32_t n_branches,
+                     int32_t conv_k, int32_t conv_mode, double eps, uint32_t flags, int32_t dtype,
+                     const void *emb, const void *h, const void *w_k, const void *w_v,
+                     const float *gamma_h, const float *gamma_k, const float *conv_w,
+                     const void *dout, double *dh, double *demb, double *dw_k, double *dw_v,
+                     double *dgamma_h, double *dgamma_k, double *dconv_w) {
+    if (batch < 1 || seqlen < 1 || d < 1 || De < 1 || n_branches < 1 || conv_k < 1) return 1;
+    const int64_t n_tok = batch * seqlen;
+    const size_t es = dtype == ORC_BF16 ? 2 : 4;
+    const double sqd = sqrt((double)d);
+    memset(dh, 0, sizeof(double) * (size_t)(n_branches * n_tok * d));
+    memset(demb, 0, sizeof(double) * (size_t)(n_tok * De));
+    memset(dw_k, 0, sizeof(double) * (size_t)((int64_t)n_branches * d * De));
+    memset(dw_v, 0, sizeof(double) * (size_t)((int64_t)d * De));
+    memset(dgamma_h, 0, sizeof(double) * (size_t)(n_branches * d));
+    memset(dgamma_k, 0, sizeof(double) * (size_t)(n_branches * d));
+    memset(dconv_w, 0, sizeof(double) * (size_t)(d * conv_k));
+
+    double *V = (double *)malloc(sizeof(double) * (size_t)(seqlen * d));   /* v of every position */
+    double *DV = (double *)malloc(sizeof(double) * (size_t)(seqlen * d));  /* dv, summed over branches */
+    double *Kk = (double *)malloc(sizeof(double) * (size_t)(seqlen * d));  /* k of this branch */
+    double *U = (double *)malloc(sizeof(double) * (size_t)(seqlen * d));
+    double *CV = (double *)malloc(sizeof(double) * (size_t)(seqlen * d));  /* conv */
+    double *DC = (double *)malloc(sizeof(double) * (size_t)(seqlen * d));  /* dconv */
+    double *DU = (double *)malloc(sizeof(double) * (size_t)(seqlen * d));
+    double *al = (double *)malloc(sizeof(double) * (size_t)seqlen);
+    double *rh = (double *)malloc(sizeof(double) * (size_t)seqlen);
+    double *rk = (double *)malloc(sizeof(double) * (size_t)seqlen);
+    double *dk = (double *)malloc(sizeof(double) * (size_t)d);
+
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t t = 0; t < seqlen; ++t)
+            orc_project((const char *)emb + (size_t)(b * seqlen + t) * De * es, w_v, d, De, dtype, V + t * d);
+        memset(DV, 0, sizeof(double) * (size_t)(seqlen * d));
+        for (int32_t m = 0; m < n_branches; ++m) {
+            const char *hm = (const char *)h + (size_t)m * n_tok * d * es;
+            const char *wkm = (const char *)w_k + (size_t)m * d * De * es;
+            const char *gm = (const char *)dout + (size_t)m * n_tok * d * es;
+            const float *gh = gamma_h + (size_t)m * d, *gk = gamma_k + (size_t)m * d;
+            /* forward: k, the gate and the gated values */
+            for (int64_t t = 0; t < seqlen; ++t) {
+                const int64_t row = b * seqlen + t;
+                double *kt = Kk + t * d;
+                orc_project((const char *)emb + (size_t)row * De * es, wkm, d, De, dtype, kt);
+                double sh = 0.0, sk = 0.0;
+                for (int32_t n = 0; n < d; ++n) {
+                    double hn = orc_load(hm, row * d + n, dtype);
+                    sh += hn * hn;
+                    sk += kt[n] * kt[n];
+                }
+                rh[t] = sqrt(sh / d + eps);
+                rk[t] = sqrt(sk / d + eps);
+                double dot = 0.0;
+                for (int32_t n = 0; n < d; ++n)
+                    dot += (orc_load(hm, row * d + n, dtype) * gh[n] / rh[t]) * (kt[n] * gk[n] / rk[t]);
+                al[t] = 1.0 / (1.0 + exp(-dot / sqd));
+                for (int32_t n = 0; n < d; ++n) U[t * d + n] = al[t] * V[t * d + n];
+            }
+            for (int64_t t = 0; t < seqlen; ++t)
+                for (int32_t n = 0; n < d; ++n) {
+                    double c = 0.0;
+                    for (int32_t j = 0; j < conv_k && j <= t; ++j)
+                        c += (double)conv_w[(int64_t)n * conv_k + (conv_k - 1 - j)] * U[(t - j) * d + n];
+                    CV[t * d + n] = c;
+                }
+            /* backward through the output, the conv and the gated value */
+            for (int64_t t = 0; t < seqlen; ++t) {
+                const int64_t row = b * seqlen + t;
+                for (int32_t n = 0; n < d; ++n) {
+                    double g = orc_load(gm, row * d + n, dtype);
+                    double c = CV[t * d + n];
+                    double dc = g;
+                    if (conv_mode == ORC_CONV_SILU_SKIP) {
+                        double sg = 1.0 / (1.0 + exp(-c));
+                        dc = g * (sg + c * sg * (1.0 - sg));
+                    }
+                    DC[t * d + n] = dc;
+                    if (!(flags & ORC_OUT_DELTA)) dh[((int64_t)m * n_tok + row) * d + n] = g;
+                }
+            }
+            for (int64_t t = 0; t < seqlen; ++t) {
+                const int64_t row = b * seqlen + t;
+                for (int32_t n = 0; n < d; ++n) {
+                    double du = conv_mode == ORC_CONV_SILU_SKIP ? orc_load(gm, row * d + n, dtype) : 0.0;
+                    for (int32_t j = 0; j < conv_k && t + j < seqlen; ++j)
+                        du += (double)conv_w[(int64_t)n * conv_k + (conv_k - 1 - j)] * DC[(t + j) * d + n];
+                    DU[t * d + n] = du;
+                    for (int32_t j = 0; j < conv_k && j <= t; ++j)
+                        dconv_w[(int64_t)n * conv_k + (conv_k - 1 - j)] += U[(t - j) * d + n] * DC[t * d + n];
+                }
+            }
+            /* backward through the gate, both RMSNorms and W_k */
+            for (int64_t t = 0; t < seqlen; ++t) {
+                const int64_t row = b * seqlen + t;
+                const double *kt = Kk + t * d;
+                double dal = 0.0;
+                for (int32_t n = 0; n < d; ++n) {
+                    dal += V[t * d + n] * DU[t * d + n];
+                    DV[t * d + n] += al[t] * DU[t * d + n];
+                }
+                const double ds = dal * al[t] * (1.0 - al[t]);
+                double Sh = 0.0, Sk = 0.0;
+                for (int32_t n = 0; n < d; ++n) {
+                    const double hn = orc_load(hm, row * d + n, dtype);
+                    const double an = gh[n] * hn / rh[t], bn = gk[n] * kt[n] / rk[t];
+                    const double da = ds * bn / sqd, db = ds * an / sqd;
+                    dgamma_h[(int64_t)m * d + n] += da * hn / rh[t];
+                    dgamma_k[(int64_t)m * d + n] += db * kt[n] / rk[t];
+                    Sh += gh[n] * da * (hn / rh[t]);
+                    Sk += gk[n] * db * (kt[n] / rk[t]);
+                }
+                for (int32_t n = 0; n < d; ++n) {
+                    const double hn = orc_load(hm, row * d + n, dtype);
+                    const double an = gh[n] * hn / rh[t], bn = gk[n] * kt[n] / rk[t];
+                    const double da = ds * bn / sqd, db = ds * an / sqd;
+                    dh[((int64_t)m * n_tok + row) * d + n] += (gh[n] * da - (hn / rh[t]) * Sh / d) / rh[t];
+                    dk[n] = (gk[n] * db - (kt[n] / rk[t]) * Sk / d) / rk[t];
+                }
+                for (int32_t n = 0; n < d; ++n)
+                    for (int32_t j = 0; j < De; ++j) {
+                        const double ej = orc_load((const char *)emb + (size_t)row * De * es, j, dtype);
+                        dw_k[((int64_t)m * d + n) * De + j] += dk[n] * ej;
+                        demb[row * De + j] += orc_load(wkm, (int64_t)n * De + j, dtype) * dk[n];
+                    }
+            }
+        }
+        /* W_v, shared by the branches */
+        for (int64_t t = 0; t < seqlen; ++t) {
+            const int64_t row = b * seqlen + t;
+            for (int32_t n = 0; n < d; ++n)
+                for (int32_t j = 0; j < De; ++j) {
+                    const double ej = orc_load((const char *)emb + (size_t)row * De * es, j, dtype);
+                    dw_v[(int64_t)n * De + j] += DV[t * d + n] * ej;
+                    demb[row * De + j] += orc_load(w_v, (int64_t)n * De + j, dtype) * DV[t * d + n];
+                }
+        }
+    }
+    free(V); free(DV); free(Kk); free(U); free(CV); free(DC); free(DU);
+    free(al); free(rh); free(rk); free(dk);
+    return 0;
+}
+
+/* One (row, token) pair of a table's gathered rows, for the sort below. */
+typedef struct {
+    uint32_t row;
+    int64_t t;
+} orc_row_use;
+
+static int orc_row_use_cmp(const void *x, const void *y) {
+    const orc_row_use *a = (const orc_row_use *)x, *b = (const orc_row_use *)y;
+    if (a->row != b->row) return a->row < b->row ? -1 : 1;
+    return a->t < b->t ? -1 : (a->t > b->t);
+}
+
+/*
+ * Gradient of the table rows a chunk gathered: token t's row of table tau,
+ * idx[t][tau], receives demb[t][tau*head_dim : (tau+1)*head_dim].  Per table,
+ * the distinct rows in ascending order and each row's summed gradient (added
+ * in ascending token order).
+ *   rows   [n_tables][n_tok]            (the first counts[tau] entries used)
+ *   grads  [n_tables][n_tok][head_dim]  (likewise)
+ *   counts [n_tables]
+ */
+void orc_table_grad(const uint32_t *idx, int64_t n_tok, int32_t n_tables, int32_t head_dim,
+                    const double *demb, uint32_t *rows, double *grads, int64_t *counts) {
+    const int64_t De = (int64_t)n_tables * head_dim;
+    orc_row_use *use = (orc_row_use *)malloc(sizeof(orc_row_use) * (size_t)n_tok);
+    for (int32_t tau = 0; tau < n_tables; ++tau) {
+        for (int64_t t = 0; t < n_tok; ++t) {
+            use[t].row = idx[t * n_tables + tau];
+            use[t].t = t;
+        }
+        qsort(use, (size_t)n_tok, sizeof(orc_row_use), orc_row_use_cmp);
+        int64_t r = -1;
+        for (int64_t i = 0; i < n_tok; ++i) {
+            if (i == 0 || use[i].row != use[i - 1].row) {
+                ++r;
+                rows[(int64_t)tau * n_tok + r] = use[i].row;
+                for (int32_t c = 0; c < head_dim; ++c) grads[((int64_t)tau * n_tok + r) * head_dim + c] = 0.0;
+            }
+            for (int32_t c = 0; c < head_dim; ++c)
+                grads[((int64_t)tau * n_tok + r) * head_dim + c] += demb[use[i].t * De + (int64_t)tau * head_dim + c];
+        }
+        counts[tau] = r + 1;
+    }
+    free(use);
+}
