@@ -25,7 +25,8 @@ F32, BF16 = 0, 1
 CONV_LINEAR, CONV_SILU_SKIP = 0, 1
 OUT_DELTA = 1
 MAX_TABLES, MAX_BRANCHES = 32, 4
-KERNEL_NAMES = ("hash", "gather", "gemm", "fuse", "aux", "gemm_v", "gate", "seam")
+KERNEL_NAMES = ("hash", "gather", "gemm", "fuse", "aux", "gemm_v", "gate", "seam", "bwd_gemm", "bwd_fuse",
+                "bwd_table")
 
 
 class EngramError(RuntimeError):
@@ -53,7 +54,15 @@ class WeightsC(C.Structure):
 
 
 class ProfileC(C.Structure):
-    _fields_ = [("total_ms", C.c_double * 8), ("launches", C.c_int64 * 8), ("dropped", C.c_int64)]
+    _fields_ = [("total_ms", C.c_double * len(KERNEL_NAMES)), ("launches", C.c_int64 * len(KERNEL_NAMES)),
+                ("dropped", C.c_int64)]
+
+
+class GradsC(C.Structure):
+    _fields_ = [
+        ("dw", C.c_void_p), ("dgamma_h", C.c_void_p), ("dgamma_k", C.c_void_p), ("dconv_w", C.c_void_p),
+        ("row_ids", C.c_void_p), ("row_grads", C.c_void_p), ("row_counts", C.c_void_p),
+    ]
 
 
 _lib = None
@@ -89,6 +98,11 @@ def lib() -> C.CDLL:
         L.engram_forward.restype = C.c_int
         L.engram_forward.argtypes = [P, P, i32, i32, P, P, P, P, C.POINTER(WeightsC), P, P, P, u32,
                                      P, C.c_size_t, P, P]
+        L.engram_backward_workspace_size.restype = C.c_size_t
+        L.engram_backward_workspace_size.argtypes = [P, i32, i32]
+        L.engram_backward.restype = C.c_int
+        L.engram_backward.argtypes = [P, P, P, P, C.POINTER(WeightsC), P, i32, i32, u32, P, C.POINTER(GradsC),
+                                      P, C.c_size_t, P]
         L.engram_profile_begin.restype = C.c_int
         L.engram_profile_begin.argtypes = [P, i32, u32]
         L.engram_profile_end.restype = C.c_int
@@ -124,6 +138,23 @@ def _stream(stream) -> C.c_void_p:
 
 def _torch_dtype(dt: int):
     return torch.bfloat16 if dt == BF16 else torch.float32
+
+
+class Grads:
+    """Device tensors receiving engram_backward's gradients (fp32), plus their C struct."""
+
+    def __init__(self, n_branches: int, d: int, emb_dim: int, conv_k: int, n_tables: int, n_tok: int,
+                 head_dim: int, device="cuda"):
+        f = dict(dtype=torch.float32, device=device)
+        self.dw = torch.zeros((n_branches + 1, d, emb_dim), **f)
+        self.dgamma_h = torch.zeros((n_branches, d), **f)
+        self.dgamma_k = torch.zeros((n_branches, d), **f)
+        self.dconv_w = torch.zeros((d, conv_k), **f)
+        self.row_ids = torch.zeros((n_tables, n_tok), dtype=torch.int32, device=device)
+        self.row_grads = torch.zeros((n_tables, n_tok, head_dim), **f)
+        self.row_counts = torch.zeros((n_tables,), dtype=torch.int32, device=device)
+        self.c = GradsC(*[C.c_void_p(t.data_ptr()) for t in (self.dw, self.dgamma_h, self.dgamma_k, self.dconv_w,
+                                                            self.row_ids, self.row_grads, self.row_counts)])
 
 
 class Weights:
@@ -221,6 +252,24 @@ class Plan:
             _ptr(alpha, "alpha", torch.float32), flags, _ptr(workspace, "workspace"),
             workspace.numel() * workspace.element_size(),
             _ptr(bad_tokens, "bad_tokens", (torch.int32, torch.uint32)), _stream(stream)))
+
+    def engram_backward_workspace_size(self, batch: int, seqlen: int) -> int:
+        return int(lib().engram_backward_workspace_size(self._h, batch, seqlen))
+
+    def engram_backward(self, idx, tables: Sequence[torch.Tensor], h, weights: "Weights", dout, dh,
+                        grads: "Grads", workspace, batch: int, seqlen: int, flags: int = 0, stream=None):
+        ptrs = (C.c_void_p * len(tables))(*[_ptr(t, "table").value for t in tables])
+        _check("engram_backward", lib().engram_backward(
+            self._h, _ptr(idx, "idx", (torch.int32, torch.uint32)), ptrs, _ptr(h, "h", self.torch_dtype),
+            C.byref(weights.c), _ptr(dout, "dout", self.torch_dtype), batch, seqlen, flags,
+            _ptr(dh, "dh", self.torch_dtype), C.byref(grads.c), _ptr(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _stream(stream)))
+
+    def backward_workspace(self, batch: int, seqlen: int, device="cuda") -> torch.Tensor:
+        n = self.engram_backward_workspace_size(batch, seqlen)
+        if n == 0:
+            raise EngramError("engram_backward_workspace_size", E_UNSUPPORTED, "unsupported shape")
+        return torch.empty(n, dtype=torch.uint8, device=device)
 
     def engram_profile_begin(self, max_launches: int = 4096, kinds: Optional[Sequence[str]] = None):
         """Time launches of the named kinds (KERNEL_NAMES; None: all)."""

@@ -1,0 +1,458 @@
+// backward.hip -- the backward of one Engram layer on gfx950, for training
+// ([csdn] 实际效果到底有多好: the table slots become meaningful through the
+// gradients that reach them).  The derivative of the forward of
+// proj_bf16.hip / fuse.hip, for whole sequences (no carried state):
+//   bwd_gate_stats_kernel  rh, rk, s and alpha of every token and branch, from
+//                          h and the recomputed k
+//   bwd_conv_kernel        dconv from dout, du through the transposed
+//                          (anti-causal) conv, dalpha = <v, du>, dv = sum over
+//                          branches of alpha du, and the conv taps' gradient
+//   bwd_gate_kernel        ds = dalpha alpha (1 - alpha), then both RMSNorms
+//                          backwards: dh, dk and the gammas' gradients
+//   bwd_transpose_kernel   operands of dE = [dk | dv] W and dW = [dk | dv]^T E
+//                          made K-contiguous for the MFMA main loop
+//   table rows             (table, row) keys sorted stably, one wave per run of
+//                          equal keys adds the tokens' dE slices in token order
+// The contractions themselves run on proj_bf16.hip's main loop (plain mode).
+#include <cstring>
+
+#include <rocprim/device/device_radix_sort.hpp>
+#include <rocprim/device/device_scan.hpp>
+
+#include "engram_internal.h"
+
+namespace engram {
+namespace {
+
+constexpr int kConvPos = 32;     // positions per bwd_conv_kernel workgroup
+constexpr int kGateTok = 64;     // tokens per bwd_gate_kernel workgroup
+
+template <typename T, int N>
+__device__ __forceinline__ T pick_arg(const T (&arr)[N], int i) {
+    T p = arr[0];
+#pragma unroll
+    for (int j = 1; j < N; ++j)
+        if (i == j) p = arr[j];
+    return p;
+}
+
+__device__ __forceinline__ float sigmoid_b(float x) { return 1.f / (1.f + expf(-x)); }
+
+__device__ __forceinline__ f32x4_t load_bf16x4(const void *base, int64_t elem) {
+    const u32x2_t x = *reinterpret_cast<const u32x2_t *>(reinterpret_cast<const uint16_t *>(base) + elem);
+    return f32x4_t{bf16_to_f32(x[0] & 0xFFFFu), bf16_to_f32(x[0] >> 16), bf16_to_f32(x[1] & 0xFFFFu),
+                   bf16_to_f32(x[1] >> 16)};
+}
+
+__device__ __forceinline__ void store_bf16x4(void *base, int64_t elem, f32x4_t v) {
+    *reinterpret_cast<u32x2_t *>(reinterpret_cast<uint16_t *>(base) + elem) =
+        u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+
+// Sum over the 64 lanes of a wave (fixed butterfly order).
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+// ---------------------------------------------------------------- gate statistics
+// One workgroup per (token, branch).  stats = [rh | rk | s | alpha], each [B_r][n_tok].
+__global__ __launch_bounds__(256) void bwd_gate_stats_kernel(BwdArgs a) {
+    __shared__ float red[3][4];
+    const int64_t t = blockIdx.x;
+    const int m = blockIdx.y;
+    const int d = a.d;
+    const float *gh = pick_arg(a.gamma_h, m), *gk = pick_arg(a.gamma_k, m);
+    const float *k = a.kv + t * a.kv_ld + (int64_t)m * d;
+    float shh = 0.f, skk = 0.f, shk = 0.f;
+    for (int c = 4 * threadIdx.x; c < d; c += 4 * 256) {
+        const f32x4_t hv = load_bf16x4(a.h, ((int64_t)m * a.n_tok + t) * d + c);
+        const f32x4_t kv = *reinterpret_cast<const f32x4_t *>(k + c);
+        const f32x4_t g1 = *reinterpret_cast<const f32x4_t *>(gh + c);
+        const f32x4_t g2 = *reinterpret_cast<const f32x4_t *>(gk + c);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            shh += hv[r] * hv[r];
+            skk += kv[r] * kv[r];
+            shk += (g1[r] * hv[r]) * (g2[r] * kv[r]);
+        }
+    }
+    shh = wave_sum(shh);
+    skk = wave_sum(skk);
+    shk = wave_sum(shk);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        red[0][wave] = shh;
+        red[1][wave] = skk;
+        red[2][wave] = shk;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const float sh = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
+        const float sk = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+        const float dot = (red[2][0] + red[2][1]) + (red[2][2] + red[2][3]);
+        const float rh = sqrtf(sh / (float)d + a.eps);
+        const float rk = sqrtf(sk / (float)d + a.eps);
+        const float s = dot / (rh * rk) * rsqrtf((float)d);
+        const int64_t plane = (int64_t)a.n_branches * a.n_tok;
+        const int64_t i = (int64_t)m * a.n_tok + t;
+        a.stats[i] = rh;
+        a.stats[plane + i] = rk;
+        a.stats[2 * plane + i] = s;
+        a.stats[3 * plane + i] = sigmoid_b(s);
+    }
+}
+
+// ---------------------------------------------------------------- conv and gated value
+// Workgroup (position chunk, sequence, 1024-channel stripe); each thread owns
+// four channels and walks positions p = t0-3 .. t1+2 once, all branches
+// together, with sliding windows of the last values:
+//   u_p = alpha_p v_p;  conv_p = sum_j w[K-1-j] u_{p-j}
+//   dconv_p = dout_p (LINEAR) or dout_p (sig + conv sig (1 - sig)) (SILU_SKIP)
+//   du_t = [SILU_SKIP] dout_t + sum_j w[K-1-j] dconv_{t+j}  (ready at p = t+3)
+//   dw[K-1-j] += u_{t-j} dconv_t for the chunk's own positions t
+// Out: dv_t (bf16, into the v columns of dkv), the workgroup's share of
+// dalpha_t = <v_t, du_t> per branch, and its share of the taps' gradient.
+template <int BR, bool SILU>
+__global__ __launch_bounds__(256) void bwd_conv_kernel(BwdArgs a) {
+    __shared__ float alpha_s[BR][kConvPos + 6];   // positions t0-3 .. t1+2
+    __shared__ float red[BR][kConvPos][4];        // per-wave dalpha shares
+    const int T = a.seqlen;
+    const int b = blockIdx.y;
+    const int t0 = blockIdx.x * kConvPos;
+    const int t1 = min(t0 + kConvPos, T);
+    const int64_t row0 = (int64_t)b * T;
+    const int d = a.d;
+    const int kc = a.conv_k;
+    const int tid = threadIdx.x;
+    const int c0 = (blockIdx.z * 256 + tid) * 4;
+    const bool live = c0 < d;
+    const float *alpha_all = a.stats + 3 * (int64_t)a.n_branches * a.n_tok;
+
+    for (int x = tid; x < BR * (kConvPos + 6); x += 256) {
+        const int m = x / (kConvPos + 6), j = x - m * (kConvPos + 6);
+        const int p = t0 - 3 + j;
+        alpha_s[m][j] = (p >= 0 && p < T) ? alpha_all[(int64_t)m * a.n_tok + row0 + p] : 0.f;
+    }
+    __syncthreads();
+
+    f32x4_t wt[4];  // wt[j][c]: tap multiplying u_{t-j} (zero beyond K_c)
+    f32x4_t dw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        dw[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            wt[j][r] = (live && j < kc) ? a.conv_w[(int64_t)(c0 + r) * kc + (kc - 1 - j)] : 0.f;
+    }
+    // windows, index 0 = most recent: u and dconv per branch, v and dout
+    f32x4_t uw[BR][4], dcw[BR][4], gw[BR][4], vw[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        vw[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < BR; ++m) {
+            uw[m][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            dcw[m][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            gw[m][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    const float *vcol = a.kv + (int64_t)a.n_branches * d + c0;
+
+    for (int p = t0 - 3; p <= t1 + 2; ++p) {
+        const bool in_seq = p >= 0 && p < T;
+        // shift the windows
+#pragma unroll
+        for (int q = 3; q > 0; --q) {
+            vw[q] = vw[q - 1];
+#pragma unroll
+            for (int m = 0; m < BR; ++m) {
+                uw[m][q] = uw[m][q - 1];
+                dcw[m][q] = dcw[m][q - 1];
+                gw[m][q] = gw[m][q - 1];
+            }
+        }
+        f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+        if (live && in_seq) v = *reinterpret_cast<const f32x4_t *>(vcol + (row0 + p) * a.kv_ld);
+        vw[0] = v;
+        const int j_al = p - t0 + 3;
+#pragma unroll
+        for (int m = 0; m < BR; ++m) {
+            const float al = alpha_s[m][j_al];
+            f32x4_t g = {0.f, 0.f, 0.f, 0.f};
+            if (live && in_seq) g = load_bf16x4(a.dout, ((int64_t)m * a.n_tok + row0 + p) * d + c0);
+            gw[m][0] = g;
+            f32x4_t u, dc;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                u[r] = al * v[r];
+                const float conv = wt[0][r] * u[r] + wt[1][r] * uw[m][1][r] + wt[2][r] * uw[m][2][r] +
+                                   wt[3][r] * uw[m][3][r];
+                if (SILU) {
+                    const float sg = sigmoid_b(conv);
+                    dc[r] = g[r] * (sg + conv * sg * (1.f - sg));
+                } else {
+                    dc[r] = g[r];
+                }
+            }
+            uw[m][0] = u;
+            dcw[m][0] = dc;  // zero outside the sequence (g is zero there)
+            if (p >= t0 && p < t1) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dw[j][r] += uw[m][j][r] * dc[r];
+            }
+        }
+        // du of position t = p - 3, now that dconv_{t..t+3} is known
+        const int t = p - 3;
+        if (t >= t0 && t < t1) {
+            f32x4_t dv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < BR; ++m) {
+                const float al = alpha_s[m][t - t0 + 3];
+                float part = 0.f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float du = SILU ? gw[m][3][r] : 0.f;
+                    du += wt[0][r] * dcw[m][3][r] + wt[1][r] * dcw[m][2][r] + wt[2][r] * dcw[m][1][r] +
+                          wt[3][r] * dcw[m][0][r];
+                    part += vw[3][r] * du;
+                    dv[r] += al * du;
+                }
+                part = wave_sum(part);
+                if ((tid & 63) == 0) red[m][t - t0][tid >> 6] = part;
+            }
+            if (live) store_bf16x4(a.dkv, (row0 + t) * a.dkv_ld + (int64_t)a.n_branches * d + c0, dv);
+        }
+    }
+    __syncthreads();
+    // this stripe's dalpha of every position and branch, waves added in order
+    for (int x = tid; x < BR * kConvPos; x += 256) {
+        const int m = x / kConvPos, tt = x - m * kConvPos;
+        if (t0 + tt >= t1) continue;
+        const float s = (red[m][tt][0] + red[m][tt][1]) + (red[m][tt][2] + red[m][tt][3]);
+        a.dalpha_part[((int64_t)m * a.n_stripes + blockIdx.z) * a.n_tok + row0 + t0 + tt] = s;
+    }
+    if (live) {
+        float *dst = a.dconv_part + ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * (int64_t)d * kc;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            for (int j = 0; j < kc; ++j) dst[(int64_t)(c0 + r) * kc + (kc - 1 - j)] = dw[j][r];
+    }
+}
+
+// ---------------------------------------------------------------- gate and RMSNorms
+// Workgroup (token chunk, branch, stripe); each thread four channels of
+// kGateTok tokens.  With a = gh*h/rh, b = gk*k/rk, s = <a, b>/sqrt(d):
+//   ds = dalpha alpha (1 - alpha), da = ds b/sqrt(d), db = ds a/sqrt(d)
+//   dh = [dout] + (gh da - (h/rh) S/d)/rh,  dk = (gk db - (k/rk) S/d)/rk
+// where S = <gh da, h/rh> = <gk db, k/rk> = ds s (both equal ds <a, b>/sqrt(d)).
+__global__ __launch_bounds__(256) void bwd_gate_kernel(BwdArgs a) {
+    __shared__ float sc[5][kGateTok];  // rh, rk, s, alpha, dalpha of the chunk's tokens
+    const int m = blockIdx.y;
+    const int64_t tb = (int64_t)blockIdx.x * kGateTok;
+    const int d = a.d;
+    const int tid = threadIdx.x;
+    const int64_t plane = (int64_t)a.n_branches * a.n_tok;
+    for (int x = tid; x < kGateTok; x += 256) {
+        const int64_t t = tb + x;
+        if (t >= a.n_tok) continue;
+        const int64_t i = (int64_t)m * a.n_tok + t;
+        sc[0][x] = a.stats[i];
+        sc[1][x] = a.stats[plane + i];
+        sc[2][x] = a.stats[2 * plane + i];
+        sc[3][x] = a.stats[3 * plane + i];
+        float dal = 0.f;
+        for (int z = 0; z < a.n_stripes; ++z) dal += a.dalpha_part[((int64_t)m * a.n_stripes + z) * a.n_tok + t];
+        sc[4][x] = dal;
+    }
+    __syncthreads();
+    const int c0 = (blockIdx.z * 256 + tid) * 4;
+    if (c0 >= d) return;
+    const bool delta = (a.flags & ENGRAM_OUT_DELTA) != 0;
+    const f32x4_t gh = *reinterpret_cast<const f32x4_t *>(pick_arg(a.gamma_h, m) + c0);
+    const f32x4_t gk = *reinterpret_cast<const f32x4_t *>(pick_arg(a.gamma_k, m) + c0);
+    const float inv_sqd = rsqrtf((float)d);
+    f32x4_t dgh = {0.f, 0.f, 0.f, 0.f}, dgk = {0.f, 0.f, 0.f, 0.f};
+    for (int x = 0; x < kGateTok; ++x) {
+        const int64_t t = tb + x;
+        if (t >= a.n_tok) break;
+        const float rh = sc[0][x], rk = sc[1][x], s = sc[2][x], al = sc[3][x];
+        const float ds = sc[4][x] * al * (1.f - al);
+        const float corr = ds * s / (float)d;
+        const int64_t hi = ((int64_t)m * a.n_tok + t) * d + c0;
+        const f32x4_t hv = load_bf16x4(a.h, hi);
+        const f32x4_t kv = *reinterpret_cast<const f32x4_t *>(a.kv + t * a.kv_ld + (int64_t)m * d + c0);
+        const f32x4_t g = delta ? f32x4_t{0.f, 0.f, 0.f, 0.f} : load_bf16x4(a.dout, hi);
+        f32x4_t dh, dk;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float hn = hv[r] / rh, kn = kv[r] / rk;
+            const float da = ds * (gk[r] * kn) * inv_sqd;
+            const float db = ds * (gh[r] * hn) * inv_sqd;
+            dgh[r] += da * hn;
+            dgk[r] += db * kn;
+            dh[r] = g[r] + (gh[r] * da - hn * corr) / rh;
+            dk[r] = (gk[r] * db - kn * corr) / rk;
+        }
+        store_bf16x4(a.dh, hi, dh);
+        store_bf16x4(a.dkv, t * a.dkv_ld + (int64_t)m * d + c0, dk);
+    }
+    const int64_t pr = ((int64_t)m * gridDim.x + blockIdx.x) * d + c0;
+    *reinterpret_cast<f32x4_t *>(a.dg_part + pr) = dgh;
+    *reinterpret_cast<f32x4_t *>(a.dg_part + (int64_t)a.n_branches * gridDim.x * d + pr) = dgk;
+}
+
+// out[g][i] = sum over r of in[g][r][i], r ascending (one thread per (g, i)).
+__global__ __launch_bounds__(256) void bwd_sum_rows_kernel(const float *in, int64_t groups, int64_t rows,
+                                                           int64_t width, float *out) {
+    const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (x >= groups * width) return;
+    const int64_t gi = x / width, i = x - gi * width;
+    const float *p = in + gi * rows * width + i;
+    float s = 0.f;
+    for (int64_t r = 0; r < rows; ++r) s += p[r * width];
+    out[x] = s;
+}
+
+// dst[c][r] = src[r][c] for r < rows; zero for rows <= r < dst_cols.  64 x 64
+// tiles through LDS; bf16 moved as 16-bit words.
+__global__ __launch_bounds__(256) void bwd_transpose_kernel(const uint16_t *src, int64_t rows, int64_t cols,
+                                                            int64_t src_ld, uint16_t *dst, int64_t dst_ld,
+                                                            int64_t dst_cols) {
+    __shared__ uint16_t tile[64][65];
+    const int64_t c_base = (int64_t)blockIdx.x * 64, r_base = (int64_t)blockIdx.y * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int i = ty; i < 64; i += 4) {
+        const int64_t r = r_base + i, c = c_base + tx;
+        tile[i][tx] = (r < rows && c < cols) ? src[r * src_ld + c] : (uint16_t)0;
+    }
+    __syncthreads();
+    for (int i = ty; i < 64; i += 4) {
+        const int64_t c = c_base + i, r = r_base + tx;
+        if (c < cols && r < dst_cols) dst[c * dst_ld + r] = tile[tx][i];
+    }
+}
+
+// ---------------------------------------------------------------- table rows
+// Item i = tau * n_tok + t: key (tau, idx[t][tau]), value t.
+__global__ __launch_bounds__(256) void bwd_keys_kernel(const uint32_t *idx, int64_t n_tok, int32_t n_tables,
+                                                       uint64_t *keys, uint32_t *vals) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n_tok * n_tables) return;
+    const int64_t tau = i / n_tok, t = i - tau * n_tok;
+    keys[i] = ((uint64_t)tau << 32) | idx[t * n_tables + tau];
+    vals[i] = (uint32_t)t;
+}
+
+__global__ __launch_bounds__(256) void bwd_heads_kernel(const uint64_t *keys, int64_t n, uint32_t *head) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    head[i] = (i == 0 || keys[i] != keys[i - 1]) ? 1u : 0u;
+}
+
+// One wave per sorted item; the wave of each run's first item adds the
+// run's dE slices (tokens ascending: the sort is stable) and writes the
+// row's entry.  The wave of each table's first item also writes its count.
+__global__ __launch_bounds__(256) void bwd_row_sums_kernel(const uint64_t *keys, const uint32_t *vals,
+                                                           const uint32_t *head, const uint32_t *incl,
+                                                           const float *demb, int64_t n_tok, int32_t n_tables,
+                                                           int32_t head_dim, uint32_t *row_ids, float *row_grads,
+                                                           int32_t *row_counts) {
+    const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (i >= n_tok * n_tables || !head[i]) return;
+    const int64_t tau = i / n_tok;
+    const int64_t first = tau * n_tok, end = first + n_tok;
+    const int64_t local = (int64_t)incl[i] - (int64_t)incl[first];
+    if (i == first && lane == 0) row_counts[tau] = (int32_t)(incl[end - 1] - incl[first] + 1);
+    const int64_t De = (int64_t)n_tables * head_dim;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t j = i; j < end && (j == i || !head[j]); ++j) {
+        const float *src = demb + (int64_t)vals[j] * De + tau * head_dim;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (lane + 64 * q < head_dim) acc[q] += src[lane + 64 * q];
+    }
+    if (lane == 0) row_ids[first + local] = (uint32_t)keys[i];
+    float *dst = row_grads + (first + local) * head_dim;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        if (lane + 64 * q < head_dim) dst[lane + 64 * q] = acc[q];
+}
+
+}  // namespace
+
+void launch_bwd_gate_stats(const BwdArgs &a, hipStream_t s) {
+    launch_kernel(bwd_gate_stats_kernel, dim3((unsigned)a.n_tok, a.n_branches), dim3(256), s, a);
+}
+
+void launch_bwd_conv(const BwdArgs &a, hipStream_t s) {
+    const dim3 grid((a.seqlen + kConvPos - 1) / kConvPos, a.batch, a.n_stripes);
+    const bool silu = a.conv_mode == ENGRAM_CONV_SILU_SKIP;
+#define ENGRAM_BWD_CONV(BR)                                                                     \
+    do {                                                                                        \
+        if (silu)                                                                               \
+            launch_kernel((bwd_conv_kernel<BR, true>), grid, dim3(256), s, a);                  \
+        else                                                                                    \
+            launch_kernel((bwd_conv_kernel<BR, false>), grid, dim3(256), s, a);                 \
+    } while (0)
+    switch (a.n_branches) {
+        case 1: ENGRAM_BWD_CONV(1); break;
+        case 2: ENGRAM_BWD_CONV(2); break;
+        case 3: ENGRAM_BWD_CONV(3); break;
+        default: ENGRAM_BWD_CONV(4); break;
+    }
+#undef ENGRAM_BWD_CONV
+}
+
+int32_t bwd_conv_blocks(int32_t batch, int32_t seqlen) { return batch * ((seqlen + kConvPos - 1) / kConvPos); }
+int32_t bwd_gate_chunks(int64_t n_tok) { return (int32_t)((n_tok + kGateTok - 1) / kGateTok); }
+
+void launch_bwd_gate(const BwdArgs &a, hipStream_t s) {
+    launch_kernel(bwd_gate_kernel, dim3((unsigned)bwd_gate_chunks(a.n_tok), a.n_branches, a.n_stripes), dim3(256),
+                  s, a);
+}
+
+void launch_bwd_sum_rows(const float *in, int64_t groups, int64_t rows, int64_t width, float *out, hipStream_t s) {
+    const int64_t n = groups * width;
+    launch_kernel(bwd_sum_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), s, in, groups, rows, width, out);
+}
+
+void launch_bwd_transpose(const uint16_t *src, int64_t rows, int64_t cols, int64_t src_ld, uint16_t *dst,
+                          int64_t dst_ld, int64_t dst_cols, hipStream_t s) {
+    const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((dst_cols + 63) / 64));
+    launch_kernel(bwd_transpose_kernel, grid, dim3(256), s, src, rows, cols, src_ld, dst, dst_ld, dst_cols);
+}
+
+size_t bwd_table_temp_bytes(int64_t n_items) {
+    size_t sort_bytes = 0, scan_bytes = 0;
+    (void)rocprim::radix_sort_pairs(nullptr, sort_bytes, (uint64_t *)nullptr, (uint64_t *)nullptr,
+                                    (uint32_t *)nullptr, (uint32_t *)nullptr, (size_t)n_items, 0, 64);
+    (void)rocprim::inclusive_scan(nullptr, scan_bytes, (uint32_t *)nullptr, (uint32_t *)nullptr, (size_t)n_items,
+                                  rocprim::plus<uint32_t>());
+    return std::max(sort_bytes, scan_bytes);
+}
+
+hipError_t launch_bwd_table_grad(const BwdTableArgs &t, hipStream_t s) {
+    const int64_t n = t.n_tok * t.n_tables;
+    launch_kernel(bwd_keys_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), s, t.idx, t.n_tok, t.n_tables,
+                  t.keys_in, t.vals_in);
+    int end_bit = 32;
+    while ((1ll << (end_bit - 32)) < t.n_tables) ++end_bit;
+    size_t bytes = t.temp_bytes;
+    hipError_t e = rocprim::radix_sort_pairs(t.temp, bytes, t.keys_in, t.keys_out, t.vals_in, t.vals_out, (size_t)n,
+                                             0, end_bit, s);
+    if (e != hipSuccess) return e;
+    launch_kernel(bwd_heads_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), s, t.keys_out, n, t.head);
+    bytes = t.temp_bytes;
+    e = rocprim::inclusive_scan(t.temp, bytes, t.head, t.incl, (size_t)n, rocprim::plus<uint32_t>(), s);
+    if (e != hipSuccess) return e;
+    launch_kernel(bwd_row_sums_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), s, t.keys_out, t.vals_out, t.head,
+                  t.incl, t.demb, t.n_tok, t.n_tables, t.head_dim, t.row_ids, t.row_grads, t.row_counts);
+    return hipGetLastError();
+}
+
+}  // namespace engram

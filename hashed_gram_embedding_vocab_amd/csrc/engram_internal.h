@@ -144,6 +144,10 @@ struct ProjArgs {
     float *seam_v;                         // [token tiles][6][d] fp32 v of each tile's first and last 3 rows
     int32_t batch, seqlen, conv_k, conv_mode;
     uint32_t flags;
+    // plain launch only (mode 3): C[t][n] = sum_k W[n][k] E[t][k] stored fp32
+    float *out_f32;                        // element (t, n) at out_f32[t * out_ld + n]
+    int64_t out_ld;
+    int32_t n_rows;                        // rows of W to store (n < n_rows)
 };
 
 constexpr int kPartCols = 128;  // columns of d summed into one gate partial (bf16 path)
@@ -157,6 +161,11 @@ void launch_proj_bf16(const ProjArgs &a, hipStream_t s);
 // tile are left to launch_seam.
 constexpr int kTokTile = 256;
 void launch_proj_v_fused_bf16(const ProjArgs &a, hipStream_t s);
+// Plain contraction C[t][n] = sum_k W[n][k] E[t][k] (bf16 operands, fp32
+// accumulate and result) on the same MFMA main loop: W rows are the n_mats
+// matrices of a.w stacked (a.d rows each), E has a.n_tok rows, K = a.K
+// (K % 128 == 0); rows n >= a.n_rows and tokens t >= a.n_tok are not stored.
+void launch_proj_plain_bf16(const ProjArgs &a, hipStream_t s);
 void launch_proj_f32(const ProjArgs &a, hipStream_t s);  // k into kbuf, v, then partials
 
 // ---------------------------------------------------------------- fusion
@@ -227,6 +236,55 @@ struct FuseArgs {
 };
 
 void launch_fuse(const FuseArgs &a, engram_dtype dt, hipStream_t s);
+
+// ---------------------------------------------------------------- backward
+struct BwdArgs {
+    const void *h;                          // [B_r][n_tok][d] bf16
+    const void *dout;                       // [B_r][n_tok][d] bf16
+    void *dh;                               // [B_r][n_tok][d] bf16 (out)
+    const float *kv;                        // [n_tok][kv_ld]: k of every branch, then v (fp32)
+    int64_t kv_ld;                          // (B_r + 1) d
+    float *stats;                           // [4][B_r][n_tok]: rh, rk, s, alpha
+    float *dalpha_part;                     // [B_r][n_stripes][n_tok]
+    float *dconv_part;                      // [conv blocks][d][K_c]
+    float *dg_part;                         // [2][B_r][gate chunks][d]: gamma_h, then gamma_k
+    uint16_t *dkv;                          // [n_tok][dkv_ld] bf16: dk of every branch, then dv
+    int64_t dkv_ld;                         // (B_r + 1) d
+    const float *gamma_h[kMaxBranches];
+    const float *gamma_k[kMaxBranches];
+    const float *conv_w;                    // [d][K_c]
+    int64_t n_tok;
+    int32_t batch, seqlen, d, n_branches, conv_k, conv_mode;
+    int32_t n_stripes;                      // ceil(d / 1024)
+    uint32_t flags;
+    float eps;
+};
+void launch_bwd_gate_stats(const BwdArgs &a, hipStream_t s);
+void launch_bwd_conv(const BwdArgs &a, hipStream_t s);
+void launch_bwd_gate(const BwdArgs &a, hipStream_t s);
+int32_t bwd_conv_blocks(int32_t batch, int32_t seqlen);
+int32_t bwd_gate_chunks(int64_t n_tok);
+// out[g][i] = sum over r (ascending) of in[g][r][i]
+void launch_bwd_sum_rows(const float *in, int64_t groups, int64_t rows, int64_t width, float *out, hipStream_t s);
+// dst[c][r] = src[r][c] (bf16), zero for rows <= r < dst_cols
+void launch_bwd_transpose(const uint16_t *src, int64_t rows, int64_t cols, int64_t src_ld, uint16_t *dst,
+                          int64_t dst_ld, int64_t dst_cols, hipStream_t s);
+
+struct BwdTableArgs {
+    const uint32_t *idx;                    // [n_tok][n_tables]
+    const float *demb;                      // [n_tok][n_tables * head_dim]
+    int64_t n_tok;
+    int32_t n_tables, head_dim;
+    uint64_t *keys_in, *keys_out;           // [n_tables * n_tok]
+    uint32_t *vals_in, *vals_out, *head, *incl;
+    void *temp;                             // sort / scan scratch
+    size_t temp_bytes;
+    uint32_t *row_ids;
+    float *row_grads;
+    int32_t *row_counts;
+};
+size_t bwd_table_temp_bytes(int64_t n_items);
+hipError_t launch_bwd_table_grad(const BwdTableArgs &t, hipStream_t s);
 
 // ---------------------------------------------------------------- synthetic tables
 // ---------------------------------------------------------------- copies

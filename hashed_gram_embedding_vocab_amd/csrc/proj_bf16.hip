@@ -469,6 +469,7 @@ __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t 
 template <int MODE, int BR, bool SILU, bool NARROW>
 __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_bf16_kernel(ProjArgs a) {
     static_assert(!(NARROW && MODE == 1), "the fused value epilogue is written for the wide tile");
+    static_assert(MODE == 0 || MODE == 1 || MODE == 3, "mode");
     typedef TileCfg<NARROW> C;
     constexpr int TBN = C::BN, TBT = C::BT, TTHREADS = C::kThreads, TWAVES = C::kWaves, TWGN = C::kWavesN;
     constexpr int TWT = C::WT, TFT = C::FT, TOPB = C::kOperandBytes, TBPW = C::kBlocksPerWave;
@@ -653,7 +654,7 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
             __builtin_amdgcn_raw_ptr_buffer_load_lds(hres, (lds_void_t *)(hA + k * 1024), 16,
                                                      chunk_offset(k, lane, rowbase, t0, a.n_tok, d, nl), 0, 0, 0);
     };
-    constexpr int kEarlyH = MODE == 0 ? TWT / 8 : 8;  // loads issued in the ring's tail
+    constexpr int kEarlyH = MODE == 0 ? TWT / 8 : (MODE == 1 ? 8 : 0);  // loads issued in the ring's tail
 
     // the last four stages: ks = k_steps - 4; stages ks..ks+2 are in flight
     wait_vmcnt<2 * kLoadsPerStage>();
@@ -678,7 +679,20 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
     //      of token t = tw + 16j + lane%16.
     const int sub = 4 * (lane >> 4);
 
-    if constexpr (MODE == 0) {
+    if constexpr (MODE == 3) {
+        // plain contraction: every tile stores its fp32 block, four
+        // consecutive rows n (16 bytes) of one token t per lane and block
+#pragma unroll
+        for (int j = 0; j < TFT; ++j) {
+            const int64_t t = tw + 16 * j + (lane & 15);
+            if (t >= a.n_tok) continue;
+#pragma unroll
+            for (int i = 0; i < FN; ++i) {
+                const int n = nw + 16 * i + sub;
+                if (n < a.n_rows) *reinterpret_cast<f32x4_t *>(a.out_f32 + t * a.out_ld + n) = acc[i][j];
+            }
+        }
+    } else if constexpr (MODE == 0) {
     if (mat < a.n_branches) {
         // gate partials of branch `mat` over channels [nl, nl+128).
         // gamma_h * gamma_k for the wave's channels goes through LDS, so it
@@ -755,6 +769,17 @@ void launch_proj_bf16(const ProjArgs &a, hipStream_t s) {
         launch_kernel((proj_bf16_kernel<0, 1, false, true>), dim3((unsigned)blocks), dim3(256), s, a);
     } else {
         launch_kernel((proj_bf16_kernel<0, 1, false, false>), dim3((unsigned)wide), dim3(kThreads), s, a);
+    }
+}
+
+void launch_proj_plain_bf16(const ProjArgs &a, hipStream_t s) {
+    const int n_total = a.n_mats * a.d;
+    const int64_t wide = (int64_t)((n_total + BN - 1) / BN) * ((a.n_tok + BT - 1) / BT);
+    if (wide < 256) {
+        const int64_t blocks = (int64_t)((n_total + 127) / 128) * ((a.n_tok + 127) / 128);
+        launch_kernel((proj_bf16_kernel<3, 1, false, true>), dim3((unsigned)blocks), dim3(256), s, a);
+    } else {
+        launch_kernel((proj_bf16_kernel<3, 1, false, false>), dim3((unsigned)wide), dim3(kThreads), s, a);
     }
 }
 

@@ -108,7 +108,11 @@ enum {
     ENGRAM_K_GEMM_V = 5,  /* W_v e with gated value, conv, residual, state fused (prefill)     */
     ENGRAM_K_GATE = 6,    /* gate per token and branch from the partial sums                  */
     ENGRAM_K_SEAM = 7,    /* rows at 256-token tile seams left by ENGRAM_K_GEMM_V             */
-    ENGRAM_K_COUNT = 8
+    ENGRAM_K_BWD_GEMM = 8,  /* engram_backward: the MFMA contractions (k and v again, dE, dW)  */
+    ENGRAM_K_BWD_FUSE = 9,  /* engram_backward: gate statistics, conv / gate / RMSNorm backward,
+                               transposes and the reductions of the small gradients           */
+    ENGRAM_K_BWD_TABLE = 10,/* engram_backward: sort, scan and per-row sums of the table gradient */
+    ENGRAM_K_COUNT = 11
 };
 
 typedef struct {
@@ -206,6 +210,49 @@ ENGRAM_API engram_status engram_forward(engram_plan p, const int32_t *d_tokens, 
                              const engram_weights *w, float *d_conv_state, void *d_out,
                              float *d_alpha, uint32_t flags, void *d_workspace,
                              size_t workspace_bytes, uint32_t *d_bad_tokens, hipStream_t stream);
+
+/* Gradients written by engram_backward (fp32, caller-owned device memory,
+ * overwritten). */
+typedef struct {
+    float *dw;           /* [n_branches + 1][d][D_e]: dL/dW_k of each branch, then dL/dW_v  */
+    float *dgamma_h;     /* [n_branches][d]                                                 */
+    float *dgamma_k;     /* [n_branches][d]                                                 */
+    float *dconv_w;      /* [d][K_c]                                                        */
+    uint32_t *row_ids;   /* [n_tables][batch*seqlen]: the rows of table tau that the chunk
+                            gathered, distinct, ascending (the first row_counts[tau] entries) */
+    float *row_grads;    /* [n_tables][batch*seqlen][d_e]: dL/d(row) of each listed row, the
+                            sum over the tokens that gathered it                            */
+    int32_t *row_counts; /* [n_tables]                                                      */
+} engram_grads;
+
+/* Bytes of device workspace engram_backward needs for batch*seqlen tokens
+ * (0 on invalid arguments or an unsupported shape). */
+ENGRAM_API size_t engram_backward_workspace_size(engram_plan p, int32_t batch, int32_t seqlen);
+
+/*
+ * Backward of engram_forward for whole sequences (no carried context or conv
+ * state), for training ([csdn] 实际效果到底有多好: the slots become meaningful
+ * through the gradients that reach them).  Given dL/dout, the chain rule
+ * through the residual, the conv, the gated value, the sigmoid gate, both
+ * RMSNorms and the projections, and the table rows each token gathered:
+ *   d_idx       [batch*seqlen][n_tables] slots from engram_hash of the same tokens
+ *   table_ptrs  as engram_gather (HOST array of DEVICE pointers)
+ *   d_h, w      the forward's hidden state and weights
+ *   d_dout      [n_branches][batch*seqlen][d] dL/dout, plan dtype
+ *   flags       ENGRAM_OUT_DELTA if the forward wrote y (then dout reaches h
+ *               only through the gate)
+ *   d_dh        [n_branches][batch*seqlen][d] dL/dh, plan dtype (out)
+ *   g           the other gradients (out)
+ * Every table row's gradient is the sum over the tokens that gathered it,
+ * added in token order: the result does not depend on scheduling.
+ * Supported: bf16 plans with d % 256 == 0 and D_e % 128 == 0 (the forward's
+ * MFMA shapes); anything else returns ENGRAM_E_UNSUPPORTED.
+ */
+ENGRAM_API engram_status engram_backward(engram_plan p, const uint32_t *d_idx, const void *const *table_ptrs,
+                              const void *d_h, const engram_weights *w, const void *d_dout,
+                              int32_t batch, int32_t seqlen, uint32_t flags, void *d_dh,
+                              const engram_grads *g, void *d_workspace, size_t workspace_bytes,
+                              hipStream_t stream);
 
 /*
  * Profiling: while on, each launch of a kind selected by kind_mask (bit k

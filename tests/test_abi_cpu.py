@@ -160,3 +160,36 @@ def test_bf16_shape_support_is_checked(B):
     ws = p.engram_workspace_size(1, 4)
     assert L.engram_gate_fuse(p._h, fake, fake, 1, 4, C.byref(w), None, fake, None, 0,
                               C.c_void_p(0x100000), ws, None) == B.E_UNSUPPORTED
+
+
+def test_backward_argument_checks(B):
+    _no_gpu()
+    L = B.lib()
+    fake = C.c_void_p(0x10000)
+    w = B.WeightsC()
+    w.w_k[0] = w.w_v = w.gamma_h[0] = w.gamma_k[0] = w.conv_w = 0x10000
+    g = B.GradsC(*([C.c_void_p(0x10000)] * 7))
+    tabs = (C.c_void_p * 4)(*([0x10000] * 4))
+    # the fp32 path has no backward: no workspace size, UNSUPPORTED
+    p32 = B.Plan(vocab=1000, vocab_comp=770, heads=2, head_dim=32, table_rows=[10007] * 4, hash_seed=1,
+                 d_model=256, dtype=B.F32)
+    assert p32.engram_backward_workspace_size(2, 8) == 0
+    assert L.engram_backward(p32._h, fake, tabs, fake, C.byref(w), fake, 2, 8, 0, fake, C.byref(g),
+                             C.c_void_p(0x100000), 1 << 30, None) == B.E_UNSUPPORTED
+    p = B.Plan(vocab=1000, vocab_comp=770, heads=2, head_dim=32, table_rows=[10007] * 4, hash_seed=1,
+               d_model=256, dtype=B.BF16)
+    ws = p.engram_backward_workspace_size(2, 8)
+    assert ws > 0
+    assert p.engram_backward_workspace_size(0, 8) == 0
+    args = [p._h, fake, tabs, fake, C.byref(w), fake, 2, 8, 0, fake, C.byref(g), C.c_void_p(0x100000), ws, None]
+    for i, bad in [(1, None), (3, None), (5, None), (9, None), (10, None), (11, None),
+                   (12, ws - 1), (8, 0x4), (5, C.c_void_p(0x10004)), (11, C.c_void_p(0x100010))]:
+        a = list(args)
+        a[i] = bad
+        assert L.engram_backward(*a) == B.E_INVALID_ARG, (i, bad)
+    g2 = B.GradsC(*([C.c_void_p(0x10000)] * 6 + [None]))
+    a = list(args); a[10] = C.byref(g2)
+    assert L.engram_backward(*a) == B.E_INVALID_ARG
+    tabs_bad = (C.c_void_p * 4)(*([0x10000] * 3 + [0]))
+    a = list(args); a[2] = tabs_bad
+    assert L.engram_backward(*a) == B.E_INVALID_ARG

@@ -544,3 +544,84 @@ def test_unsupported_bf16_shape_is_rejected(B):
         dl = make_device_layer(wl)
         forward(dl, W.make_tokens(wl))
     assert e.value.status == B.E_UNSUPPORTED
+
+
+# ----------------------------------------------------------------------------
+# backward (training): engram_backward against the oracle's chain rule
+# ----------------------------------------------------------------------------
+
+def grad_within(got, ref, what, rel=2e-2, frac=1e-2):
+    """fp32 gradients fed by bf16 operands (dk and dv enter the contractions
+    rounded to bf16, as E and the weights do in the forward): |d| <= frac *
+    rms(row of ref) + rel * |ref|, rows along the last axis."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), what + ": non-finite"
+    bound = frac * (np.sqrt(np.mean(ref ** 2, axis=-1, keepdims=True)) + 1e-30) + rel * np.abs(ref)
+    ratio = np.abs(got - ref) / bound
+    worst = np.unravel_index(np.argmax(ratio), ratio.shape)
+    assert ratio.max() <= 1.0, "%s: max |d|/bound = %.3f at %s (got %r, ref %r)" % (
+        what, ratio.max(), worst, got[worst], ref[worst])
+
+
+def _backward(dl, idx, dout, flags=0):
+    wl = dl.wl
+    batch, seqlen = wl.batch, wl.seqlen
+    n_tok = batch * seqlen
+    from hashed_gram_embedding_vocab_amd import binding
+    grads = binding.Grads(wl.n_branches, wl.d_model, wl.emb_dim, wl.conv_kernel, wl.n_tables, n_tok, wl.head_dim)
+    dh = torch.empty_like(dl.h)
+    ws = dl.plan.backward_workspace(batch, seqlen)
+    dl.plan.engram_backward(idx, dl.tables, dl.h, dl.weights, dout, dh, grads, ws, batch, seqlen, flags=flags)
+    torch.cuda.synchronize()
+    return dh, grads
+
+
+@pytest.mark.parametrize("br,batch,seqlen,kc,mode,flags,d", [
+    (1, 2, 77, 4, oracle.CONV_LINEAR, 0, 256),
+    (2, 2, 300, 4, oracle.CONV_SILU_SKIP, 0, 256),
+    (4, 3, 33, 3, oracle.CONV_LINEAR, oracle.OUT_DELTA, 256),
+    (1, 1, 1, 4, oracle.CONV_LINEAR, 0, 256),
+    (3, 2, 40, 1, oracle.CONV_SILU_SKIP, 0, 256),
+    (1, 1, 64, 2, oracle.CONV_LINEAR, 0, 1280),
+])
+def test_backward_matches_oracle(B, br, batch, seqlen, kc, mode, flags, d):
+    say("backward", br, batch, seqlen, kc, mode, flags, d)
+    wl = small_wl(n_branches=br, batch=batch, seqlen=seqlen, conv_kernel=kc, d_model=d)
+    dl = make_device_layer(wl, conv_mode=mode)
+    toks = W.make_tokens(wl)
+    n_tok = batch * seqlen
+    idx = torch.zeros((n_tok, wl.n_tables), dtype=torch.int32, device="cuda")
+    dl.plan.engram_hash(dev_i32(toks), dl.comp_map, idx)
+    rng = np.random.default_rng(br * 1000 + seqlen)
+    dout_f = rng.standard_normal((br, n_tok, d)).astype(np.float32)
+    dout = torch.from_numpy(dout_f).to(torch.bfloat16).cuda()
+    dh, g = _backward(dl, idx, dout, flags)
+    # the same call again: the same bits
+    dh2, g2 = _backward(dl, idx, dout, flags)
+    assert torch.equal(dh, dh2)
+    for name in ("dw", "dgamma_h", "dgamma_k", "dconv_w", "row_ids", "row_grads", "row_counts"):
+        assert torch.equal(getattr(g, name), getattr(g2, name)), name
+
+    idx_ref, _, _ = oracle_indices(wl, dl.li, toks, dl.comp_map_host)
+    assert np.array_equal(idx.cpu().numpy().view(np.uint32), idx_ref)
+    L = oracle_layer(wl, dl.li, idx_ref, batch, seqlen, conv_mode=mode, flags=flags)
+    ref = L.backward(dout.float().cpu().numpy())
+    assert_within(host(dh), ref["dh"], "bf16", "dh")
+    grad_within(g.dw[:br].cpu().numpy(), ref["dw_k"], "dW_k")
+    grad_within(g.dw[br].cpu().numpy(), ref["dw_v"], "dW_v")
+    grad_within(g.dgamma_h.cpu().numpy(), ref["dgamma_h"], "dgamma_h")
+    grad_within(g.dgamma_k.cpu().numpy(), ref["dgamma_k"], "dgamma_k")
+    grad_within(g.dconv_w.cpu().numpy(), ref["dconv_w"], "dconv_w")
+    rows, grads, counts = oracle.table_grad(idx_ref, ref["demb"], wl.head_dim)
+    got_counts = g.row_counts.cpu().numpy()
+    assert np.array_equal(got_counts, counts)
+    got_rows = g.row_ids.cpu().numpy().view(np.uint32)
+    got_grads = g.row_grads.cpu().numpy()
+    for tau in range(wl.n_tables):
+        c = int(counts[tau])
+        assert np.array_equal(got_rows[tau, :c], rows[tau, :c]), tau
+        grad_within(got_grads[tau, :c], grads[tau, :c], "table %d rows" % tau)
+    del dl
+    torch.cuda.empty_cache()
