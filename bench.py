@@ -47,6 +47,8 @@ def parse():
                     help="steps of the separate pass that times every kernel")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time only whole steps (no per-launch events; no roofline)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time engram_backward (training) instead of the forward: one JSON line of its own")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB 5 times (counter calibration)")
     return ap.parse_args()
@@ -152,6 +154,9 @@ def main():
     B.lib()
     torch.cuda.set_device(0)
     wl = W.workload(args.workload)
+    if args.backward:
+        backward_bench(args, wl)
+        return
     n_tok = wl.n_tokens
     R = max(1, args.rotate)
 
@@ -346,6 +351,139 @@ def main():
         "gate_gemm": gate_gemm,
         "kernels": per_kernel,
         "kernel_avg_us": kernels_us,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def backward_cpu_baseline(wl, budget_s: float):
+    """The backward oracle, as it stands, on one sequence prefix of the
+    workload's widths (hash, gather and the chain rule; about budget_s of
+    single-threaded CPU work), in tokens per second."""
+    import numpy as np
+
+    import oracle
+    from synthetic import workloads as W
+
+    def run(n_pos):
+        toks = np.ascontiguousarray(W.make_tokens(wl)[:1, :n_pos])
+        li = W.make_layer_inputs(wl, 0, batch=1, seqlen=n_pos)
+        comp = W.compression_map(wl.vocab, wl.vocab_comp, wl.seed(1))
+        dt = oracle.BF16 if wl.dtype == "bf16" else oracle.F32
+        dout = np.random.default_rng(1).standard_normal((wl.n_branches, n_pos, wl.d_model)).astype(np.float32)
+        t0 = time.perf_counter()
+        idx, _, _ = oracle.hash_tokens(toks, comp, wl.vocab, wl.vocab_comp, wl.heads, wl.primes(), li.hash_seed,
+                                       orders=wl.orders)
+        emb = oracle.gather_synth(idx, wl.head_dim, li.table_seed, dt)
+        L = oracle.Layer(emb, li.h, li.w_k, li.w_v, li.gamma_h, li.gamma_k, li.conv_w, 1, n_pos, dt)
+        g = L.backward(dout)
+        oracle.table_grad(idx, g["demb"], wl.head_dim)
+        return time.perf_counter() - t0
+
+    n = 16
+    dt = run(n)
+    while dt < budget_s / 8 and n < wl.seqlen:
+        n = min(wl.seqlen, n * 4)
+        dt = run(n)
+    if n < wl.seqlen:
+        n = min(wl.seqlen, max(n, int(n * budget_s / dt)))
+        dt = run(n)
+    return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "positions 0..%d of one sequence (%d tokens, 1 layer; single-threaded C, fp64), %.1f s"
+                      % (n - 1, n, dt)}
+
+
+def backward_bench(args, wl):
+    """engram_backward over the workload's tokens (every layer of a step), the
+    retrieval indices computed beforehand as the forward pass would have."""
+    import numpy as np
+    import torch
+
+    from hashed_gram_embedding_vocab_amd import binding as B
+    from synthetic import workloads as W
+    from synthetic.device import make_device_layer, to_device
+
+    if wl.dtype != "bf16" or wl.decode:
+        print("the backward covers bf16 whole sequences", file=sys.stderr)
+        sys.exit(2)
+    n_tok = wl.n_tokens
+    R = max(1, args.rotate)
+    gen = torch.Generator().manual_seed(11)
+    layers = []
+    for slot in range(len(wl.layers)):
+        dl = make_device_layer(wl, layer_slot=slot)
+        toks = [to_device(W.make_tokens(wl, seed=wl.seed(2) + 17 * r), torch.int32, "cuda") for r in range(R)]
+        idx = []
+        for r in range(R):
+            x = torch.empty((n_tok, wl.n_tables), dtype=torch.int32, device="cuda")
+            dl.plan.engram_hash(toks[r], dl.comp_map, x)
+            idx.append(x)
+        hs = [dl.h] + [torch.randn(dl.h.shape, generator=gen).to(dl.h.dtype).cuda() for _ in range(R - 1)]
+        douts = [torch.randn(dl.h.shape, generator=gen).to(dl.h.dtype).cuda() for _ in range(R)]
+        dh = torch.empty_like(dl.h)
+        grads = B.Grads(wl.n_branches, wl.d_model, wl.emb_dim, wl.conv_kernel, wl.n_tables, n_tok, wl.head_dim)
+        ws = dl.plan.backward_workspace(wl.batch, wl.seqlen)
+        layers.append((dl, idx, hs, douts, dh, grads, ws))
+    torch.cuda.synchronize()
+
+    def step(i):
+        r = i % R
+        for dl, idx, hs, douts, dh, grads, ws in layers:
+            dl.plan.engram_backward(idx[r], dl.tables, hs[r], dl.weights, douts[r], dh, grads, ws,
+                                    wl.batch, wl.seqlen)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    def timed(steps, kinds):
+        if kinds != []:
+            for dl, *_ in layers:
+                dl.plan.engram_profile_begin(8 * steps + 64, kinds)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        profs = [dl.plan.engram_profile_end() for dl, *_ in layers] if kinds != [] else None
+        return wall, profs
+
+    _, profs = timed(args.breakdown_steps, None)
+    per_call = {}
+    for k in ("gather", "bwd_gemm", "bwd_fuse", "bwd_table"):
+        tot = sum(p[k]["total_ms"] for p in profs)
+        calls = args.breakdown_steps * len(layers)
+        per_call[k] = round(tot / calls * 1e3, 2)  # us per engram_backward call
+    wall, _ = timed(args.steps, [])
+    De, d, Br = wl.emb_dim, wl.d_model, wl.n_branches
+    n_pad = (n_tok + 127) // 128 * 128
+    # k and v again, dE and dW: three contractions of (B_r + 1) d x D_e over the tokens
+    flops = 2.0 * De * (Br + 1) * d * (2 * n_tok + n_pad)
+    tf = flops / (per_call["bwd_gemm"] * 1e-6) / 1e12
+    cpu = None if args.no_cpu_baseline else backward_cpu_baseline(wl, args.cpu_seconds)
+    line = {
+        "metric": "Engram bwd tokens/sec",
+        "value": round(n_tok * args.steps / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic: Zipf(%s) token ids, seeded Philox tables, N(0,1) hidden states and output gradients"
+                % wl.zipf_s,
+        "config": {"workload": wl.name, "batch": wl.batch, "seq_len": wl.seqlen, "tokens_per_step": n_tok,
+                   "layers": list(wl.layers), "n_branches": Br, "d_model": d, "emb_dim": De,
+                   "rotated_buffers": R, "parallelism": "single GPU"},
+        "roofline": {"kernel": "proj_bf16_kernel<3> (k and v, dE, dW)", "bound": "mfma", "achieved": round(tf, 2),
+                     "peak": MFMA_PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+                     "frac": round(tf / MFMA_PEAK_TFLOPS["bf16"], 4), "flops_per_call": flops,
+                     "us_per_call": per_call["bwd_gemm"], "traffic": None},
+        "us_per_call": per_call,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

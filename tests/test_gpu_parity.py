@@ -625,3 +625,69 @@ def test_backward_matches_oracle(B, br, batch, seqlen, kc, mode, flags, d):
         grad_within(got_grads[tau, :c], grads[tau, :c], "table %d rows" % tau)
     del dl
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name,br,batch,seqlen", [("small", 1, 1, 96), ("layer27b", 1, 1, 40),
+                                                   ("multibranch_prefill", 4, 1, 12)])
+def test_backward_full_width_against_oracle(B, name, br, batch, seqlen):
+    """The configs' own widths (d, tables, d_e, branches), on few enough
+    tokens for the oracle's chain rule to finish in seconds."""
+    say("backward full width", name, batch, seqlen)
+    wl = dataclasses.replace(W.workload(name), batch=batch, seqlen=seqlen)
+    dl = make_device_layer(wl, batch=batch, seqlen=seqlen)
+    toks = W.make_tokens(wl, batch=batch, seqlen=seqlen)
+    n_tok = batch * seqlen
+    idx = torch.zeros((n_tok, wl.n_tables), dtype=torch.int32, device="cuda")
+    dl.plan.engram_hash(dev_i32(toks), dl.comp_map, idx)
+    rng = np.random.default_rng(5)
+    dout = torch.from_numpy(rng.standard_normal((br, n_tok, wl.d_model)).astype(np.float32)).to(torch.bfloat16).cuda()
+    dh, g = _backward(dl, idx, dout)
+    idx_ref, _, _ = oracle_indices(wl, dl.li, toks, dl.comp_map_host)
+    L = oracle_layer(wl, dl.li, idx_ref, batch, seqlen)
+    ref = L.backward(dout.float().cpu().numpy())
+    assert_within(host(dh), ref["dh"], "bf16", "dh")
+    grad_within(g.dw[:br].cpu().numpy(), ref["dw_k"], "dW_k")
+    grad_within(g.dw[br].cpu().numpy(), ref["dw_v"], "dW_v")
+    grad_within(g.dgamma_h.cpu().numpy(), ref["dgamma_h"], "dgamma_h")
+    grad_within(g.dgamma_k.cpu().numpy(), ref["dgamma_k"], "dgamma_k")
+    grad_within(g.dconv_w.cpu().numpy(), ref["dconv_w"], "dconv_w")
+    rows, grads, counts = oracle.table_grad(idx_ref, ref["demb"], wl.head_dim)
+    assert np.array_equal(g.row_counts.cpu().numpy(), counts)
+    got_rows = g.row_ids.cpu().numpy().view(np.uint32)
+    got_grads = g.row_grads.cpu().numpy()
+    for tau in range(wl.n_tables):
+        c = int(counts[tau])
+        assert np.array_equal(got_rows[tau, :c], rows[tau, :c])
+        grad_within(got_grads[tau, :c], grads[tau, :c], "table %d rows" % tau)
+    del dl
+    torch.cuda.empty_cache()
+
+
+def test_backward_full_size_rows_and_determinism(B):
+    """32,768 tokens of the small config: the listed rows of every table are
+    exactly the distinct slots the tokens hashed to (ascending), and a second
+    call gives the same bits."""
+    say("backward full size")
+    wl = W.workload("small")
+    dl = make_device_layer(wl)
+    toks = W.make_tokens(wl)
+    n_tok = wl.n_tokens
+    idx = torch.zeros((n_tok, wl.n_tables), dtype=torch.int32, device="cuda")
+    dl.plan.engram_hash(dev_i32(toks), dl.comp_map, idx)
+    dout = (torch.randn((1, n_tok, wl.d_model), generator=torch.Generator().manual_seed(3))
+            .to(torch.bfloat16).cuda())
+    dh, g = _backward(dl, idx, dout)
+    dh2, g2 = _backward(dl, idx, dout)
+    assert torch.equal(dh, dh2)
+    for name in ("dw", "dgamma_h", "dgamma_k", "dconv_w", "row_ids", "row_grads", "row_counts"):
+        assert torch.equal(getattr(g, name), getattr(g2, name)), name
+    assert torch.isfinite(dh.float()).all() and torch.isfinite(g.dw).all() and torch.isfinite(g.row_grads).all()
+    idx_h = idx.cpu().numpy().view(np.uint32)
+    counts = g.row_counts.cpu().numpy()
+    rows = g.row_ids.cpu().numpy().view(np.uint32)
+    for tau in range(wl.n_tables):
+        used = np.unique(idx_h[:, tau])
+        assert counts[tau] == len(used)
+        assert np.array_equal(rows[tau, :counts[tau]], used)
+    del dl
+    torch.cuda.empty_cache()
