@@ -506,10 +506,10 @@ namespace {
 
 struct BwdLayout {
     size_t E, KV, stats, dalpha, dconv, dg, dkv, wt, et, dkvt, demb, keys_in, keys_out, vals_in, vals_out, head,
-        incl, temp, total;
+        incl, temp, sum_part, dw_part, lead, tail, cflags, tinfo, total;
     size_t temp_bytes;
     int64_t n_pad;
-    int32_t n_stripes, conv_blocks, gate_chunks;
+    int32_t n_stripes, conv_blocks, gate_chunks, dw_splits;
 };
 
 // The shapes engram_backward covers (status ENGRAM_OK), with its workspace.
@@ -554,6 +554,15 @@ engram_status bwd_layout_of(const engram_plan_s &p, int32_t batch, int32_t seqle
     L.head = take((size_t)n_items * 4);
     L.incl = take((size_t)n_items * 4);
     L.temp = take(L.temp_bytes);
+    const int64_t slabs = std::max(bwd_sum_slabs(L.gate_chunks), bwd_sum_slabs(L.conv_blocks));
+    L.sum_part = take((size_t)(std::max(Br * d, d * p.cfg.conv_kernel) * slabs * 4));
+    L.dw_splits = plain_k_splits(N, De, n_pad);
+    L.dw_part = take(L.dw_splits > 1 ? (size_t)(L.dw_splits * N * De * 4) : 0);
+    const int64_t chunks = bwd_row_chunks(n_items);
+    L.lead = take((size_t)(chunks * p.cfg.head_dim * 4));
+    L.tail = take((size_t)(chunks * p.cfg.head_dim * 4));
+    L.cflags = take((size_t)(chunks * 4));
+    L.tinfo = take((size_t)(chunks * 8));
     L.total = off;
     return ENGRAM_OK;
 }
@@ -658,9 +667,11 @@ engram_status engram_backward(engram_plan p, const uint32_t *d_idx, const void *
         launch_bwd_gate_stats(ba, stream);
         launch_bwd_conv(ba, stream);
         launch_bwd_gate(ba, stream);
-        launch_bwd_sum_rows(ba.dg_part, Br, L.gate_chunks, d, g->dgamma_h, stream);
-        launch_bwd_sum_rows(ba.dg_part + (int64_t)Br * L.gate_chunks * d, Br, L.gate_chunks, d, g->dgamma_k, stream);
-        launch_bwd_sum_rows(ba.dconv_part, 1, L.conv_blocks, (int64_t)d * kc, g->dconv_w, stream);
+        float *part = reinterpret_cast<float *>(base + L.sum_part);
+        launch_bwd_sum_rows(ba.dg_part, Br, L.gate_chunks, d, part, g->dgamma_h, stream);
+        launch_bwd_sum_rows(ba.dg_part + (int64_t)Br * L.gate_chunks * d, Br, L.gate_chunks, d, part, g->dgamma_k,
+                            stream);
+        launch_bwd_sum_rows(ba.dconv_part, 1, L.conv_blocks, (int64_t)d * kc, part, g->dconv_w, stream);
         for (int m = 0; m <= Br; ++m)
             launch_bwd_transpose(static_cast<const uint16_t *>(m < Br ? w->w_k[m] : w->w_v), d, De, De,
                                  wt + (int64_t)m * d, N, d, stream);
@@ -682,17 +693,23 @@ engram_status engram_backward(engram_plan p, const uint32_t *d_idx, const void *
         pe.out_ld = De;
         pe.n_rows = De;
         launch_proj_plain_bf16(pe, stream);
+        // dW contracts over every token: few output tiles, so K is split
+        // until the chip is full and the partial results summed in order
         ProjArgs pw{};
         pw.emb = dkvt;
         for (int m = 0; m <= kMaxBranches; ++m) pw.w[m] = et;
         pw.n_tok = N;
-        pw.K = (int32_t)L.n_pad;
+        pw.K = (int32_t)(L.n_pad / L.dw_splits);
+        pw.k_ld = (int32_t)L.n_pad;
         pw.d = De;
         pw.n_mats = 1;
-        pw.out_f32 = g->dw;
+        pw.out_f32 = L.dw_splits > 1 ? reinterpret_cast<float *>(base + L.dw_part) : g->dw;
         pw.out_ld = De;
+        pw.out_split = N * De;
         pw.n_rows = De;
-        launch_proj_plain_bf16(pw, stream);
+        launch_proj_plain_bf16(pw, stream, L.dw_splits);
+        if (L.dw_splits > 1)
+            launch_bwd_sum_parts(reinterpret_cast<float *>(base + L.dw_part), 1, N * De, L.dw_splits, g->dw, stream);
     }
     if (last_launch_status() != ENGRAM_OK) return ENGRAM_E_DEVICE;
     {
@@ -713,6 +730,10 @@ engram_status engram_backward(engram_plan p, const uint32_t *d_idx, const void *
         ta.row_ids = g->row_ids;
         ta.row_grads = g->row_grads;
         ta.row_counts = g->row_counts;
+        ta.lead = reinterpret_cast<float *>(base + L.lead);
+        ta.tail = reinterpret_cast<float *>(base + L.tail);
+        ta.cflags = reinterpret_cast<uint32_t *>(base + L.cflags);
+        ta.tinfo = reinterpret_cast<uint32_t *>(base + L.tinfo);
         Launch l(P, ENGRAM_K_BWD_TABLE, stream);
         if (launch_bwd_table_grad(ta, stream) != hipSuccess) return ENGRAM_E_DEVICE;
     }

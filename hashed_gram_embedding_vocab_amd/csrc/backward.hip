@@ -305,15 +305,39 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(BwdArgs a) {
     *reinterpret_cast<f32x4_t *>(a.dg_part + (int64_t)a.n_branches * gridDim.x * d + pr) = dgk;
 }
 
-// out[g][i] = sum over r of in[g][r][i], r ascending (one thread per (g, i)).
-__global__ __launch_bounds__(256) void bwd_sum_rows_kernel(const float *in, int64_t groups, int64_t rows,
-                                                           int64_t width, float *out) {
+// Sums over the rows of in[g][rows][width], in a fixed order, in two
+// stages.  Stage 1: slab s of S holds rows [s*rows/S, (s+1)*rows/S); four
+// threads per column each add every fourth row of the slab, ascending, and
+// the four sums are added in thread order into part[g][s][i].
+__global__ __launch_bounds__(256) void bwd_sum_slabs_kernel(const float *in, int64_t rows, int64_t width, int32_t S,
+                                                            float *part) {
+    __shared__ float red[4][64];
+    const int c = threadIdx.x & 63, q = threadIdx.x >> 6;
+    const int64_t i = (int64_t)blockIdx.x * 64 + c;
+    const int64_t g = blockIdx.y, s = blockIdx.z;
+    const int64_t r0 = s * rows / S, r1 = (s + 1) * rows / S;
+    float acc = 0.f;
+    if (i < width) {
+        const float *p = in + g * rows * width + i;
+#pragma unroll 4
+        for (int64_t r = r0 + q; r < r1; r += 4) acc += p[r * width];
+    }
+    red[q][c] = acc;
+    __syncthreads();
+    if (q == 0 && i < width) part[(g * S + s) * width + i] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+}
+
+// Stage 2 (and the split-K sum of a contraction): out[g][i] = sum over
+// s = 0..S-1, ascending, of part[g][s][i].
+__global__ __launch_bounds__(256) void bwd_sum_parts_kernel(const float *part, int64_t groups, int64_t width,
+                                                            int32_t S, float *out) {
     const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (x >= groups * width) return;
     const int64_t gi = x / width, i = x - gi * width;
-    const float *p = in + gi * rows * width + i;
+    const float *p = part + gi * S * width + i;
     float s = 0.f;
-    for (int64_t r = 0; r < rows; ++r) s += p[r * width];
+#pragma unroll 16
+    for (int k = 0; k < S; ++k) s += p[k * width];
     out[x] = s;
 }
 
@@ -353,34 +377,120 @@ __global__ __launch_bounds__(256) void bwd_heads_kernel(const uint64_t *keys, in
     head[i] = (i == 0 || keys[i] != keys[i - 1]) ? 1u : 0u;
 }
 
-// One wave per sorted item; the wave of each run's first item adds the
-// run's dE slices (tokens ascending: the sort is stable) and writes the
-// row's entry.  The wave of each table's first item also writes its count.
-__global__ __launch_bounds__(256) void bwd_row_sums_kernel(const uint64_t *keys, const uint32_t *vals,
-                                                           const uint32_t *head, const uint32_t *incl,
-                                                           const float *demb, int64_t n_tok, int32_t n_tables,
-                                                           int32_t head_dim, uint32_t *row_ids, float *row_grads,
-                                                           int32_t *row_counts) {
-    const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+// Per-table row gradients as a segmented sum over the sorted items, in two
+// passes over fixed 64-item chunks, one wave per chunk.  Pass 1 adds the
+// chunk's dE slices in item order (tokens ascending within each run: the sort
+// is stable).  A run that starts and ends inside the chunk is written to its
+// row slot directly; the part of a run that began in an earlier chunk goes
+// to lead[chunk], the part of the chunk's last run that continues past the
+// chunk goes to tail[chunk] (with its slot and row).  Pass 2 adds, for every
+// chunk with a tail, the lead parts of the following chunks in chunk order.
+// The order of every sum depends only on the sorted items, so the result is
+// the same on every run.
+constexpr int kRowChunk = 64;
+constexpr uint32_t kChunkHasHead = 1u, kChunkLead = 2u, kChunkTail = 4u;
+
+template <int NQ>  // head_dim <= 64 * NQ
+__global__ __launch_bounds__(256) void bwd_row_chunks_kernel(const uint64_t *keys, const uint32_t *vals,
+                                                             const uint32_t *head, const uint32_t *incl,
+                                                             const float *demb, int64_t n_tok, int32_t n_tables,
+                                                             int32_t head_dim, uint32_t *row_ids, float *row_grads,
+                                                             int32_t *row_counts, float *lead, float *tail,
+                                                             uint32_t *cflags, uint32_t *tinfo) {
+    const int64_t n = n_tok * n_tables;
+    const int64_t c = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    if (i >= n_tok * n_tables || !head[i]) return;
-    const int64_t tau = i / n_tok;
-    const int64_t first = tau * n_tok, end = first + n_tok;
-    const int64_t local = (int64_t)incl[i] - (int64_t)incl[first];
-    if (i == first && lane == 0) row_counts[tau] = (int32_t)(incl[end - 1] - incl[first] + 1);
-    const int64_t De = (int64_t)n_tables * head_dim;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t j = i; j < end && (j == i || !head[j]); ++j) {
-        const float *src = demb + (int64_t)vals[j] * De + tau * head_dim;
+    const int64_t base = c * kRowChunk;
+    if (base >= n) return;
+    const int cnt = (int)min((int64_t)kRowChunk, n - base);
+    const int64_t j = base + lane;
+    const bool in = lane < cnt;
+    uint32_t my_off = 0, my_slot = 0, my_row = 0;
+    bool my_head = false;
+    if (in) {
+        const int64_t tau = j / n_tok, first = tau * n_tok;
+        const uint32_t inc = incl[j];
+        my_head = head[j] != 0;
+        my_row = (uint32_t)keys[j];
+        my_slot = (uint32_t)(first + inc - incl[first]);
+        my_off = vals[j] * (uint32_t)(n_tables * head_dim) + (uint32_t)(tau * head_dim);
+        if (j == first) row_counts[tau] = (int32_t)(incl[first + n_tok - 1] - inc + 1);
+    }
+    const uint64_t hmask = __ballot(my_head);
+    const bool next_head = (base + cnt >= n) || head[base + cnt] != 0;
+    bool has_tail = false;
+    float acc[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) acc[q] = 0.f;
+    for (int k0 = 0; k0 < cnt; k0 += 8) {
+        float v[8][NQ];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int k = min(k0 + u, cnt - 1);
+            const float *src = demb + (uint32_t)__builtin_amdgcn_readlane((int)my_off, k);
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) v[u][q] = (lane + 64 * q < head_dim) ? src[lane + 64 * q] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int k = k0 + u;
+            if (k >= cnt) break;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) acc[q] += v[u][q];
+            const bool last = k == cnt - 1;
+            const bool ends = last ? next_head : ((hmask >> (k + 1)) & 1ull) != 0;
+            if (!(ends || last)) continue;
+            const bool started_here = (hmask & ((2ull << k) - 1ull)) != 0;
+            float *dst;
+            if (!started_here) {
+                dst = lead + c * head_dim;
+            } else {
+                const uint32_t slot = (uint32_t)__builtin_amdgcn_readlane((int)my_slot, k);
+                const uint32_t row = (uint32_t)__builtin_amdgcn_readlane((int)my_row, k);
+                if (ends) {
+                    dst = row_grads + (int64_t)slot * head_dim;
+                    if (lane == 0) row_ids[slot] = row;
+                } else {
+                    dst = tail + c * head_dim;
+                    has_tail = true;
+                    if (lane == 0) {
+                        tinfo[2 * c] = slot;
+                        tinfo[2 * c + 1] = row;
+                    }
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                if (lane + 64 * q < head_dim) dst[lane + 64 * q] = acc[q];
+                acc[q] = 0.f;
+            }
+        }
+    }
+    if (lane == 0)
+        cflags[c] = (hmask ? kChunkHasHead : 0u) | ((hmask & 1ull) ? 0u : kChunkLead) | (has_tail ? kChunkTail : 0u);
+}
+
+__global__ __launch_bounds__(256) void bwd_row_chain_kernel(const float *lead, const float *tail,
+                                                            const uint32_t *cflags, const uint32_t *tinfo,
+                                                            int64_t n_chunks, int32_t head_dim, uint32_t *row_ids,
+                                                            float *row_grads) {
+    const int64_t c = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (c >= n_chunks || !(cflags[c] & kChunkTail)) return;
+    float acc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = (lane + 64 * q < head_dim) ? tail[c * head_dim + lane + 64 * q] : 0.f;
+    for (int64_t k = c + 1; k < n_chunks; ++k) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            if (lane + 64 * q < head_dim) acc[q] += src[lane + 64 * q];
+            if (lane + 64 * q < head_dim) acc[q] += lead[k * head_dim + lane + 64 * q];
+        if ((cflags[k] & kChunkHasHead) || k + 1 == n_chunks || !(cflags[k + 1] & kChunkLead)) break;
     }
-    if (lane == 0) row_ids[first + local] = (uint32_t)keys[i];
-    float *dst = row_grads + (first + local) * head_dim;
+    const uint32_t slot = tinfo[2 * c];
+    if (lane == 0) row_ids[slot] = tinfo[2 * c + 1];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-        if (lane + 64 * q < head_dim) dst[lane + 64 * q] = acc[q];
+        if (lane + 64 * q < head_dim) row_grads[(int64_t)slot * head_dim + lane + 64 * q] = acc[q];
 }
 
 }  // namespace
@@ -416,9 +526,19 @@ void launch_bwd_gate(const BwdArgs &a, hipStream_t s) {
                   s, a);
 }
 
-void launch_bwd_sum_rows(const float *in, int64_t groups, int64_t rows, int64_t width, float *out, hipStream_t s) {
+int32_t bwd_sum_slabs(int64_t rows) { return (int32_t)std::min<int64_t>(64, rows); }
+
+void launch_bwd_sum_rows(const float *in, int64_t groups, int64_t rows, int64_t width, float *part, float *out,
+                         hipStream_t s) {
+    const int32_t S = bwd_sum_slabs(rows);
+    launch_kernel(bwd_sum_slabs_kernel, dim3((unsigned)((width + 63) / 64), (unsigned)groups, (unsigned)S),
+                  dim3(256), s, in, rows, width, S, part);
+    launch_bwd_sum_parts(part, groups, width, S, out, s);
+}
+
+void launch_bwd_sum_parts(const float *part, int64_t groups, int64_t width, int32_t S, float *out, hipStream_t s) {
     const int64_t n = groups * width;
-    launch_kernel(bwd_sum_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), s, in, groups, rows, width, out);
+    launch_kernel(bwd_sum_parts_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), s, part, groups, width, S, out);
 }
 
 void launch_bwd_transpose(const uint16_t *src, int64_t rows, int64_t cols, int64_t src_ld, uint16_t *dst,
@@ -426,6 +546,8 @@ void launch_bwd_transpose(const uint16_t *src, int64_t rows, int64_t cols, int64
     const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((dst_cols + 63) / 64));
     launch_kernel(bwd_transpose_kernel, grid, dim3(256), s, src, rows, cols, src_ld, dst, dst_ld, dst_cols);
 }
+
+int64_t bwd_row_chunks(int64_t n_items) { return (n_items + kRowChunk - 1) / kRowChunk; }
 
 size_t bwd_table_temp_bytes(int64_t n_items) {
     size_t sort_bytes = 0, scan_bytes = 0;
@@ -450,8 +572,21 @@ hipError_t launch_bwd_table_grad(const BwdTableArgs &t, hipStream_t s) {
     bytes = t.temp_bytes;
     e = rocprim::inclusive_scan(t.temp, bytes, t.head, t.incl, (size_t)n, rocprim::plus<uint32_t>(), s);
     if (e != hipSuccess) return e;
-    launch_kernel(bwd_row_sums_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), s, t.keys_out, t.vals_out, t.head,
-                  t.incl, t.demb, t.n_tok, t.n_tables, t.head_dim, t.row_ids, t.row_grads, t.row_counts);
+    const int64_t chunks = bwd_row_chunks(n);
+    const dim3 grid((unsigned)((chunks + 3) / 4));
+#define ENGRAM_ROW_CHUNKS(NQ)                                                                              \
+    launch_kernel(bwd_row_chunks_kernel<NQ>, grid, dim3(256), s, t.keys_out, t.vals_out, t.head, t.incl, t.demb, \
+                  t.n_tok, t.n_tables, t.head_dim, t.row_ids, t.row_grads, t.row_counts, t.lead, t.tail,        \
+                  t.cflags, t.tinfo)
+    if (t.head_dim <= 64)
+        ENGRAM_ROW_CHUNKS(1);
+    else if (t.head_dim <= 128)
+        ENGRAM_ROW_CHUNKS(2);
+    else
+        ENGRAM_ROW_CHUNKS(4);
+#undef ENGRAM_ROW_CHUNKS
+    launch_kernel(bwd_row_chain_kernel, grid, dim3(256), s, t.lead, t.tail, t.cflags, t.tinfo, chunks, t.head_dim,
+                  t.row_ids, t.row_grads);
     return hipGetLastError();
 }
 

@@ -148,6 +148,10 @@ struct ProjArgs {
     float *out_f32;                        // element (t, n) at out_f32[t * out_ld + n]
     int64_t out_ld;
     int32_t n_rows;                        // rows of W to store (n < n_rows)
+    // split K: launch z contracts k in [z K, (z+1) K) of rows k_ld long and
+    // stores at out_f32 + z * out_split (k_ld 0: one launch, rows K long)
+    int32_t k_ld;
+    int64_t out_split;
 };
 
 constexpr int kPartCols = 128;  // columns of d summed into one gate partial (bf16 path)
@@ -165,7 +169,12 @@ void launch_proj_v_fused_bf16(const ProjArgs &a, hipStream_t s);
 // accumulate and result) on the same MFMA main loop: W rows are the n_mats
 // matrices of a.w stacked (a.d rows each), E has a.n_tok rows, K = a.K
 // (K % 128 == 0); rows n >= a.n_rows and tokens t >= a.n_tok are not stored.
-void launch_proj_plain_bf16(const ProjArgs &a, hipStream_t s);
+// splits > 1: a.K is the share of each of the splits launches (a.k_ld =
+// splits * a.K), each storing its own partial result (see ProjArgs).
+void launch_proj_plain_bf16(const ProjArgs &a, hipStream_t s, int splits = 1);
+// How many K splits fill the chip for a plain contraction of n_tok x rows
+// outputs over K (a power of two; K / splits stays a multiple of 128).
+int plain_k_splits(int64_t n_tok, int64_t rows, int64_t K);
 void launch_proj_f32(const ProjArgs &a, hipStream_t s);  // k into kbuf, v, then partials
 
 // ---------------------------------------------------------------- fusion
@@ -264,8 +273,13 @@ void launch_bwd_conv(const BwdArgs &a, hipStream_t s);
 void launch_bwd_gate(const BwdArgs &a, hipStream_t s);
 int32_t bwd_conv_blocks(int32_t batch, int32_t seqlen);
 int32_t bwd_gate_chunks(int64_t n_tok);
-// out[g][i] = sum over r (ascending) of in[g][r][i]
-void launch_bwd_sum_rows(const float *in, int64_t groups, int64_t rows, int64_t width, float *out, hipStream_t s);
+// out[g][i] = sum over r of in[g][r][i] in a fixed order (rows split into
+// bwd_sum_slabs(rows) slabs, each summed into part[g][slab][i] first)
+int32_t bwd_sum_slabs(int64_t rows);
+void launch_bwd_sum_rows(const float *in, int64_t groups, int64_t rows, int64_t width, float *part, float *out,
+                         hipStream_t s);
+// out[g][i] = sum over s = 0..S-1, ascending, of part[g][s][i]
+void launch_bwd_sum_parts(const float *part, int64_t groups, int64_t width, int32_t S, float *out, hipStream_t s);
 // dst[c][r] = src[r][c] (bf16), zero for rows <= r < dst_cols
 void launch_bwd_transpose(const uint16_t *src, int64_t rows, int64_t cols, int64_t src_ld, uint16_t *dst,
                           int64_t dst_ld, int64_t dst_cols, hipStream_t s);
@@ -282,7 +296,13 @@ struct BwdTableArgs {
     uint32_t *row_ids;
     float *row_grads;
     int32_t *row_counts;
+    // per 64-item chunk of the sorted items: partial sums of the runs that
+    // cross its start (lead) and its end (tail), flags, tail slot and row
+    float *lead, *tail;                     // [chunks][head_dim]
+    uint32_t *cflags;                       // [chunks]
+    uint32_t *tinfo;                        // [chunks][2]
 };
+int64_t bwd_row_chunks(int64_t n_items);
 size_t bwd_table_temp_bytes(int64_t n_items);
 hipError_t launch_bwd_table_grad(const BwdTableArgs &t, hipStream_t s);
 

@@ -505,8 +505,11 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
     // d % 256 == 0, so a 256-row weight tile lies inside one matrix
     const int mat0 = min(n0, n_total - 1) / d;
     const char *wmat = reinterpret_cast<const char *>(pick(a.w, mat0));
-    const __amdgpu_buffer_rsrc_t wres = make_rsrc(wmat, (uint32_t)d * K * 2u);
-    const __amdgpu_buffer_rsrc_t eres = make_rsrc(a.emb, (uint32_t)(a.n_tok * K * 2));
+    // operand row length (a split-K launch reads its share of longer rows)
+    const int ld = (MODE == 3 && a.k_ld > 0) ? a.k_ld : K;
+    const int kbase = MODE == 3 ? (int)blockIdx.y * K : 0;
+    const __amdgpu_buffer_rsrc_t wres = make_rsrc(wmat, (uint32_t)d * ld * 2u);
+    const __amdgpu_buffer_rsrc_t eres = make_rsrc(a.emb, (uint32_t)(a.n_tok * ld * 2));
     // (a template-dependent bound here keeps the host pass from emitting the
     // kernel's launch stub, so the bound is the namespace constant both tiles share)
     static_assert(TBPW == kBlocksPerWave, "two row blocks per wave and operand in both tiles");
@@ -519,8 +522,8 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
         // order 4 * row + block (see the mode-1 epilogue)
         const int trow = MODE == 1 ? 64 * (blk >> 2) + 4 * lr + (blk & 3) : row;
         const int64_t t = min(max(t0 + trow, (int64_t)0), a.n_tok - 1);
-        woff[i] = (uint32_t)((n0 - mat0 * d + row) * K + lchunk * 8) * 2u;
-        eoff[i] = (uint32_t)(t * K + lchunk * 8) * 2u;
+        woff[i] = (uint32_t)((n0 - mat0 * d + row) * ld + lchunk * 8) * 2u;
+        eoff[i] = (uint32_t)(t * ld + lchunk * 8) * 2u;
     }
 
 // The immediate offset of a buffer load with an LDS destination moves the LDS
@@ -528,7 +531,7 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
 // moves the global address.
 #define ENGRAM_ISSUE(STG, k0)                                                                    \
     do {                                                                                         \
-        const int kbytes = (k0) * 2;                                                             \
+        const int kbytes = (kbase + (k0)) * 2;                                                   \
         _Pragma("unroll") for (int i = 0; i < TBPW; ++i) {                             \
             const int blk = wave * TBPW + i;                                           \
             __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void_t *)&STG.w[blk * kBlockBytes], \
@@ -682,6 +685,7 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
     if constexpr (MODE == 3) {
         // plain contraction: every tile stores its fp32 block, four
         // consecutive rows n (16 bytes) of one token t per lane and block
+        float *out = a.out_f32 + (int64_t)blockIdx.y * a.out_split;
 #pragma unroll
         for (int j = 0; j < TFT; ++j) {
             const int64_t t = tw + 16 * j + (lane & 15);
@@ -689,7 +693,7 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
 #pragma unroll
             for (int i = 0; i < FN; ++i) {
                 const int n = nw + 16 * i + sub;
-                if (n < a.n_rows) *reinterpret_cast<f32x4_t *>(a.out_f32 + t * a.out_ld + n) = acc[i][j];
+                if (n < a.n_rows) *reinterpret_cast<f32x4_t *>(out + t * a.out_ld + n) = acc[i][j];
             }
         }
     } else if constexpr (MODE == 0) {
@@ -772,15 +776,24 @@ void launch_proj_bf16(const ProjArgs &a, hipStream_t s) {
     }
 }
 
-void launch_proj_plain_bf16(const ProjArgs &a, hipStream_t s) {
+void launch_proj_plain_bf16(const ProjArgs &a, hipStream_t s, int splits) {
     const int n_total = a.n_mats * a.d;
     const int64_t wide = (int64_t)((n_total + BN - 1) / BN) * ((a.n_tok + BT - 1) / BT);
-    if (wide < 256) {
+    if (wide < 256 || splits > 1) {
         const int64_t blocks = (int64_t)((n_total + 127) / 128) * ((a.n_tok + 127) / 128);
-        launch_kernel((proj_bf16_kernel<3, 1, false, true>), dim3((unsigned)blocks), dim3(256), s, a);
+        launch_kernel((proj_bf16_kernel<3, 1, false, true>), dim3((unsigned)blocks, (unsigned)splits), dim3(256), s,
+                      a);
     } else {
         launch_kernel((proj_bf16_kernel<3, 1, false, false>), dim3((unsigned)wide), dim3(kThreads), s, a);
     }
+}
+
+int plain_k_splits(int64_t n_tok, int64_t rows, int64_t K) {
+    // the narrow tile runs two workgroups per CU: 512 fill the chip once
+    const int64_t blocks = ((rows + 127) / 128) * ((n_tok + 127) / 128);
+    int splits = 1;
+    while (blocks * splits * 2 <= 512 && K % (128 * splits * 2) == 0 && K / (splits * 2) >= 1024) splits *= 2;
+    return splits;
 }
 
 void launch_proj_v_fused_bf16(const ProjArgs &a, hipStream_t s) {
