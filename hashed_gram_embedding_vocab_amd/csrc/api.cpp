@@ -719,8 +719,9 @@ engram_status engram_backward(engram_plan p, const uint32_t *d_idx, const void *
         ta.n_tok = n_tok;
         ta.n_tables = p->n_tables;
         ta.head_dim = p->cfg.head_dim;
-        ta.keys_in = reinterpret_cast<uint64_t *>(base + L.keys_in);
-        ta.keys_out = reinterpret_cast<uint64_t *>(base + L.keys_out);
+        ta.table_rows = p->cfg.table_rows;
+        ta.keys_in = base + L.keys_in;
+        ta.keys_out = base + L.keys_out;
         ta.vals_in = reinterpret_cast<uint32_t *>(base + L.vals_in);
         ta.vals_out = reinterpret_cast<uint32_t *>(base + L.vals_out);
         ta.head = reinterpret_cast<uint32_t *>(base + L.head);

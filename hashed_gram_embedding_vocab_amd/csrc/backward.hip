@@ -341,37 +341,56 @@ __global__ __launch_bounds__(256) void bwd_sum_parts_kernel(const float *part, i
     out[x] = s;
 }
 
-// dst[c][r] = src[r][c] for r < rows; zero for rows <= r < dst_cols.  64 x 64
-// tiles through LDS; bf16 moved as 16-bit words.
+// dst[c][r] = src[r][c] (16-bit elements) for r < rows, zero for
+// rows <= r < dst_cols.  Each thread moves one 8 x 8 block: eight 16-byte row
+// loads, a transpose in registers, eight 16-byte row stores.  Lanes with the
+// same row group cover 128 contiguous source bytes, lanes with the same column
+// group 128 contiguous destination bytes.  cols, dst_cols and both leading
+// dimensions are multiples of 8, both pointers 16-byte aligned.
 __global__ __launch_bounds__(256) void bwd_transpose_kernel(const uint16_t *src, int64_t rows, int64_t cols,
                                                             int64_t src_ld, uint16_t *dst, int64_t dst_ld,
                                                             int64_t dst_cols) {
-    __shared__ uint16_t tile[64][65];
-    const int64_t c_base = (int64_t)blockIdx.x * 64, r_base = (int64_t)blockIdx.y * 64;
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-    for (int i = ty; i < 64; i += 4) {
-        const int64_t r = r_base + i, c = c_base + tx;
-        tile[i][tx] = (r < rows && c < cols) ? src[r * src_ld + c] : (uint16_t)0;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t c0 = (int64_t)blockIdx.x * 64 + 8 * (lane & 7);
+    const int64_t r0 = ((int64_t)blockIdx.y * 4 + wave) * 64 + 8 * (lane >> 3);
+    if (c0 >= cols || r0 >= dst_cols) return;
+    uint32_t in[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint4 x = make_uint4(0u, 0u, 0u, 0u);
+        if (r0 + i < rows) x = *reinterpret_cast<const uint4 *>(src + (r0 + i) * src_ld + c0);
+        in[i][0] = x.x;
+        in[i][1] = x.y;
+        in[i][2] = x.z;
+        in[i][3] = x.w;
     }
-    __syncthreads();
-    for (int i = ty; i < 64; i += 4) {
-        const int64_t c = c_base + i, r = r_base + tx;
-        if (c < cols && r < dst_cols) dst[c * dst_ld + r] = tile[tx][i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        // element j of every source row: 16-bit half (j & 1) of word (j >> 1)
+        uint32_t o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t A = in[2 * q][j >> 1], B = in[2 * q + 1][j >> 1];
+            o[q] = (j & 1) ? ((A >> 16) | (B & 0xffff0000u)) : ((A & 0xffffu) | (B << 16));
+        }
+        *reinterpret_cast<uint4 *>(dst + (c0 + j) * dst_ld + r0) = make_uint4(o[0], o[1], o[2], o[3]);
     }
 }
 
 // ---------------------------------------------------------------- table rows
-// Item i = tau * n_tok + t: key (tau, idx[t][tau]), value t.
+// Item i = tau * n_tok + t: key tau << row_bits | idx[t][tau], value t.
+template <typename KeyT>
 __global__ __launch_bounds__(256) void bwd_keys_kernel(const uint32_t *idx, int64_t n_tok, int32_t n_tables,
-                                                       uint64_t *keys, uint32_t *vals) {
+                                                       int32_t row_bits, KeyT *keys, uint32_t *vals) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n_tok * n_tables) return;
     const int64_t tau = i / n_tok, t = i - tau * n_tok;
-    keys[i] = ((uint64_t)tau << 32) | idx[t * n_tables + tau];
+    keys[i] = (KeyT)(((uint64_t)tau << row_bits) | idx[t * n_tables + tau]);
     vals[i] = (uint32_t)t;
 }
 
-__global__ __launch_bounds__(256) void bwd_heads_kernel(const uint64_t *keys, int64_t n, uint32_t *head) {
+template <typename KeyT>
+__global__ __launch_bounds__(256) void bwd_heads_kernel(const KeyT *keys, int64_t n, uint32_t *head) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
     head[i] = (i == 0 || keys[i] != keys[i - 1]) ? 1u : 0u;
@@ -390,8 +409,8 @@ __global__ __launch_bounds__(256) void bwd_heads_kernel(const uint64_t *keys, in
 constexpr int kRowChunk = 64;
 constexpr uint32_t kChunkHasHead = 1u, kChunkLead = 2u, kChunkTail = 4u;
 
-template <int NQ>  // head_dim <= 64 * NQ
-__global__ __launch_bounds__(256) void bwd_row_chunks_kernel(const uint64_t *keys, const uint32_t *vals,
+template <int NQ, typename KeyT>  // head_dim <= 64 * NQ
+__global__ __launch_bounds__(256) void bwd_row_chunks_kernel(const KeyT *keys, uint64_t row_mask, const uint32_t *vals,
                                                              const uint32_t *head, const uint32_t *incl,
                                                              const float *demb, int64_t n_tok, int32_t n_tables,
                                                              int32_t head_dim, uint32_t *row_ids, float *row_grads,
@@ -411,7 +430,7 @@ __global__ __launch_bounds__(256) void bwd_row_chunks_kernel(const uint64_t *key
         const int64_t tau = j / n_tok, first = tau * n_tok;
         const uint32_t inc = incl[j];
         my_head = head[j] != 0;
-        my_row = (uint32_t)keys[j];
+        my_row = (uint32_t)(keys[j] & (KeyT)row_mask);
         my_slot = (uint32_t)(first + inc - incl[first]);
         my_off = vals[j] * (uint32_t)(n_tables * head_dim) + (uint32_t)(tau * head_dim);
         if (j == first) row_counts[tau] = (int32_t)(incl[first + n_tok - 1] - inc + 1);
@@ -543,41 +562,52 @@ void launch_bwd_sum_parts(const float *part, int64_t groups, int64_t width, int3
 
 void launch_bwd_transpose(const uint16_t *src, int64_t rows, int64_t cols, int64_t src_ld, uint16_t *dst,
                           int64_t dst_ld, int64_t dst_cols, hipStream_t s) {
-    const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((dst_cols + 63) / 64));
+    // every caller passes cols, dst_cols, src_ld and dst_ld as multiples of 8
+    // and 16-byte aligned pointers (the kernel moves 8 x 8 blocks)
+    const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((dst_cols + 255) / 256));
     launch_kernel(bwd_transpose_kernel, grid, dim3(256), s, src, rows, cols, src_ld, dst, dst_ld, dst_cols);
 }
 
 int64_t bwd_row_chunks(int64_t n_items) { return (n_items + kRowChunk - 1) / kRowChunk; }
 
-size_t bwd_table_temp_bytes(int64_t n_items) {
+namespace {
+// radix (onesweep) at every size above one block: the merge path rocPRIM
+// picks by default below 2^20 items takes about twice as long here
+typedef rocprim::radix_sort_config<rocprim::default_config, rocprim::default_config, rocprim::default_config, 0>
+    SortCfg;
+
+template <typename KeyT>
+size_t table_temp_bytes(int64_t n_items) {
     size_t sort_bytes = 0, scan_bytes = 0;
-    (void)rocprim::radix_sort_pairs(nullptr, sort_bytes, (uint64_t *)nullptr, (uint64_t *)nullptr,
-                                    (uint32_t *)nullptr, (uint32_t *)nullptr, (size_t)n_items, 0, 64);
+    (void)rocprim::radix_sort_pairs<SortCfg>(nullptr, sort_bytes, (KeyT *)nullptr, (KeyT *)nullptr,
+                                             (uint32_t *)nullptr, (uint32_t *)nullptr, (size_t)n_items, 0,
+                                             (unsigned)(8 * sizeof(KeyT)));
     (void)rocprim::inclusive_scan(nullptr, scan_bytes, (uint32_t *)nullptr, (uint32_t *)nullptr, (size_t)n_items,
                                   rocprim::plus<uint32_t>());
     return std::max(sort_bytes, scan_bytes);
 }
 
-hipError_t launch_bwd_table_grad(const BwdTableArgs &t, hipStream_t s) {
+template <typename KeyT>
+hipError_t table_grad(const BwdTableArgs &t, int32_t row_bits, int32_t key_bits, hipStream_t s) {
     const int64_t n = t.n_tok * t.n_tables;
-    launch_kernel(bwd_keys_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), s, t.idx, t.n_tok, t.n_tables,
-                  t.keys_in, t.vals_in);
-    int end_bit = 32;
-    while ((1ll << (end_bit - 32)) < t.n_tables) ++end_bit;
+    KeyT *keys_in = static_cast<KeyT *>(t.keys_in), *keys_out = static_cast<KeyT *>(t.keys_out);
+    launch_kernel(bwd_keys_kernel<KeyT>, dim3((unsigned)((n + 255) / 256)), dim3(256), s, t.idx, t.n_tok,
+                  t.n_tables, row_bits, keys_in, t.vals_in);
     size_t bytes = t.temp_bytes;
-    hipError_t e = rocprim::radix_sort_pairs(t.temp, bytes, t.keys_in, t.keys_out, t.vals_in, t.vals_out, (size_t)n,
-                                             0, end_bit, s);
+    hipError_t e = rocprim::radix_sort_pairs<SortCfg>(t.temp, bytes, keys_in, keys_out, t.vals_in, t.vals_out,
+                                                      (size_t)n, 0, (unsigned)key_bits, s);
     if (e != hipSuccess) return e;
-    launch_kernel(bwd_heads_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), s, t.keys_out, n, t.head);
+    launch_kernel(bwd_heads_kernel<KeyT>, dim3((unsigned)((n + 255) / 256)), dim3(256), s, keys_out, n, t.head);
     bytes = t.temp_bytes;
     e = rocprim::inclusive_scan(t.temp, bytes, t.head, t.incl, (size_t)n, rocprim::plus<uint32_t>(), s);
     if (e != hipSuccess) return e;
     const int64_t chunks = bwd_row_chunks(n);
     const dim3 grid((unsigned)((chunks + 3) / 4));
-#define ENGRAM_ROW_CHUNKS(NQ)                                                                              \
-    launch_kernel(bwd_row_chunks_kernel<NQ>, grid, dim3(256), s, t.keys_out, t.vals_out, t.head, t.incl, t.demb, \
-                  t.n_tok, t.n_tables, t.head_dim, t.row_ids, t.row_grads, t.row_counts, t.lead, t.tail,        \
-                  t.cflags, t.tinfo)
+    const uint64_t row_mask = (row_bits >= 64) ? ~0ull : ((1ull << row_bits) - 1ull);
+#define ENGRAM_ROW_CHUNKS(NQ)                                                                                   \
+    launch_kernel((bwd_row_chunks_kernel<NQ, KeyT>), grid, dim3(256), s, keys_out, row_mask, t.vals_out, t.head, \
+                  t.incl, t.demb, t.n_tok, t.n_tables, t.head_dim, t.row_ids, t.row_grads, t.row_counts, t.lead,  \
+                  t.tail, t.cflags, t.tinfo)
     if (t.head_dim <= 64)
         ENGRAM_ROW_CHUNKS(1);
     else if (t.head_dim <= 128)
@@ -588,6 +618,24 @@ hipError_t launch_bwd_table_grad(const BwdTableArgs &t, hipStream_t s) {
     launch_kernel(bwd_row_chain_kernel, grid, dim3(256), s, t.lead, t.tail, t.cflags, t.tinfo, chunks, t.head_dim,
                   t.row_ids, t.row_grads);
     return hipGetLastError();
+}
+}  // namespace
+
+size_t bwd_table_temp_bytes(int64_t n_items) {
+    return std::max(table_temp_bytes<uint32_t>(n_items), table_temp_bytes<uint64_t>(n_items));
+}
+
+hipError_t launch_bwd_table_grad(const BwdTableArgs &t, hipStream_t s) {
+    // key = tau << row_bits | row, in 32 bits when the widest table and the
+    // table count fit there
+    uint32_t max_row = 0;
+    for (int tau = 0; tau < t.n_tables; ++tau) max_row = std::max(max_row, t.table_rows[tau] - 1u);
+    int32_t row_bits = 1, tau_bits = 0;
+    while (row_bits < 32 && (max_row >> row_bits) != 0) ++row_bits;
+    while ((1 << tau_bits) < t.n_tables) ++tau_bits;
+    const int32_t key_bits = row_bits + tau_bits;
+    if (key_bits <= 32) return table_grad<uint32_t>(t, row_bits, key_bits, s);
+    return table_grad<uint64_t>(t, row_bits, key_bits, s);
 }
 
 }  // namespace engram

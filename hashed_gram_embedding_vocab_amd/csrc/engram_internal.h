@@ -289,7 +289,8 @@ struct BwdTableArgs {
     const float *demb;                      // [n_tok][n_tables * head_dim]
     int64_t n_tok;
     int32_t n_tables, head_dim;
-    uint64_t *keys_in, *keys_out;           // [n_tables * n_tok]
+    const uint32_t *table_rows;             // [n_tables] rows of each table
+    void *keys_in, *keys_out;               // [n_tables * n_tok], 32- or 64-bit keys (8 bytes each reserved)
     uint32_t *vals_in, *vals_out, *head, *incl;
     void *temp;                             // sort / scan scratch
     size_t temp_bytes;
