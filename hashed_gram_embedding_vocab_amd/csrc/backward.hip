@@ -106,18 +106,28 @@ __global__ __launch_bounds__(256) void bwd_gate_stats_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- conv and gated value
 // Workgroup (position chunk, sequence, 1024-channel stripe); each thread owns
-// four channels and walks positions p = t0-3 .. t1+2 once, all branches
-// together, with sliding windows of the last values:
+// four channels of the chunk's positions, taken kConvSub at a time.  For the
+// outputs t = s0 .. s0+kConvSub-1 of one batch, every value the batch needs
+// is loaded at once (v at s0-3 .. s0+kConvSub-1, or .. s0+kConvSub+2 with
+// SILU_SKIP, and every branch's dout at s0 .. s0+kConvSub+2), so a thread
+// waits for memory once per batch instead of once per position; the halo
+// positions shared by neighbouring batches come from the caches.  Per branch:
 //   u_p = alpha_p v_p;  conv_p = sum_j w[K-1-j] u_{p-j}
 //   dconv_p = dout_p (LINEAR) or dout_p (sig + conv sig (1 - sig)) (SILU_SKIP)
-//   du_t = [SILU_SKIP] dout_t + sum_j w[K-1-j] dconv_{t+j}  (ready at p = t+3)
-//   dw[K-1-j] += u_{t-j} dconv_t for the chunk's own positions t
-// Out: dv_t (bf16, into the v columns of dkv), the workgroup's share of
-// dalpha_t = <v_t, du_t> per branch, and its share of the taps' gradient.
+//   du_t = [SILU_SKIP] dout_t + sum_j w[K-1-j] dconv_{t+j}
+//   dw[K-1-j] += u_{t-j} dconv_t
+// Out: dv_t = sum_m alpha_t du_t (bf16, into the v columns of dkv), the
+// workgroup's share of dalpha_t = <v_t, du_t> per branch, and its share of
+// the taps' gradient.
+constexpr int kConvSub = 4;
+
 template <int BR, bool SILU>
 __global__ __launch_bounds__(256) void bwd_conv_kernel(BwdArgs a) {
     __shared__ float alpha_s[BR][kConvPos + 6];   // positions t0-3 .. t1+2
     __shared__ float red[BR][kConvPos][4];        // per-wave dalpha shares
+    constexpr int P = kConvSub;
+    constexpr int NV = SILU ? P + 6 : P + 3;      // v at s0-3 .. s0-3+NV-1
+    constexpr int NG = P + 3;                     // dout at s0 .. s0+P+2
     const int T = a.seqlen;
     const int b = blockIdx.y;
     const int t0 = blockIdx.x * kConvPos;
@@ -146,85 +156,91 @@ __global__ __launch_bounds__(256) void bwd_conv_kernel(BwdArgs a) {
         for (int r = 0; r < 4; ++r)
             wt[j][r] = (live && j < kc) ? a.conv_w[(int64_t)(c0 + r) * kc + (kc - 1 - j)] : 0.f;
     }
-    // windows, index 0 = most recent: u and dconv per branch, v and dout
-    f32x4_t uw[BR][4], dcw[BR][4], gw[BR][4], vw[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        vw[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < BR; ++m) {
-            uw[m][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            dcw[m][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            gw[m][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
-    }
-    const float *vcol = a.kv + (int64_t)a.n_branches * d + c0;
+    // loads read a valid address (position and channel clamped) and are
+    // zeroed afterwards: no branch around them, so all of a batch's loads are
+    // in flight together
+    const int cc = live ? c0 : 0;
+    const float *vcol = a.kv + (int64_t)a.n_branches * d + cc;
+    const uint16_t *gcol = reinterpret_cast<const uint16_t *>(a.dout) + row0 * d + cc;
+    const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+    auto unpack = [](u32x2_t x) {
+        return f32x4_t{bf16_to_f32(x[0] & 0xFFFFu), bf16_to_f32(x[0] >> 16), bf16_to_f32(x[1] & 0xFFFFu),
+                       bf16_to_f32(x[1] >> 16)};
+    };
+    auto inseq = [&](int p) { return live && p >= 0 && p < T; };
 
-    for (int p = t0 - 3; p <= t1 + 2; ++p) {
-        const bool in_seq = p >= 0 && p < T;
-        // shift the windows
+    for (int s0 = t0; s0 < t1; s0 += P) {
+        f32x4_t vv[NV];
+        u32x2_t gg[BR][NG];
 #pragma unroll
-        for (int q = 3; q > 0; --q) {
-            vw[q] = vw[q - 1];
-#pragma unroll
-            for (int m = 0; m < BR; ++m) {
-                uw[m][q] = uw[m][q - 1];
-                dcw[m][q] = dcw[m][q - 1];
-                gw[m][q] = gw[m][q - 1];
-            }
+        for (int i = 0; i < NV; ++i) {
+            const int pc = min(max(s0 - 3 + i, 0), T - 1);
+            vv[i] = *reinterpret_cast<const f32x4_t *>(vcol + (row0 + pc) * a.kv_ld);
         }
-        f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-        if (live && in_seq) v = *reinterpret_cast<const f32x4_t *>(vcol + (row0 + p) * a.kv_ld);
-        vw[0] = v;
-        const int j_al = p - t0 + 3;
+#pragma unroll
+        for (int m = 0; m < BR; ++m)
+#pragma unroll
+            for (int i = 0; i < NG; ++i) {
+                const int pc = min(s0 + i, T - 1);
+                gg[m][i] = *reinterpret_cast<const u32x2_t *>(gcol + ((int64_t)m * a.n_tok + pc) * d);
+            }
+#pragma unroll
+        for (int i = 0; i < NV; ++i) vv[i] = inseq(s0 - 3 + i) ? vv[i] : zero4;
+
+        f32x4_t dv[P];
+#pragma unroll
+        for (int k = 0; k < P; ++k) dv[k] = zero4;
 #pragma unroll
         for (int m = 0; m < BR; ++m) {
-            const float al = alpha_s[m][j_al];
-            f32x4_t g = {0.f, 0.f, 0.f, 0.f};
-            if (live && in_seq) g = load_bf16x4(a.dout, ((int64_t)m * a.n_tok + row0 + p) * d + c0);
-            gw[m][0] = g;
-            f32x4_t u, dc;
+            // alpha at s0-3+i (LDS index s0-t0+i)
+            float al[NV];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                u[r] = al * v[r];
-                const float conv = wt[0][r] * u[r] + wt[1][r] * uw[m][1][r] + wt[2][r] * uw[m][2][r] +
-                                   wt[3][r] * uw[m][3][r];
-                if (SILU) {
-                    const float sg = sigmoid_b(conv);
-                    dc[r] = g[r] * (sg + conv * sg * (1.f - sg));
+            for (int i = 0; i < NV; ++i) al[i] = alpha_s[m][s0 - t0 + i];
+            // dconv at s0+i, zero outside the sequence
+            f32x4_t dc[NG];
+#pragma unroll
+            for (int i = 0; i < NG; ++i) {
+                const f32x4_t g = inseq(s0 + i) ? unpack(gg[m][i]) : zero4;
+                if constexpr (SILU) {
+                    // conv at s0+i from u at s0+i-3 .. s0+i (v index i .. i+3)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float conv = wt[0][r] * (al[i + 3] * vv[i + 3][r]) + wt[1][r] * (al[i + 2] * vv[i + 2][r]) +
+                                           wt[2][r] * (al[i + 1] * vv[i + 1][r]) + wt[3][r] * (al[i] * vv[i][r]);
+                        const float sg = sigmoid_b(conv);
+                        dc[i][r] = g[r] * (sg + conv * sg * (1.f - sg));
+                    }
                 } else {
-                    dc[r] = g[r];
+                    dc[i] = g;
                 }
             }
-            uw[m][0] = u;
-            dcw[m][0] = dc;  // zero outside the sequence (g is zero there)
-            if (p >= t0 && p < t1) {
+#pragma unroll
+            for (int k = 0; k < P; ++k) {
+                const int t = s0 + k;
+                if (t >= t1) break;
+                // taps: u_{t-j} is v index k+3-j
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) dw[j][r] += uw[m][j][r] * dc[r];
-            }
-        }
-        // du of position t = p - 3, now that dconv_{t..t+3} is known
-        const int t = p - 3;
-        if (t >= t0 && t < t1) {
-            f32x4_t dv = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int m = 0; m < BR; ++m) {
-                const float al = alpha_s[m][t - t0 + 3];
+                    for (int r = 0; r < 4; ++r) dw[j][r] += (al[k + 3 - j] * vv[k + 3 - j][r]) * dc[k][r];
+                const f32x4_t g = SILU ? (inseq(t) ? unpack(gg[m][k]) : zero4) : zero4;
                 float part = 0.f;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    float du = SILU ? gw[m][3][r] : 0.f;
-                    du += wt[0][r] * dcw[m][3][r] + wt[1][r] * dcw[m][2][r] + wt[2][r] * dcw[m][1][r] +
-                          wt[3][r] * dcw[m][0][r];
-                    part += vw[3][r] * du;
-                    dv[r] += al * du;
+                    float du = SILU ? g[r] : 0.f;
+                    du += wt[0][r] * dc[k][r] + wt[1][r] * dc[k + 1][r] + wt[2][r] * dc[k + 2][r] +
+                          wt[3][r] * dc[k + 3][r];
+                    part += vv[k + 3][r] * du;
+                    dv[k][r] += al[k + 3] * du;
                 }
                 part = wave_sum(part);
                 if ((tid & 63) == 0) red[m][t - t0][tid >> 6] = part;
             }
-            if (live) store_bf16x4(a.dkv, (row0 + t) * a.dkv_ld + (int64_t)a.n_branches * d + c0, dv);
+        }
+        if (live) {
+#pragma unroll
+            for (int k = 0; k < P; ++k)
+                if (s0 + k < t1) store_bf16x4(a.dkv, (row0 + s0 + k) * a.dkv_ld + (int64_t)a.n_branches * d + c0, dv[k]);
         }
     }
     __syncthreads();
@@ -571,10 +587,10 @@ void launch_bwd_transpose(const uint16_t *src, int64_t rows, int64_t cols, int64
 int64_t bwd_row_chunks(int64_t n_items) { return (n_items + kRowChunk - 1) / kRowChunk; }
 
 namespace {
-// radix (onesweep) at every size above one block: the merge path rocPRIM
-// picks by default below 2^20 items takes about twice as long here
-typedef rocprim::radix_sort_config<rocprim::default_config, rocprim::default_config, rocprim::default_config, 0>
-    SortCfg;
+// rocPRIM's default choice (block sort and merges below 2^20 items): its
+// onesweep path is no faster at these sizes and clears its look-back state
+// with memset nodes, which a captured graph must not hold
+typedef rocprim::default_config SortCfg;
 
 template <typename KeyT>
 size_t table_temp_bytes(int64_t n_items) {

@@ -776,23 +776,34 @@ void launch_proj_bf16(const ProjArgs &a, hipStream_t s) {
     }
 }
 
+// 256 x 256 tiles when they (times the K splits) occupy at least three
+// quarters of the CUs in a round; else 128 x 128 tiles, two per CU
+static bool plain_wide(int64_t wide_blocks, int splits) { return wide_blocks * splits >= 192; }
+
 void launch_proj_plain_bf16(const ProjArgs &a, hipStream_t s, int splits) {
     const int n_total = a.n_mats * a.d;
     const int64_t wide = (int64_t)((n_total + BN - 1) / BN) * ((a.n_tok + BT - 1) / BT);
-    if (wide < 256 || splits > 1) {
+    if (!plain_wide(wide, splits)) {
         const int64_t blocks = (int64_t)((n_total + 127) / 128) * ((a.n_tok + 127) / 128);
         launch_kernel((proj_bf16_kernel<3, 1, false, true>), dim3((unsigned)blocks, (unsigned)splits), dim3(256), s,
                       a);
     } else {
-        launch_kernel((proj_bf16_kernel<3, 1, false, false>), dim3((unsigned)wide), dim3(kThreads), s, a);
+        launch_kernel((proj_bf16_kernel<3, 1, false, false>), dim3((unsigned)wide, (unsigned)splits),
+                      dim3(kThreads), s, a);
     }
 }
 
 int plain_k_splits(int64_t n_tok, int64_t rows, int64_t K) {
-    // the narrow tile runs two workgroups per CU: 512 fill the chip once
-    const int64_t blocks = ((rows + 127) / 128) * ((n_tok + 127) / 128);
+    auto can_double = [&](int splits) { return K % (128 * splits * 2) == 0 && K / (splits * 2) >= 1024; };
+    // wide tiles, one workgroup per CU: split until a round is (nearly) full
+    const int64_t wide = ((rows + 255) / 256) * ((n_tok + 255) / 256);
     int splits = 1;
-    while (blocks * splits * 2 <= 512 && K % (128 * splits * 2) == 0 && K / (splits * 2) >= 1024) splits *= 2;
+    while (wide * splits * 2 <= 256 && can_double(splits)) splits *= 2;
+    if (plain_wide(wide, splits)) return splits;
+    // narrow tiles run two workgroups per CU: 512 fill the chip once
+    const int64_t narrow = ((rows + 127) / 128) * ((n_tok + 127) / 128);
+    splits = 1;
+    while (narrow * splits * 2 <= 512 && can_double(splits)) splits *= 2;
     return splits;
 }
 
