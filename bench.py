@@ -14,6 +14,11 @@ kernel (the one with the most time per step, timed live with HIP events
 recorded by the library around each of its launches on the launch stream),
 every kernel's roofline figures and the CPU oracle's tokens/s on a bounded
 sample of the same workload.
+
+`--backward` times the training step's backward instead: one engram_backward
+call per Engram layer over the workload's tokens (indices computed
+beforehand, as the forward pass would have), with its own JSON line in the
+same form (metric "Engram bwd tokens/sec").
 """
 
 from __future__ import annotations
@@ -449,18 +454,48 @@ def backward_bench(args, wl):
         profs = [dl.plan.engram_profile_end() for dl, *_ in layers] if kinds != [] else None
         return wall, profs
 
+    # breakdown pass: every kind timed by its own dispatch events; the
+    # measured run below times only the kind with the most time per step
     _, profs = timed(args.breakdown_steps, None)
-    per_call = {}
-    for k in ("gather", "bwd_gemm", "bwd_fuse", "bwd_table"):
-        tot = sum(p[k]["total_ms"] for p in profs)
-        calls = args.breakdown_steps * len(layers)
-        per_call[k] = round(tot / calls * 1e3, 2)  # us per engram_backward call
-    wall, _ = timed(args.steps, [])
+    kinds = ("gather", "bwd_gemm", "bwd_fuse", "bwd_table")
+    calls = args.breakdown_steps * len(layers)
+    per_call = {k: sum(p[k]["total_ms"] for p in profs) / calls * 1e3 for k in kinds}  # us per engram_backward call
+    dominant = max(kinds, key=lambda k: per_call[k])
+    wall, profs_m = timed(args.steps, [dominant])
+    dom_us = sum(p[dominant]["total_ms"] for p in profs_m) / (args.steps * len(layers)) * 1e3
     De, d, Br = wl.emb_dim, wl.d_model, wl.n_branches
+    N = (Br + 1) * d
     n_pad = (n_tok + 127) // 128 * 128
-    # k and v again, dE and dW: three contractions of (B_r + 1) d x D_e over the tokens
-    flops = 2.0 * De * (Br + 1) * d * (2 * n_tok + n_pad)
-    tf = flops / (per_call["bwd_gemm"] * 1e-6) / 1e12
+    eb = 2
+    # work per engram_backward call.  Contractions: k and v again, dE and dW,
+    # each 2 (B_r + 1) d D_e flop per token.  HBM kinds: the bytes their
+    # kernels move in this design (fp32 k and v read back, bf16 dk/dv, the
+    # operand transposes; table rows: dE slices read, row gradients written).
+    models = {
+        "bwd_gemm": ("mfma", 2.0 * De * N * (2 * n_tok + n_pad)),
+        "gather": ("hbm", n_tok * (wl.n_tables * 4 + 2 * De * eb)),
+        "bwd_fuse": ("hbm", Br * n_tok * d * (eb + 4)                      # gate statistics: h, k
+                     + n_tok * d * (4 + 2) + Br * n_tok * d * eb            # conv: v, dout; dv
+                     + Br * n_tok * d * (eb + 4 + eb + eb + 2)              # gate: h, k, dout; dh, dk
+                     + 2 * 2 * (N * De + n_tok * De + n_tok * N)),          # transposes
+        "bwd_table": ("hbm", wl.n_tables * n_tok * (wl.head_dim * 4 * 2 + 4 * 8)),
+    }
+
+    def figures(kind, us):
+        bound, work = models[kind]
+        if bound == "mfma":
+            ach, peak, unit = work / (us * 1e-6) / 1e12, MFMA_PEAK_TFLOPS["bf16"], "TFLOP/s"
+        else:
+            ach, peak, unit = work / (us * 1e-6) / 1e9, HBM_PEAK_GBS, "GB/s"
+        return {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
+                ("flops_per_call" if bound == "mfma" else "bytes_per_call"): work, "us_per_call": round(us, 2)}
+
+    kernel_of = {"bwd_gemm": "proj_bf16_kernel<3> (k and v, dE, dW with its split-K sum)",
+                 "bwd_fuse": "bwd_gate_stats, bwd_conv, bwd_gate, ordered sums, transposes",
+                 "bwd_table": "table-row gradients (keys, rocPRIM sort and scan, segmented sums)",
+                 "gather": "gather_kernel"}
+    per_kind = {k: dict(figures(k, per_call[k]), kernel=kernel_of[k]) for k in kinds}
+    roofline = dict(figures(dominant, dom_us), kernel=kernel_of[dominant], timed_in="measured run", traffic=None)
     cpu = None if args.no_cpu_baseline else backward_cpu_baseline(wl, args.cpu_seconds)
     line = {
         "metric": "Engram bwd tokens/sec",
@@ -479,11 +514,9 @@ def backward_bench(args, wl):
         "config": {"workload": wl.name, "batch": wl.batch, "seq_len": wl.seqlen, "tokens_per_step": n_tok,
                    "layers": list(wl.layers), "n_branches": Br, "d_model": d, "emb_dim": De,
                    "rotated_buffers": R, "parallelism": "single GPU"},
-        "roofline": {"kernel": "proj_bf16_kernel<3> (k and v, dE, dW)", "bound": "mfma", "achieved": round(tf, 2),
-                     "peak": MFMA_PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
-                     "frac": round(tf / MFMA_PEAK_TFLOPS["bf16"], 4), "flops_per_call": flops,
-                     "us_per_call": per_call["bwd_gemm"], "traffic": None},
-        "us_per_call": per_call,
+        "roofline": roofline,
+        "kinds": per_kind,
+        "us_per_call": {k: round(v, 2) for k, v in per_call.items()},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
