@@ -54,6 +54,13 @@ def parse():
                     help="time only whole steps (no per-launch events; no roofline)")
     ap.add_argument("--backward", action="store_true",
                     help="time engram_backward (training) instead of the forward: one JSON line of its own")
+    ap.add_argument("--offload", action="store_true",
+                    help="retrieval from tables in pinned host memory (with and without the hot-row cache in HBM) "
+                         "and its overlap with device compute: one JSON line of its own")
+    ap.add_argument("--cache-rows", type=int, default=131072, help="hot rows per table cached in HBM (--offload)")
+    ap.add_argument("--cal-batches", type=int, default=32, help="calibration batches that pick the hot rows")
+    ap.add_argument("--prefetch-wgs", type=int, default=8,
+                    help="workgroups of the capped prefetch gather (--offload)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB 5 times (counter calibration)")
     return ap.parse_args()
@@ -161,6 +168,9 @@ def main():
     wl = W.workload(args.workload)
     if args.backward:
         backward_bench(args, wl)
+        return
+    if args.offload:
+        offload_bench(args, wl)
         return
     n_tok = wl.n_tokens
     R = max(1, args.rotate)
@@ -518,6 +528,205 @@ def backward_bench(args, wl):
         "kinds": per_kind,
         "us_per_call": {k: round(v, 2) for k, v in per_call.items()},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def offload_bench(args, wl):
+    """Retrieval with the tables in pinned host memory (the GPU reads the rows
+    over the host link), without and with the hot rows cached in HBM, next to
+    the same gather from HBM-resident tables; then the cached host gather of
+    the next batch on a second stream while a stand-in for the backbone's
+    earlier layers (bf16 matrix products) runs on the first."""
+    import numpy as np
+    import torch
+
+    from hashed_gram_embedding_vocab_amd import binding as B
+    from synthetic import workloads as W
+    from synthetic.device import make_device_layer, to_device
+
+    if wl.decode:
+        print("--offload measures whole prefill batches", file=sys.stderr)
+        sys.exit(2)
+    n_tok = wl.n_tokens
+    R = max(1, args.rotate)
+    dl_dev = make_device_layer(wl)
+    dl_host = make_device_layer(wl, host_tables=True)
+    plan = dl_dev.plan
+    tdt = dl_dev.h.dtype
+    # every batch draws from one rank->token permutation: the same tokens
+    # (hence n-grams, hence rows) are frequent in all of them
+    perm_seed = wl.seed(2) + 1
+    idx = []
+    for r in range(R):
+        toks = to_device(W.make_tokens(wl, seed=wl.seed(2) + 17 * r, perm_seed=perm_seed), torch.int32, "cuda")
+        x = torch.empty((n_tok, wl.n_tables), dtype=torch.int32, device="cuda")
+        plan.engram_hash(toks, dl_dev.comp_map, x)
+        idx.append(x)
+    # hot rows: the most frequent slots of separate calibration traffic
+    # (args.cal_batches batches, none of them a measured one)
+    cal_h = []
+    for c in range(args.cal_batches):
+        cal_t = to_device(W.make_tokens(wl, seed=wl.seed(2) + 1000 + 17 * c, perm_seed=perm_seed), torch.int32,
+                          "cuda")
+        cal = torch.empty((n_tok, wl.n_tables), dtype=torch.int32, device="cuda")
+        plan.engram_hash(cal_t, dl_dev.comp_map, cal)
+        cal_h.append(cal.cpu().numpy().view(np.uint32))
+    cal_h = np.concatenate(cal_h)
+    n_hot = args.cache_rows
+    hot = np.zeros((wl.n_tables, n_hot), np.uint32)
+    for tau in range(wl.n_tables):
+        u, c = np.unique(cal_h[:, tau], return_counts=True)
+        top = u[np.argsort(-c, kind="stable")][:n_hot]
+        hot[tau, :len(top)] = top
+        hot[tau, len(top):] = 0xFFFFFFFF  # past every table: skipped
+    cap = 1
+    while cap < 2 * n_hot:
+        cap *= 2
+    cache = B.RowCache(wl.n_tables, cap, wl.head_dim, tdt)
+    plan.engram_cache_build(to_device(hot.view(np.int32), torch.int32, "cuda"), dl_host.tables, cache)
+    # hit rate of the measured batches (host side, from the indices)
+    hits = 0
+    for r in range(R):
+        ih = idx[r].cpu().numpy().view(np.uint32)
+        hits += sum(int(np.isin(ih[:, tau], hot[tau]).sum()) for tau in range(wl.n_tables))
+    hit_rate = hits / (R * n_tok * wl.n_tables)
+    emb = [torch.empty((n_tok, wl.emb_dim), dtype=tdt, device="cuda") for _ in range(2)]
+    torch.cuda.synchronize()
+
+    def time_gather(fn, steps):
+        for i in range(3):
+            fn(i, emb[0], None)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            fn(i, emb[i & 1], None)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps  # ms per gather
+
+    g_dev = lambda i, e, s: plan.engram_gather(idx[i % R], dl_dev.tables, e, stream=s)
+    g_host = lambda i, e, s: plan.engram_gather(idx[i % R], dl_host.tables, e, stream=s)
+    g_cached = lambda i, e, s, wg=0: plan.engram_gather_cached(idx[i % R], dl_host.tables, cache, e,
+                                                               max_workgroups=wg, stream=s)
+    steps = max(4, args.steps // 5)
+    ms_dev = time_gather(g_dev, steps)
+    ms_host = time_gather(g_host, steps)
+    ms_cached = time_gather(g_cached, steps)
+    row_b = wl.head_dim * (2 if wl.dtype == "bf16" else 4)
+    link_bytes = n_tok * wl.n_tables * row_b  # every row over the link
+    # whole forward with host tables (retrieval inside engram_forward reads them)
+    out = torch.empty_like(dl_host.h)
+    ws = plan.workspace(wl.batch, wl.seqlen)
+    toks0 = to_device(W.make_tokens(wl, seed=wl.seed(2)), torch.int32, "cuda")
+    fwd = lambda dl: dl.plan.engram_forward(toks0, dl.comp_map, dl.tables, dl.h, dl.weights, out, ws)
+
+    def time_fwd(dl, k=10):
+        for _ in range(3):
+            fwd(dl)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(k):
+            fwd(dl)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / k
+
+    fwd_dev_ms, fwd_host_ms = time_fwd(dl_dev), time_fwd(dl_host)
+
+    # overlap: cached host gathers of later batches on a second stream under
+    # a stand-in for the backbone's earlier layers: bf16 products of
+    # 16384 x 4096 by 4096 x 16384 (4096 tiles of 256 x 256, sixteen rounds
+    # on 256 CUs, so a few CUs taken by the prefetch cost a few percent, not
+    # a whole round), as many as take about twice the prefetch alone.  First
+    # one workgroup per token group, then capped at args.prefetch_wgs
+    # workgroups that keep their CU slots for the whole gather.
+    Mb, Kb = 16384, 4096
+    x = torch.randn((Mb, Kb), device="cuda").to(torch.bfloat16)
+    y = torch.randn((Kb, Mb), device="cuda").to(torch.bfloat16)
+    z = torch.empty((Mb, Mb), device="cuda", dtype=torch.bfloat16)
+    n_g = 4
+
+    def wall(fns):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for f in fns:
+            f()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3
+
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def backbone_of(n_mm):
+        def backbone():
+            with torch.cuda.stream(sa):
+                for _ in range(n_mm):
+                    torch.mm(x, y, out=z)
+        return backbone
+
+    def prefetch_of(wg):
+        def prefetch():
+            for i in range(n_g):
+                g_cached(i, emb[i & 1], sb, wg)
+        return prefetch
+
+    one = backbone_of(1)
+    for _ in range(2):
+        wall([one])
+    mm_ms = min(wall([one]) for _ in range(3))
+    pf0 = prefetch_of(0)
+    wall([pf0])
+    pf_est = min(wall([pf0]) for _ in range(2))
+    n_mm = max(2, int(np.ceil(2.0 * pf_est / mm_ms)))
+    backbone = backbone_of(n_mm)
+
+    def overlap(wg):
+        # the prefetch is issued first: a step's indices are known before its
+        # layers run, so its gathers are queued ahead of them
+        prefetch = prefetch_of(wg)
+        for _ in range(2):
+            wall([prefetch, backbone])
+        bb = min(wall([backbone]) for _ in range(3))
+        pf = min(wall([prefetch]) for _ in range(3))
+        both = min(wall([prefetch, backbone]) for _ in range(3))
+        return bb, pf, both
+
+    bb_full, pf_full, both_full = overlap(0)
+    bb_cap, pf_cap, both_cap = overlap(args.prefetch_wgs)
+    mm_flops = 2.0 * Mb * Mb * Kb * n_mm
+    line = {
+        "metric": "Engram host-table gather tokens/sec",
+        "value": round(n_tok / (ms_cached * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": 3,
+        "ms_per_step": round(ms_cached, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic: Zipf(%s) token ids, seeded Philox tables in pinned host memory" % wl.zipf_s,
+        "config": {"workload": wl.name, "tokens_per_step": n_tok, "n_tables": wl.n_tables, "head_dim": wl.head_dim,
+                   "table_bytes": sum(wl.primes()) * row_b, "cache_rows_per_table": n_hot,
+                   "cache_slots_per_table": cap, "cache_bytes": wl.n_tables * cap * (row_b + 4),
+                   "rotated_batches": R, "parallelism": "single GPU"},
+        "gather_ms": {"hbm_tables": round(ms_dev, 4), "host_tables": round(ms_host, 4),
+                      "host_tables_cached": round(ms_cached, 4)},
+        "host_link_GBs_uncached": round(link_bytes / (ms_host * 1e-3) / 1e9, 2),
+        "host_link_GBs_cached": round(link_bytes * (1 - hit_rate) / (ms_cached * 1e-3) / 1e9, 2),
+        "cache_hit_rate": round(hit_rate, 4),
+        "forward_ms": {"hbm_tables": round(fwd_dev_ms, 4), "host_tables": round(fwd_host_ms, 4)},
+        # overhead_frac: extra time of backbone + prefetch over the backbone
+        # alone on the whole chip
+        "overlap": {"backbone_matmuls": "%d x bf16 %dx%d by %dx%d" % (n_mm, Mb, Kb, Kb, Mb), "prefetch_gathers": n_g,
+                    "uncapped": {"backbone_ms": round(bb_full, 3),
+                                 "backbone_TFLOPs": round(mm_flops / (bb_full * 1e-3) / 1e12, 1),
+                                 "prefetch_ms": round(pf_full, 3), "together_ms": round(both_full, 3),
+                                 "overhead_frac": round((both_full - bb_full) / bb_full, 4)},
+                    "capped": {"prefetch_workgroups": args.prefetch_wgs, "backbone_ms": round(bb_cap, 3),
+                               "prefetch_ms": round(pf_cap, 3), "together_ms": round(both_cap, 3),
+                               "overhead_frac": round((both_cap - bb_cap) / bb_cap, 4)}},
     }
     print(json.dumps(line), flush=True)
 

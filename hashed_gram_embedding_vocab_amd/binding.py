@@ -10,9 +10,11 @@ fallback.
 
 from __future__ import annotations
 
+import atexit
 import ctypes as C
 import os
 import threading
+import weakref
 from typing import Dict, Optional, Sequence
 
 import torch
@@ -65,6 +67,10 @@ class GradsC(C.Structure):
     ]
 
 
+class RowCacheC(C.Structure):
+    _fields_ = [("keys", C.c_void_p), ("rows", C.c_void_p), ("capacity", C.c_uint32)]
+
+
 _lib = None
 _lock = threading.Lock()
 
@@ -107,6 +113,14 @@ def lib() -> C.CDLL:
         L.engram_profile_begin.argtypes = [P, i32, u32]
         L.engram_profile_end.restype = C.c_int
         L.engram_profile_end.argtypes = [P, C.POINTER(ProfileC)]
+        L.engram_host_alloc.restype = C.c_int
+        L.engram_host_alloc.argtypes = [C.c_size_t, C.POINTER(C.c_void_p)]
+        L.engram_host_free.restype = C.c_int
+        L.engram_host_free.argtypes = [P]
+        L.engram_cache_build.restype = C.c_int
+        L.engram_cache_build.argtypes = [P, P, i32, P, C.POINTER(RowCacheC), P]
+        L.engram_gather_cached.restype = C.c_int
+        L.engram_gather_cached.argtypes = [P, P, i64, P, C.POINTER(RowCacheC), P, i32, P]
         L.engram_synth_fill_table.restype = C.c_int
         L.engram_synth_fill_table.argtypes = [i32, u64, i32, i64, i32, P, P]
         _lib = L
@@ -128,6 +142,60 @@ def _ptr(t: Optional[torch.Tensor], name: str, dtype=None):
     if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
         raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
     return C.c_void_p(t.data_ptr())
+
+
+_live_host_buffers = weakref.WeakSet()
+
+
+class HostBuffer:
+    """Pinned host memory from engram_host_alloc that the GPU reads directly
+    (tables kept in host DRAM).  `tensor` is a CPU view of it; the memory is
+    released by free(), when the object is collected, or at interpreter exit
+    (before the HIP runtime shuts down); no kernel may still read it then."""
+
+    def __init__(self, nbytes: int):
+        p = C.c_void_p()
+        _check("engram_host_alloc", lib().engram_host_alloc(nbytes, C.byref(p)))
+        self.ptr = p.value
+        self.nbytes = nbytes
+        self.tensor = torch.frombuffer((C.c_uint8 * nbytes).from_address(self.ptr), dtype=torch.uint8)
+        _live_host_buffers.add(self)
+
+    def view(self, dtype, shape):
+        return self.tensor.view(dtype).view(shape)
+
+    def free(self):
+        if getattr(self, "ptr", None):
+            self.tensor = None
+            lib().engram_host_free(C.c_void_p(self.ptr))
+            self.ptr = None
+
+    def __del__(self):
+        self.free()
+
+
+@atexit.register
+def _free_host_buffers():
+    for hb in list(_live_host_buffers):
+        hb.free()
+
+
+def _table_ptr(t) -> int:
+    """Device address of a table: a HIP tensor, or a HostBuffer's memory."""
+    if isinstance(t, HostBuffer):
+        return t.ptr
+    return _ptr(t, "table").value
+
+
+class RowCache:
+    """Device buffers of a hot-row cache: keys [n_tables][capacity] uint32 and
+    rows [n_tables][capacity][d_e]."""
+
+    def __init__(self, n_tables: int, capacity: int, head_dim: int, dtype, device="cuda"):
+        self.capacity = capacity
+        self.keys = torch.zeros((n_tables, max(capacity, 1)), dtype=torch.int32, device=device)
+        self.rows = torch.zeros((n_tables, max(capacity, 1), head_dim), dtype=dtype, device=device)
+        self.c = RowCacheC(C.c_void_p(self.keys.data_ptr()), C.c_void_p(self.rows.data_ptr()), capacity)
 
 
 def _stream(stream) -> C.c_void_p:
@@ -225,10 +293,27 @@ class Plan:
 
     def engram_gather(self, idx, tables: Sequence[torch.Tensor], emb, stream=None):
         n_tok = idx.shape[0]
-        ptrs = (C.c_void_p * len(tables))(*[_ptr(t, "table").value for t in tables])
+        ptrs = (C.c_void_p * len(tables))(*[_table_ptr(t) for t in tables])
         _check("engram_gather", lib().engram_gather(
             self._h, _ptr(idx, "idx", (torch.int32, torch.uint32)), n_tok, ptrs,
             _ptr(emb, "emb", self.torch_dtype), _stream(stream)))
+
+    def engram_cache_build(self, hot, tables, cache: RowCache, stream=None):
+        """hot: [n_tables][n_hot] int32 device tensor of row numbers."""
+        ptrs = (C.c_void_p * len(tables))(*[_table_ptr(t) for t in tables])
+        n_hot = 0 if hot is None else hot.shape[1]
+        _check("engram_cache_build", lib().engram_cache_build(
+            self._h, _ptr(hot, "hot", (torch.int32, torch.uint32)), n_hot, ptrs, C.byref(cache.c),
+            _stream(stream)))
+
+    def engram_gather_cached(self, idx, tables, cache: Optional[RowCache], emb, max_workgroups: int = 0,
+                             stream=None):
+        n_tok = idx.shape[0]
+        ptrs = (C.c_void_p * len(tables))(*[_table_ptr(t) for t in tables])
+        _check("engram_gather_cached", lib().engram_gather_cached(
+            self._h, _ptr(idx, "idx", (torch.int32, torch.uint32)), n_tok, ptrs,
+            None if cache is None else C.byref(cache.c), _ptr(emb, "emb", self.torch_dtype), max_workgroups,
+            _stream(stream)))
 
     def engram_gate_fuse(self, emb, h, weights: Weights, out, workspace, batch: int, seqlen: int,
                          conv_state=None, alpha=None, flags: int = 0, stream=None):
@@ -243,7 +328,7 @@ class Plan:
                        out, workspace, prev_ctx=None, conv_state=None, alpha=None, flags: int = 0,
                        bad_tokens=None, stream=None):
         batch, seqlen = tokens.shape
-        ptrs = (C.c_void_p * len(tables))(*[_ptr(t, "table").value for t in tables])
+        ptrs = (C.c_void_p * len(tables))(*[_table_ptr(t) for t in tables])
         _check("engram_forward", lib().engram_forward(
             self._h, _ptr(tokens, "tokens", torch.int32), batch, seqlen,
             _ptr(comp_map, "comp_map", torch.int32), _ptr(prev_ctx, "prev_ctx", torch.int32), ptrs,
@@ -258,7 +343,7 @@ class Plan:
 
     def engram_backward(self, idx, tables: Sequence[torch.Tensor], h, weights: "Weights", dout, dh,
                         grads: "Grads", workspace, batch: int, seqlen: int, flags: int = 0, stream=None):
-        ptrs = (C.c_void_p * len(tables))(*[_ptr(t, "table").value for t in tables])
+        ptrs = (C.c_void_p * len(tables))(*[_table_ptr(t) for t in tables])
         _check("engram_backward", lib().engram_backward(
             self._h, _ptr(idx, "idx", (torch.int32, torch.uint32)), ptrs, _ptr(h, "h", self.torch_dtype),
             C.byref(weights.c), _ptr(dout, "dout", self.torch_dtype), batch, seqlen, flags,

@@ -455,6 +455,68 @@ engram_status engram_gather(engram_plan p, const uint32_t *d_idx, int64_t n_toke
     return do_gather(*p, d_idx, n_tokens, table_ptrs, d_emb, stream);
 }
 
+// ---------------------------------------------------------------- host-resident tables
+
+engram_status engram_host_alloc(size_t bytes, void **ptr) {
+    if (!ptr) return ENGRAM_E_INVALID_ARG;
+    *ptr = nullptr;
+    if (bytes == 0) return ENGRAM_E_INVALID_ARG;
+    // mapped into every device's address space; non-coherent, so the GPU may
+    // keep what it reads in its caches (the tables are read-only while used)
+    if (hipHostMalloc(ptr, bytes, hipHostMallocMapped | hipHostMallocNonCoherent) != hipSuccess) {
+        (void)hipGetLastError();
+        *ptr = nullptr;
+        return ENGRAM_E_NOMEM;
+    }
+    return ENGRAM_OK;
+}
+
+engram_status engram_host_free(void *ptr) {
+    if (!ptr) return ENGRAM_OK;
+    return hipHostFree(ptr) == hipSuccess ? ENGRAM_OK : ENGRAM_E_DEVICE;
+}
+
+namespace {
+constexpr uint32_t kMaxCacheSlots = 1u << 28;
+
+bool valid_cache(const engram_row_cache *c) {
+    if (!c || c->capacity == 0) return true;
+    return c->keys && c->rows && aligned16(c->keys) && aligned16(c->rows) && c->capacity <= kMaxCacheSlots &&
+           (c->capacity & (c->capacity - 1u)) == 0;
+}
+}  // namespace
+
+engram_status engram_cache_build(engram_plan p, const uint32_t *d_hot, int32_t n_hot, const void *const *table_ptrs,
+                                 const engram_row_cache *cache, hipStream_t stream) {
+    if (!p || !table_ptrs || !cache || cache->capacity == 0 || !valid_cache(cache)) return ENGRAM_E_INVALID_ARG;
+    if (n_hot < 0 || (n_hot > 0 && !d_hot) || 2 * (int64_t)n_hot > (int64_t)cache->capacity)
+        return ENGRAM_E_INVALID_ARG;
+    for (int t = 0; t < p->n_tables; ++t)
+        if (!table_ptrs[t] || !aligned16(table_ptrs[t])) return ENGRAM_E_INVALID_ARG;
+    const GatherConsts gc = gather_consts(*p, table_ptrs);
+    {
+        Launch l(*p, ENGRAM_K_GATHER, stream);
+        launch_cache_build(gc, cache->capacity, d_hot, n_hot, cache->keys, cache->rows, stream);
+    }
+    return last_launch_status();
+}
+
+engram_status engram_gather_cached(engram_plan p, const uint32_t *d_idx, int64_t n_tokens,
+                                   const void *const *table_ptrs, const engram_row_cache *cache, void *d_emb,
+                                   int32_t max_workgroups, hipStream_t stream) {
+    engram_status st = check_gather_args(p, d_idx, n_tokens, table_ptrs, d_emb);
+    if (st != ENGRAM_OK) return st;
+    if (!valid_cache(cache) || max_workgroups < 0) return ENGRAM_E_INVALID_ARG;
+    const GatherConsts gc = gather_consts(*p, table_ptrs);
+    const uint32_t capacity = cache ? cache->capacity : 0u;
+    {
+        Launch l(*p, ENGRAM_K_GATHER, stream);
+        launch_cached_gather(gc, capacity, d_idx, n_tokens, capacity ? cache->keys : nullptr,
+                             capacity ? cache->rows : nullptr, d_emb, max_workgroups, stream);
+    }
+    return last_launch_status();
+}
+
 engram_status engram_gate_fuse(engram_plan p, const void *d_emb, const void *d_h, int32_t batch,
                                int32_t seqlen, const engram_weights *w, float *d_conv_state,
                                void *d_out, float *d_alpha, uint32_t flags, void *d_workspace,

@@ -113,6 +113,16 @@ struct GatherConsts {
 
 void launch_gather(const GatherConsts &gc, const uint32_t *idx, int64_t n_tok, void *emb,
                    hipStream_t s);
+// Tables in host memory with a hot-row cache in HBM: the cache of table tau
+// is capacity slots of keys (row + 1, 0 = free; open addressing, linear
+// probing) and rows [capacity][d_e].  capacity 0: no cache.
+void launch_cache_build(const GatherConsts &gc, uint32_t capacity, const uint32_t *hot, int32_t n_hot,
+                        uint32_t *keys, void *rows, hipStream_t s);
+// max_workgroups > 0 caps the launch; each workgroup then loops over its
+// share of the token groups
+void launch_cached_gather(const GatherConsts &gc, uint32_t capacity, const uint32_t *idx, int64_t n_tok,
+                          const uint32_t *keys, const void *rows, void *emb, int32_t max_workgroups,
+                          hipStream_t s);
 // Retrieval in one pass (engram_forward): every lane hashes the n-gram of its
 // own (token, table) pair and copies its 16-byte chunk of that row.
 void launch_hash_gather(const HashConsts &hc, const GatherConsts &gc, const int32_t *tokens,

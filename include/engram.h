@@ -171,6 +171,60 @@ ENGRAM_API engram_status engram_gather(engram_plan p, const uint32_t *d_idx, int
                             const void *const *table_ptrs, void *d_emb, hipStream_t stream);
 
 /*
+ * Tables in host memory ([rep] 工程实现与硬件效率: the pages' deployment keeps
+ * the tables in host DRAM and fetches a step's rows over the host link ahead
+ * of the layer, since the indices depend only on the tokens; [rep] 技术方案:
+ * a multi-level cache, because n-gram accesses are Zipfian).
+ *
+ * engram_host_alloc returns `bytes` of pinned host memory that every GPU can
+ * read directly (mapped, and cacheable by the GPU: contents must not change
+ * while kernels read them).  Tables placed there are passed to engram_gather,
+ * engram_gather_cached or engram_forward like device tables; each row read
+ * then crosses the host link.  *ptr is set to NULL and ENGRAM_E_NOMEM returned
+ * when the allocation fails.  engram_host_free releases such memory (NULL is
+ * accepted); the caller makes sure no kernel still reads it.
+ */
+ENGRAM_API engram_status engram_host_alloc(size_t bytes, void **ptr);
+ENGRAM_API engram_status engram_host_free(void *ptr);
+
+/* A per-table cache of hot rows in device memory: open addressing over
+ * `capacity` slots per table (linear probing from a multiplicative hash of
+ * the row number).  All pointers are caller-owned device memory. */
+typedef struct {
+    uint32_t *keys;     /* [n_tables][capacity]: row + 1 of the row in each slot, 0 = free */
+    void *rows;         /* [n_tables][capacity][d_e] plan dtype: copies of those rows      */
+    uint32_t capacity;  /* slots per table, a power of two; 0 = no cache                   */
+} engram_row_cache;
+
+/*
+ * Fill `cache` with rows d_hot[tau][0..n_hot) of every table tau, copied from
+ * table_ptrs (host or device tables).  Entries >= table_rows[tau] are
+ * skipped, repeated entries stored once.  Requires 2 * n_hot <= capacity (the
+ * load factor stays at most 1/2, so every lookup ends within a few probes),
+ * 16-byte aligned keys and rows.  Which rows are hot is the caller's choice
+ * (e.g. the most frequent slots of a sample of traffic).  Slot placement may
+ * differ between builds; what a lookup returns does not.
+ */
+ENGRAM_API engram_status engram_cache_build(engram_plan p, const uint32_t *d_hot, int32_t n_hot,
+                                            const void *const *table_ptrs, const engram_row_cache *cache,
+                                            hipStream_t stream);
+
+/*
+ * engram_gather with the rows found in `cache` read from it instead of the
+ * tables (NULL cache or capacity 0: every row from the tables).  The result
+ * is bit-identical to engram_gather on the same tables, provided the cache
+ * was built from them.  max_workgroups > 0 caps the launch at that many
+ * workgroups, each looping over its share of the tokens: a prefetch issued
+ * on its own stream beside a model's other kernels then keeps the CU slots
+ * it holds from start to end, instead of queueing one short workgroup per
+ * 1024/n_tables tokens behind them (the host link needs few CUs to stay busy).
+ * 0: one workgroup per 1024/n_tables tokens.  Other arguments as engram_gather.
+ */
+ENGRAM_API engram_status engram_gather_cached(engram_plan p, const uint32_t *d_idx, int64_t n_tokens,
+                                              const void *const *table_ptrs, const engram_row_cache *cache,
+                                              void *d_emb, int32_t max_workgroups, hipStream_t stream);
+
+/*
  * Fusion ([club] 1.(2); [csdn] third and fourth steps), per branch m and token t:
  *   k = W_k^(m) e_t, v = W_v e_t                      (fp32 accumulation)
  *   alpha = sigmoid( <RMSNorm_{gamma_h}(h_t), RMSNorm_{gamma_k}(k)> / sqrt(d) )

@@ -39,7 +39,10 @@ def to_device(x: np.ndarray, dtype: torch.dtype, device) -> torch.Tensor:
 
 def make_device_layer(wl: W.Workload, layer_slot: int = 0, device="cuda", batch: Optional[int] = None,
                       seqlen: Optional[int] = None, with_tables: bool = True,
-                      conv_mode: int = 0, rms_eps: float = 1e-6) -> DeviceLayer:
+                      conv_mode: int = 0, rms_eps: float = 1e-6, host_tables: bool = False) -> DeviceLayer:
+    """host_tables: the tables go to pinned host memory (HostBuffer objects,
+    read by the GPU over the host link), generated on the device one at a time
+    and copied there."""
     from hashed_gram_embedding_vocab_amd import binding as B
 
     li = W.make_layer_inputs(wl, layer_slot, batch=batch, seqlen=seqlen)
@@ -55,7 +58,13 @@ def make_device_layer(wl: W.Workload, layer_slot: int = 0, device="cuda", batch:
         for tau, p in enumerate(primes):
             t = torch.empty((p, wl.head_dim), dtype=tdt, device=device)
             B.engram_synth_fill_table(t, li.table_seed, tau, dt)
-            tables.append(t)
+            if host_tables:
+                hb = B.HostBuffer(t.numel() * t.element_size())
+                hb.view(tdt, t.shape).copy_(t.cpu())
+                del t
+                tables.append(hb)
+            else:
+                tables.append(t)
     h = to_device(li.h, tdt, device)
     weights = B.Weights(
         w_k=[to_device(li.w_k[m], tdt, device) for m in range(wl.n_branches)],

@@ -201,8 +201,11 @@ def _zipf_ranks(n: int, vocab: int, s: float, rng: np.random.Generator) -> np.nd
 
 
 def make_tokens(wl: Workload, seed: Optional[int] = None, batch: Optional[int] = None,
-                seqlen: Optional[int] = None, zipf_s: Optional[float] = "default") -> np.ndarray:
-    """Raw token ids [batch][seqlen] int32: Zipf over a seeded rank->id permutation."""
+                seqlen: Optional[int] = None, zipf_s: Optional[float] = "default",
+                perm_seed: Optional[int] = None) -> np.ndarray:
+    """Raw token ids [batch][seqlen] int32: Zipf over a seeded rank->id
+    permutation (seed + 1 unless perm_seed is given: batches that share a
+    perm_seed share which tokens are frequent, as text of one language does)."""
     seed = wl.seed(2) if seed is None else seed
     batch = wl.batch if batch is None else batch
     seqlen = wl.seqlen if seqlen is None else seqlen
@@ -212,7 +215,7 @@ def make_tokens(wl: Workload, seed: Optional[int] = None, batch: Optional[int] =
     if s is None:
         ids = rng.integers(0, wl.vocab, n)
     else:
-        perm = np.random.default_rng(seed + 1).permutation(wl.vocab)
+        perm = np.random.default_rng(seed + 1 if perm_seed is None else perm_seed).permutation(wl.vocab)
         ids = perm[_zipf_ranks(n, wl.vocab, s, rng)]
     return ids.astype(np.int32).reshape(batch, seqlen)
 

@@ -193,3 +193,34 @@ def test_backward_argument_checks(B):
     tabs_bad = (C.c_void_p * 4)(*([0x10000] * 3 + [0]))
     a = list(args); a[2] = tabs_bad
     assert L.engram_backward(*a) == B.E_INVALID_ARG
+
+
+def test_row_cache_argument_checks(B):
+    """engram_cache_build / engram_gather_cached reject bad caches before any launch."""
+    _no_gpu()
+    L = B.lib()
+    fake = C.c_void_p(0x10000)
+    tabs = (C.c_void_p * 4)(*([0x10000] * 4))
+    p = B.Plan(vocab=1000, vocab_comp=770, heads=2, head_dim=32, table_rows=[10007] * 4, hash_seed=1,
+               d_model=256, dtype=B.BF16)
+    for keys, rows, cap, n_hot in [(0x10000, 0x20000, 0, 1),       # no slots
+                                   (0x10000, 0x20000, 6, 1),       # not a power of two
+                                   (0x10000, 0x20000, 4, 3),       # load factor above 1/2
+                                   (0x10004, 0x20000, 8, 1),       # keys misaligned
+                                   (0x10000, None, 8, 1),          # no rows
+                                   (0x10000, 0x20000, 1 << 29, 1)]:  # too many slots
+        c = B.RowCacheC(keys, rows, cap)
+        assert L.engram_cache_build(p._h, fake, n_hot, tabs, C.byref(c), None) == B.E_INVALID_ARG, (keys, rows, cap)
+    c = B.RowCacheC(0x10000, 0x20000, 8)
+    assert L.engram_cache_build(p._h, None, 1, tabs, C.byref(c), None) == B.E_INVALID_ARG  # no hot rows
+    assert L.engram_cache_build(p._h, fake, -1, tabs, C.byref(c), None) == B.E_INVALID_ARG
+    assert L.engram_cache_build(p._h, fake, 1, tabs, None, None) == B.E_INVALID_ARG
+    bad_tabs = (C.c_void_p * 4)(*([0x10000] * 3 + [0x10008]))
+    assert L.engram_cache_build(p._h, fake, 1, bad_tabs, C.byref(c), None) == B.E_INVALID_ARG
+    bad = B.RowCacheC(0x10000, 0x20000, 6)
+    assert L.engram_gather_cached(p._h, fake, 10, tabs, C.byref(bad), fake, 0, None) == B.E_INVALID_ARG
+    assert L.engram_gather_cached(p._h, None, 10, tabs, C.byref(c), fake, 0, None) == B.E_INVALID_ARG
+    assert L.engram_gather_cached(p._h, fake, 0, tabs, C.byref(c), fake, 0, None) == B.E_INVALID_ARG
+    assert L.engram_gather_cached(p._h, fake, 10, tabs, C.byref(c), fake, -1, None) == B.E_INVALID_ARG
+    assert L.engram_host_alloc(1, None) == B.E_INVALID_ARG
+    assert L.engram_host_free(None) == B.OK
