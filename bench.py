@@ -59,6 +59,7 @@ def parse():
                          "and its overlap with device compute: one JSON line of its own")
     ap.add_argument("--cache-rows", type=int, default=131072, help="hot rows per table cached in HBM (--offload)")
     ap.add_argument("--cal-batches", type=int, default=32, help="calibration batches that pick the hot rows")
+    ap.add_argument("--host-threads", type=int, default=16, help="host threads of the prefetcher (--offload)")
     ap.add_argument("--prefetch-wgs", type=int, default=8,
                     help="workgroups of the capped prefetch gather (--offload)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -694,6 +695,45 @@ def offload_bench(args, wl):
     bb_full, pf_full, both_full = overlap(0)
     bb_cap, pf_cap, both_cap = overlap(args.prefetch_wgs)
     mm_flops = 2.0 * Mb * Mb * Kb * n_mm
+
+    # host-gather prefetcher: host threads copy the missed rows, a DMA
+    # engine stages them, one assembly kernel builds E; begin before the
+    # backbone, finish after it
+    pfr = B.Prefetcher(plan, dl_host.tables, cache, max_tokens=n_tok, n_threads=args.host_threads)
+
+    def host_job(i):
+        pfr.begin(idx[i % R], stream=sb)
+        return pfr.finish(emb[i & 1], stream=sb)
+
+    for i in range(3):
+        host_job(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    misses = 0
+    for i in range(n_g):
+        misses += host_job(i)
+    torch.cuda.synchronize()
+    hg_ms = (time.perf_counter() - t0) * 1e3 / n_g
+
+    # each job under its share of the backbone: begin, that many products
+    # on the other stream, finish (the pipeline of one layer per job)
+    slice_fn = backbone_of(max(1, n_mm // n_g))
+
+    def host_overlap():
+        for i in range(n_g):
+            pfr.begin(idx[i % R], stream=sb)
+            slice_fn()
+            pfr.finish(emb[i & 1], stream=sb)
+
+    def slices():
+        for _ in range(n_g):
+            slice_fn()
+
+    for _ in range(2):
+        wall([host_overlap])
+    both_host = min(wall([host_overlap]) for _ in range(3))
+    bb_host = min(wall([slices]) for _ in range(3))
+    pfr.close()
     line = {
         "metric": "Engram host-table gather tokens/sec",
         "value": round(n_tok / (ms_cached * 1e-3), 1),
@@ -726,7 +766,14 @@ def offload_bench(args, wl):
                                  "overhead_frac": round((both_full - bb_full) / bb_full, 4)},
                     "capped": {"prefetch_workgroups": args.prefetch_wgs, "backbone_ms": round(bb_cap, 3),
                                "prefetch_ms": round(pf_cap, 3), "together_ms": round(both_cap, 3),
-                               "overhead_frac": round((both_cap - bb_cap) / bb_cap, 4)}},
+                               "overhead_frac": round((both_cap - bb_cap) / bb_cap, 4)},
+                    # n_g jobs, each begun before its share of the backbone and finished after it
+                    "host_gather": {"backbone_matmuls": "%d x %d" % (n_g, max(1, n_mm // n_g)),
+                                    "host_threads": args.host_threads, "backbone_ms": round(bb_host, 3),
+                                    "prefetch_ms": round(hg_ms * n_g, 3), "together_ms": round(both_host, 3),
+                                    "overhead_frac": round((both_host - bb_host) / bb_host, 4)}},
+        "host_gather_ms": round(hg_ms, 4),
+        "host_gather_miss_frac": round(misses / (n_g * n_tok * wl.n_tables), 4),
     }
     print(json.dumps(line), flush=True)
 

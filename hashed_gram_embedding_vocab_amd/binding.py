@@ -117,6 +117,14 @@ def lib() -> C.CDLL:
         L.engram_host_alloc.argtypes = [C.c_size_t, C.POINTER(C.c_void_p)]
         L.engram_host_free.restype = C.c_int
         L.engram_host_free.argtypes = [P]
+        L.engram_prefetcher_create.restype = C.c_int
+        L.engram_prefetcher_create.argtypes = [P, P, C.POINTER(RowCacheC), i64, i32, C.POINTER(C.c_void_p)]
+        L.engram_prefetcher_destroy.restype = C.c_int
+        L.engram_prefetcher_destroy.argtypes = [P]
+        L.engram_prefetch_begin.restype = C.c_int
+        L.engram_prefetch_begin.argtypes = [P, P, i64, P]
+        L.engram_prefetch_finish.restype = C.c_int
+        L.engram_prefetch_finish.argtypes = [P, P, C.POINTER(C.c_uint32), P]
         L.engram_cache_build.restype = C.c_int
         L.engram_cache_build.argtypes = [P, P, i32, P, C.POINTER(RowCacheC), P]
         L.engram_gather_cached.restype = C.c_int
@@ -185,6 +193,49 @@ def _table_ptr(t) -> int:
     if isinstance(t, HostBuffer):
         return t.ptr
     return _ptr(t, "table").value
+
+
+def _host_table_ptr(t) -> int:
+    """Host address of a table the host threads read: a HostBuffer or a
+    contiguous CPU tensor."""
+    if isinstance(t, HostBuffer):
+        return t.ptr
+    if not isinstance(t, torch.Tensor) or t.is_cuda or not t.is_contiguous():
+        raise TypeError("host tables must be HostBuffer objects or contiguous CPU tensors")
+    return t.data_ptr()
+
+
+class Prefetcher:
+    """engram_prefetcher_*: host threads gather the rows that miss the HBM
+    cache from host tables; a DMA engine copies them to the GPU."""
+
+    def __init__(self, plan: "Plan", host_tables, cache: Optional["RowCache"], max_tokens: int, n_threads: int = 8):
+        self._tables = list(host_tables)  # kept alive while the prefetcher may read them
+        self._cache = cache
+        ptrs = (C.c_void_p * len(self._tables))(*[_host_table_ptr(t) for t in self._tables])
+        h = C.c_void_p()
+        _check("engram_prefetcher_create", lib().engram_prefetcher_create(
+            plan._h, ptrs, None if cache is None else C.byref(cache.c), max_tokens, n_threads, C.byref(h)))
+        self._h = h
+
+    def begin(self, idx, stream=None):
+        _check("engram_prefetch_begin", lib().engram_prefetch_begin(
+            self._h, _ptr(idx, "idx", (torch.int32, torch.uint32)), idx.shape[0], _stream(stream)))
+
+    def finish(self, emb, stream=None) -> int:
+        """Enqueue E's assembly; returns how many (token, table) pairs missed the cache."""
+        n = C.c_uint32(0)
+        _check("engram_prefetch_finish", lib().engram_prefetch_finish(
+            self._h, _ptr(emb, "emb"), C.byref(n), _stream(stream)))
+        return int(n.value)
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().engram_prefetcher_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
 
 
 class RowCache:

@@ -123,6 +123,10 @@ void launch_cache_build(const GatherConsts &gc, uint32_t capacity, const uint32_
 void launch_cached_gather(const GatherConsts &gc, uint32_t capacity, const uint32_t *idx, int64_t n_tok,
                           const uint32_t *keys, const void *rows, void *emb, int32_t max_workgroups,
                           hipStream_t s);
+// Host-gather prefetch: E assembled from cache rows and staged miss rows
+// (code[pair] = cache slot, or 0x80000000 | staged row).
+void launch_prefetch_assemble(const GatherConsts &gc, int64_t n_tok, const uint32_t *code, const void *cache_rows,
+                              const void *staged, void *emb, hipStream_t s);
 // Retrieval in one pass (engram_forward): every lane hashes the n-gram of its
 // own (token, table) pair and copies its 16-byte chunk of that row.
 void launch_hash_gather(const HashConsts &hc, const GatherConsts &gc, const int32_t *tokens,

@@ -137,6 +137,37 @@ __global__ __launch_bounds__(kThreads) void cached_gather_kernel(GatherConsts gc
     }
 }
 
+// Host-gather prefetch: the host threads looked every (token, table) pair up
+// in a copy of the cache keys; code[pair] is the cache slot of a hit, or
+// kMissBit | the staged row of a miss.
+constexpr uint32_t kMissBit = 0x80000000u;
+
+// E from the cache rows (hits) and the staged rows (misses), one
+// 16-byte chunk per thread, kUnroll in flight.
+__global__ __launch_bounds__(kThreads) void prefetch_assemble_kernel(GatherConsts gc, int64_t total_chunks,
+                                                                     const uint32_t *__restrict__ code,
+                                                                     const u32x4_t *__restrict__ cache_rows,
+                                                                     const u32x4_t *__restrict__ staged,
+                                                                     u32x4_t *__restrict__ emb) {
+    const int64_t base = (int64_t)blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
+    u32x4_t val[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const int64_t c = min(base + u * kThreads, total_chunks - 1);
+        const int64_t pr = c / gc.row_chunks;
+        const int ch = (int)(c - pr * gc.row_chunks);
+        const uint32_t k = code[pr];
+        const u32x4_t *src = (k & kMissBit) ? staged + (int64_t)(k & ~kMissBit) * gc.row_chunks
+                                            : cache_rows + (int64_t)k * gc.row_chunks;
+        val[u] = src[ch];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const int64_t c = base + u * kThreads;
+        if (c < total_chunks) emb[c] = val[u];
+    }
+}
+
 }  // namespace
 
 void launch_cache_build(const GatherConsts &gc, uint32_t capacity, const uint32_t *hot, int32_t n_hot,
@@ -164,4 +195,14 @@ void launch_cached_gather(const GatherConsts &gc, uint32_t capacity, const uint3
                   keys, reinterpret_cast<const u32x4_t *>(rows), reinterpret_cast<u32x4_t *>(emb));
 }
 
+void launch_prefetch_assemble(const GatherConsts &gc, int64_t n_tok, const uint32_t *code, const void *cache_rows,
+                              const void *staged, void *emb, hipStream_t s) {
+    const int64_t total = n_tok * gc.tok_chunks;
+    const int64_t per_block = (int64_t)kThreads * kUnroll;
+    launch_kernel(prefetch_assemble_kernel, dim3((unsigned)((total + per_block - 1) / per_block)), dim3(kThreads), s,
+                  gc, total, code, reinterpret_cast<const u32x4_t *>(cache_rows),
+                  reinterpret_cast<const u32x4_t *>(staged), reinterpret_cast<u32x4_t *>(emb));
+}
+
 }  // namespace engram
+

@@ -225,6 +225,51 @@ ENGRAM_API engram_status engram_gather_cached(engram_plan p, const uint32_t *d_i
                                               void *d_emb, int32_t max_workgroups, hipStream_t stream);
 
 /*
+ * Host-gather prefetch: the pages' deployment of host-resident tables ([rep]
+ * 工程实现与硬件效率: the rows of a step are fetched from host DRAM while
+ * earlier layers compute, since the indices depend only on the tokens).
+ * Host threads look every (token, table) pair up in the HBM cache's keys and
+ * copy the rows that miss into pinned staging; a DMA engine copies the
+ * indices in and the staged rows out.  Until E is assembled the prefetch
+ * queues no kernel, so it never waits for compute units behind the model's
+ * kernels.
+ *
+ * engram_prefetcher_create: host_tables are HOST pointers (any host memory:
+ * the host threads read them, the GPU never does), `cache` an optional
+ * hot-row cache built from the same tables and left unchanged while the
+ * prefetcher lives (its keys are copied to the host here; NULL: every row
+ * comes from the host).  The prefetcher owns n_threads host threads
+ * (1..256), a copy stream at the default priority, and staging for
+ * max_tokens tokens: 2 * max_tokens * n_tables * (4 + d_e * elem) bytes of
+ * device memory and max_tokens * n_tables * (8 + d_e * elem) bytes of pinned
+ * host memory.  Synchronous.
+ *
+ * engram_prefetch_begin: once the work queued so far on `stream` is done
+ * (so the indices may come from a kernel on it), d_idx [n_tok][n_tables]
+ * (n_tok <= max_tokens) is copied to the host and the host threads start.
+ * Returns at once.  d_idx must stay unchanged until finish returns.  One job
+ * at a time: a second begin before finish returns ENGRAM_E_INVALID_ARG.
+ *
+ * engram_prefetch_finish blocks the calling host thread until the job's
+ * rows are staged and their copy to the GPU is enqueued, then makes `stream`
+ * wait for that copy and enqueues the assembly of d_emb [n_tok][n_tables*d_e]
+ * (bit-identical to engram_gather on the same tables).  *h_misses_out (if
+ * not NULL) receives the number of (token, table) pairs that missed the cache.
+ *
+ * engram_prefetcher_destroy waits for a job in flight, then releases
+ * everything the prefetcher owns.
+ */
+typedef struct engram_prefetcher_s *engram_prefetcher;
+ENGRAM_API engram_status engram_prefetcher_create(engram_plan p, const void *const *host_tables,
+                                                  const engram_row_cache *cache, int64_t max_tokens,
+                                                  int32_t n_threads, engram_prefetcher *out);
+ENGRAM_API engram_status engram_prefetcher_destroy(engram_prefetcher f);
+ENGRAM_API engram_status engram_prefetch_begin(engram_prefetcher f, const uint32_t *d_idx, int64_t n_tok,
+                                               hipStream_t stream);
+ENGRAM_API engram_status engram_prefetch_finish(engram_prefetcher f, void *d_emb, uint32_t *h_misses_out,
+                                                hipStream_t stream);
+
+/*
  * Fusion ([club] 1.(2); [csdn] third and fourth steps), per branch m and token t:
  *   k = W_k^(m) e_t, v = W_v e_t                      (fp32 accumulation)
  *   alpha = sigmoid( <RMSNorm_{gamma_h}(h_t), RMSNorm_{gamma_k}(k)> / sqrt(d) )

@@ -224,3 +224,29 @@ def test_row_cache_argument_checks(B):
     assert L.engram_gather_cached(p._h, fake, 10, tabs, C.byref(c), fake, -1, None) == B.E_INVALID_ARG
     assert L.engram_host_alloc(1, None) == B.E_INVALID_ARG
     assert L.engram_host_free(None) == B.OK
+
+
+def test_prefetcher_argument_checks(B):
+    """The host-gather prefetcher rejects bad arguments before touching the device."""
+    _no_gpu()
+    L = B.lib()
+    fake = C.c_void_p(0x10000)
+    tabs = (C.c_void_p * 4)(*([0x10000] * 4))
+    p = B.Plan(vocab=1000, vocab_comp=770, heads=2, head_dim=32, table_rows=[10007] * 4, hash_seed=1,
+               d_model=256, dtype=B.BF16)
+    out = C.c_void_p()
+    assert L.engram_prefetcher_create(p._h, tabs, None, 100, 4, None) == B.E_INVALID_ARG
+    assert L.engram_prefetcher_create(None, tabs, None, 100, 4, C.byref(out)) == B.E_INVALID_ARG
+    assert L.engram_prefetcher_create(p._h, None, None, 100, 4, C.byref(out)) == B.E_INVALID_ARG
+    assert L.engram_prefetcher_create(p._h, tabs, None, 0, 4, C.byref(out)) == B.E_INVALID_ARG
+    assert L.engram_prefetcher_create(p._h, tabs, None, 100, 0, C.byref(out)) == B.E_INVALID_ARG
+    assert L.engram_prefetcher_create(p._h, tabs, None, 100, 257, C.byref(out)) == B.E_INVALID_ARG
+    bad_tabs = (C.c_void_p * 4)(*([0x10000] * 3 + [0x10004]))
+    assert L.engram_prefetcher_create(p._h, bad_tabs, None, 100, 4, C.byref(out)) == B.E_INVALID_ARG
+    bad_cache = B.RowCacheC(0x10000, 0x20000, 6)
+    assert L.engram_prefetcher_create(p._h, tabs, C.byref(bad_cache), 100, 4, C.byref(out)) == B.E_INVALID_ARG
+    assert L.engram_prefetcher_create(p._h, tabs, None, 1 << 30, 4, C.byref(out)) == B.E_UNSUPPORTED
+    assert out.value is None
+    assert L.engram_prefetcher_destroy(None) == B.E_INVALID_ARG
+    assert L.engram_prefetch_begin(None, fake, 10, None) == B.E_INVALID_ARG
+    assert L.engram_prefetch_finish(None, fake, None, None) == B.E_INVALID_ARG

@@ -238,3 +238,75 @@ def test_capped_gather_beside_busy_stream(B):
     ref = oracle.gather_synth(idx, head_dim, seed, oracle.BF16).view(np.uint8)
     assert np.array_equal(emb_bytes(emb, dt), ref)
 
+
+
+@pytest.mark.parametrize("kind", ["pinned", "pageable"])
+@pytest.mark.parametrize("cached", ["none", "some", "all"])
+def test_prefetcher_bit_exact_over_jobs(B, kind, cached):
+    """Host threads gather the missed rows, a DMA engine stages them, the GPU
+    assembles E: bit-exact with the oracle over consecutive jobs of different
+    sizes, and the reported miss count is the number of pairs not cached."""
+    say("prefetcher", kind, cached)
+    primes = W.largest_primes_at_most(2003, 6)
+    head_dim, dt, seed = 80, "bf16", 53
+    plan = plan_for(B, primes, head_dim, dt)
+    dev_tables = tables_for(B, primes, head_dim, seed, dt, "device")
+    if kind == "pinned":
+        tables = []
+        for t in dev_tables:
+            hb = B.HostBuffer(t.numel() * t.element_size())
+            hb.view(torch.bfloat16, t.shape).copy_(t.cpu())
+            tables.append(hb)
+    else:
+        tables = [t.cpu().contiguous() for t in dev_tables]
+    n_tables = len(primes)
+    cache, hot_sets = None, [set() for _ in primes]
+    if cached != "none":
+        n_hot = 2003 if cached == "all" else 100
+        hot = np.stack([(np.arange(n_hot) * 7 + tau) % p for tau, p in enumerate(primes)]).astype(np.uint32)
+        cache = B.RowCache(n_tables, 4096, head_dim, torch.bfloat16)
+        plan.engram_cache_build(dev_i32(hot.view(np.int32)), dev_tables, cache)
+        hot_sets = [set(hot[tau].tolist()) for tau in range(n_tables)]
+    pf = B.Prefetcher(plan, tables, cache, max_tokens=3000, n_threads=4)
+    for job, n_tok in enumerate([3000, 1, 1777, 3000]):
+        idx = zipf_idx(primes, n_tok, 100 + job)
+        emb = torch.zeros((n_tok, n_tables * head_dim), dtype=torch.bfloat16, device="cuda")
+        pf.begin(dev_i32(idx.view(np.int32)))
+        if job == 0:
+            with pytest.raises(B.EngramError):  # one job at a time
+                pf.begin(dev_i32(idx.view(np.int32)))
+        n_miss = pf.finish(emb)
+        torch.cuda.synchronize()
+        ref = oracle.gather_synth(idx, head_dim, seed, oracle.BF16).view(np.uint8)
+        assert np.array_equal(emb_bytes(emb, dt), ref), (job, n_tok)
+        want = sum(int(r) not in hot_sets[tau] for tau in range(n_tables) for r in idx[:, tau])
+        assert n_miss == want, (job, n_miss, want)
+    with pytest.raises(B.EngramError):  # nothing begun
+        pf.finish(emb)
+    pf.close()
+
+
+def test_prefetcher_beside_busy_stream(B):
+    """begin on one stream, matrix products on another, finish on a third:
+    the assembled E still equals the oracle's rows."""
+    say("prefetcher beside a busy stream")
+    primes = W.largest_primes_at_most(3001, 4)
+    head_dim, dt, seed = 64, "bf16", 61
+    plan = plan_for(B, primes, head_dim, dt)
+    tables = tables_for(B, primes, head_dim, seed, dt, "host")
+    pf = B.Prefetcher(plan, tables, None, max_tokens=5000, n_threads=8)
+    idx = zipf_idx(primes, 5000, 4)
+    emb = torch.empty((5000, len(primes) * head_dim), dtype=torch.bfloat16, device="cuda")
+    s1, s2, s3 = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    x = torch.randn((2048, 2048), device="cuda").to(torch.bfloat16)
+    idx_d = dev_i32(idx.view(np.int32))
+    torch.cuda.synchronize()
+    pf.begin(idx_d, stream=s1)
+    with torch.cuda.stream(s2):
+        for _ in range(4):
+            x = torch.mm(x, x) * 0.01
+    pf.finish(emb, stream=s3)
+    torch.cuda.synchronize()
+    ref = oracle.gather_synth(idx, head_dim, seed, oracle.BF16).view(np.uint8)
+    assert np.array_equal(emb_bytes(emb, dt), ref)
+    pf.close()
