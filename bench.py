@@ -52,6 +52,8 @@ def parse():
                     help="steps of the separate pass that times every kernel")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time only whole steps (no per-launch events; no roofline)")
+    ap.add_argument("--retrieve-in-projection", action="store_true",
+                    help="engram_forward flag: short chunks retrieve inside the projection launch")
     ap.add_argument("--backward", action="store_true",
                     help="time engram_backward (training) instead of the forward: one JSON line of its own")
     ap.add_argument("--offload", action="store_true",
@@ -175,6 +177,7 @@ def main():
         return
     n_tok = wl.n_tokens
     R = max(1, args.rotate)
+    fwd_flags = B.RETRIEVE_IN_PROJECTION if args.retrieve_in_projection else 0
 
     layers = []
     for slot in range(len(wl.layers)):
@@ -194,7 +197,7 @@ def main():
         r = i % R
         for dl, hs, out, ws, ctx, conv in layers:
             dl.plan.engram_forward(toks[r], dl.comp_map, dl.tables, hs[r], dl.weights, out, ws,
-                                   prev_ctx=ctx, conv_state=conv)
+                                   prev_ctx=ctx, conv_state=conv, flags=fwd_flags)
 
     for i in range(args.warmup):
         step(i)
@@ -361,7 +364,8 @@ def main():
                    "tokens_per_step": tokens_per_step, "layers": list(wl.layers),
                    "n_branches": Br, "d_model": d, "heads_per_order": wl.heads,
                    "head_dim": wl.head_dim, "emb_dim": De, "table_params": sum(wl.primes()) * wl.head_dim,
-                   "rotated_buffers": R, "parallelism": "single GPU"},
+                   "rotated_buffers": R, "parallelism": "single GPU",
+                   "retrieval_in_projection": bool(fwd_flags)},
         "roofline": roofline,
         "gather": gather,
         "gate_gemm": gate_gemm,

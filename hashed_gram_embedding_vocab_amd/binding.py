@@ -26,6 +26,7 @@ OK, E_INVALID_ARG, E_UNSUPPORTED, E_DEVICE, E_NOMEM = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 CONV_LINEAR, CONV_SILU_SKIP = 0, 1
 OUT_DELTA = 1
+RETRIEVE_IN_PROJECTION = 2  # engram_forward: short chunks retrieve inside the projection launch
 MAX_TABLES, MAX_BRANCHES = 32, 4
 KERNEL_NAMES = ("hash", "gather", "gemm", "fuse", "aux", "gemm_v", "gate", "seam", "bwd_gemm", "bwd_fuse",
                 "bwd_table")

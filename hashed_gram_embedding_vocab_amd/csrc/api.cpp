@@ -223,10 +223,32 @@ engram_status check_fuse_args(const engram_plan_s *p, const void *emb, const voi
     return ENGRAM_OK;
 }
 
+// Retrieval done by the projection launch itself (short chunks): what it needs.
+struct InLaunchRetrieval {
+    const int32_t *tokens;
+    const int32_t *comp_map;
+    const int32_t *prev_ctx;
+    uint32_t *bad;
+    const void *const *tables;
+};
+
+// Whether engram_forward leaves retrieval to the projection launch: the
+// fusion-kernel route (W_k and W_v in one launch) on 128 x 128 tiles, where
+// a separate retrieval kernel would be a latency-bound launch of its own.
+bool retrieval_in_projection(const engram_plan_s &p, int32_t batch, int32_t seqlen) {
+    if (p.cfg.dtype != ENGRAM_BF16 || fused_value_path(p, batch, seqlen)) return false;
+    ProjArgs pa{};
+    pa.n_mats = p.cfg.n_branches + 1;
+    pa.d = p.cfg.d_model;
+    pa.n_tok = (int64_t)batch * seqlen;
+    pa.K = p.emb_dim;
+    return proj_gather_ok(pa, p.n_tables);
+}
+
 engram_status do_fuse(engram_plan_s &p, const void *emb, const void *h, int32_t batch, int32_t seqlen,
                       const engram_weights *w, float *conv_state, void *out, float *alpha,
                       uint32_t flags, void *ws, hipStream_t s,
-                      const CtxUpdate &ctx = CtxUpdate{}) {
+                      const CtxUpdate &ctx = CtxUpdate{}, const InLaunchRetrieval *rin = nullptr) {
     Layout L;
     layout_of(p, batch, seqlen, L);
     char *base = static_cast<char *>(ws);
@@ -262,9 +284,21 @@ engram_status do_fuse(engram_plan_s &p, const void *emb, const void *h, int32_t 
 
     // W_k of every branch (gate partials); on the fusion-kernel path W_v too
     pa.n_mats = fused_v ? Br : Br + 1;
+    if (rin) {
+        pa.tokens = rin->tokens;
+        pa.comp_map = rin->comp_map;
+        pa.prev_ctx = rin->prev_ctx;
+        pa.bad = rin->bad;
+        pa.seqlen = seqlen;
+        pa.hc = p.hc;
+        for (int t = 0; t < kMaxTables; ++t)
+            pa.tables[t] = static_cast<const char *>(rin->tables[t < p.n_tables ? t : 0]);
+    }
     {
         Launch l(p, ENGRAM_K_GEMM, s);
-        if (p.cfg.dtype == ENGRAM_BF16)
+        if (rin)
+            launch_proj_gather_bf16(pa, s);
+        else if (p.cfg.dtype == ENGRAM_BF16)
             launch_proj_bf16(pa, s);
         else
             launch_proj_f32(pa, s);
@@ -780,6 +814,8 @@ engram_status engram_forward(engram_plan p, const int32_t *d_tokens, int32_t bat
                              float *d_alpha, uint32_t flags, void *d_workspace,
                              size_t workspace_bytes, uint32_t *d_bad_tokens, hipStream_t stream) {
     if (!p || !d_workspace) return ENGRAM_E_INVALID_ARG;
+    const bool in_proj = (flags & ENGRAM_RETRIEVE_IN_PROJECTION) != 0;
+    flags &= ~(uint32_t)ENGRAM_RETRIEVE_IN_PROJECTION;
     Layout L;
     if (!layout_of(*p, batch, seqlen, L)) return ENGRAM_E_INVALID_ARG;
     char *base = static_cast<char *>(d_workspace);
@@ -791,18 +827,24 @@ engram_status engram_forward(engram_plan p, const int32_t *d_tokens, int32_t bat
         st = check_fuse_args(p, emb, d_h, batch, seqlen, w, d_out, d_alpha, d_conv_state, flags,
                              d_workspace, workspace_bytes);
     if (st != ENGRAM_OK) return st;
-    // retrieval in one kernel: hash every (token, table) pair and copy its row
-    st = do_hash_gather(*p, d_tokens, batch, seqlen, d_comp_map, d_prev_ctx, d_bad_tokens, table_ptrs,
-                        emb, stream);
-    if (st != ENGRAM_OK) return st;
     // the carried context is updated by a later kernel of this call, after
-    // the retrieval kernel has read the old one
+    // retrieval has read the old one
     CtxUpdate ctx{};
     ctx.tokens = d_tokens;
     ctx.comp_map = d_comp_map;
     ctx.prev_ctx = d_prev_ctx;
     ctx.vocab = p->cfg.vocab;
     ctx.vocab_comp = p->cfg.vocab_comp;
+    if (in_proj && retrieval_in_projection(*p, batch, seqlen)) {
+        // short chunks: the projection launch hashes and gathers itself
+        const InLaunchRetrieval rin{d_tokens, d_comp_map, d_prev_ctx, d_bad_tokens, table_ptrs};
+        return do_fuse(*p, emb, d_h, batch, seqlen, w, d_conv_state, d_out, d_alpha, flags, d_workspace, stream,
+                       ctx, &rin);
+    }
+    // retrieval in one kernel: hash every (token, table) pair and copy its row
+    st = do_hash_gather(*p, d_tokens, batch, seqlen, d_comp_map, d_prev_ctx, d_bad_tokens, table_ptrs,
+                        emb, stream);
+    if (st != ENGRAM_OK) return st;
     return do_fuse(*p, emb, d_h, batch, seqlen, w, d_conv_state, d_out, d_alpha, flags, d_workspace,
                    stream, ctx);
 }

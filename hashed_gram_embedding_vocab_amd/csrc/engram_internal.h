@@ -166,6 +166,14 @@ struct ProjArgs {
     // stores at out_f32 + z * out_split (k_ld 0: one launch, rows K long)
     int32_t k_ld;
     int64_t out_split;
+    // retrieval inside the launch (mode 2): every block hashes its tokens'
+    // n-grams and reads its E operand straight from the table rows
+    const int32_t *tokens;                 // [batch][seqlen] raw ids
+    const int32_t *comp_map;               // [V]
+    const int32_t *prev_ctx;               // [batch][2] or null
+    uint32_t *bad;                         // counter of raw ids outside [0, V), or null
+    const char *tables[kMaxTables];
+    HashConsts hc;
 };
 
 constexpr int kPartCols = 128;  // columns of d summed into one gate partial (bf16 path)
@@ -173,6 +181,14 @@ constexpr int kPartCols = 128;  // columns of d summed into one gate partial (bf
 // W_k^(m) (and, when n_mats == n_branches + 1, W_v) projections: gate
 // partials from W_k tiles, fp32 v from W_v tiles.
 void launch_proj_bf16(const ProjArgs &a, hipStream_t s);
+// The same launch (W_k of every branch and W_v, gate partials and fp32 v)
+// with retrieval inside: each block hashes the n-grams of its tokens and
+// loads E straight from the tables into its operand ring, so E never reaches
+// memory.  Only where launch_proj_bf16 takes 128 x 128 tiles and
+// n_tables <= kGatherMaxTables (proj_gather_ok).
+constexpr int kGatherMaxTables = 16;
+bool proj_gather_ok(const ProjArgs &a, int32_t n_tables);
+void launch_proj_gather_bf16(const ProjArgs &a, hipStream_t s);
 // W_v projection with the gate, gated value, depthwise causal conv, residual
 // and conv-state update fused into the epilogue (needs seqlen >= K_c - 1).
 // Rows 0..2 of each 256-token tile whose conv history lies in the previous

@@ -461,7 +461,10 @@ __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t 
 }
 
 // MODE 0, or MODE 1 with BR branches and the conv output passed through
-// SiLU plus the skip term (SILU) or not.  NARROW (mode 0 only): tiles of 128
+// SiLU plus the skip term (SILU) or not.  MODE 2 is mode 0 (narrow tile only)
+// with its E operand read from the tables: the block first hashes the
+// n-grams of its 128 tokens into LDS, then each lane's 16-byte piece of a
+// stage comes from the table row its token's slot names.  NARROW (modes 0, 2, 3): tiles of 128
 // weight rows x 128 tokens and 4 waves of 128 x 32, for launches with too few
 // 256 x 256 tiles to fill the chip (decode).  A wave always owns 128 output
 // channels in the same MFMA layout, so the gate partial sums come out
@@ -469,13 +472,18 @@ __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t 
 template <int MODE, int BR, bool SILU, bool NARROW>
 __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_bf16_kernel(ProjArgs a) {
     static_assert(!(NARROW && MODE == 1), "the fused value epilogue is written for the wide tile");
-    static_assert(MODE == 0 || MODE == 1 || MODE == 3, "mode");
+    static_assert(MODE == 0 || MODE == 1 || MODE == 2 || MODE == 3, "mode");
+    static_assert(MODE != 2 || NARROW, "retrieval inside the launch is written for the narrow tile");
+    constexpr bool kGather = MODE == 2;
+    constexpr bool kGateK = MODE == 0 || MODE == 2;  // W_k / W_v launch with the gate-partial epilogue
     typedef TileCfg<NARROW> C;
     constexpr int TBN = C::BN, TBT = C::BT, TTHREADS = C::kThreads, TWAVES = C::kWaves, TWGN = C::kWavesN;
     constexpr int TWT = C::WT, TFT = C::FT, TOPB = C::kOperandBytes, TBPW = C::kBlocksPerWave;
     __shared__ StageT<TOPB> st0, st1, st2, st3;
     __shared__ float alpha_s[MODE == 1 ? BR : 1][TBT];
-    __shared__ __attribute__((aligned(16))) float gsm_s[MODE == 0 ? TWAVES * WN : 4];
+    __shared__ __attribute__((aligned(16))) float gsm_s[kGateK ? TWAVES * WN : 4];
+    __shared__ uint32_t idx_s[kGather ? 128 * kGatherMaxTables : 1];  // slot of (token of the tile, table)
+    __shared__ const char *tab_s[kGather ? kGatherMaxTables : 1];
     __shared__ __attribute__((aligned(16))) float taps_s[MODE == 1 ? 4 * TBN : 4];
     __shared__ __attribute__((aligned(16))) float halo_s[MODE == 1 ? TWAVES * kHalo * WN : 4];
 
@@ -526,18 +534,87 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
         eoff[i] = (uint32_t)(t * ld + lchunk * 8) * 2u;
     }
 
+    // Mode 2: the slots of the tile's tokens (tokens past n_tok: slot 0) and
+    // the table bases go to LDS before the first stage.  A lane's 16-byte K
+    // piece of stage s is element 32 s + 8 lchunk of E, i.e. element goff of
+    // table gtau (d_e % 8 == 0: a piece never straddles two tables); the
+    // stages are issued in K order, so (gtau, goff) advance by BK each.
+    int gtau = 0, goff = 0;
+    const int g_nt = kGather ? a.hc.n_tables : 0;
+    const uint32_t g_row_bytes = kGather ? (uint32_t)(K / (g_nt > 0 ? g_nt : 1)) * 2u : 0u;
+    if constexpr (kGather) {
+        const int de = K / g_nt;
+        const int32_t pad = a.hc.vocab_comp;
+        const uint64_t Bv = (uint64_t)a.hc.vocab_comp + 1u;
+        // one thread per token of the tile: its ids are read and compressed
+        // once, then hashed into every table
+        if (tid < TBT) {
+            const int tl = tid;
+            const int64_t tok = t0 + tl;
+            const bool live_tok = tok < a.n_tok;
+            int32_t c0 = pad, c1 = pad, c2 = pad;
+            if (live_tok) {
+                const int64_t b = tok / a.seqlen;
+                const int32_t t = (int32_t)(tok - b * a.seqlen);
+                const int32_t x0 = a.tokens[tok];
+                c0 = compress_id(x0, a.comp_map, a.hc.vocab, pad);
+                if (t >= 1) c1 = compress_id(a.tokens[tok - 1], a.comp_map, a.hc.vocab, pad);
+                else c1 = a.prev_ctx ? a.prev_ctx[b * 2 + 1] : pad;
+                if (t >= 2) c2 = compress_id(a.tokens[tok - 2], a.comp_map, a.hc.vocab, pad);
+                else if (t == 1) c2 = a.prev_ctx ? a.prev_ctx[b * 2 + 1] : pad;
+                else c2 = a.prev_ctx ? a.prev_ctx[b * 2 + 0] : pad;
+                // one count per raw id: the blocks of the first weight tile
+                if (a.bad && tile_n == 0 && (x0 < 0 || x0 >= a.hc.vocab)) atomicAdd(a.bad, 1u);
+            }
+            const uint64_t k2 = (uint64_t)c1 * Bv + (uint64_t)c0;
+            const uint64_t k3 = ((uint64_t)c2 * Bv + (uint64_t)c1) * Bv + (uint64_t)c0;
+            for (int tau = 0; tau < g_nt; ++tau) {
+                const uint64_t key = a.hc.order_of[tau] == 2 ? k2 : k3;
+                idx_s[tl * g_nt + tau] =
+                    live_tok ? mod_prime(mix64(key ^ a.hc.seed[tau]), a.hc.rows[tau], a.hc.magic[tau]) : 0u;
+            }
+        }
+        if (tid < g_nt) tab_s[tid] = pick(a.tables, tid);
+        goff = 8 * lchunk;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const bool c = goff >= de;
+            goff -= c ? de : 0;
+            gtau += c ? 1 : 0;
+        }
+        __syncthreads();
+    }
+
 // The immediate offset of a buffer load with an LDS destination moves the LDS
 // address as well, so the K position travels in the scalar offset, which only
 // moves the global address.
 #define ENGRAM_ISSUE(STG, k0)                                                                    \
     do {                                                                                         \
         const int kbytes = (kbase + (k0)) * 2;                                                   \
-        _Pragma("unroll") for (int i = 0; i < TBPW; ++i) {                             \
-            const int blk = wave * TBPW + i;                                           \
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void_t *)&STG.w[blk * kBlockBytes], \
-                                                     16, woff[i], kbytes, 0, 0);                 \
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(eres, (lds_void_t *)&STG.e[blk * kBlockBytes], \
-                                                     16, eoff[i], kbytes, 0, 0);                 \
+        if constexpr (kGather) {                                                                 \
+            const char *tb = tab_s[gtau];                                                        \
+            _Pragma("unroll") for (int i = 0; i < TBPW; ++i) {                                   \
+                const int blk = wave * TBPW + i;                                                 \
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void_t *)&STG.w[blk * kBlockBytes], \
+                                                         16, woff[i], kbytes, 0, 0);             \
+                const uint32_t ix = idx_s[(blk * 16 + lr) * g_nt + gtau];                        \
+                __builtin_amdgcn_global_load_lds(tb + (uint64_t)ix * g_row_bytes + 2 * goff,     \
+                                                 (lds_void_t *)&STG.e[blk * kBlockBytes], 16, 0, 0); \
+            }                                                                                    \
+            goff += BK;                                                                          \
+            _Pragma("unroll") for (int r = 0; r < 4; ++r) {                                      \
+                const bool c = goff >= (int)(g_row_bytes / 2u);                                  \
+                goff -= c ? (int)(g_row_bytes / 2u) : 0;                                         \
+                gtau += c ? 1 : 0;                                                               \
+            }                                                                                    \
+        } else {                                                                                 \
+            _Pragma("unroll") for (int i = 0; i < TBPW; ++i) {                                   \
+                const int blk = wave * TBPW + i;                                                 \
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void_t *)&STG.w[blk * kBlockBytes], \
+                                                         16, woff[i], kbytes, 0, 0);             \
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(eres, (lds_void_t *)&STG.e[blk * kBlockBytes], \
+                                                         16, eoff[i], kbytes, 0, 0);             \
+            }                                                                                    \
         }                                                                                        \
     } while (0)
     constexpr int kLoadsPerStage = 2 * TBPW;  // per wave
@@ -657,7 +734,7 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
             __builtin_amdgcn_raw_ptr_buffer_load_lds(hres, (lds_void_t *)(hA + k * 1024), 16,
                                                      chunk_offset(k, lane, rowbase, t0, a.n_tok, d, nl), 0, 0, 0);
     };
-    constexpr int kEarlyH = MODE == 0 ? TWT / 8 : (MODE == 1 ? 8 : 0);  // loads issued in the ring's tail
+    constexpr int kEarlyH = kGateK ? TWT / 8 : (MODE == 1 ? 8 : 0);  // loads issued in the ring's tail
 
     // the last four stages: ks = k_steps - 4; stages ks..ks+2 are in flight
     wait_vmcnt<2 * kLoadsPerStage>();
@@ -669,7 +746,7 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
     ENGRAM_COMPUTE(st1);
     wait_vmcnt<kLoadsPerStage>();
     block_barrier();  // buffers 0 and 1 are done with
-    if constexpr (MODE == 0) h_issue(0);
+    if constexpr (kGateK) h_issue(0);
     if constexpr (MODE == 1) chunk0_issue();
     ENGRAM_COMPUTE(st2);
     wait_vmcnt<kEarlyH>();
@@ -696,7 +773,7 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
                 if (n < a.n_rows) *reinterpret_cast<f32x4_t *>(out + t * a.out_ld + n) = acc[i][j];
             }
         }
-    } else if constexpr (MODE == 0) {
+    } else if constexpr (kGateK) {
     if (mat < a.n_branches) {
         // gate partials of branch `mat` over channels [nl, nl+128).
         // gamma_h * gamma_k for the wave's channels goes through LDS, so it
@@ -791,6 +868,19 @@ void launch_proj_plain_bf16(const ProjArgs &a, hipStream_t s, int splits) {
         launch_kernel((proj_bf16_kernel<3, 1, false, false>), dim3((unsigned)wide, (unsigned)splits),
                       dim3(kThreads), s, a);
     }
+}
+
+bool proj_gather_ok(const ProjArgs &a, int32_t n_tables) {
+    const int n_total = a.n_mats * a.d;
+    const int64_t wide = (int64_t)((n_total + BN - 1) / BN) * ((a.n_tok + BT - 1) / BT);
+    return wide < 256 && n_tables >= 1 && n_tables <= kGatherMaxTables && a.K % n_tables == 0 &&
+           (a.K / n_tables) % 8 == 0;
+}
+
+void launch_proj_gather_bf16(const ProjArgs &a, hipStream_t s) {
+    const int n_total = a.n_mats * a.d;
+    const int64_t blocks = (int64_t)((n_total + 127) / 128) * ((a.n_tok + 127) / 128);
+    launch_kernel((proj_bf16_kernel<2, 1, false, true>), dim3((unsigned)blocks), dim3(256), s, a);
 }
 
 int plain_k_splits(int64_t n_tok, int64_t rows, int64_t K) {

@@ -62,6 +62,13 @@ enum { ENGRAM_CONV_LINEAR = 0, ENGRAM_CONV_SILU_SKIP = 1 };
 
 /* engram_gate_fuse / engram_forward flag: write y instead of h + y. */
 enum { ENGRAM_OUT_DELTA = 1u << 0 };
+/* engram_forward flag: on chunks shorter than K_c - 1 (decode), where W_k and
+ * W_v go through one launch on 128 x 128 tiles, that launch also retrieves:
+ * each workgroup hashes the n-grams of its tokens and loads its E operand
+ * straight from the table rows (E never reaches memory; n_tables <= 16).
+ * Same results bit for bit; measured no faster than the separate retrieval
+ * kernel, so off by default.  Ignored where it does not apply. */
+enum { ENGRAM_RETRIEVE_IN_PROJECTION = 1u << 1 };
 
 #define ENGRAM_MAX_TABLES 32
 #define ENGRAM_MAX_BRANCHES 4

@@ -521,9 +521,9 @@ def test_profiling_counts_launches(B):
         assert prof[k]["launches"] == n, (k, prof)
         assert (prof[k]["total_ms"] > 0) == (n > 0)
     assert prof["dropped"] == 0
-    # bf16 prefill: the W_k launch, the gate, then the W_v launch with the
-    # fusion step in its epilogue and, past one 256-token tile, the seam
-    # rows; chunks shorter than K_c - 1 use the fusion kernel
+    # bf16 prefill: retrieval, the W_k launch, the gate, then the W_v launch
+    # with the fusion step in its epilogue and, past one 256-token tile, the
+    # seam rows; chunks shorter than K_c - 1 use the fusion kernel
     for seqlen, seams in ((50, 0), (300, 1)):
         wl = small_wl(n_branches=2, batch=2, seqlen=seqlen)
         dl = make_device_layer(wl)
@@ -691,3 +691,64 @@ def test_backward_full_size_rows_and_determinism(B):
         assert np.array_equal(rows[tau, :counts[tau]], used)
     del dl
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("in_proj", [False, True])
+@pytest.mark.parametrize("batch,seqlen,heads", [(300, 1, 8), (5, 2, 2), (129, 1, 4)])
+def test_short_chunks_retrieval_in_projection(B, batch, seqlen, heads, in_proj):
+    """Short chunks, retrieval by its own kernel or inside the projection
+    launch (E never materialised): out-of-range ids are counted once each and
+    hash as PAD, and the result equals the split calls bit for bit and the
+    oracle."""
+    say("short chunks", batch, seqlen, heads, "retrieval in projection" if in_proj else "")
+    wl = small_wl(n_branches=2, batch=batch, seqlen=seqlen, heads=heads, head_dim=32)
+    dl = make_device_layer(wl)
+    toks = W.make_tokens(wl)
+    toks[0, 0] = -5
+    toks[-1, -1] = wl.vocab + 3
+    if batch > 3:
+        toks[3, 0] = 2 ** 31 - 1
+    n_bad = int(((toks < 0) | (toks >= wl.vocab)).sum())
+    rng = np.random.default_rng(batch)
+    prev = rng.integers(0, wl.vocab_comp + 1, (batch, 2)).astype(np.int32)
+    state0 = rng.standard_normal((wl.n_branches, batch, wl.conv_kernel - 1, wl.d_model)).astype(np.float32)
+    ctx = dev_i32(prev)
+    state = to_device(state0, torch.float32, "cuda")
+    out, alpha, bad = forward(dl, toks, prev_ctx=ctx, conv_state=state,
+                              flags=B.RETRIEVE_IN_PROJECTION if in_proj else 0)
+    assert bad == n_bad
+    # split calls: hash, gather, gate_fuse on the same inputs
+    n_tok = batch * seqlen
+    idx = torch.empty((n_tok, wl.n_tables), dtype=torch.int32, device="cuda")
+    dl.plan.engram_hash(dev_i32(toks), dl.comp_map, idx, prev_ctx=dev_i32(prev))
+    emb = torch.empty((n_tok, wl.emb_dim), dtype=torch.bfloat16, device="cuda")
+    dl.plan.engram_gather(idx, dl.tables, emb)
+    out2 = torch.empty_like(dl.h)
+    state2 = to_device(state0, torch.float32, "cuda")
+    dl.plan.engram_gate_fuse(emb, dl.h, dl.weights, out2, dl.plan.workspace(batch, seqlen), batch, seqlen,
+                             conv_state=state2)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.view(torch.int16).cpu().numpy(), out2.view(torch.int16).cpu().numpy())
+    assert np.array_equal(state.cpu().numpy(), state2.cpu().numpy())
+    ref_idx, _, new_ctx = oracle_indices(wl, dl.li, toks, dl.comp_map_host, prev_ctx=prev)
+    assert np.array_equal(idx.cpu().numpy().view(np.uint32), ref_idx)
+    assert np.array_equal(ctx.cpu().numpy(), new_ctx)
+    L = oracle_layer(wl, dl.li, ref_idx, batch, seqlen, conv_state=state0)
+    ref, ref_alpha, _ = L.forward_all()
+    assert_within(host(out), ref, "bf16", "short chunks, retrieval in projection")
+    assert np.abs(host(alpha) - ref_alpha).max() <= alpha_tol("bf16")
+
+
+def test_retrieval_in_projection_profile(B):
+    """With the flag, a decode step launches no retrieval kernel."""
+    wl = small_wl(n_branches=2, batch=64, seqlen=1)
+    dl = make_device_layer(wl)
+    toks = W.make_tokens(wl)
+    dl.plan.engram_profile_begin(64)
+    forward(dl, toks, flags=B.RETRIEVE_IN_PROJECTION)
+    forward(dl, toks)
+    torch.cuda.synchronize()
+    prof = dl.plan.engram_profile_end()
+    for k, n in (("hash", 0), ("gather", 1), ("gemm", 2), ("fuse", 2)):
+        assert prof[k]["launches"] == n, (k, prof)
+
