@@ -49,7 +49,7 @@ extern "C" {
 typedef enum {
     ENGRAM_OK = 0,
     ENGRAM_E_INVALID_ARG = 1, /* null pointer, bad size, misalignment, short workspace */
-    ENGRAM_E_UNSUPPORTED = 2, /* a shape this build's kernels do not cover */
+    ENGRAM_E_UNSUPPORTED = 2, /* a shape the library's kernels do not cover */
     ENGRAM_E_DEVICE = 3,      /* a HIP runtime call or kernel launch failed */
     ENGRAM_E_NOMEM = 4        /* host allocation of the plan failed */
 } engram_status;
