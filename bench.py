@@ -507,7 +507,7 @@ def backward_bench(args, wl):
 
     kernel_of = {"bwd_gemm": "proj_bf16_kernel<3> (k and v, dE, dW with its split-K sum)",
                  "bwd_fuse": "bwd_gate_stats, bwd_conv, bwd_gate, ordered sums, transposes",
-                 "bwd_table": "table-row gradients (keys, rocPRIM sort and scan, segmented sums)",
+                 "bwd_table": "table-row gradients (keys, segmented radix sort, run-head scan, segmented sums)",
                  "gather": "gather_kernel"}
     per_kind = {k: dict(figures(k, per_call[k]), kernel=kernel_of[k]) for k in kinds}
     roofline = dict(figures(dominant, dom_us), kernel=kernel_of[dominant], timed_in="measured run", traffic=None)

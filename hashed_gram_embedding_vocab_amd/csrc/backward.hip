@@ -16,7 +16,6 @@
 // The contractions themselves run on proj_bf16.hip's main loop (plain mode).
 #include <cstring>
 
-#include <rocprim/device/device_radix_sort.hpp>
 #include <rocprim/device/device_scan.hpp>
 
 #include "engram_internal.h"
@@ -405,6 +404,184 @@ __global__ __launch_bounds__(256) void bwd_keys_kernel(const uint32_t *idx, int6
     vals[i] = (uint32_t)t;
 }
 
+// Stable LSD radix sort of the keys by their row bits, one table at a time.
+// The keys arrive grouped by table (item tau * n_tok + t is token t's key in
+// table tau, tokens ascending), so sorting each table's segment by row is
+// sorting by (table, row), and stability keeps the tokens of one row in
+// ascending order.  A pass takes `bits` digit bits from `shift` up:
+//   sort_count_kernel    digit counts of every block of kSortItems items
+//   sort_scan_kernel     per table, exclusive offsets in (digit, block) order
+//   sort_scatter_kernel  each wave walks its quarter of the block in order,
+//                        64 items at a time; a lane's rank among the lanes
+//                        holding its digit comes from `bits` ballots, so the
+//                        order of the items is kept without atomics
+constexpr int kSortThreads = 256;
+constexpr int kSortWaves = kSortThreads / 64;
+constexpr int kSortItems = 2048;  // per block: 512 per wave
+constexpr int kSortMaxBits = 11;
+
+// lanes of the wave (among those with `valid`) whose digit equals this lane's
+__device__ __forceinline__ uint64_t digit_peers(uint32_t digit, int bits, bool valid) {
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < bits; ++b) {
+        const bool set = (digit >> b) & 1u;
+        const uint64_t m = __ballot(set);
+        peers &= set ? m : ~m;
+    }
+    return peers;
+}
+
+// Each wave owns a contiguous quarter of its block's items, kSortGroups
+// groups of 64, and loads all of them before it ranks any (one memory round
+// trip per kernel instead of one per group).
+constexpr int kSortGroups = kSortItems / kSortWaves / 64;
+
+template <typename KeyT>
+__device__ __forceinline__ void sort_load(const KeyT *k, int wlo, int whi, int lane, KeyT (&key)[kSortGroups]) {
+#pragma unroll
+    for (int g = 0; g < kSortGroups; ++g) {
+        const int i = wlo + 64 * g + lane;
+        key[g] = i < whi ? k[i] : (KeyT)0;
+    }
+}
+
+template <typename KeyT>
+__global__ __launch_bounds__(kSortThreads) void sort_count_kernel(const KeyT *keys, int64_t seg, int32_t nbpt,
+                                                                  int32_t shift, int32_t bits, uint32_t *hist) {
+    __shared__ uint32_t cnt[1 << kSortMaxBits];
+    const int nd = 1 << bits;
+    const int tau = blockIdx.y, blk = blockIdx.x;
+    const int64_t lo = (int64_t)blk * kSortItems;
+    const int n = (int)min<int64_t>(kSortItems, seg - lo);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wlo = w * (kSortItems / kSortWaves), whi = min(wlo + kSortItems / kSortWaves, n);
+    KeyT key[kSortGroups];
+    sort_load(keys + (int64_t)tau * seg + lo, wlo, whi, lane, key);
+    for (int i = threadIdx.x; i < nd; i += kSortThreads) cnt[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < kSortGroups; ++g) {
+        const bool valid = wlo + 64 * g + lane < whi;
+        const uint32_t digit = (uint32_t)(key[g] >> shift) & (uint32_t)(nd - 1);
+        const uint64_t peers = digit_peers(digit, bits, valid);
+        // the lowest lane of each digit adds the lanes that share it
+        if (valid && (peers & ((1ull << lane) - 1ull)) == 0ull) atomicAdd(&cnt[digit], (uint32_t)__popcll(peers));
+    }
+    __syncthreads();
+    uint32_t *h = hist + (int64_t)tau * nd * nbpt;
+    for (int dg = threadIdx.x; dg < nd; dg += kSortThreads) h[(int64_t)dg * nbpt + blk] = cnt[dg];
+}
+
+// One workgroup of 16 waves per table: hist[tau][0..per_table) becomes its
+// exclusive prefix sum, in chunks of 16 x kScanRows x 64 counts.  Wave w
+// takes a contiguous kScanRows x 64 of the chunk and loads it row by row
+// (lane l of row j holds count 64 j + l: every access is coalesced); each row
+// is scanned across the lanes and carried to the next, the waves' totals are
+// scanned in LDS, and the prefixes go back the way they came.
+constexpr int kScanRows = 16;
+
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+__global__ __launch_bounds__(1024) void sort_scan_kernel(uint32_t *hist, int64_t per_table) {
+    __shared__ uint32_t wtot[16];
+    uint32_t *h = hist + (int64_t)blockIdx.x * per_table;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint32_t carry = 0u;  // total of the earlier chunks
+    for (int64_t c0 = 0; c0 < per_table; c0 += 16 * kScanRows * 64) {
+        const int64_t base = c0 + (int64_t)w * kScanRows * 64 + lane;
+        uint32_t x[kScanRows];
+#pragma unroll
+        for (int j = 0; j < kScanRows; ++j) x[j] = base + 64 * j < per_table ? h[base + 64 * j] : 0u;
+        uint32_t run = 0u;  // this wave's total so far
+#pragma unroll
+        for (int j = 0; j < kScanRows; ++j) {
+            const uint32_t incl = wave_incl_scan(x[j], lane);
+            const uint32_t tot = __shfl(incl, 63);
+            x[j] = run + incl - x[j];
+            run += tot;
+        }
+        if (lane == 0) wtot[w] = run;
+        __syncthreads();
+        uint32_t woff = carry, all = 0u;
+        for (int ww = 0; ww < 16; ++ww) {
+            const uint32_t t = wtot[ww];
+            woff += ww < w ? t : 0u;
+            all += t;
+        }
+#pragma unroll
+        for (int j = 0; j < kScanRows; ++j)
+            if (base + 64 * j < per_table) h[base + 64 * j] = woff + x[j];
+        carry += all;
+        __syncthreads();  // wtot is rewritten by the next chunk
+    }
+}
+
+template <typename KeyT>
+__global__ __launch_bounds__(kSortThreads) void sort_scatter_kernel(const KeyT *kin, const uint32_t *vin, KeyT *kout,
+                                                                    uint32_t *vout, int64_t seg, int32_t nbpt,
+                                                                    int32_t shift, int32_t bits,
+                                                                    const uint32_t *hist) {
+    __shared__ uint32_t wbase[kSortWaves][1 << kSortMaxBits];
+    const int nd = 1 << bits;
+    const int tau = blockIdx.y, blk = blockIdx.x;
+    const int64_t lo = (int64_t)blk * kSortItems;
+    const int n = (int)min<int64_t>(kSortItems, seg - lo);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const uint64_t below = (1ull << lane) - 1ull;
+    const int wlo = w * (kSortItems / kSortWaves), whi = min(wlo + kSortItems / kSortWaves, n);
+    KeyT key[kSortGroups];
+    uint32_t val[kSortGroups];
+    sort_load(kin + (int64_t)tau * seg + lo, wlo, whi, lane, key);
+    sort_load(vin + (int64_t)tau * seg + lo, wlo, whi, lane, val);
+    for (int i = threadIdx.x; i < kSortWaves * nd; i += kSortThreads) wbase[i / nd][i % nd] = 0u;
+    __syncthreads();
+    // digit counts of each wave's quarter
+    uint64_t peers[kSortGroups];
+#pragma unroll
+    for (int g = 0; g < kSortGroups; ++g) {
+        const bool valid = wlo + 64 * g + lane < whi;
+        const uint32_t digit = (uint32_t)(key[g] >> shift) & (uint32_t)(nd - 1);
+        peers[g] = digit_peers(digit, bits, valid);
+        if (valid && (peers[g] & below) == 0ull) wbase[w][digit] += (uint32_t)__popcll(peers[g]);
+    }
+    __syncthreads();
+    // first output slot of each (wave, digit): the block's offset plus the
+    // counts of the earlier waves
+    const uint32_t *h = hist + (int64_t)tau * nd * nbpt;
+    for (int dg = threadIdx.x; dg < nd; dg += kSortThreads) {
+        uint32_t run = h[(int64_t)dg * nbpt + blk];
+#pragma unroll
+        for (int ww = 0; ww < kSortWaves; ++ww) {
+            const uint32_t c = wbase[ww][dg];
+            wbase[ww][dg] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    KeyT *ko = kout + (int64_t)tau * seg;
+    uint32_t *vo = vout + (int64_t)tau * seg;
+#pragma unroll
+    for (int g = 0; g < kSortGroups; ++g) {
+        const bool valid = wlo + 64 * g + lane < whi;
+        const uint32_t digit = (uint32_t)(key[g] >> shift) & (uint32_t)(nd - 1);
+        const uint32_t pos = wbase[w][digit] + (uint32_t)__popcll(peers[g] & below);
+        if (valid) {
+            ko[pos] = key[g];
+            vo[pos] = val[g];
+        }
+        // every peer has read the base (the wave's LDS accesses complete in
+        // order); the highest peer moves it past the group
+        if (valid && (peers[g] >> lane) == 1ull) wbase[w][digit] = pos + 1u;
+    }
+}
+
 template <typename KeyT>
 __global__ __launch_bounds__(256) void bwd_heads_kernel(const KeyT *keys, int64_t n, uint32_t *head) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -587,35 +764,47 @@ void launch_bwd_transpose(const uint16_t *src, int64_t rows, int64_t cols, int64
 int64_t bwd_row_chunks(int64_t n_items) { return (n_items + kRowChunk - 1) / kRowChunk; }
 
 namespace {
-// rocPRIM's default choice (block sort and merges below 2^20 items): its
-// onesweep path is no faster at these sizes and clears its look-back state
-// with memset nodes, which a captured graph must not hold
-typedef rocprim::default_config SortCfg;
+size_t sort_hist_bytes(int64_t n_items) {
+    // (digits x blocks) counts per table: at most 2^kSortMaxBits per block
+    // of kSortItems items, plus one partial block per table (<= 32 tables)
+    return (size_t)(n_items + (int64_t)32 * kSortItems) * 4u;
+}
 
-template <typename KeyT>
 size_t table_temp_bytes(int64_t n_items) {
-    size_t sort_bytes = 0, scan_bytes = 0;
-    (void)rocprim::radix_sort_pairs<SortCfg>(nullptr, sort_bytes, (KeyT *)nullptr, (KeyT *)nullptr,
-                                             (uint32_t *)nullptr, (uint32_t *)nullptr, (size_t)n_items, 0,
-                                             (unsigned)(8 * sizeof(KeyT)));
+    size_t scan_bytes = 0;
     (void)rocprim::inclusive_scan(nullptr, scan_bytes, (uint32_t *)nullptr, (uint32_t *)nullptr, (size_t)n_items,
                                   rocprim::plus<uint32_t>());
-    return std::max(sort_bytes, scan_bytes);
+    return std::max(scan_bytes, sort_hist_bytes(n_items));
 }
 
 template <typename KeyT>
-hipError_t table_grad(const BwdTableArgs &t, int32_t row_bits, int32_t key_bits, hipStream_t s) {
+hipError_t table_grad(const BwdTableArgs &t, int32_t row_bits, hipStream_t s) {
     const int64_t n = t.n_tok * t.n_tables;
-    KeyT *keys_in = static_cast<KeyT *>(t.keys_in), *keys_out = static_cast<KeyT *>(t.keys_out);
+    // passes of at most kSortMaxBits digit bits over the row bits; the keys
+    // start in the buffer that makes the last pass end in keys_out
+    const int passes = (row_bits + kSortMaxBits - 1) / kSortMaxBits;
+    const int bits = (row_bits + passes - 1) / passes;
+    KeyT *kb[2] = {static_cast<KeyT *>(t.keys_in), static_cast<KeyT *>(t.keys_out)};
+    uint32_t *vb[2] = {t.vals_in, t.vals_out};
+    int cur = passes % 2 == 0 ? 1 : 0;
     launch_kernel(bwd_keys_kernel<KeyT>, dim3((unsigned)((n + 255) / 256)), dim3(256), s, t.idx, t.n_tok,
-                  t.n_tables, row_bits, keys_in, t.vals_in);
-    size_t bytes = t.temp_bytes;
-    hipError_t e = rocprim::radix_sort_pairs<SortCfg>(t.temp, bytes, keys_in, keys_out, t.vals_in, t.vals_out,
-                                                      (size_t)n, 0, (unsigned)key_bits, s);
-    if (e != hipSuccess) return e;
+                  t.n_tables, row_bits, kb[cur], vb[cur]);
+    const int32_t nbpt = (int32_t)((t.n_tok + kSortItems - 1) / kSortItems);
+    uint32_t *hist = static_cast<uint32_t *>(t.temp);
+    const dim3 sgrid((unsigned)nbpt, (unsigned)t.n_tables);
+    for (int p = 0, shift = 0; p < passes; ++p, shift += bits) {
+        const int pb = std::min(bits, row_bits - shift);
+        launch_kernel(sort_count_kernel<KeyT>, sgrid, dim3(kSortThreads), s, kb[cur], t.n_tok, nbpt, shift, pb, hist);
+        launch_kernel(sort_scan_kernel, dim3((unsigned)t.n_tables), dim3(1024), s, hist,
+                      (int64_t)nbpt << pb);
+        launch_kernel(sort_scatter_kernel<KeyT>, sgrid, dim3(kSortThreads), s, kb[cur], vb[cur], kb[cur ^ 1],
+                      vb[cur ^ 1], t.n_tok, nbpt, shift, pb, hist);
+        cur ^= 1;
+    }
+    KeyT *keys_out = kb[1];
     launch_kernel(bwd_heads_kernel<KeyT>, dim3((unsigned)((n + 255) / 256)), dim3(256), s, keys_out, n, t.head);
-    bytes = t.temp_bytes;
-    e = rocprim::inclusive_scan(t.temp, bytes, t.head, t.incl, (size_t)n, rocprim::plus<uint32_t>(), s);
+    size_t bytes = t.temp_bytes;
+    const hipError_t e = rocprim::inclusive_scan(t.temp, bytes, t.head, t.incl, (size_t)n, rocprim::plus<uint32_t>(), s);
     if (e != hipSuccess) return e;
     const int64_t chunks = bwd_row_chunks(n);
     const dim3 grid((unsigned)((chunks + 3) / 4));
@@ -637,9 +826,7 @@ hipError_t table_grad(const BwdTableArgs &t, int32_t row_bits, int32_t key_bits,
 }
 }  // namespace
 
-size_t bwd_table_temp_bytes(int64_t n_items) {
-    return std::max(table_temp_bytes<uint32_t>(n_items), table_temp_bytes<uint64_t>(n_items));
-}
+size_t bwd_table_temp_bytes(int64_t n_items) { return table_temp_bytes(n_items); }
 
 hipError_t launch_bwd_table_grad(const BwdTableArgs &t, hipStream_t s) {
     // key = tau << row_bits | row, in 32 bits when the widest table and the
@@ -650,8 +837,8 @@ hipError_t launch_bwd_table_grad(const BwdTableArgs &t, hipStream_t s) {
     while (row_bits < 32 && (max_row >> row_bits) != 0) ++row_bits;
     while ((1 << tau_bits) < t.n_tables) ++tau_bits;
     const int32_t key_bits = row_bits + tau_bits;
-    if (key_bits <= 32) return table_grad<uint32_t>(t, row_bits, key_bits, s);
-    return table_grad<uint64_t>(t, row_bits, key_bits, s);
+    if (key_bits <= 32) return table_grad<uint32_t>(t, row_bits, s);
+    return table_grad<uint64_t>(t, row_bits, s);
 }
 
 }  // namespace engram
