@@ -663,6 +663,37 @@ def test_backward_full_width_against_oracle(B, name, br, batch, seqlen):
     torch.cuda.empty_cache()
 
 
+def test_backward_table_rows_three_sort_passes(B):
+    """Tables of about 8.4M rows (24 row bits: three radix passes of 8 bits)
+    and 4,500 tokens, so each table's items span two full 2,048-item sort
+    blocks and a ragged third: rows, counts and row sums against the oracle."""
+    say("backward table rows, three sort passes")
+    wl = dataclasses.replace(small_wl(batch=3, seqlen=1500), table_target=8_400_000)
+    assert all(p >= 1 << 23 for p in wl.primes())
+    dl = make_device_layer(wl)
+    toks = W.make_tokens(wl)
+    n_tok = wl.n_tokens
+    idx = torch.zeros((n_tok, wl.n_tables), dtype=torch.int32, device="cuda")
+    dl.plan.engram_hash(dev_i32(toks), dl.comp_map, idx)
+    rng = np.random.default_rng(11)
+    dout = torch.from_numpy(rng.standard_normal((1, n_tok, wl.d_model)).astype(np.float32)).to(torch.bfloat16).cuda()
+    dh, g = _backward(dl, idx, dout)
+    idx_ref, _, _ = oracle_indices(wl, dl.li, toks, dl.comp_map_host)
+    assert np.array_equal(idx.cpu().numpy().view(np.uint32), idx_ref)
+    L = oracle_layer(wl, dl.li, idx_ref, wl.batch, wl.seqlen)
+    ref = L.backward(dout.float().cpu().numpy())
+    rows, grads, counts = oracle.table_grad(idx_ref, ref["demb"], wl.head_dim)
+    assert np.array_equal(g.row_counts.cpu().numpy(), counts)
+    got_rows = g.row_ids.cpu().numpy().view(np.uint32)
+    got_grads = g.row_grads.cpu().numpy()
+    for tau in range(wl.n_tables):
+        c = int(counts[tau])
+        assert np.array_equal(got_rows[tau, :c], rows[tau, :c]), tau
+        grad_within(got_grads[tau, :c], grads[tau, :c], "table %d rows" % tau)
+    del dl
+    torch.cuda.empty_cache()
+
+
 def test_backward_full_size_rows_and_determinism(B):
     """32,768 tokens of the small config: the listed rows of every table are
     exactly the distinct slots the tokens hashed to (ascending), and a second
