@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
     ap.add_argument("--breakdown-steps", type=int, default=20,
                     help="steps of the separate pass that times every kernel")
+    ap.add_argument("--timed-every", type=int, default=4,
+                    help="in the measured run, time one launch in this many of the dominant kernel (events "
+                         "in a dispatch delay the launches around it)")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time only whole steps (no per-launch events; no roofline)")
     ap.add_argument("--retrieve-in-projection", action="store_true",
@@ -203,11 +206,13 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    def timed(steps, kinds):
+    def timed(steps, kinds, every=1):
         """steps steps between a barrier + synchronize on both sides; launches
-        of `kinds` (None: all, []: none) timed by their own dispatch events."""
+        of `kinds` (None: all, []: none) timed by their own dispatch events,
+        one launch in `every` of each kind."""
         if kinds != []:
             for dl, *_ in layers:
+                dl.plan.engram_profile_every(every)
                 dl.plan.engram_profile_begin(8 * steps + 64, kinds)
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         if torch.distributed.is_available() and torch.distributed.is_initialized():
@@ -245,7 +250,7 @@ def main():
     _, _, profs_all = timed(args.breakdown_steps, None)
     kern = kern_of(profs_all)
     dominant = max(("gather", "gemm", "gate", "gemm_v", "seam", "fuse"), key=lambda k: kern(k)[0] * kern(k)[1])
-    wall, gpu_ms, profs = timed(args.steps, [dominant])
+    wall, gpu_ms, profs = timed(args.steps, [dominant], max(1, args.timed_every))
     kern_dom = kern_of(profs)
 
     ms_per_step = wall * 1e3 / args.steps
@@ -318,9 +323,10 @@ def main():
         ach = work / (ms * 1e-3) / 1e12
     else:
         ach = work / (ms * 1e-3) / 1e9
+    per_step = kern(dom)[1] / args.breakdown_steps  # launches of the kernel per step
     roofline.update({"achieved": round(ach, 2), "frac": round(ach / roofline["peak"], 4),
-                     "avg_launch_us": round(ms * 1e3, 2), "launches": n,
-                     "ms_per_step": round(ms * n / args.steps, 4), "timed_in": "measured run"})
+                     "avg_launch_us": round(ms * 1e3, 2), "launches": n, "timed_every": max(1, args.timed_every),
+                     "ms_per_step": round(ms * per_step, 4), "timed_in": "measured run"})
     if dom in mem_bytes:
         gbs = mem_bytes[dom] / (ms * 1e-3) / 1e9
         roofline.update({"hbm_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})

@@ -114,6 +114,8 @@ def lib() -> C.CDLL:
         L.engram_profile_begin.argtypes = [P, i32, u32]
         L.engram_profile_end.restype = C.c_int
         L.engram_profile_end.argtypes = [P, C.POINTER(ProfileC)]
+        L.engram_profile_every.restype = C.c_int
+        L.engram_profile_every.argtypes = [P, i32]
         L.engram_host_alloc.restype = C.c_int
         L.engram_host_alloc.argtypes = [C.c_size_t, C.POINTER(C.c_void_p)]
         L.engram_host_free.restype = C.c_int
@@ -412,6 +414,10 @@ class Plan:
         """Time launches of the named kinds (KERNEL_NAMES; None: all)."""
         mask = 0 if kinds is None else sum(1 << KERNEL_NAMES.index(k) for k in kinds)
         _check("engram_profile_begin", lib().engram_profile_begin(self._h, max_launches, mask))
+
+    def engram_profile_every(self, every: int):
+        """Time one launch in `every` of each selected kind (1: all)."""
+        _check("engram_profile_every", lib().engram_profile_every(self._h, every))
 
     def engram_profile_end(self) -> Dict[str, Dict[str, float]]:
         p = ProfileC()

@@ -516,10 +516,17 @@ engram_status engram_profile_begin(engram_plan p, int32_t max_launches, uint32_t
             if (hipEventCreate(&e) != hipSuccess) return ENGRAM_E_DEVICE;
     }
     p->prof_kind.assign(max_launches, 0);
+    for (int64_t &c : p->prof_seen) c = 0;
     p->prof_max = max_launches;
     p->prof_used = 0;
     p->prof_dropped = 0;
     p->prof_on = true;
+    return ENGRAM_OK;
+}
+
+engram_status engram_profile_every(engram_plan p, int32_t every) {
+    if (!p || every < 1) return ENGRAM_E_INVALID_ARG;
+    p->prof_every = every;
     return ENGRAM_OK;
 }
 

@@ -25,6 +25,8 @@ struct engram_plan_s {
     int32_t prof_max = 0;
     int32_t prof_used = 0;
     int64_t prof_dropped = 0;
+    int32_t prof_every = 1;                 // time one launch in prof_every of each kind
+    int64_t prof_seen[ENGRAM_K_COUNT] = {};  // launches of each selected kind since profiling began
     std::vector<hipEvent_t> prof_ev;
     std::vector<int32_t> prof_kind;
 };
@@ -43,6 +45,7 @@ struct Launch {
     int32_t slot = -1;
     Launch(engram_plan_s &pl, int32_t kind, hipStream_t) : p(pl) {
         if (!p.prof_on || !((p.prof_mask >> kind) & 1u)) return;
+        if (p.prof_seen[kind]++ % p.prof_every != 0) return;
         if (p.prof_used < p.prof_max) {
             slot = p.prof_used++;
             p.prof_kind[slot] = kind;

@@ -370,6 +370,14 @@ ENGRAM_API engram_status engram_backward(engram_plan p, const uint32_t *d_idx, c
  */
 ENGRAM_API engram_status engram_profile_begin(engram_plan p, int32_t max_launches, uint32_t kind_mask);
 ENGRAM_API engram_status engram_profile_end(engram_plan p, engram_profile *out);
+/*
+ * Sampling for the profiling above: from the next engram_profile_begin on,
+ * only the first launch of every `every` launches of each selected kind is
+ * timed (1, the default, times them all), so that timing a kind inside a
+ * measured loop adds its event overhead to one launch in `every`.  The
+ * setting stays until changed.  ENGRAM_E_INVALID_ARG for every < 1.
+ */
+ENGRAM_API engram_status engram_profile_every(engram_plan p, int32_t every);
 
 #ifdef __cplusplus
 }

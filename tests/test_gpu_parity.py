@@ -536,6 +536,16 @@ def test_profiling_counts_launches(B):
         for k, n in (("hash", 0), ("gather", 2), ("gemm", 2), ("gate", 1), ("fuse", 1), ("gemm_v", 1),
                      ("seam", seams), ("aux", 0)):
             assert prof[k]["launches"] == n, (seqlen, k, prof)
+    # sampled timing: one launch in three of each selected kind (the 1st, 4th, 7th)
+    dl.plan.engram_profile_every(3)
+    dl.plan.engram_profile_begin(64, ["gemm", "gemm_v"])
+    for _ in range(7):
+        forward(dl, toks)
+    torch.cuda.synchronize()
+    prof = dl.plan.engram_profile_end()
+    dl.plan.engram_profile_every(1)
+    assert prof["gemm"]["launches"] == 3 and prof["gemm_v"]["launches"] == 3, prof
+    assert prof["gather"]["launches"] == 0 and prof["dropped"] == 0, prof
 
 
 def test_unsupported_bf16_shape_is_rejected(B):
