@@ -14,7 +14,7 @@ using namespace engram::host;
 namespace {
 
 struct BwdLayout {
-    size_t E, KV, stats, dalpha, dconv, dg, dkv, wt, et, dkvt, demb, keys_in, keys_out, vals_in, vals_out, head,
+    size_t E, KV, stats, dalpha, dconv, dg, dkv, wt, demb, keys_in, keys_out, vals_in, vals_out, head,
         incl, temp, sum_part, dw_part, lead, tail, cflags, tinfo, total;
     size_t temp_bytes;
     int64_t n_pad;
@@ -53,8 +53,6 @@ engram_status bwd_layout_of(const engram_plan_s &p, int32_t batch, int32_t seqle
     L.dg = take((size_t)(2 * Br * L.gate_chunks * d * 4));
     L.dkv = take((size_t)(n_tok * N * 2));
     L.wt = take((size_t)(De * N * 2));
-    L.et = take((size_t)(De * n_pad * 2));
-    L.dkvt = take((size_t)(N * n_pad * 2));
     L.demb = take((size_t)(n_tok * De * 4));
     L.keys_in = take((size_t)n_items * 8);
     L.keys_out = take((size_t)n_items * 8);
@@ -119,8 +117,6 @@ engram_status engram_backward(engram_plan p, const uint32_t *d_idx, const void *
     float *KV = reinterpret_cast<float *>(base + L.KV);
     uint16_t *dkv = reinterpret_cast<uint16_t *>(base + L.dkv);
     uint16_t *wt = reinterpret_cast<uint16_t *>(base + L.wt);
-    uint16_t *et = reinterpret_cast<uint16_t *>(base + L.et);
-    uint16_t *dkvt = reinterpret_cast<uint16_t *>(base + L.dkvt);
     float *demb = reinterpret_cast<float *>(base + L.demb);
     engram_plan_s &P = *p;
 
@@ -174,7 +170,8 @@ engram_status engram_backward(engram_plan p, const uint32_t *d_idx, const void *
     ba.eps = p->cfg.rms_eps;
     {
         // gate statistics, the conv / gated value and the gate / RMSNorm
-        // backward, the small gradients' reductions and the operand transposes
+        // backward, the small gradients' reductions and W's transpose (the
+        // dE operand; dW reads E and [dk | dv] as they are)
         Launch l(P, ENGRAM_K_BWD_FUSE, stream);
         launch_bwd_gate_stats(ba, stream);
         launch_bwd_conv(ba, stream);
@@ -187,8 +184,6 @@ engram_status engram_backward(engram_plan p, const uint32_t *d_idx, const void *
         for (int m = 0; m <= Br; ++m)
             launch_bwd_transpose(static_cast<const uint16_t *>(m < Br ? w->w_k[m] : w->w_v), d, De, De,
                                  wt + (int64_t)m * d, N, d, stream);
-        launch_bwd_transpose(static_cast<const uint16_t *>(E), n_tok, De, De, et, L.n_pad, L.n_pad, stream);
-        launch_bwd_transpose(dkv, n_tok, N, N, dkvt, L.n_pad, L.n_pad, stream);
     }
     if (last_launch_status() != ENGRAM_OK) return ENGRAM_E_DEVICE;
     {
@@ -206,20 +201,24 @@ engram_status engram_backward(engram_plan p, const uint32_t *d_idx, const void *
         pe.n_rows = De;
         launch_proj_plain_bf16(pe, stream);
         // dW contracts over every token: few output tiles, so K is split
-        // until the chip is full and the partial results summed in order
+        // until the chip is full and the partial results summed in order.
+        // Both operands are token-major, i.e. K-major for this contraction
+        // (tokens past n_tok up to n_pad read as zeros).
         ProjArgs pw{};
-        pw.emb = dkvt;
-        for (int m = 0; m <= kMaxBranches; ++m) pw.w[m] = et;
+        pw.emb = dkv;
+        for (int m = 0; m <= kMaxBranches; ++m) pw.w[m] = E;
         pw.n_tok = N;
         pw.K = (int32_t)(L.n_pad / L.dw_splits);
-        pw.k_ld = (int32_t)L.n_pad;
+        pw.k_rows = n_tok;
+        pw.w_ld = De;
+        pw.e_ld = (int32_t)N;
         pw.d = De;
         pw.n_mats = 1;
         pw.out_f32 = L.dw_splits > 1 ? reinterpret_cast<float *>(base + L.dw_part) : g->dw;
         pw.out_ld = De;
         pw.out_split = N * De;
         pw.n_rows = De;
-        launch_proj_plain_bf16(pw, stream, L.dw_splits);
+        launch_proj_plain_kmajor_bf16(pw, stream, L.dw_splits);
         if (L.dw_splits > 1)
             launch_bwd_sum_parts(reinterpret_cast<float *>(base + L.dw_part), 1, N * De, L.dw_splits, g->dw, stream);
     }

@@ -166,6 +166,10 @@ struct ProjArgs {
     // stores at out_f32 + z * out_split (k_ld 0: one launch, rows K long)
     int32_t k_ld;
     int64_t out_split;
+    // mode 4 (both operands K-major): w[0] is [k_rows][w_ld] and emb
+    // [k_rows][e_ld]; row k of each holds that k for every column
+    int64_t k_rows;
+    int32_t w_ld, e_ld;
     // retrieval inside the launch (mode 2): every block hashes its tokens'
     // n-grams and reads its E operand straight from the table rows
     const int32_t *tokens;                 // [batch][seqlen] raw ids
@@ -202,6 +206,11 @@ void launch_proj_v_fused_bf16(const ProjArgs &a, hipStream_t s);
 // splits > 1: a.K is the share of each of the splits launches (a.k_ld =
 // splits * a.K), each storing its own partial result (see ProjArgs).
 void launch_proj_plain_bf16(const ProjArgs &a, hipStream_t s, int splits = 1);
+// The same contraction with both operands stored K-major: C[t][n] = sum_k
+// w[0][k][n] emb[k][t] over k in [z K, (z+1) K) for launch z of `splits`
+// (k-rows past k_rows count as zero); fp32 out as above.  K % 128 == 0,
+// w_ld, e_ld and the column counts multiples of 8.
+void launch_proj_plain_kmajor_bf16(const ProjArgs &a, hipStream_t s, int splits = 1);
 // How many K splits fill the chip for a plain contraction of n_tok x rows
 // outputs over K (a power of two; K / splits stays a multiple of 128).
 int plain_k_splits(int64_t n_tok, int64_t rows, int64_t K);

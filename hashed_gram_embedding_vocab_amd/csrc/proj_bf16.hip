@@ -6,6 +6,13 @@
 //   mode 0: the weight rows of the launch's matrices (all W_k^(m), optionally
 //     followed by W_v) form the N dimension; W_k tiles leave gate partials,
 //     W_v tiles store v.
+//   mode 3: a plain contraction C[t][n] = sum_k W[n][k] E[t][k], fp32 out
+//     (the backward's k, v and dE), optionally split over K.
+//   mode 4: the same with both operands stored K-major (W^T and E^T, rows
+//     of k): the backward's dW = [dk | dv]^T E contracts over tokens, and
+//     both of its operands are token-major in memory.  The stages hold 32
+//     k-rows of the tile's columns and the fragments come from transposing
+//     LDS reads (ds_read_b64_tr_b16), so no operand is transposed in HBM.
 //   mode 1: W_v only, with the rest of the fusion step in the epilogue:
 //     alpha from the gate partials of a preceding mode-0 launch, u = alpha v,
 //     the short depthwise causal conv over tokens, the residual into h and
@@ -93,6 +100,22 @@ struct __attribute__((aligned(1024))) StageT {
 typedef StageT<kOperandBytes> Stage;
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+// Mode 4 stages: k-row kr of an operand is RB = 2 x (tile columns) bytes of
+// LDS, 16-byte chunks; chunk pair q (columns 16q..16q+15) of row kr sits at
+// pair position q ^ kswz(kr).  One transposing read covers 16 k-rows
+// kr = 8g + 4h + r (g, r = 0..3) of one column block; kswz sends them to
+// distinct pair positions (16 in a 512-byte row, 8 in a 256-byte one).
+template <int PAIRS>
+__device__ __forceinline__ int kswz(int kr) {
+    return ((kr & 3) | (((kr >> 3) & 3) << 2)) & (PAIRS - 1);
+}
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4_t lds_read_tr(const unsigned char *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) bf16x4_t *)(const_cast<unsigned char *>(p)));
+}
 
 // Hardware hands consecutive block ids to the 8 XCDs round-robin.  Remap so
 // every XCD walks one contiguous range of the logical tile order (its own
@@ -472,7 +495,9 @@ __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t 
 template <int MODE, int BR, bool SILU, bool NARROW>
 __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_bf16_kernel(ProjArgs a) {
     static_assert(!(NARROW && MODE == 1), "the fused value epilogue is written for the wide tile");
-    static_assert(MODE == 0 || MODE == 1 || MODE == 2 || MODE == 3, "mode");
+    static_assert(MODE >= 0 && MODE <= 4, "mode");
+    constexpr bool kKMaj = MODE == 4;                // both operands stored K-major
+    constexpr bool kPlain = MODE == 3 || MODE == 4;  // fp32 store epilogue
     static_assert(MODE != 2 || NARROW, "retrieval inside the launch is written for the narrow tile");
     constexpr bool kGather = MODE == 2;
     constexpr bool kGateK = MODE == 0 || MODE == 2;  // W_k / W_v launch with the gate-partial epilogue
@@ -515,9 +540,12 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
     const char *wmat = reinterpret_cast<const char *>(pick(a.w, mat0));
     // operand row length (a split-K launch reads its share of longer rows)
     const int ld = (MODE == 3 && a.k_ld > 0) ? a.k_ld : K;
-    const int kbase = MODE == 3 ? (int)blockIdx.y * K : 0;
-    const __amdgpu_buffer_rsrc_t wres = make_rsrc(wmat, (uint32_t)d * ld * 2u);
-    const __amdgpu_buffer_rsrc_t eres = make_rsrc(a.emb, (uint32_t)(a.n_tok * ld * 2));
+    const int kbase = kPlain ? (int)blockIdx.y * K : 0;
+    // mode 4: operands [k_rows][w_ld] and [k_rows][e_ld]; k-rows past k_rows read as zeros
+    const __amdgpu_buffer_rsrc_t wres =
+        kKMaj ? make_rsrc(wmat, (uint32_t)(a.k_rows * a.w_ld * 2)) : make_rsrc(wmat, (uint32_t)d * ld * 2u);
+    const __amdgpu_buffer_rsrc_t eres = kKMaj ? make_rsrc(a.emb, (uint32_t)(a.k_rows * a.e_ld * 2))
+                                              : make_rsrc(a.emb, (uint32_t)(a.n_tok * ld * 2));
     // (a template-dependent bound here keeps the host pass from emitting the
     // kernel's launch stub, so the bound is the namespace constant both tiles share)
     static_assert(TBPW == kBlocksPerWave, "two row blocks per wave and operand in both tiles");
@@ -532,6 +560,16 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
         const int64_t t = min(max(t0 + trow, (int64_t)0), a.n_tok - 1);
         woff[i] = (uint32_t)((n0 - mat0 * d + row) * ld + lchunk * 8) * 2u;
         eoff[i] = (uint32_t)(t * ld + lchunk * 8) * 2u;
+        if constexpr (kKMaj) {
+            // instruction i of this wave fills k-rows RPI (TBPW wave + i) + lane / LPR,
+            // LDS chunk lane % LPR of each, which holds the tile's column chunk
+            // (lane % LPR) ^ 2 kswz(kr)
+            constexpr int LPR = TBN / 8, RPI = 64 / LPR;
+            const int kr = RPI * blk + lane / LPR;
+            const int ch = (lane % LPR) ^ (2 * kswz<TBN / 16>(kr));
+            woff[i] = (uint32_t)((int64_t)kr * a.w_ld + n0 + 8 * ch) * 2u;
+            eoff[i] = (uint32_t)((int64_t)kr * a.e_ld + t0 + 8 * ch) * 2u;
+        }
     }
 
     // Mode 2: the slots of the tile's tokens (tokens past n_tok: slot 0) and
@@ -607,6 +645,16 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
                 goff -= c ? (int)(g_row_bytes / 2u) : 0;                                         \
                 gtau += c ? 1 : 0;                                                               \
             }                                                                                    \
+        } else if constexpr (kKMaj) {                                                            \
+            const int kw = (kbase + (k0)) * a.w_ld * 2, ke = (kbase + (k0)) * a.e_ld * 2;         \
+            _Pragma("unroll") for (int i = 0; i < TBPW; ++i) {                                   \
+                const int blk = wave * TBPW + i;                                                 \
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void_t *)&STG.w[blk * kBlockBytes], \
+                                                         16, woff[i], kw, 0, 0);                 \
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(eres, (lds_void_t *)&STG.e[blk * kBlockBytes], \
+                                                         16, eoff[i], ke, 0, 0);                 \
+            }                                                                                    \
+            (void)kbytes;                                                                        \
         } else {                                                                                 \
             _Pragma("unroll") for (int i = 0; i < TBPW; ++i) {                                   \
                 const int blk = wave * TBPW + i;                                                 \
@@ -630,13 +678,36 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
     const int fr = lane & 15;                    // fragment row
     const int fpos = fr * 64 + ((lane >> 4) ^ swz(fr)) * 16;  // byte offset inside a 1 KB block
 
+    // mode 4 fragment of column block q: lane 16g + m takes k-rows 8g + 4h + m/4
+    // (h = 0, 1), columns 16q + 4(m % 4) .. + 3 of each; the transposing read
+    // hands lane 16g + m column 16q + m at k = 8g .. 8g + 7
+    constexpr int kRowBytes = TBN * 2;
+    int tr_row[2], tr_sw[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int kr = 8 * (lane >> 4) + 4 * h + ((lane & 15) >> 2);
+        tr_row[h] = kr * kRowBytes + ((lane & 3) >> 1) * 16 + (lane & 1) * 8;
+        tr_sw[h] = kswz<TBN / 16>(kr);
+    }
+    auto frag_tr = [&](const unsigned char *opnd, int q) -> bf16x8_t {
+        const bf16x4_t lo = lds_read_tr(opnd + tr_row[0] + ((q ^ tr_sw[0]) << 5));
+        const bf16x4_t hi = lds_read_tr(opnd + tr_row[1] + ((q ^ tr_sw[1]) << 5));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    (void)frag_tr;
+
 #define ENGRAM_COMPUTE(STG)                                                                      \
     do {                                                                                         \
         bf16x8_t fa[FN], fb[TFT];                                                                 \
-        _Pragma("unroll") for (int i = 0; i < FN; ++i) fa[i] =                                   \
-            *reinterpret_cast<const bf16x8_t *>(&STG.w[(wn_blk + i) * kBlockBytes + fpos]);      \
-        _Pragma("unroll") for (int j = 0; j < TFT; ++j) fb[j] =                                   \
-            *reinterpret_cast<const bf16x8_t *>(&STG.e[(wt_blk + j) * kBlockBytes + fpos]);      \
+        if constexpr (kKMaj) {                                                                   \
+            _Pragma("unroll") for (int i = 0; i < FN; ++i) fa[i] = frag_tr(STG.w, wn_blk + i);   \
+            _Pragma("unroll") for (int j = 0; j < TFT; ++j) fb[j] = frag_tr(STG.e, wt_blk + j);   \
+        } else {                                                                                 \
+            _Pragma("unroll") for (int i = 0; i < FN; ++i) fa[i] =                               \
+                *reinterpret_cast<const bf16x8_t *>(&STG.w[(wn_blk + i) * kBlockBytes + fpos]);  \
+            _Pragma("unroll") for (int j = 0; j < TFT; ++j) fb[j] =                               \
+                *reinterpret_cast<const bf16x8_t *>(&STG.e[(wt_blk + j) * kBlockBytes + fpos]);  \
+        }                                                                                        \
         _Pragma("unroll") for (int i = 0; i < FN; ++i)                                           \
             _Pragma("unroll") for (int j = 0; j < TFT; ++j)                                       \
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0); \
@@ -759,7 +830,7 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
     //      of token t = tw + 16j + lane%16.
     const int sub = 4 * (lane >> 4);
 
-    if constexpr (MODE == 3) {
+    if constexpr (kPlain) {
         // plain contraction: every tile stores its fp32 block, four
         // consecutive rows n (16 bytes) of one token t per lane and block
         float *out = a.out_f32 + (int64_t)blockIdx.y * a.out_split;
@@ -866,6 +937,19 @@ void launch_proj_plain_bf16(const ProjArgs &a, hipStream_t s, int splits) {
                       a);
     } else {
         launch_kernel((proj_bf16_kernel<3, 1, false, false>), dim3((unsigned)wide, (unsigned)splits),
+                      dim3(kThreads), s, a);
+    }
+}
+
+void launch_proj_plain_kmajor_bf16(const ProjArgs &a, hipStream_t s, int splits) {
+    const int n_total = a.n_mats * a.d;
+    const int64_t wide = (int64_t)((n_total + BN - 1) / BN) * ((a.n_tok + BT - 1) / BT);
+    if (!plain_wide(wide, splits)) {
+        const int64_t blocks = (int64_t)((n_total + 127) / 128) * ((a.n_tok + 127) / 128);
+        launch_kernel((proj_bf16_kernel<4, 1, false, true>), dim3((unsigned)blocks, (unsigned)splits), dim3(256), s,
+                      a);
+    } else {
+        launch_kernel((proj_bf16_kernel<4, 1, false, false>), dim3((unsigned)wide, (unsigned)splits),
                       dim3(kThreads), s, a);
     }
 }
