@@ -9,11 +9,14 @@
 //                          branches of alpha du, and the conv taps' gradient
 //   bwd_gate_kernel        ds = dalpha alpha (1 - alpha), then both RMSNorms
 //                          backwards: dh, dk and the gammas' gradients
-//   bwd_transpose_kernel   operands of dE = [dk | dv] W and dW = [dk | dv]^T E
-//                          made K-contiguous for the MFMA main loop
-//   table rows             (table, row) keys sorted stably, one wave per run of
-//                          equal keys adds the tokens' dE slices in token order
-// The contractions themselves run on proj_bf16.hip's main loop (plain mode).
+//   bwd_transpose_kernel   W transposed, so the dE = [dk | dv] W operand is
+//                          K-contiguous for the MFMA main loop
+//   table rows             (table, row) keys sorted stably by a segmented
+//                          radix sort; fixed 64-item chunks of the sorted items
+//                          add the tokens' dE slices in token order
+// The contractions themselves run on proj_bf16.hip's main loop: plain mode
+// for k, v and dE, K-major mode for dW (its operands E and [dk | dv] are
+// token-major, the contraction runs over tokens).
 #include <cstring>
 
 #include <rocprim/device/device_scan.hpp>
