@@ -14,7 +14,7 @@ using namespace engram::host;
 namespace {
 
 struct BwdLayout {
-    size_t E, KV, stats, dalpha, dconv, dg, dkv, wt, demb, keys_in, keys_out, vals_in, vals_out, head,
+    size_t E, KV, parts, stats, dalpha, dconv, dg, dkv, wt, demb, keys_in, keys_out, vals_in, vals_out, head,
         incl, temp, sum_part, dw_part, lead, tail, cflags, tinfo, total;
     size_t temp_bytes;
     int64_t n_pad;
@@ -47,6 +47,7 @@ engram_status bwd_layout_of(const engram_plan_s &p, int32_t batch, int32_t seqle
     };
     L.E = take((size_t)(n_tok * De * 2));
     L.KV = take((size_t)(n_tok * N * 4));
+    L.parts = take((size_t)(Br * (d / 128) * 3 * n_tok * 4));
     L.stats = take((size_t)(4 * Br * n_tok * 4));
     L.dalpha = take((size_t)(Br * L.n_stripes * n_tok * 4));
     L.dconv = take((size_t)L.conv_blocks * (size_t)(d * p.cfg.conv_kernel * 4));
@@ -123,11 +124,20 @@ engram_status engram_backward(engram_plan p, const uint32_t *d_idx, const void *
     // retrieval again: E of the chunk
     st = do_gather(P, d_idx, n_tok, table_ptrs, E, stream);
     if (st != ENGRAM_OK) return st;
-    // k of every branch and v, fp32
+    // k of every branch and v, fp32, and the gate partial sums of the W_k
+    // rows (the forward's: h gamma_h gamma_k k, k^2, h^2 per 128 channels)
+    float *parts = reinterpret_cast<float *>(base + L.parts);
     {
         ProjArgs pa{};
         pa.emb = E;
         for (int m = 0; m <= kMaxBranches; ++m) pa.w[m] = m < Br ? w->w_k[m] : w->w_v;
+        for (int m = 0; m < kMaxBranches; ++m) {
+            pa.gamma_h[m] = w->gamma_h[m < Br ? m : 0];
+            pa.gamma_k[m] = w->gamma_k[m < Br ? m : 0];
+        }
+        pa.h = d_h;
+        pa.partials = parts;
+        pa.n_parts = d / 128;
         pa.n_tok = n_tok;
         pa.K = De;
         pa.d = d;
@@ -137,7 +147,7 @@ engram_status engram_backward(engram_plan p, const uint32_t *d_idx, const void *
         pa.out_ld = N;
         pa.n_rows = (int32_t)N;
         Launch l(P, ENGRAM_K_BWD_GEMM, stream);
-        launch_proj_plain_bf16(pa, stream);
+        launch_proj_kv_partials_bf16(pa, stream);
     }
     if (last_launch_status() != ENGRAM_OK) return ENGRAM_E_DEVICE;
 
@@ -148,6 +158,8 @@ engram_status engram_backward(engram_plan p, const uint32_t *d_idx, const void *
     ba.kv = KV;
     ba.kv_ld = N;
     ba.stats = reinterpret_cast<float *>(base + L.stats);
+    ba.partials = parts;
+    ba.n_parts = d / 128;
     ba.dalpha_part = reinterpret_cast<float *>(base + L.dalpha);
     ba.dconv_part = reinterpret_cast<float *>(base + L.dconv);
     ba.dg_part = reinterpret_cast<float *>(base + L.dg);

@@ -3,7 +3,7 @@
 // gradients that reach them).  The derivative of the forward of
 // proj_bf16.hip / fuse.hip, for whole sequences (no carried state):
 //   bwd_gate_stats_kernel  rh, rk, s and alpha of every token and branch, from
-//                          h and the recomputed k
+//                          the gate partials that the k/v recompute leaves
 //   bwd_conv_kernel        dconv from dout, du through the transposed
 //                          (anti-causal) conv, dalpha = <v, du>, dv = sum over
 //                          branches of alpha du, and the conv taps' gradient
@@ -60,50 +60,30 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 // ---------------------------------------------------------------- gate statistics
 // One workgroup per (token, branch).  stats = [rh | rk | s | alpha], each [B_r][n_tok].
+// One thread per (token, branch): the three sums over d (h gamma_h gamma_k k,
+// k^2, h^2), added part by part in order from the k/v projection's
+// per-128-channel partials, give rh, rk, s and alpha.
 __global__ __launch_bounds__(256) void bwd_gate_stats_kernel(BwdArgs a) {
-    __shared__ float red[3][4];
-    const int64_t t = blockIdx.x;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int m = blockIdx.y;
+    if (t >= a.n_tok) return;
+    const float *pp = a.partials + (int64_t)m * a.n_parts * 3 * a.n_tok + t;
+    float shk = 0.f, skk = 0.f, shh = 0.f;
+    for (int q = 0; q < a.n_parts; ++q) {
+        shk += pp[(3 * q + 0) * a.n_tok];
+        skk += pp[(3 * q + 1) * a.n_tok];
+        shh += pp[(3 * q + 2) * a.n_tok];
+    }
     const int d = a.d;
-    const float *gh = pick_arg(a.gamma_h, m), *gk = pick_arg(a.gamma_k, m);
-    const float *k = a.kv + t * a.kv_ld + (int64_t)m * d;
-    float shh = 0.f, skk = 0.f, shk = 0.f;
-    for (int c = 4 * threadIdx.x; c < d; c += 4 * 256) {
-        const f32x4_t hv = load_bf16x4(a.h, ((int64_t)m * a.n_tok + t) * d + c);
-        const f32x4_t kv = *reinterpret_cast<const f32x4_t *>(k + c);
-        const f32x4_t g1 = *reinterpret_cast<const f32x4_t *>(gh + c);
-        const f32x4_t g2 = *reinterpret_cast<const f32x4_t *>(gk + c);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            shh += hv[r] * hv[r];
-            skk += kv[r] * kv[r];
-            shk += (g1[r] * hv[r]) * (g2[r] * kv[r]);
-        }
-    }
-    shh = wave_sum(shh);
-    skk = wave_sum(skk);
-    shk = wave_sum(shk);
-    const int wave = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) {
-        red[0][wave] = shh;
-        red[1][wave] = skk;
-        red[2][wave] = shk;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const float sh = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
-        const float sk = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
-        const float dot = (red[2][0] + red[2][1]) + (red[2][2] + red[2][3]);
-        const float rh = sqrtf(sh / (float)d + a.eps);
-        const float rk = sqrtf(sk / (float)d + a.eps);
-        const float s = dot / (rh * rk) * rsqrtf((float)d);
-        const int64_t plane = (int64_t)a.n_branches * a.n_tok;
-        const int64_t i = (int64_t)m * a.n_tok + t;
-        a.stats[i] = rh;
-        a.stats[plane + i] = rk;
-        a.stats[2 * plane + i] = s;
-        a.stats[3 * plane + i] = sigmoid_b(s);
-    }
+    const float rh = sqrtf(shh / (float)d + a.eps);
+    const float rk = sqrtf(skk / (float)d + a.eps);
+    const float s = shk / (rh * rk) * rsqrtf((float)d);
+    const int64_t plane = (int64_t)a.n_branches * a.n_tok;
+    const int64_t i = (int64_t)m * a.n_tok + t;
+    a.stats[i] = rh;
+    a.stats[plane + i] = rk;
+    a.stats[2 * plane + i] = s;
+    a.stats[3 * plane + i] = sigmoid_b(s);
 }
 
 // ---------------------------------------------------------------- conv and gated value
@@ -711,7 +691,7 @@ __global__ __launch_bounds__(256) void bwd_row_chain_kernel(const float *lead, c
 }  // namespace
 
 void launch_bwd_gate_stats(const BwdArgs &a, hipStream_t s) {
-    launch_kernel(bwd_gate_stats_kernel, dim3((unsigned)a.n_tok, a.n_branches), dim3(256), s, a);
+    launch_kernel(bwd_gate_stats_kernel, dim3((unsigned)((a.n_tok + 255) / 256), a.n_branches), dim3(256), s, a);
 }
 
 void launch_bwd_conv(const BwdArgs &a, hipStream_t s) {

@@ -211,6 +211,10 @@ void launch_proj_plain_bf16(const ProjArgs &a, hipStream_t s, int splits = 1);
 // (k-rows past k_rows count as zero); fp32 out as above.  K % 128 == 0,
 // w_ld, e_ld and the column counts multiples of 8.
 void launch_proj_plain_kmajor_bf16(const ProjArgs &a, hipStream_t s, int splits = 1);
+// The plain contraction over the stacked [W_k^(m); W_v] (n_mats = n_branches
+// + 1, K = D_e, no split) that also leaves, for the W_k rows, the gate
+// partial sums of launch_proj_bf16 (h, gamma_h, gamma_k, partials, n_parts).
+void launch_proj_kv_partials_bf16(const ProjArgs &a, hipStream_t s);
 // How many K splits fill the chip for a plain contraction of n_tok x rows
 // outputs over K (a power of two; K / splits stays a multiple of 128).
 int plain_k_splits(int64_t n_tok, int64_t rows, int64_t K);
@@ -293,6 +297,8 @@ struct BwdArgs {
     const float *kv;                        // [n_tok][kv_ld]: k of every branch, then v (fp32)
     int64_t kv_ld;                          // (B_r + 1) d
     float *stats;                           // [4][B_r][n_tok]: rh, rk, s, alpha
+    const float *partials;                  // [B_r][n_parts][3][n_tok]: the k/v projection's gate partials
+    int32_t n_parts;                        // d / 128
     float *dalpha_part;                     // [B_r][n_stripes][n_tok]
     float *dconv_part;                      // [conv blocks][d][K_c]
     float *dg_part;                         // [2][B_r][gate chunks][d]: gamma_h, then gamma_k

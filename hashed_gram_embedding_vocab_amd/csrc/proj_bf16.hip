@@ -13,6 +13,8 @@
 //     both of its operands are token-major in memory.  The stages hold 32
 //     k-rows of the tile's columns and the fragments come from transposing
 //     LDS reads (ds_read_b64_tr_b16), so no operand is transposed in HBM.
+//   mode 5: mode 3 over [W_k^(m); W_v] whose W_k tiles also leave mode 0's
+//     gate partials (the backward's k and v, and its gate statistics).
 //   mode 1: W_v only, with the rest of the fusion step in the epilogue:
 //     alpha from the gate partials of a preceding mode-0 launch, u = alpha v,
 //     the short depthwise causal conv over tokens, the residual into h and
@@ -495,12 +497,12 @@ __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t 
 template <int MODE, int BR, bool SILU, bool NARROW>
 __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_bf16_kernel(ProjArgs a) {
     static_assert(!(NARROW && MODE == 1), "the fused value epilogue is written for the wide tile");
-    static_assert(MODE >= 0 && MODE <= 4, "mode");
+    static_assert(MODE >= 0 && MODE <= 5, "mode");
     constexpr bool kKMaj = MODE == 4;                // both operands stored K-major
-    constexpr bool kPlain = MODE == 3 || MODE == 4;  // fp32 store epilogue
+    constexpr bool kPlain = MODE == 3 || MODE == 4 || MODE == 5;  // fp32 store epilogue
     static_assert(MODE != 2 || NARROW, "retrieval inside the launch is written for the narrow tile");
     constexpr bool kGather = MODE == 2;
-    constexpr bool kGateK = MODE == 0 || MODE == 2;  // W_k / W_v launch with the gate-partial epilogue
+    constexpr bool kGateK = MODE == 0 || MODE == 2 || MODE == 5;  // W_k / W_v launch with the gate-partial epilogue
     typedef TileCfg<NARROW> C;
     constexpr int TBN = C::BN, TBT = C::BT, TTHREADS = C::kThreads, TWAVES = C::kWaves, TWGN = C::kWavesN;
     constexpr int TWT = C::WT, TFT = C::FT, TOPB = C::kOperandBytes, TBPW = C::kBlocksPerWave;
@@ -830,21 +832,9 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
     //      of token t = tw + 16j + lane%16.
     const int sub = 4 * (lane >> 4);
 
-    if constexpr (kPlain) {
-        // plain contraction: every tile stores its fp32 block, four
-        // consecutive rows n (16 bytes) of one token t per lane and block
-        float *out = a.out_f32 + (int64_t)blockIdx.y * a.out_split;
-#pragma unroll
-        for (int j = 0; j < TFT; ++j) {
-            const int64_t t = tw + 16 * j + (lane & 15);
-            if (t >= a.n_tok) continue;
-#pragma unroll
-            for (int i = 0; i < FN; ++i) {
-                const int n = nw + 16 * i + sub;
-                if (n < a.n_rows) *reinterpret_cast<f32x4_t *>(out + t * a.out_ld + n) = acc[i][j];
-            }
-        }
-    } else if constexpr (kGateK) {
+    // gate partials first (mode 5 then also stores k): the partial sums wait
+    // for all of this wave's memory operations, which the stores would join
+    if constexpr (kGateK) {
     if (mat < a.n_branches) {
         // gate partials of branch `mat` over channels [nl, nl+128).
         // gamma_h * gamma_k for the wave's channels goes through LDS, so it
@@ -893,7 +883,7 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
                 pbase[2 * a.n_tok + t] = s_hh;
             }
         }
-    } else {
+    } else if constexpr (!kPlain) {
         // v = W_v e, kept fp32 [n_tok][d]: rounding it to bf16 here would add
         // up to half a bf16 ulp of |v| to every gated value the conv sums.
 #pragma unroll
@@ -905,7 +895,22 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
                 *reinterpret_cast<f32x4_t *>(a.v + t * d + nl + 16 * i + sub) = acc[i][j];
         }
     }
-    } else {
+    }
+    if constexpr (kPlain) {
+        // plain contraction: every tile stores its fp32 block, four
+        // consecutive rows n (16 bytes) of one token t per lane and block
+        float *out = a.out_f32 + (int64_t)blockIdx.y * a.out_split;
+#pragma unroll
+        for (int j = 0; j < TFT; ++j) {
+            const int64_t t = tw + 16 * j + (lane & 15);
+            if (t >= a.n_tok) continue;
+#pragma unroll
+            for (int i = 0; i < FN; ++i) {
+                const int n = nw + 16 * i + sub;
+                if (n < a.n_rows) *reinterpret_cast<f32x4_t *>(out + t * a.out_ld + n) = acc[i][j];
+            }
+        }
+    } else if constexpr (!kGateK) {
         // each wave's two chunk buffers: 8 KB of st0/st1 (A) and of st2/st3 (B)
         fused_value_epilogue<BR, SILU>(a, acc, alpha_s, halo_s, taps_s, hA, hB, wave, lane, nl, n0, tile_t, t0);
     }
@@ -938,6 +943,17 @@ void launch_proj_plain_bf16(const ProjArgs &a, hipStream_t s, int splits) {
     } else {
         launch_kernel((proj_bf16_kernel<3, 1, false, false>), dim3((unsigned)wide, (unsigned)splits),
                       dim3(kThreads), s, a);
+    }
+}
+
+void launch_proj_kv_partials_bf16(const ProjArgs &a, hipStream_t s) {
+    const int n_total = a.n_mats * a.d;
+    const int64_t wide = (int64_t)((n_total + BN - 1) / BN) * ((a.n_tok + BT - 1) / BT);
+    if (wide < 256) {
+        const int64_t blocks = (int64_t)((n_total + 127) / 128) * ((a.n_tok + 127) / 128);
+        launch_kernel((proj_bf16_kernel<5, 1, false, true>), dim3((unsigned)blocks), dim3(256), s, a);
+    } else {
+        launch_kernel((proj_bf16_kernel<5, 1, false, false>), dim3((unsigned)wide), dim3(kThreads), s, a);
     }
 }
 
