@@ -250,3 +250,20 @@ def test_prefetcher_argument_checks(B):
     assert L.engram_prefetcher_destroy(None) == B.E_INVALID_ARG
     assert L.engram_prefetch_begin(None, fake, 10, None) == B.E_INVALID_ARG
     assert L.engram_prefetch_finish(None, fake, None, None) == B.E_INVALID_ARG
+
+
+def test_profiling_argument_checks(B):
+    """Profiling control is host-only: a null plan, a non-positive launch
+    budget, an unknown kind bit and a sampling period below one are refused;
+    the sampling period itself is accepted without a device."""
+    L = B.lib()
+    p = B.Plan(vocab=1000, vocab_comp=770, heads=4, head_dim=32, table_rows=[10007] * 8, hash_seed=1,
+               d_model=256, dtype=B.F32)
+    assert L.engram_profile_every(None, 2) == B.E_INVALID_ARG
+    assert L.engram_profile_every(p._h, 0) == B.E_INVALID_ARG
+    assert L.engram_profile_every(p._h, -4) == B.E_INVALID_ARG
+    assert L.engram_profile_every(p._h, 3) == 0
+    assert L.engram_profile_every(p._h, 1) == 0
+    assert L.engram_profile_begin(None, 8, 0) == B.E_INVALID_ARG
+    assert L.engram_profile_begin(p._h, 0, 0) == B.E_INVALID_ARG
+    assert L.engram_profile_begin(p._h, 8, 1 << 30) == B.E_INVALID_ARG
