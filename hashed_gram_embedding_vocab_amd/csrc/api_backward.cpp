@@ -14,7 +14,7 @@ using namespace engram::host;
 namespace {
 
 struct BwdLayout {
-    size_t E, KV, parts, stats, dalpha, dconv, dg, dkv, wt, demb, keys_in, keys_out, vals_in, vals_out, head,
+    size_t E, KV, parts, stats, dalpha, dconv, dg, dkv, demb, keys_in, keys_out, vals_in, vals_out, head,
         incl, temp, sum_part, dw_part, lead, tail, cflags, tinfo, total;
     size_t temp_bytes;
     int64_t n_pad;
@@ -53,7 +53,6 @@ engram_status bwd_layout_of(const engram_plan_s &p, int32_t batch, int32_t seqle
     L.dconv = take((size_t)L.conv_blocks * (size_t)(d * p.cfg.conv_kernel * 4));
     L.dg = take((size_t)(2 * Br * L.gate_chunks * d * 4));
     L.dkv = take((size_t)(n_tok * N * 2));
-    L.wt = take((size_t)(De * N * 2));
     L.demb = take((size_t)(n_tok * De * 4));
     L.keys_in = take((size_t)n_items * 8);
     L.keys_out = take((size_t)n_items * 8);
@@ -117,7 +116,6 @@ engram_status engram_backward(engram_plan p, const uint32_t *d_idx, const void *
     void *E = base + L.E;
     float *KV = reinterpret_cast<float *>(base + L.KV);
     uint16_t *dkv = reinterpret_cast<uint16_t *>(base + L.dkv);
-    uint16_t *wt = reinterpret_cast<uint16_t *>(base + L.wt);
     float *demb = reinterpret_cast<float *>(base + L.demb);
     engram_plan_s &P = *p;
 
@@ -182,8 +180,8 @@ engram_status engram_backward(engram_plan p, const uint32_t *d_idx, const void *
     ba.eps = p->cfg.rms_eps;
     {
         // gate statistics, the conv / gated value and the gate / RMSNorm
-        // backward, the small gradients' reductions and W's transpose (the
-        // dE operand; dW reads E and [dk | dv] as they are)
+        // backward and the small gradients' reductions (no operand is
+        // transposed: dE reads W, and dW reads E and [dk | dv], as they are)
         Launch l(P, ENGRAM_K_BWD_FUSE, stream);
         launch_bwd_gate_stats(ba, stream);
         launch_bwd_conv(ba, stream);
@@ -193,9 +191,6 @@ engram_status engram_backward(engram_plan p, const uint32_t *d_idx, const void *
         launch_bwd_sum_rows(ba.dg_part + (int64_t)Br * L.gate_chunks * d, Br, L.gate_chunks, d, part, g->dgamma_k,
                             stream);
         launch_bwd_sum_rows(ba.dconv_part, 1, L.conv_blocks, (int64_t)d * kc, part, g->dconv_w, stream);
-        for (int m = 0; m <= Br; ++m)
-            launch_bwd_transpose(static_cast<const uint16_t *>(m < Br ? w->w_k[m] : w->w_v), d, De, De,
-                                 wt + (int64_t)m * d, N, d, stream);
     }
     if (last_launch_status() != ENGRAM_OK) return ENGRAM_E_DEVICE;
     {
@@ -203,7 +198,9 @@ engram_status engram_backward(engram_plan p, const uint32_t *d_idx, const void *
         Launch l(P, ENGRAM_K_BWD_GEMM, stream);
         ProjArgs pe{};
         pe.emb = dkv;
-        for (int m = 0; m <= kMaxBranches; ++m) pe.w[m] = wt;
+        for (int m = 0; m <= kMaxBranches; ++m) pe.w[m] = m < Br ? w->w_k[m] : w->w_v;
+        pe.k_mat_rows = d;  // k = row of [W_k^(0); ..; W_v], d rows per matrix
+        pe.w_ld = De;
         pe.n_tok = n_tok;
         pe.K = (int32_t)N;
         pe.d = De;
@@ -211,7 +208,7 @@ engram_status engram_backward(engram_plan p, const uint32_t *d_idx, const void *
         pe.out_f32 = demb;
         pe.out_ld = De;
         pe.n_rows = De;
-        launch_proj_plain_bf16(pe, stream);
+        launch_proj_plain_kmajor_w_bf16(pe, stream);
         // dW contracts over every token: few output tiles, so K is split
         // until the chip is full and the partial results summed in order.
         // Both operands are token-major, i.e. K-major for this contraction

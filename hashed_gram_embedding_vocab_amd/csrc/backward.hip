@@ -9,14 +9,13 @@
 //                          branches of alpha du, and the conv taps' gradient
 //   bwd_gate_kernel        ds = dalpha alpha (1 - alpha), then both RMSNorms
 //                          backwards: dh, dk and the gammas' gradients
-//   bwd_transpose_kernel   W transposed, so the dE = [dk | dv] W operand is
-//                          K-contiguous for the MFMA main loop
 //   table rows             (table, row) keys sorted stably by a segmented
 //                          radix sort; fixed 64-item chunks of the sorted items
 //                          add the tokens' dE slices in token order
-// The contractions themselves run on proj_bf16.hip's main loop: plain mode
-// for k, v and dE, K-major mode for dW (its operands E and [dk | dv] are
-// token-major, the contraction runs over tokens).
+// The contractions themselves run on proj_bf16.hip's main loop: k and v
+// (with the gate partials) in mode 5, dE in mode 6 (W read K-major: the
+// contraction runs over its rows), dW in mode 4 (E and [dk | dv] read
+// K-major: the contraction runs over tokens).  No operand is transposed.
 #include <cstring>
 
 #include <rocprim/device/device_scan.hpp>
@@ -337,42 +336,6 @@ __global__ __launch_bounds__(256) void bwd_sum_parts_kernel(const float *part, i
 #pragma unroll 16
     for (int k = 0; k < S; ++k) s += p[k * width];
     out[x] = s;
-}
-
-// dst[c][r] = src[r][c] (16-bit elements) for r < rows, zero for
-// rows <= r < dst_cols.  Each thread moves one 8 x 8 block: eight 16-byte row
-// loads, a transpose in registers, eight 16-byte row stores.  Lanes with the
-// same row group cover 128 contiguous source bytes, lanes with the same column
-// group 128 contiguous destination bytes.  cols, dst_cols and both leading
-// dimensions are multiples of 8, both pointers 16-byte aligned.
-__global__ __launch_bounds__(256) void bwd_transpose_kernel(const uint16_t *src, int64_t rows, int64_t cols,
-                                                            int64_t src_ld, uint16_t *dst, int64_t dst_ld,
-                                                            int64_t dst_cols) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t c0 = (int64_t)blockIdx.x * 64 + 8 * (lane & 7);
-    const int64_t r0 = ((int64_t)blockIdx.y * 4 + wave) * 64 + 8 * (lane >> 3);
-    if (c0 >= cols || r0 >= dst_cols) return;
-    uint32_t in[8][4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        uint4 x = make_uint4(0u, 0u, 0u, 0u);
-        if (r0 + i < rows) x = *reinterpret_cast<const uint4 *>(src + (r0 + i) * src_ld + c0);
-        in[i][0] = x.x;
-        in[i][1] = x.y;
-        in[i][2] = x.z;
-        in[i][3] = x.w;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        // element j of every source row: 16-bit half (j & 1) of word (j >> 1)
-        uint32_t o[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t A = in[2 * q][j >> 1], B = in[2 * q + 1][j >> 1];
-            o[q] = (j & 1) ? ((A >> 16) | (B & 0xffff0000u)) : ((A & 0xffffu) | (B << 16));
-        }
-        *reinterpret_cast<uint4 *>(dst + (c0 + j) * dst_ld + r0) = make_uint4(o[0], o[1], o[2], o[3]);
-    }
 }
 
 // ---------------------------------------------------------------- table rows
@@ -734,14 +697,6 @@ void launch_bwd_sum_rows(const float *in, int64_t groups, int64_t rows, int64_t 
 void launch_bwd_sum_parts(const float *part, int64_t groups, int64_t width, int32_t S, float *out, hipStream_t s) {
     const int64_t n = groups * width;
     launch_kernel(bwd_sum_parts_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), s, part, groups, width, S, out);
-}
-
-void launch_bwd_transpose(const uint16_t *src, int64_t rows, int64_t cols, int64_t src_ld, uint16_t *dst,
-                          int64_t dst_ld, int64_t dst_cols, hipStream_t s) {
-    // every caller passes cols, dst_cols, src_ld and dst_ld as multiples of 8
-    // and 16-byte aligned pointers (the kernel moves 8 x 8 blocks)
-    const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((dst_cols + 255) / 256));
-    launch_kernel(bwd_transpose_kernel, grid, dim3(256), s, src, rows, cols, src_ld, dst, dst_ld, dst_cols);
 }
 
 int64_t bwd_row_chunks(int64_t n_items) { return (n_items + kRowChunk - 1) / kRowChunk; }

@@ -170,6 +170,9 @@ struct ProjArgs {
     // [k_rows][e_ld]; row k of each holds that k for every column
     int64_t k_rows;
     int32_t w_ld, e_ld;
+    // mode 6 (weight side K-major): k-row n of the stacked w[] is row
+    // n % k_mat_rows of matrix n / k_mat_rows, each [k_mat_rows][w_ld]
+    int32_t k_mat_rows;
     // retrieval inside the launch (mode 2): every block hashes its tokens'
     // n-grams and reads its E operand straight from the table rows
     const int32_t *tokens;                 // [batch][seqlen] raw ids
@@ -211,6 +214,10 @@ void launch_proj_plain_bf16(const ProjArgs &a, hipStream_t s, int splits = 1);
 // (k-rows past k_rows count as zero); fp32 out as above.  K % 128 == 0,
 // w_ld, e_ld and the column counts multiples of 8.
 void launch_proj_plain_kmajor_bf16(const ProjArgs &a, hipStream_t s, int splits = 1);
+// C[t][n] = sum_k W[k][n] emb[t][k] with the k-rows of W taken from the
+// stacked matrices w[0..] (k_mat_rows rows of w_ld each; k_mat_rows % 32 == 0),
+// emb K-contiguous as in mode 3; fp32 out, no split.
+void launch_proj_plain_kmajor_w_bf16(const ProjArgs &a, hipStream_t s);
 // The plain contraction over the stacked [W_k^(m); W_v] (n_mats = n_branches
 // + 1, K = D_e, no split) that also leaves, for the W_k rows, the gate
 // partial sums of launch_proj_bf16 (h, gamma_h, gamma_k, partials, n_parts).
@@ -325,9 +332,6 @@ void launch_bwd_sum_rows(const float *in, int64_t groups, int64_t rows, int64_t 
                          hipStream_t s);
 // out[g][i] = sum over s = 0..S-1, ascending, of part[g][s][i]
 void launch_bwd_sum_parts(const float *part, int64_t groups, int64_t width, int32_t S, float *out, hipStream_t s);
-// dst[c][r] = src[r][c] (bf16), zero for rows <= r < dst_cols
-void launch_bwd_transpose(const uint16_t *src, int64_t rows, int64_t cols, int64_t src_ld, uint16_t *dst,
-                          int64_t dst_ld, int64_t dst_cols, hipStream_t s);
 
 struct BwdTableArgs {
     const uint32_t *idx;                    // [n_tok][n_tables]

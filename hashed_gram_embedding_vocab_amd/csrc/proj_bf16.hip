@@ -15,6 +15,9 @@
 //     LDS reads (ds_read_b64_tr_b16), so no operand is transposed in HBM.
 //   mode 5: mode 3 over [W_k^(m); W_v] whose W_k tiles also leave mode 0's
 //     gate partials (the backward's k and v, and its gate statistics).
+//   mode 6: mode 3 whose weight side is read K-major from the stacked
+//     matrices themselves (the backward's dE = [dk | dv] [W_k; W_v]: its
+//     contraction runs over the matrices' rows), so W is not transposed.
 //   mode 1: W_v only, with the rest of the fusion step in the epilogue:
 //     alpha from the gate partials of a preceding mode-0 launch, u = alpha v,
 //     the short depthwise causal conv over tokens, the residual into h and
@@ -497,9 +500,10 @@ __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t 
 template <int MODE, int BR, bool SILU, bool NARROW>
 __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_bf16_kernel(ProjArgs a) {
     static_assert(!(NARROW && MODE == 1), "the fused value epilogue is written for the wide tile");
-    static_assert(MODE >= 0 && MODE <= 5, "mode");
-    constexpr bool kKMaj = MODE == 4;                // both operands stored K-major
-    constexpr bool kPlain = MODE == 3 || MODE == 4 || MODE == 5;  // fp32 store epilogue
+    static_assert(MODE >= 0 && MODE <= 6, "mode");
+    constexpr bool kKMajW = MODE == 4 || MODE == 6;  // weight-side operand stored K-major
+    constexpr bool kKMajE = MODE == 4;               // token-side operand stored K-major
+    constexpr bool kPlain = MODE == 3 || MODE == 4 || MODE == 5 || MODE == 6;  // fp32 store epilogue
     static_assert(MODE != 2 || NARROW, "retrieval inside the launch is written for the narrow tile");
     constexpr bool kGather = MODE == 2;
     constexpr bool kGateK = MODE == 0 || MODE == 2 || MODE == 5;  // W_k / W_v launch with the gate-partial epilogue
@@ -545,8 +549,8 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
     const int kbase = kPlain ? (int)blockIdx.y * K : 0;
     // mode 4: operands [k_rows][w_ld] and [k_rows][e_ld]; k-rows past k_rows read as zeros
     const __amdgpu_buffer_rsrc_t wres =
-        kKMaj ? make_rsrc(wmat, (uint32_t)(a.k_rows * a.w_ld * 2)) : make_rsrc(wmat, (uint32_t)d * ld * 2u);
-    const __amdgpu_buffer_rsrc_t eres = kKMaj ? make_rsrc(a.emb, (uint32_t)(a.k_rows * a.e_ld * 2))
+        kKMajW ? make_rsrc(wmat, (uint32_t)(a.k_rows * a.w_ld * 2)) : make_rsrc(wmat, (uint32_t)d * ld * 2u);
+    const __amdgpu_buffer_rsrc_t eres = kKMajE ? make_rsrc(a.emb, (uint32_t)(a.k_rows * a.e_ld * 2))
                                               : make_rsrc(a.emb, (uint32_t)(a.n_tok * ld * 2));
     // (a template-dependent bound here keeps the host pass from emitting the
     // kernel's launch stub, so the bound is the namespace constant both tiles share)
@@ -562,15 +566,15 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
         const int64_t t = min(max(t0 + trow, (int64_t)0), a.n_tok - 1);
         woff[i] = (uint32_t)((n0 - mat0 * d + row) * ld + lchunk * 8) * 2u;
         eoff[i] = (uint32_t)(t * ld + lchunk * 8) * 2u;
-        if constexpr (kKMaj) {
+        if constexpr (kKMajW || kKMajE) {
             // instruction i of this wave fills k-rows RPI (TBPW wave + i) + lane / LPR,
             // LDS chunk lane % LPR of each, which holds the tile's column chunk
             // (lane % LPR) ^ 2 kswz(kr)
             constexpr int LPR = TBN / 8, RPI = 64 / LPR;
             const int kr = RPI * blk + lane / LPR;
             const int ch = (lane % LPR) ^ (2 * kswz<TBN / 16>(kr));
-            woff[i] = (uint32_t)((int64_t)kr * a.w_ld + n0 + 8 * ch) * 2u;
-            eoff[i] = (uint32_t)((int64_t)kr * a.e_ld + t0 + 8 * ch) * 2u;
+            if constexpr (kKMajW) woff[i] = (uint32_t)((int64_t)kr * a.w_ld + n0 + 8 * ch) * 2u;
+            if constexpr (kKMajE) eoff[i] = (uint32_t)((int64_t)kr * a.e_ld + t0 + 8 * ch) * 2u;
         }
     }
 
@@ -647,16 +651,24 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
                 goff -= c ? (int)(g_row_bytes / 2u) : 0;                                         \
                 gtau += c ? 1 : 0;                                                               \
             }                                                                                    \
-        } else if constexpr (kKMaj) {                                                            \
-            const int kw = (kbase + (k0)) * a.w_ld * 2, ke = (kbase + (k0)) * a.e_ld * 2;         \
+        } else if constexpr (kKMajW || kKMajE) {                                                 \
+            /* mode 6: the weight side's k-rows are the stacked matrices' rows,                 \
+               k_mat_rows per matrix, and a stage never straddles two */                          \
+            __amdgpu_buffer_rsrc_t wr = wres;                                                    \
+            int kw = (kbase + (k0)) * a.w_ld * 2;                                                \
+            if constexpr (MODE == 6) {                                                           \
+                const int kg = kbase + (k0), m6 = kg / a.k_mat_rows;                             \
+                wr = make_rsrc(pick(a.w, m6), (uint32_t)a.k_mat_rows * a.w_ld * 2u);             \
+                kw = (kg - m6 * a.k_mat_rows) * a.w_ld * 2;                                      \
+            }                                                                                    \
+            const int ke = kKMajE ? (kbase + (k0)) * a.e_ld * 2 : kbytes;                        \
             _Pragma("unroll") for (int i = 0; i < TBPW; ++i) {                                   \
                 const int blk = wave * TBPW + i;                                                 \
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void_t *)&STG.w[blk * kBlockBytes], \
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void_t *)&STG.w[blk * kBlockBytes], \
                                                          16, woff[i], kw, 0, 0);                 \
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(eres, (lds_void_t *)&STG.e[blk * kBlockBytes], \
                                                          16, eoff[i], ke, 0, 0);                 \
             }                                                                                    \
-            (void)kbytes;                                                                        \
         } else {                                                                                 \
             _Pragma("unroll") for (int i = 0; i < TBPW; ++i) {                                   \
                 const int blk = wave * TBPW + i;                                                 \
@@ -701,12 +713,15 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
 #define ENGRAM_COMPUTE(STG)                                                                      \
     do {                                                                                         \
         bf16x8_t fa[FN], fb[TFT];                                                                 \
-        if constexpr (kKMaj) {                                                                   \
+        if constexpr (kKMajW) {                                                                  \
             _Pragma("unroll") for (int i = 0; i < FN; ++i) fa[i] = frag_tr(STG.w, wn_blk + i);   \
-            _Pragma("unroll") for (int j = 0; j < TFT; ++j) fb[j] = frag_tr(STG.e, wt_blk + j);   \
         } else {                                                                                 \
             _Pragma("unroll") for (int i = 0; i < FN; ++i) fa[i] =                               \
                 *reinterpret_cast<const bf16x8_t *>(&STG.w[(wn_blk + i) * kBlockBytes + fpos]);  \
+        }                                                                                        \
+        if constexpr (kKMajE) {                                                                  \
+            _Pragma("unroll") for (int j = 0; j < TFT; ++j) fb[j] = frag_tr(STG.e, wt_blk + j);   \
+        } else {                                                                                 \
             _Pragma("unroll") for (int j = 0; j < TFT; ++j) fb[j] =                               \
                 *reinterpret_cast<const bf16x8_t *>(&STG.e[(wt_blk + j) * kBlockBytes + fpos]);  \
         }                                                                                        \
@@ -954,6 +969,17 @@ void launch_proj_kv_partials_bf16(const ProjArgs &a, hipStream_t s) {
         launch_kernel((proj_bf16_kernel<5, 1, false, true>), dim3((unsigned)blocks), dim3(256), s, a);
     } else {
         launch_kernel((proj_bf16_kernel<5, 1, false, false>), dim3((unsigned)wide), dim3(kThreads), s, a);
+    }
+}
+
+void launch_proj_plain_kmajor_w_bf16(const ProjArgs &a, hipStream_t s) {
+    const int n_total = a.n_mats * a.d;
+    const int64_t wide = (int64_t)((n_total + BN - 1) / BN) * ((a.n_tok + BT - 1) / BT);
+    if (!plain_wide(wide, 1)) {
+        const int64_t blocks = (int64_t)((n_total + 127) / 128) * ((a.n_tok + 127) / 128);
+        launch_kernel((proj_bf16_kernel<6, 1, false, true>), dim3((unsigned)blocks), dim3(256), s, a);
+    } else {
+        launch_kernel((proj_bf16_kernel<6, 1, false, false>), dim3((unsigned)wide), dim3(kThreads), s, a);
     }
 }
 
