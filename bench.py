@@ -491,15 +491,13 @@ def backward_bench(args, wl):
     # work per engram_backward call.  Contractions: k and v again, dE and dW,
     # each 2 (B_r + 1) d D_e flop per token.  HBM kinds: the bytes their
     # kernels move in this design (gate partials, fp32 k and v read back,
-    # bf16 dk/dv, W's transpose; table rows: dE slices read, row gradients
-    # written).
+    # bf16 dk/dv; table rows: dE slices read, row gradients written).
     models = {
         "bwd_gemm": ("mfma", 2.0 * De * N * (2 * n_tok + n_pad)),
         "gather": ("hbm", n_tok * (wl.n_tables * 4 + 2 * De * eb)),
         "bwd_fuse": ("hbm", Br * n_tok * (3 * 4 * (d // 128) + 16)          # gate statistics: partials; rh, rk, s, alpha
                      + n_tok * d * (4 + 2) + Br * n_tok * d * eb            # conv: v, dout; dv
-                     + Br * n_tok * d * (eb + 4 + eb + eb + 2)              # gate: h, k, dout; dh, dk
-                     + 2 * 2 * N * De),                                     # W transposed
+                     + Br * n_tok * d * (eb + 4 + eb + eb + 2)),            # gate: h, k, dout; dh, dk
         "bwd_table": ("hbm", wl.n_tables * n_tok * (wl.head_dim * 4 * 2 + 4 * 8)),
     }
 
@@ -512,9 +510,9 @@ def backward_bench(args, wl):
         return {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
                 ("flops_per_call" if bound == "mfma" else "bytes_per_call"): work, "us_per_call": round(us, 2)}
 
-    kernel_of = {"bwd_gemm": "proj_bf16_kernel<5> (k and v, gate partials), <3> (dE), <4> (dW from token-major "
-                             "operands, with its split-K sum)",
-                 "bwd_fuse": "bwd_gate_stats, bwd_conv, bwd_gate, ordered sums, W transpose",
+    kernel_of = {"bwd_gemm": "proj_bf16_kernel<5> (k and v, gate partials), <6> (dE, W read K-major), <4> (dW from "
+                             "token-major operands, with its split-K sum)",
+                 "bwd_fuse": "bwd_gate_stats, bwd_conv, bwd_gate, ordered sums",
                  "bwd_table": "table-row gradients (keys, segmented radix sort, run-head scan, segmented sums)",
                  "gather": "gather_kernel"}
     per_kind = {k: dict(figures(k, per_call[k]), kernel=kernel_of[k]) for k in kinds}
