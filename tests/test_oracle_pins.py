@@ -175,11 +175,67 @@ def test_compression_map_surjective():
 TINY_V, TINY_VC = 7, 5
 
 
-def _tiny_setup(heads=2, prime=13, seed=0x1234):
+# Per-table primes of the tiny-vocabulary pins.  They all differ and are not
+# sorted (the order-3 tables' primes exceed the order-2 tables'), and each is
+# well below the number of distinct n-grams its table sees, so a hash that
+# reduced every table by one table's prime, by a head's prime instead of the
+# table's, or by the tables' primes in another order, leaves residues of p_tau
+# unreached or reaches values >= p_tau, and these pins fail.
+TINY_PRIMES = {2: [7, 5, 13, 11], 3: [5, 3, 2, 23, 19, 17]}
+
+
+def _tiny_setup(heads=2, seed=0x1234):
     comp = W.compression_map(TINY_V, TINY_VC, 99)
     pre = {int(c): int(np.nonzero(comp == c)[0][0]) for c in range(TINY_VC)}  # one raw id per class
-    primes = [prime] * (2 * heads)
+    primes = list(TINY_PRIMES[heads])
+    assert len(set(primes)) == 2 * heads and all(_is_prime_sieve(q) for q in primes)
     return comp, pre, primes, seed
+
+
+# SplitMix64 from its published definition (Steele, Lea & Flood 2014): the
+# state advances by the golden-ratio increment and each output is the state
+# passed through the finalizer.  Written here with Python integers, apart from
+# the oracle, for direct evaluation of single n-grams.
+_GOLDEN = 0x9E3779B97F4A7C15
+_M64 = (1 << 64) - 1
+
+
+def _py_mix64(z):
+    z &= _M64
+    z ^= z >> 30
+    z = (z * 0xBF58476D1CE4E5B9) & _M64
+    z ^= z >> 27
+    z = (z * 0x94D049BB133111EB) & _M64
+    return z ^ (z >> 31)
+
+
+def _py_slot(g, vocab_comp, hash_seed, tau, prime):
+    """Slot of n-gram g (oldest id first) in table tau: the base-(V'+1) key,
+    mixed with the tau-th SplitMix64 output of the hash seed, reduced by that
+    table's own prime."""
+    key = 0
+    for c in g:
+        key = key * (vocab_comp + 1) + int(c)
+    s_tau = _py_mix64(hash_seed + (tau + 1) * _GOLDEN)
+    return _py_mix64(key ^ s_tau) % prime
+
+
+def test_splitmix64_sequence_gives_table_seeds():
+    # the first five outputs of SplitMix64 seeded with 0 (Vigna's reference
+    # splitmix64.c); table tau's seed under hash seed 0 is output tau
+    seq = [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F, 0xF88BB8A8724C81EC,
+           0x1B39896A51A8749B]
+    assert [oracle.table_seed(0, t) for t in range(5)] == seq
+    assert [_py_mix64((t + 1) * _GOLDEN) for t in range(5)] == seq
+
+
+def _check_table_ranges(idx, primes):
+    """Table tau's slots lie in [0, p_tau) and, over a stream that holds far
+    more distinct n-grams than p_tau, reach every residue of p_tau."""
+    for tau, p in enumerate(primes):
+        col = idx[:, tau].astype(np.int64)
+        assert col.min() >= 0 and col.max() < p, (tau, p, int(col.max()))
+        assert len(np.unique(col)) == p, (tau, p, len(np.unique(col)))
 
 
 def test_ngram_key_injective_exhaustive():
@@ -212,6 +268,8 @@ def test_hash_bruteforce_all_trigrams():
                     tau = o * heads + k
                     assert row[tau] == oracle.ngram_slot(g, TINY_VC, oracle.table_seed(seed, tau),
                                                          primes[tau])
+                    assert row[tau] == _py_slot(g, TINY_VC, seed, tau, primes[tau])
+    _check_table_ranges(idx, primes)
 
 
 def _de_bruijn(k, n):
@@ -234,7 +292,7 @@ def _de_bruijn(k, n):
 
 def test_hash_de_bruijn_stream():
     heads = 3
-    comp, pre, primes, seed = _tiny_setup(heads, prime=101)
+    comp, pre, primes, seed = _tiny_setup(heads)
     s = _de_bruijn(TINY_VC, 3)
     s = s + s[:2]  # cyclic -> linear: every 3-gram appears exactly once
     assert len(set(zip(s, s[1:], s[2:]))) == TINY_VC**3 == len(s) - 2
@@ -246,6 +304,9 @@ def test_hash_de_bruijn_stream():
                 tau = o * heads + k
                 assert idx[t, tau] == oracle.ngram_slot(g, TINY_VC, oracle.table_seed(seed, tau),
                                                         primes[tau])
+                assert idx[t, tau] == _py_slot(g, TINY_VC, seed, tau, primes[tau])
+    # from position 2 on: 25 distinct 2-grams and 125 distinct 3-grams
+    _check_table_ranges(idx[2:], primes)
 
 
 def test_identical_ngrams_hit_identical_slots():
@@ -295,9 +356,13 @@ def test_hash_out_of_range_tokens_are_pad():
     # PAD id = vocab_comp occupies the bad positions
     P = TINY_VC
     c = [1, P, 3, P]
+    ext = [P, P] + c
     for t in range(4):
-        g3 = [([P, P] + c)[t + i] for i in range(3)]
-        assert idx_bad[t, 2] == oracle.ngram_slot(g3, TINY_VC, oracle.table_seed(seed, 2), primes[2])
+        g2, g3 = ext[t + 1:t + 3], ext[t:t + 3]
+        for tau in range(4):
+            g = g2 if tau < 2 else g3
+            assert idx_bad[t, tau] == oracle.ngram_slot(g, TINY_VC, oracle.table_seed(seed, tau), primes[tau])
+            assert idx_bad[t, tau] == _py_slot(g, TINY_VC, seed, tau, primes[tau])
 
 
 def test_hash_uniformity_chi2():
