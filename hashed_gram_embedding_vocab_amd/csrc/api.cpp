@@ -19,15 +19,6 @@ using namespace engram::host;
 namespace {
 
 // SplitMix64 output function, used to derive the per-table hash seeds.
-uint64_t host_mix64(uint64_t z) {
-    z ^= z >> 30;
-    z *= 0xBF58476D1CE4E5B9ull;
-    z ^= z >> 27;
-    z *= 0x94D049BB133111EBull;
-    z ^= z >> 31;
-    return z;
-}
-
 struct Layout {
     size_t idx, emb, partials, alpha, v, seam, kbuf, stage, total;
 };
@@ -415,9 +406,9 @@ engram_status engram_plan_create(const engram_config *cfg, engram_plan *out) {
     p->hc.vocab = c.vocab;
     p->hc.vocab_comp = c.vocab_comp;
     for (int t = 0; t < n_tables; ++t) {
-        p->hc.seed[t] = host_mix64(c.hash_seed + (uint64_t)(t + 1) * 0x9E3779B97F4A7C15ull);
+        p->hc.seed[t] = engram::table_seed(c.hash_seed, t);
         p->hc.rows[t] = c.table_rows[t];
-        p->hc.magic[t] = UINT64_MAX / c.table_rows[t];
+        p->hc.magic[t] = engram::mod_magic(c.table_rows[t]);
         p->hc.order_of[t] = c.orders[t / c.heads];
     }
     *out = p;

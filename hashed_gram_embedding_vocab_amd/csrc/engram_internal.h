@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "engram.h"
+#include "hash_math.h"
 
 namespace engram {
 
@@ -57,27 +58,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // ---------------------------------------------------------------- hashing
-// SplitMix64 output function (Steele, Lea & Flood 2014; Mix13 constants):
-// the deterministic mixer of the multi-head n-gram hash.
-__device__ __forceinline__ uint64_t mix64(uint64_t z) {
-    z ^= z >> 30;
-    z *= 0xBF58476D1CE4E5B9ull;
-    z ^= z >> 27;
-    z *= 0x94D049BB133111EBull;
-    z ^= z >> 31;
-    return z;
-}
-
-// z mod p for a 64-bit z and 32-bit p without a hardware divide.  With
-// m = floor((2^64-1)/p) the estimate q = floor(z*m / 2^64) satisfies
-// floor(z/p) - 2 <= q <= floor(z/p), so two conditional subtractions finish it.
-__device__ __forceinline__ uint32_t mod_prime(uint64_t z, uint32_t p, uint64_t m) {
-    const uint64_t q = __umul64hi(z, m);
-    uint64_t r = z - q * (uint64_t)p;
-    if (r >= p) r -= p;
-    if (r >= p) r -= p;
-    return (uint32_t)r;
-}
+// mix64, table_seed, mod_magic and mod_prime: hash_math.h
 
 // Vocabulary projection of one raw id; ids outside [0, vocab) become PAD.
 __device__ __forceinline__ int32_t compress_id(int32_t x, const int32_t *__restrict__ comp_map,
