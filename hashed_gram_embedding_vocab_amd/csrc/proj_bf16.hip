@@ -35,8 +35,12 @@
 // In mode 1 each lane holds four channels of one token per MFMA block and the
 // 16 lanes of a row hold 16 consecutive tokens, so the conv's neighbours
 // u_{t-1..t-3} come from DPP row rotations across lanes (plus the previous
-// block's registers); token tiles overlap by three rows so no tile needs
-// another tile's values, and neighbouring waves pass three rows via LDS.
+// block's registers), and neighbouring waves of a tile pass three rows via
+// LDS.  Token tiles do not overlap: each tile starts 256 tokens after the
+// previous one, so the first three rows of a tile lack the previous tile's v.
+// The tile leaves those rows, and saves the fp32 v of its first and last three
+// rows, for seam_kernel (fuse.hip), which finishes them with the same
+// expressions in the same order.
 //
 // Tile: 256 weight rows x 256 tokens (d % 256 == 0, so a weight tile never
 // straddles two matrices), 32 K per stage (D_e % 128 == 0), 8 waves (two per

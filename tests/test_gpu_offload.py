@@ -79,7 +79,7 @@ def zipf_idx(primes, n_tok, seed):
 
 
 CASES = [("f32", 32, [10007] * 8), ("bf16", 80, W.largest_primes_at_most(5000, 16)),
-         ("bf16", 64, W.largest_primes_at_most(3001, 4))]
+         ("bf16", 64, W.largest_primes_at_most(3001, 4)), ("bf16", 32, W.largest_primes_at_most(2003, 32))]
 
 
 @pytest.mark.parametrize("dt,head_dim,primes", CASES)

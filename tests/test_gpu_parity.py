@@ -151,6 +151,39 @@ def test_hash_shapes(B, name, batch, seqlen, with_ctx):
     assert np.array_equal(got, ref)
 
 
+# More than 16 tables (a plan accepts up to 32): fewer tokens per retrieval
+# block, 4-wide index stores across 24 or 32 slots, a single order of 32 heads.
+MANY_TABLES = [(12, (2, 3)), (16, (2, 3)), (32, (3,))]
+
+
+def many_tables_wl(heads, orders, batch, seqlen, dtype="bf16", name="many_tables"):
+    return dataclasses.replace(W.workload("small"), name=name, index=60 + heads + len(orders), batch=batch,
+                               seqlen=seqlen, d_model=256, heads=heads, head_dim=32, orders=orders,
+                               table_target=2003, same_prime=False, n_branches=1, dtype=dtype)
+
+
+@pytest.mark.parametrize("heads,orders", MANY_TABLES)
+@pytest.mark.parametrize("batch,seqlen", [(1, 1), (3, 65), (2, 1000)])
+@pytest.mark.parametrize("with_ctx", [False, True])
+def test_hash_many_tables(B, heads, orders, batch, seqlen, with_ctx):
+    say("hash many tables", heads, orders, batch, seqlen, with_ctx)
+    wl = many_tables_wl(heads, orders, batch, seqlen)
+    li = W.make_layer_inputs(wl, batch=1, seqlen=1)
+    comp = W.compression_map(wl.vocab, wl.vocab_comp, wl.seed(1))
+    toks = W.make_tokens(wl)
+    ctx = None
+    if with_ctx:
+        ctx = np.random.default_rng(4).integers(0, wl.vocab_comp + 1, (batch, 2)).astype(np.int32)
+    plan = B.Plan(vocab=wl.vocab, vocab_comp=wl.vocab_comp, heads=wl.heads, head_dim=wl.head_dim,
+                  table_rows=wl.primes(), hash_seed=li.hash_seed, d_model=wl.d_model, dtype=B.BF16,
+                  orders=wl.orders)
+    got, bad = _hash_gpu(B, plan, toks, dev_i32(comp), wl.n_tables, prev_ctx=ctx)
+    ref, rbad, _ = oracle_indices(wl, li, toks, comp, prev_ctx=ctx)
+    assert wl.n_tables in (24, 32)
+    assert bad == rbad == 0
+    assert np.array_equal(got, ref)
+
+
 def test_hash_out_of_range_tokens(B):
     say("hash bad tokens")
     wl = W.workload("tiny")
@@ -176,6 +209,9 @@ def test_hash_out_of_range_tokens(B):
     ("f32", 32, [10007] * 8),
     ("bf16", 80, W.largest_primes_at_most(5000, 16)),
     ("bf16", 64, W.largest_primes_at_most(3001, 4)),
+    ("bf16", 64, W.largest_primes_at_most(3001, 24)),
+    ("bf16", 32, W.largest_primes_at_most(2003, 32)),
+    ("f32", 32, W.largest_primes_at_most(1009, 32)),
 ])
 @pytest.mark.parametrize("n_tok", [1, 1000, 4099])
 def test_gather_bit_exact(B, dt, head_dim, primes, n_tok):
@@ -243,6 +279,40 @@ def test_forward_bf16_small_shapes_all_positions(B, n_branches, batch, seqlen):
                       flags=oracle.OUT_DELTA)
     ref_y, _, _ = L2.forward_all()
     assert_within(host(y), ref_y, "bf16", "bf16 small y (silu skip)")
+
+
+@pytest.mark.parametrize("heads,orders", MANY_TABLES)
+@pytest.mark.parametrize("dtype,batch,seqlen", [("bf16", 3, 77), ("bf16", 5, 1), ("bf16", 2, 300),
+                                                ("f32", 2, 70)])
+def test_forward_many_tables_all_positions(B, heads, orders, dtype, batch, seqlen):
+    """engram_forward with 24 or 32 tables: fused retrieval and both fusion
+    routes (prefill tiles, and the one-token route with its carried state),
+    every position against the oracle; a one-token chunk with the
+    retrieve-in-projection flag (which covers at most 16 tables, so the
+    library keeps the separate retrieval) gives the same bits."""
+    say("forward many tables", heads, orders, dtype, batch, seqlen)
+    wl = many_tables_wl(heads, orders, batch, seqlen, dtype=dtype)
+    dl = make_device_layer(wl)
+    toks = W.make_tokens(wl)
+    ctx = state = None
+    if seqlen == 1:
+        rng = np.random.default_rng(5)
+        ctx = rng.integers(0, wl.vocab_comp + 1, (batch, 2)).astype(np.int32)
+        state = rng.standard_normal((1, batch, 3, wl.d_model)).astype(np.float32)
+    st_dev = None if state is None else to_device(state, torch.float32, "cuda")
+    out, alpha, bad = forward(dl, toks, prev_ctx=None if ctx is None else dev_i32(ctx), conv_state=st_dev)
+    assert bad == 0
+    idx, _, _ = oracle_indices(wl, dl.li, toks, dl.comp_map_host, prev_ctx=ctx)
+    L = oracle_layer(wl, dl.li, idx, batch, seqlen, conv_state=state)
+    ref, ref_alpha, _ = L.forward_all()
+    assert_within(host(out), ref, dtype, "many tables out")
+    assert np.abs(host(alpha) - ref_alpha).max() <= alpha_tol(dtype)
+    if seqlen == 1:
+        st2 = None if state is None else to_device(state, torch.float32, "cuda")
+        out2, _, _ = forward(dl, toks, prev_ctx=dev_i32(ctx), conv_state=st2,
+                             flags=B.RETRIEVE_IN_PROJECTION)
+        assert torch.equal(out2.view(torch.int16) if dtype == "bf16" else out2,
+                           out.view(torch.int16) if dtype == "bf16" else out)
 
 
 def _sampled_check(wl, dl, toks, n_pos, what, prev_ctx=None, conv_state=None, seed=0):
