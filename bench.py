@@ -36,7 +36,10 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
-DEFAULT_WORKLOAD = "small"
+# The largest single-GPU configuration: 16 prime tables of ~78M rows x 80
+# bf16 values (100B parameters, 200 GB resident in HBM), d = 2560, 8 x 4096
+# Zipf(1.05) tokens per step.
+DEFAULT_WORKLOAD = "maxtable_zipf"
 
 
 def parse():
@@ -68,7 +71,11 @@ def parse():
     ap.add_argument("--prefetch-wgs", type=int, default=8,
                     help="workgroups of the capped prefetch gather (--offload)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="only run a plain device-to-device copy of this many MiB 5 times (counter calibration)")
+                    help="only run the library's streaming copy and read over this many MiB, 5 times each "
+                         "(counter calibration)")
+    ap.add_argument("--no-hbm-probe", action="store_true",
+                    help="skip the streaming read/copy ceilings and the extra gather legs")
+    ap.add_argument("--probe-gib", type=float, default=4.0, help="buffer size of the streaming ceilings")
     return ap.parse_args()
 
 
@@ -153,16 +160,19 @@ def main():
     import torch
 
     if args.copy_probe_mib:
-        # A plain copy of known size: FETCH_SIZE / WRITE_SIZE of these
-        # dispatches calibrate the counters against bytes actually moved.
+        # Streaming copies and reads of known size: FETCH_SIZE / WRITE_SIZE of
+        # these dispatches calibrate the counters against bytes actually moved.
+        from hashed_gram_embedding_vocab_amd import binding as B
         n = args.copy_probe_mib * (1 << 20)
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         for _ in range(5):
-            dst.copy_(src)
+            B.engram_probe_stream(1, src, dst, n, unroll=8, blocks=2048)
+        for _ in range(5):
+            B.engram_probe_stream(0, src, dst, n, unroll=8, blocks=2048)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_probe_bytes": n, "copies": 5}))
+        print(json.dumps({"copy_probe_bytes": n, "copies": 5, "reads": 5}))
         return
 
     from hashed_gram_embedding_vocab_amd import binding as B
@@ -347,6 +357,14 @@ def main():
                                      "frac": g["frac"], "bytes_per_launch": g["bytes_per_launch"],
                                      "avg_launch_us": g["avg_launch_us"]}
 
+    hbm = gather_uniform = None
+    if not args.no_hbm_probe:
+        hbm = hbm_ceiling(args)
+        if wl.name.startswith("maxtable"):
+            gather_uniform = uniform_gather_legs(wl, layers[0][0], args, R, models["gather"][1])
+        if gather is not None and hbm is not None:
+            gather["frac_of_stream_read"] = round(gather["achieved_GBs"] / hbm["read"]["GBs"], 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.cpu_seconds)
@@ -374,12 +392,111 @@ def main():
                    "retrieval_in_projection": bool(fwd_flags)},
         "roofline": roofline,
         "gather": gather,
+        "gather_uniform": gather_uniform,
+        "hbm_ceiling": hbm,
         "gate_gemm": gate_gemm,
         "kernels": per_kernel,
         "kernel_avg_us": kernels_us,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def hbm_ceiling(args):
+    """The box's streaming ceilings from the library's plain read and copy
+    kernels over a buffer far larger than the caches: the best of a small
+    sweep of chunks in flight per thread, workgroups and nontemporal access,
+    each timed over 5 passes after one untimed pass."""
+    import torch
+
+    from hashed_gram_embedding_vocab_amd import binding as B
+
+    n = int(args.probe_gib * (1 << 30)) // 16 * 16
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(3)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    best = {}
+    for mode, name, moved in ((0, "read", n), (1, "copy", 2 * n)):
+        for unroll in (4, 8, 16):
+            for blocks in (1024, 2048, 4096):
+                for flags in (0, B.PROBE_NONTEMPORAL):
+                    B.engram_probe_stream(mode, src, dst, n, unroll=unroll, blocks=blocks, flags=flags)
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for _ in range(5):
+                        B.engram_probe_stream(mode, src, dst, n, unroll=unroll, blocks=blocks, flags=flags)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    gbs = moved * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+                    if gbs > best.get(name, {}).get("GBs", 0):
+                        best[name] = {"GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                      "unroll": unroll, "blocks": blocks, "nontemporal": bool(flags)}
+    del src, dst
+    torch.cuda.empty_cache()
+    best["buffer_bytes"] = n
+    best["kernel"] = "stream_read_kernel / stream_copy_kernel (engram_probe_stream)"
+    return best
+
+
+def uniform_gather_legs(wl, dl, args, R, fused_bytes):
+    """On the same 200 GB of tables: the fused retrieval (hash + gather) of
+    uniformly drawn token ids, where the caches cannot help, and the
+    index-driven gather of uniformly random slots of every table (engram_gather)."""
+    import numpy as np
+    import torch
+
+    from synthetic import workloads as W
+    from synthetic.device import to_device
+
+    n_tok = wl.n_tokens
+    out = {}
+    wu = W.workload("maxtable_uniform")
+    toks = [to_device(W.make_tokens(wu, seed=wu.seed(2) + 17 * r), torch.int32, "cuda") for r in range(R)]
+    ws = dl.plan.workspace(wl.batch, wl.seqlen)
+    h_out = torch.empty_like(dl.h)
+    steps = max(8, args.breakdown_steps)
+    for i in range(4):
+        dl.plan.engram_forward(toks[i % R], dl.comp_map, dl.tables, dl.h, dl.weights, h_out, ws)
+    torch.cuda.synchronize()
+    dl.plan.engram_profile_every(1)
+    dl.plan.engram_profile_begin(8 * steps + 64, ["gather"])
+    for i in range(steps):
+        dl.plan.engram_forward(toks[i % R], dl.comp_map, dl.tables, dl.h, dl.weights, h_out, ws)
+    torch.cuda.synchronize()
+    p = dl.plan.engram_profile_end()["gather"]
+    ms = p["total_ms"] / max(p["launches"], 1)
+    gbs = fused_bytes / (ms * 1e-3) / 1e9
+    out["tokens_uniform"] = {"kernel": "hash_gather_kernel", "avg_launch_us": round(ms * 1e3, 2),
+                             "launches": p["launches"], "bytes_per_launch": fused_bytes,
+                             "achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                             "tokens": "uniform over V=%d (the maxtable_uniform stream)" % wu.vocab}
+    del toks, h_out
+    # index-driven gather of uniformly random slots: no hashing, no token reuse
+    eb = 2 if wl.dtype == "bf16" else 4
+    primes = np.array(wl.primes(), np.int64)
+    rng = np.random.default_rng(wl.seed(7))
+    idxs = []
+    for r in range(R):
+        x = (rng.random((n_tok, wl.n_tables)) * primes).astype(np.int64).astype(np.int32)
+        idxs.append(to_device(x, torch.int32, "cuda"))
+    emb = torch.empty((n_tok, wl.emb_dim), dtype=dl.h.dtype, device="cuda")
+    for i in range(4):
+        dl.plan.engram_gather(idxs[i % R], dl.tables, emb)
+    torch.cuda.synchronize()
+    dl.plan.engram_profile_begin(8 * steps + 64, ["gather"])
+    for i in range(steps):
+        dl.plan.engram_gather(idxs[i % R], dl.tables, emb)
+    torch.cuda.synchronize()
+    p = dl.plan.engram_profile_end()["gather"]
+    ms = p["total_ms"] / max(p["launches"], 1)
+    idx_bytes = n_tok * (wl.n_tables * 4 + 2 * wl.emb_dim * eb)
+    gbs = idx_bytes / (ms * 1e-3) / 1e9
+    out["slots_uniform"] = {"kernel": "gather_kernel", "avg_launch_us": round(ms * 1e3, 2),
+                            "launches": p["launches"], "bytes_per_launch": idx_bytes,
+                            "achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    del idxs, emb, ws
+    torch.cuda.empty_cache()
+    return out
 
 
 def backward_cpu_baseline(wl, budget_s: float):

@@ -134,6 +134,8 @@ def lib() -> C.CDLL:
         L.engram_gather_cached.argtypes = [P, P, i64, P, C.POINTER(RowCacheC), P, i32, P]
         L.engram_synth_fill_table.restype = C.c_int
         L.engram_synth_fill_table.argtypes = [i32, u64, i32, i64, i32, P, P]
+        L.engram_probe_stream.restype = C.c_int
+        L.engram_probe_stream.argtypes = [i32, u32, i32, i32, P, P, i64, P]
         _lib = L
         return L
 
@@ -438,3 +440,18 @@ def engram_synth_fill_table(table: torch.Tensor, seed: int, tau: int, dtype: int
     _check("engram_synth_fill_table", lib().engram_synth_fill_table(
         dtype, seed & 0xFFFFFFFFFFFFFFFF, tau, rows, head_dim,
         _ptr(table, "table", _torch_dtype(dtype)), _stream(stream)))
+
+
+PROBE_NONTEMPORAL = 1
+
+
+def engram_probe_stream(mode: int, src: torch.Tensor, dst: torch.Tensor, nbytes: int, unroll: int = 8,
+                        blocks: int = 2048, flags: int = 0, stream=None):
+    """Streaming read (mode 0) or copy (mode 1) of nbytes of src: a
+    measurement helper, not part of the method."""
+    if nbytes > src.numel() * src.element_size() or (mode == 1 and nbytes > dst.numel() * dst.element_size()):
+        raise ValueError("nbytes exceeds a buffer")
+    if mode == 0 and dst.numel() * dst.element_size() < 16:
+        raise ValueError("the read probe's sink needs 16 bytes")
+    _check("engram_probe_stream", lib().engram_probe_stream(mode, flags, unroll, blocks, _ptr(src, "src"),
+                                                            _ptr(dst, "dst"), nbytes, _stream(stream)))

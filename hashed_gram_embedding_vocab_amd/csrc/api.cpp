@@ -551,4 +551,18 @@ engram_status engram_synth_fill_table(int32_t dtype, uint64_t seed, int32_t tau,
     return last_launch_status();
 }
 
+engram_status engram_probe_stream(int32_t mode, uint32_t flags, int32_t unroll, int32_t blocks,
+                                  const void *d_src, void *d_dst, int64_t bytes, hipStream_t stream) {
+    if (mode != 0 && mode != 1) return ENGRAM_E_INVALID_ARG;
+    if ((flags & ~(uint32_t)ENGRAM_PROBE_NONTEMPORAL) != 0) return ENGRAM_E_INVALID_ARG;
+    if (unroll != 4 && unroll != 8 && unroll != 16) return ENGRAM_E_INVALID_ARG;
+    if (blocks < 1 || blocks > (1 << 20)) return ENGRAM_E_INVALID_ARG;
+    if (!d_src || !d_dst || !aligned16(d_src) || !aligned16(d_dst)) return ENGRAM_E_INVALID_ARG;
+    if (bytes <= 0 || bytes % 16 != 0) return ENGRAM_E_INVALID_ARG;
+    if (!launch_stream_probe(mode, (flags & ENGRAM_PROBE_NONTEMPORAL) != 0, unroll, d_src, d_dst, bytes, blocks,
+                             stream))
+        return ENGRAM_E_INVALID_ARG;
+    return last_launch_status();
+}
+
 }  // extern "C"

@@ -343,5 +343,9 @@ void launch_copy_f32(const float *src, float *dst, int64_t n, hipStream_t s);  /
 
 void launch_synth_fill(engram_dtype dt, uint64_t seed, int32_t tau, int64_t rows, int32_t head_dim,
                        void *table, hipStream_t s);
+// Streaming read (mode 0) or copy (mode 1) of bytes (a multiple of 16);
+// false if unroll is not 4, 8 or 16.
+bool launch_stream_probe(int mode, bool nontemporal, int unroll, const void *src, void *dst, int64_t bytes,
+                         int blocks, hipStream_t s);
 
 }  // namespace engram

@@ -267,3 +267,21 @@ def test_profiling_argument_checks(B):
     assert L.engram_profile_begin(None, 8, 0) == B.E_INVALID_ARG
     assert L.engram_profile_begin(p._h, 0, 0) == B.E_INVALID_ARG
     assert L.engram_profile_begin(p._h, 8, 1 << 30) == B.E_INVALID_ARG
+
+
+def test_probe_stream_rejects_bad_arguments_before_launching(B):
+    _no_gpu()
+    L = B.lib()
+    fake = C.c_void_p(0x10000)
+    odd = C.c_void_p(0x10008)
+    ok_args = dict(mode=0, flags=0, unroll=8, blocks=2048, src=fake, dst=fake, nbytes=1 << 20)
+
+    def call(**kw):
+        a = dict(ok_args, **kw)
+        return L.engram_probe_stream(a["mode"], a["flags"], a["unroll"], a["blocks"], a["src"], a["dst"],
+                                     a["nbytes"], None)
+
+    for kw in [dict(mode=2), dict(mode=-1), dict(flags=2), dict(unroll=5), dict(unroll=32), dict(blocks=0),
+               dict(blocks=(1 << 20) + 1), dict(src=None), dict(dst=None), dict(src=odd), dict(dst=odd),
+               dict(nbytes=0), dict(nbytes=-16), dict(nbytes=1000)]:
+        assert call(**kw) == B.E_INVALID_ARG, kw
