@@ -28,6 +28,7 @@ CONV_LINEAR, CONV_SILU_SKIP = 0, 1
 OUT_DELTA = 1
 RETRIEVE_IN_PROJECTION = 2  # engram_forward: short chunks retrieve inside the projection launch
 MAX_TABLES, MAX_BRANCHES = 32, 4
+NOALLOC_SCRATCH_BYTES = 64 << 20  # ENGRAM_NOALLOC_SCRATCH_BYTES
 KERNEL_NAMES = ("hash", "gather", "gemm", "fuse", "aux", "gemm_v", "gate", "seam", "bwd_gemm", "bwd_fuse",
                 "bwd_table")
 
@@ -105,6 +106,9 @@ def lib() -> C.CDLL:
         L.engram_forward.restype = C.c_int
         L.engram_forward.argtypes = [P, P, i32, i32, P, P, P, P, C.POINTER(WeightsC), P, P, P, u32,
                                      P, C.c_size_t, P, P]
+        L.engram_forward_noalloc.restype = C.c_int
+        L.engram_forward_noalloc.argtypes = [P, P, i32, i32, P, P, P, P, C.POINTER(WeightsC), P, P, P, u32,
+                                             P, P]
         L.engram_backward_workspace_size.restype = C.c_size_t
         L.engram_backward_workspace_size.argtypes = [P, i32, i32]
         L.engram_backward.restype = C.c_int
@@ -392,6 +396,20 @@ class Plan:
             _ptr(conv_state, "conv_state", torch.float32), _ptr(out, "out", self.torch_dtype),
             _ptr(alpha, "alpha", torch.float32), flags, _ptr(workspace, "workspace"),
             workspace.numel() * workspace.element_size(),
+            _ptr(bad_tokens, "bad_tokens", (torch.int32, torch.uint32)), _stream(stream)))
+
+    def engram_forward_noalloc(self, tokens, comp_map, tables: Sequence[torch.Tensor], h, weights: Weights,
+                               out, prev_ctx=None, conv_state=None, alpha=None, flags: int = 0,
+                               bad_tokens=None, stream=None):
+        """engram_forward on the library's per-GPU scratch array (no workspace argument)."""
+        batch, seqlen = tokens.shape
+        ptrs = (C.c_void_p * len(tables))(*[_table_ptr(t) for t in tables])
+        _check("engram_forward_noalloc", lib().engram_forward_noalloc(
+            self._h, _ptr(tokens, "tokens", torch.int32), batch, seqlen,
+            _ptr(comp_map, "comp_map", torch.int32), _ptr(prev_ctx, "prev_ctx", torch.int32), ptrs,
+            _ptr(h, "h", self.torch_dtype), C.byref(weights.c),
+            _ptr(conv_state, "conv_state", torch.float32), _ptr(out, "out", self.torch_dtype),
+            _ptr(alpha, "alpha", torch.float32), flags,
             _ptr(bad_tokens, "bad_tokens", (torch.int32, torch.uint32)), _stream(stream)))
 
     def engram_backward_workspace_size(self, batch: int, seqlen: int) -> int:

@@ -317,6 +317,34 @@ ENGRAM_API engram_status engram_forward(engram_plan p, const int32_t *d_tokens, 
                              float *d_alpha, uint32_t flags, void *d_workspace,
                              size_t workspace_bytes, uint32_t *d_bad_tokens, hipStream_t stream);
 
+/*
+ * engram_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments and results (bit for bit) as engram_forward, minus the
+ * workspace: the library keeps one scratch array of
+ * ENGRAM_NOALLOC_SCRATCH_BYTES on each GPU it runs on (a device variable of
+ * the library's code object, held until the process ends) and runs
+ * engram_forward's kernels on it.  The call allocates and frees nothing; its
+ * first call on a device looks the array's address up once.
+ *   - A call whose engram_workspace_size(p, batch, seqlen) exceeds
+ *     ENGRAM_NOALLOC_SCRATCH_BYTES returns ENGRAM_E_UNSUPPORTED and launches
+ *     nothing (64 MiB covers, for example, 256 one-token sequences of four
+ *     branches at d = 2560, or a 4096-token chunk at d = 2560 with 16 tables
+ *     of 80 dims).
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap in
+ *     time on the same GPU (other streams, other host threads) race and give
+ *     wrong results.  The caller serialises them, for instance by issuing them
+ *     all on one stream.  Calls on different GPUs do not interact.
+ *   - ENGRAM_E_DEVICE if the runtime cannot give the array's address.
+ */
+#define ENGRAM_NOALLOC_SCRATCH_BYTES (64u << 20)
+ENGRAM_API engram_status engram_forward_noalloc(engram_plan p, const int32_t *d_tokens, int32_t batch,
+                                                int32_t seqlen, const int32_t *d_comp_map, int32_t *d_prev_ctx,
+                                                const void *const *table_ptrs, const void *d_h,
+                                                const engram_weights *w, float *d_conv_state, void *d_out,
+                                                float *d_alpha, uint32_t flags, uint32_t *d_bad_tokens,
+                                                hipStream_t stream);
+
 /* Gradients written by engram_backward (fp32, caller-owned device memory,
  * overwritten). */
 typedef struct {

@@ -285,3 +285,26 @@ def test_probe_stream_rejects_bad_arguments_before_launching(B):
                dict(blocks=(1 << 20) + 1), dict(src=None), dict(dst=None), dict(src=odd), dict(dst=odd),
                dict(nbytes=0), dict(nbytes=-16), dict(nbytes=1000)]:
         assert call(**kw) == B.E_INVALID_ARG, kw
+
+
+def test_noalloc_forward_rejects_before_touching_a_device(B):
+    """engram_forward_noalloc: bad plans and shapes, and calls whose workspace
+    would exceed the library's scratch array, return before any device call."""
+    _no_gpu()
+    L = B.lib()
+    p = B.Plan(vocab=32000, vocab_comp=24640, heads=8, head_dim=64, table_rows=[500009] * 16, hash_seed=1,
+               d_model=1024, dtype=B.BF16)
+    fake = C.c_void_p(0x10000)
+    tabs = (C.c_void_p * 16)(*([0x10000] * 16))
+    w = B.WeightsC()
+
+    def call(plan, batch, seqlen):
+        return L.engram_forward_noalloc(plan, fake, batch, seqlen, fake, None, tabs, fake, C.byref(w), None, fake,
+                                        None, 0, None, None)
+
+    assert call(None, 8, 64) == B.E_INVALID_ARG
+    assert call(p._h, 0, 64) == B.E_INVALID_ARG
+    assert call(p._h, 8, -1) == B.E_INVALID_ARG
+    # 8 x 4096 tokens at d = 1024 need about 72 MiB of workspace: beyond the scratch
+    assert p.engram_workspace_size(8, 4096) > B.NOALLOC_SCRATCH_BYTES
+    assert call(p._h, 8, 4096) == B.E_UNSUPPORTED
