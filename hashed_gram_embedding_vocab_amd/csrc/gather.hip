@@ -9,6 +9,10 @@
 // in flight (indices first, then all row loads, then all stores) so enough
 // random reads are outstanding to cover HBM latency.  Zipf-hot rows are
 // re-served by L2 and the Infinity Cache without any explicit reuse logic.
+// Row loads are nontemporal: measured on the 200 GB tables, the fused
+// retrieval took 42.3 us per 32k tokens against 44.6 with ordinary loads (Zipf
+// tokens) and 42.4 against 46.8 (uniform tokens); nontemporal E stores were
+// slower (E is read again right away by the projections).
 #include "engram_internal.h"
 
 namespace engram {
@@ -16,7 +20,24 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 8;    // chunks in flight per thread (index-driven gather)
-constexpr int kHGUnroll = 10; // row chunks in flight per thread in the fused kernel
+#ifndef ENGRAM_HG_UNROLL
+#define ENGRAM_HG_UNROLL 10
+#endif
+#ifndef ENGRAM_HG_NT
+#define ENGRAM_HG_NT 1
+#endif
+constexpr int kHGUnroll = ENGRAM_HG_UNROLL; // row chunks in flight per thread in the fused kernel
+constexpr bool kNtRows = (ENGRAM_HG_NT & 1) != 0;  // nontemporal row loads
+constexpr bool kNtEmb = (ENGRAM_HG_NT & 2) != 0;   // nontemporal E stores
+
+__device__ __forceinline__ u32x4_t load_row_chunk(const u32x4_t *p) {
+    if constexpr (kNtRows) return __builtin_nontemporal_load(p);
+    return *p;
+}
+__device__ __forceinline__ void store_emb_chunk(u32x4_t *p, u32x4_t v) {
+    if constexpr (kNtEmb) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
 
 __device__ __forceinline__ uint64_t div_magic(uint64_t n, uint64_t magic, int32_t d) {
     // floor(n / d) for n < 2^40 with magic = floor(2^64 / d) + 1; d == 1 -> n
@@ -46,12 +67,12 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherConsts gc,
         const uint32_t r = min(row[u], gc.last_row[tau[u]]);
         const u32x4_t *src = reinterpret_cast<const u32x4_t *>(gc.table[tau[u]]) +
                            (int64_t)r * gc.row_chunks + ch[u];
-        val[u] = *src;
+        val[u] = load_row_chunk(src);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
         const int64_t c = base + u * kThreads;
-        if (c < total_chunks) emb[c] = val[u];
+        if (c < total_chunks) store_emb_chunk(emb + c, val[u]);
     }
 }
 
@@ -108,12 +129,12 @@ __global__ __launch_bounds__(kThreads) void hash_gather_kernel(
             const int tau = (int)div_magic((uint64_t)rem, gc.magic_row, gc.row_chunks);
             const int ch = rem - tau * gc.row_chunks;
             const uint32_t r = slot_s[tl * n_tables + tau];
-            val[u] = reinterpret_cast<const u32x4_t *>(gc.table[tau])[(int64_t)r * gc.row_chunks + ch];
+            val[u] = load_row_chunk(reinterpret_cast<const u32x4_t *>(gc.table[tau]) + (int64_t)r * gc.row_chunks + ch);
         }
 #pragma unroll
         for (int u = 0; u < kHGUnroll; ++u) {
             const int c = c0 + u * kThreads;
-            if (c < chunks) dst[c] = val[u];
+            if (c < chunks) store_emb_chunk(dst + c, val[u]);
         }
     }
 }
