@@ -76,6 +76,8 @@ def parse():
     ap.add_argument("--no-hbm-probe", action="store_true",
                     help="skip the streaming read/copy ceilings and the extra gather legs")
     ap.add_argument("--probe-gib", type=float, default=4.0, help="buffer size of the streaming ceilings")
+    ap.add_argument("--state-dtype", choices=("f32", "bf16"), default=None,
+                    help="element type of the carried conv state (default: the workload's; bf16 at decode)")
     return ap.parse_args()
 
 
@@ -182,6 +184,9 @@ def main():
     B.lib()
     torch.cuda.set_device(0)
     wl = W.workload(args.workload)
+    if args.state_dtype is not None:
+        import dataclasses
+        wl = dataclasses.replace(wl, state_dtype=args.state_dtype)
     if args.backward:
         backward_bench(args, wl)
         return
@@ -201,7 +206,7 @@ def main():
         ctx = conv = None
         if wl.decode:
             ctx = to_device(dl.li.prev_ctx, torch.int32, "cuda")
-            conv = to_device(dl.li.conv_state, torch.float32, "cuda")
+            conv = to_device(dl.li.conv_state, dl.plan.state_torch_dtype, "cuda")
         layers.append((dl, hs, out, ws, ctx, conv))
     toks = [to_device(W.make_tokens(wl, seed=wl.seed(2) + 17 * r), torch.int32, "cuda") for r in range(R)]
     torch.cuda.synchronize()
@@ -271,6 +276,7 @@ def main():
     # (flops); retrieval and the fusion kernel are HBM-bound (bytes).
     De, d, Br = wl.emb_dim, wl.d_model, wl.n_branches
     eb = 2 if wl.dtype == "bf16" else 4
+    state_eb = 2 if wl.state_dtype == "bf16" else 4
     two_launch = kern("gemm_v")[1] > 0
     n_parts = d // 128 if wl.dtype == "bf16" else 1
     # engram_forward retrieves in one kernel (hash + gather): it reads each raw
@@ -290,9 +296,10 @@ def main():
         "seam": ("hbm", (n_tok // 256) * (6 * d * 4 + 3 * Br * (2 * d * eb + 16))),
         # reads v (fp32) once, h once per branch and the partial sums (the
         # gate is computed there); writes out per branch; with a carried conv
-        # state, reads and rewrites its K_c-1 fp32 rows per sequence and branch
+        # state, reads and rewrites its K_c-1 rows (fp32 or bf16) per sequence
+        # and branch
         "fuse": ("hbm", n_tok * (4 * d + Br * 2 * d * eb) + part_bytes
-                 + (2 * Br * wl.batch * (wl.conv_kernel - 1) * d * 4 if wl.decode else 0)),
+                 + (2 * Br * wl.batch * (wl.conv_kernel - 1) * d * state_eb if wl.decode else 0)),
     }
     # HBM bytes of the projection launches as well (E, weights, h, partials,
     # and v or out): the W_v launch sits close to both roofs
@@ -389,6 +396,7 @@ def main():
                    "n_branches": Br, "d_model": d, "heads_per_order": wl.heads,
                    "head_dim": wl.head_dim, "emb_dim": De, "table_params": sum(wl.primes()) * wl.head_dim,
                    "rotated_buffers": R, "parallelism": "single GPU",
+                   "conv_state_dtype": wl.state_dtype if wl.decode else None,
                    "retrieval_in_projection": bool(fwd_flags)},
         "roofline": roofline,
         "gather": gather,

@@ -46,6 +46,7 @@ class Config(C.Structure):
         ("table_rows", C.c_uint32 * MAX_TABLES), ("hash_seed", C.c_uint64),
         ("d_model", C.c_int32), ("n_branches", C.c_int32), ("conv_kernel", C.c_int32),
         ("conv_mode", C.c_int32), ("rms_eps", C.c_float), ("dtype", C.c_int32),
+        ("state_dtype", C.c_int32),
     ]
 
 
@@ -310,7 +311,7 @@ class Plan:
     def __init__(self, vocab: int, vocab_comp: int, heads: int, head_dim: int,
                  table_rows: Sequence[int], hash_seed: int, d_model: int, n_branches: int = 1,
                  conv_kernel: int = 4, conv_mode: int = CONV_LINEAR, rms_eps: float = 1e-6,
-                 dtype: int = BF16, orders: Sequence[int] = (2, 3)):
+                 dtype: int = BF16, orders: Sequence[int] = (2, 3), state_dtype: int = F32):
         cfg = Config()
         cfg.vocab, cfg.vocab_comp = vocab, vocab_comp
         cfg.n_orders = len(orders)
@@ -324,7 +325,9 @@ class Plan:
         cfg.hash_seed = hash_seed & 0xFFFFFFFFFFFFFFFF
         cfg.d_model, cfg.n_branches = d_model, n_branches
         cfg.conv_kernel, cfg.conv_mode, cfg.rms_eps, cfg.dtype = conv_kernel, conv_mode, rms_eps, dtype
+        cfg.state_dtype = state_dtype
         self.cfg = cfg
+        self.state_torch_dtype = _torch_dtype(state_dtype)
         self.n_tables = len(orders) * heads
         self.emb_dim = self.n_tables * head_dim
         self.dtype = dtype
@@ -379,7 +382,7 @@ class Plan:
                          conv_state=None, alpha=None, flags: int = 0, stream=None):
         _check("engram_gate_fuse", lib().engram_gate_fuse(
             self._h, _ptr(emb, "emb", self.torch_dtype), _ptr(h, "h", self.torch_dtype), batch, seqlen,
-            C.byref(weights.c), _ptr(conv_state, "conv_state", torch.float32),
+            C.byref(weights.c), _ptr(conv_state, "conv_state", self.state_torch_dtype),
             _ptr(out, "out", self.torch_dtype), _ptr(alpha, "alpha", torch.float32), flags,
             _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
             _stream(stream)))
@@ -393,7 +396,7 @@ class Plan:
             self._h, _ptr(tokens, "tokens", torch.int32), batch, seqlen,
             _ptr(comp_map, "comp_map", torch.int32), _ptr(prev_ctx, "prev_ctx", torch.int32), ptrs,
             _ptr(h, "h", self.torch_dtype), C.byref(weights.c),
-            _ptr(conv_state, "conv_state", torch.float32), _ptr(out, "out", self.torch_dtype),
+            _ptr(conv_state, "conv_state", self.state_torch_dtype), _ptr(out, "out", self.torch_dtype),
             _ptr(alpha, "alpha", torch.float32), flags, _ptr(workspace, "workspace"),
             workspace.numel() * workspace.element_size(),
             _ptr(bad_tokens, "bad_tokens", (torch.int32, torch.uint32)), _stream(stream)))
@@ -408,7 +411,7 @@ class Plan:
             self._h, _ptr(tokens, "tokens", torch.int32), batch, seqlen,
             _ptr(comp_map, "comp_map", torch.int32), _ptr(prev_ctx, "prev_ctx", torch.int32), ptrs,
             _ptr(h, "h", self.torch_dtype), C.byref(weights.c),
-            _ptr(conv_state, "conv_state", torch.float32), _ptr(out, "out", self.torch_dtype),
+            _ptr(conv_state, "conv_state", self.state_torch_dtype), _ptr(out, "out", self.torch_dtype),
             _ptr(alpha, "alpha", torch.float32), flags,
             _ptr(bad_tokens, "bad_tokens", (torch.int32, torch.uint32)), _stream(stream)))
 

@@ -97,7 +97,7 @@ engram_status do_hash_gather(engram_plan_s &p, const int32_t *tokens, int32_t ba
 
 engram_status check_fuse_args(const engram_plan_s *p, const void *emb, const void *h, int32_t batch,
                               int32_t seqlen, const engram_weights *w, const void *out,
-                              const float *alpha, const float *conv_state, uint32_t flags,
+                              const float *alpha, const void *conv_state, uint32_t flags,
                               const void *ws, size_t ws_bytes) {
     if (!p || !emb || !h || !w || !out || !ws) return ENGRAM_E_INVALID_ARG;
     if (batch <= 0 || seqlen <= 0) return ENGRAM_E_INVALID_ARG;
@@ -151,7 +151,7 @@ bool retrieval_in_projection(const engram_plan_s &p, int32_t batch, int32_t seql
 }
 
 engram_status do_fuse(engram_plan_s &p, const void *emb, const void *h, int32_t batch, int32_t seqlen,
-                      const engram_weights *w, float *conv_state, void *out, float *alpha,
+                      const engram_weights *w, void *conv_state, void *out, float *alpha,
                       uint32_t flags, void *ws, hipStream_t s,
                       const CtxUpdate &ctx = CtxUpdate{}, const InLaunchRetrieval *rin = nullptr) {
     Layout L;
@@ -238,6 +238,7 @@ engram_status do_fuse(engram_plan_s &p, const void *emb, const void *h, int32_t 
         pv.conv_w = w->conv_w;
         pv.conv_state = conv_state;
         pv.state_stage = stage;
+        pv.state_bf16 = p.state_bf16;
         pv.alpha = gate;
         pv.seam_v = reinterpret_cast<float *>(base + L.seam);
         pv.batch = batch;
@@ -259,6 +260,7 @@ engram_status do_fuse(engram_plan_s &p, const void *emb, const void *h, int32_t 
             sa.out = out;
             sa.conv_w = w->conv_w;
             sa.conv_state = conv_state;
+            sa.state_bf16 = p.state_bf16;
             sa.n_tok = n_tok;
             sa.n_tiles = n_tiles;
             sa.batch = batch;
@@ -275,7 +277,7 @@ engram_status do_fuse(engram_plan_s &p, const void *emb, const void *h, int32_t 
         // a chunk of at most kFusePositions positions is one fusion-kernel
         // workgroup per sequence and channel stripe, which reads a state row
         // before it writes it: the state is updated in place
-        if (stage && seqlen <= kFusePositions) stage = conv_state;
+        const bool in_place = stage && seqlen <= kFusePositions;
         // the fusion kernel computes the gate itself (the same function as
         // the gate kernel), and the carried context
         FuseArgs fa{};
@@ -289,7 +291,10 @@ engram_status do_fuse(engram_plan_s &p, const void *emb, const void *h, int32_t 
         fa.out = out;
         fa.conv_w = w->conv_w;
         fa.conv_state = conv_state;
-        fa.state_stage = stage;
+        fa.state_stage = in_place ? conv_state : stage;
+        fa.state_bf16 = p.state_bf16;
+        fa.stage_bf16 = in_place && p.state_bf16;
+        if (in_place) stage = nullptr;
         fa.batch = batch;
         fa.seqlen = seqlen;
         fa.d = p.cfg.d_model;
@@ -301,10 +306,14 @@ engram_status do_fuse(engram_plan_s &p, const void *emb, const void *h, int32_t 
         launch_fuse(fa, p.cfg.dtype, s);
     }
     if (last_launch_status() != ENGRAM_OK) return ENGRAM_E_DEVICE;
-    if (stage && stage != conv_state) {
+    if (stage) {
+        // the staged rows (fp32) become the new state
         Launch l(p, ENGRAM_K_AUX, s);
-        const size_t bytes = (size_t)Br * batch * (p.cfg.conv_kernel - 1) * p.cfg.d_model * 4;
-        launch_copy_f32(stage, conv_state, (int64_t)(bytes / 4), s);
+        const int64_t n = (int64_t)Br * batch * (p.cfg.conv_kernel - 1) * p.cfg.d_model;
+        if (p.state_bf16)
+            launch_f32_to_bf16(stage, static_cast<uint16_t *>(conv_state), n, s);
+        else
+            launch_copy_f32(stage, static_cast<float *>(conv_state), n, s);
     }
     return ENGRAM_OK;
 }
@@ -395,6 +404,8 @@ engram_status engram_plan_create(const engram_config *cfg, engram_plan *out) {
     if (c.conv_kernel < 1 || c.conv_kernel > 4) return ENGRAM_E_INVALID_ARG;
     if (c.conv_mode != ENGRAM_CONV_LINEAR && c.conv_mode != ENGRAM_CONV_SILU_SKIP) return ENGRAM_E_INVALID_ARG;
     if (!(c.rms_eps >= 0.f)) return ENGRAM_E_INVALID_ARG;
+    if (c.state_dtype != ENGRAM_F32 && !(c.state_dtype == ENGRAM_BF16 && c.dtype == ENGRAM_BF16))
+        return ENGRAM_E_INVALID_ARG;
 
     engram_plan_s *p = new (std::nothrow) engram_plan_s();
     if (!p) return ENGRAM_E_NOMEM;
@@ -402,6 +413,7 @@ engram_status engram_plan_create(const engram_config *cfg, engram_plan *out) {
     p->n_tables = n_tables;
     p->emb_dim = n_tables * c.head_dim;
     p->elem = elem;
+    p->state_bf16 = c.state_dtype == ENGRAM_BF16;
     p->hc.n_tables = n_tables;
     p->hc.vocab = c.vocab;
     p->hc.vocab_comp = c.vocab_comp;
@@ -444,7 +456,7 @@ engram_status engram_gather(engram_plan p, const uint32_t *d_idx, int64_t n_toke
 }
 
  engram_status engram_gate_fuse(engram_plan p, const void *d_emb, const void *d_h, int32_t batch,
-                               int32_t seqlen, const engram_weights *w, float *d_conv_state,
+                               int32_t seqlen, const engram_weights *w, void *d_conv_state,
                                void *d_out, float *d_alpha, uint32_t flags, void *d_workspace,
                                size_t workspace_bytes, hipStream_t stream) {
     engram_status st = check_fuse_args(p, d_emb, d_h, batch, seqlen, w, d_out, d_alpha, d_conv_state,
@@ -457,7 +469,7 @@ engram_status engram_gather(engram_plan p, const uint32_t *d_idx, int64_t n_toke
 engram_status engram_forward(engram_plan p, const int32_t *d_tokens, int32_t batch, int32_t seqlen,
                              const int32_t *d_comp_map, int32_t *d_prev_ctx,
                              const void *const *table_ptrs, const void *d_h,
-                             const engram_weights *w, float *d_conv_state, void *d_out,
+                             const engram_weights *w, void *d_conv_state, void *d_out,
                              float *d_alpha, uint32_t flags, void *d_workspace,
                              size_t workspace_bytes, uint32_t *d_bad_tokens, hipStream_t stream) {
     if (!p || !d_workspace) return ENGRAM_E_INVALID_ARG;

@@ -50,7 +50,7 @@ extern "C" {
 engram_status engram_forward_noalloc(engram_plan p, const int32_t *d_tokens, int32_t batch, int32_t seqlen,
                                      const int32_t *d_comp_map, int32_t *d_prev_ctx,
                                      const void *const *table_ptrs, const void *d_h, const engram_weights *w,
-                                     float *d_conv_state, void *d_out, float *d_alpha, uint32_t flags,
+                                     void *d_conv_state, void *d_out, float *d_alpha, uint32_t flags,
                                      uint32_t *d_bad_tokens, hipStream_t stream) {
     if (!p || batch <= 0 || seqlen <= 0) return ENGRAM_E_INVALID_ARG;
     const size_t need = engram_workspace_size(p, batch, seqlen);

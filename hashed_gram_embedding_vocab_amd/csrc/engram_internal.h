@@ -133,8 +133,9 @@ struct ProjArgs {
     // fused value launch only (gate, gated value, conv, residual in the epilogue)
     void *out;                             // [B_r][n_tok][d]
     const float *conv_w;                   // [d][K_c]
-    const float *conv_state;               // [B_r][batch][K_c-1][d] or null
-    float *state_stage;                    // [B_r][batch][K_c-1][d] or null
+    const void *conv_state;                // [B_r][batch][K_c-1][d] fp32 (bf16 if state_bf16) or null
+    float *state_stage;                    // [B_r][batch][K_c-1][d] fp32 or null
+    int32_t state_bf16;                    // conv_state holds bf16 values
     const float *alpha;                    // [B_r][n_tok], from the gate kernel
     float *seam_v;                         // [token tiles][6][d] fp32 v of each tile's first and last 3 rows
     int32_t batch, seqlen, conv_k, conv_mode;
@@ -250,10 +251,11 @@ struct SeamArgs {
     const void *h;             // [B_r][n_tok][d] bf16
     void *out;                 // [B_r][n_tok][d] bf16
     const float *conv_w;       // [d][K_c]
-    const float *conv_state;   // [B_r][batch][K_c-1][d] or null
+    const void *conv_state;    // [B_r][batch][K_c-1][d] fp32 (bf16 if state_bf16) or null
     int64_t n_tok;
     int32_t n_tiles, batch, seqlen, d, n_branches, conv_k, conv_mode;
     uint32_t flags;
+    int32_t state_bf16;
 };
 
 void launch_seam(const SeamArgs &a, hipStream_t s);
@@ -267,8 +269,10 @@ struct FuseArgs {
     const void *h;             // [B_r][n_tok][d]
     void *out;                 // [B_r][n_tok][d]
     const float *conv_w;       // [d][K_c]
-    const float *conv_state;   // [B_r][batch][K_c-1][d] or null
-    float *state_stage;        // [B_r][batch][K_c-1][d] or null
+    const void *conv_state;    // [B_r][batch][K_c-1][d] fp32 (bf16 if state_bf16) or null
+    void *state_stage;         // [B_r][batch][K_c-1][d] fp32 (bf16 if stage_bf16) or null
+    int32_t state_bf16;        // conv_state holds bf16 values
+    int32_t stage_bf16;        // state_stage is the bf16 conv state itself (updated in place)
     int32_t batch, seqlen, d, n_branches, n_parts, conv_k, conv_mode;
     float eps;
     uint32_t flags;
@@ -340,6 +344,8 @@ hipError_t launch_bwd_table_grad(const BwdTableArgs &t, hipStream_t s);
 // ---------------------------------------------------------------- synthetic tables
 // ---------------------------------------------------------------- copies
 void launch_copy_f32(const float *src, float *dst, int64_t n, hipStream_t s);  // n % 4 == 0
+// dst[i] = src[i] rounded to nearest-even bf16 (n % 4 == 0)
+void launch_f32_to_bf16(const float *src, uint16_t *dst, int64_t n, hipStream_t s);
 
 void launch_synth_fill(engram_dtype dt, uint64_t seed, int32_t tau, int64_t rows, int32_t head_dim,
                        void *table, hipStream_t s);

@@ -17,8 +17,8 @@
 // before the block's first position are recomputed from v (or taken from the
 // carried conv state at the sequence start).  Those values, the first
 // group's v and h and the gate partials (staged in LDS by the whole block)
-// are all requested before any of them is used: at decode the kernel makes
-// one round trip to memory before it stores.
+// and the conv taps are all requested before any of them is used: at decode
+// the kernel makes one round trip to memory before it stores.
 #include "engram_internal.h"
 
 namespace engram {
@@ -59,6 +59,17 @@ struct Raw4 {
 };
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + expf(-x)); }
+
+// Four consecutive values of a carried conv-state row (element offset off):
+// fp32, or bf16 widened exactly.
+__device__ __forceinline__ f32x4_t load_state4(const void *state, bool bf16, int64_t off) {
+    if (bf16) {
+        const u32x2_t x = *reinterpret_cast<const u32x2_t *>(reinterpret_cast<const uint16_t *>(state) + off);
+        return f32x4_t{bf16_to_f32(x[0] & 0xFFFFu), bf16_to_f32(x[0] >> 16), bf16_to_f32(x[1] & 0xFFFFu),
+                       bf16_to_f32(x[1] >> 16)};
+    }
+    return *reinterpret_cast<const f32x4_t *>(reinterpret_cast<const float *>(state) + off);
+}
 
 // The gate from the three sums over d of h*gamma_h*gamma_k*k, k^2 and h^2.
 __device__ __forceinline__ float gate_finish(float s_hk, float s_kk, float s_hh, int d, float eps) {
@@ -128,8 +139,8 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
         for (int m = 0; m < BR; ++m) {
             sprev[m][s - 1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             if (live && p < 0 && a.conv_state && s <= kc - 1)
-                sprev[m][s - 1] = *reinterpret_cast<const f32x4_t *>(
-                    a.conv_state + (((int64_t)m * a.batch + b) * (kc - 1) + (kc - 1 - s)) * d + c0);
+                sprev[m][s - 1] = load_state4(a.conv_state, a.state_bf16 != 0,
+                                              (((int64_t)m * a.batch + b) * (kc - 1) + (kc - 1 - s)) * d + c0);
         }
     }
     constexpr int kGroup = BR == 1 ? 8 : (BR == 2 ? 4 : 2);
@@ -146,6 +157,13 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
         }
     };
     if (live) load_group(t0);
+    // conv taps, wt[j][c] multiplying u_{t-j}: requested with the rest
+    float wt[4][kVec];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int c = 0; c < kVec; ++c)
+            wt[j][c] = (live && j < kc) ? a.conv_w[(int64_t)(c0 + c) * kc + (kc - 1 - j)] : 0.f;
 
     // Gates of positions pa .. t1-1 (the block's and up to three before it).
     // The whole block stages the partial sums in LDS, as many parts per
@@ -201,12 +219,6 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
 
     const bool silu = a.conv_mode == ENGRAM_CONV_SILU_SKIP;
     const bool delta = (a.flags & ENGRAM_OUT_DELTA) != 0;
-    float wt[4][kVec];  // wt[j][c] multiplies u_{t-j}
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int c = 0; c < kVec; ++c)
-            wt[j][c] = j < kc ? a.conv_w[(int64_t)(c0 + c) * kc + (kc - 1 - j)] : 0.f;
 
     // win[m][s-1][c] = u_{t-s}
     float win[BR][3][kVec];
@@ -252,10 +264,17 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
 #pragma unroll
         for (int m = 0; m < BR; ++m) {
             for (int j = 0; j < kc - 1; ++j) {
-                float *st = a.state_stage + (((int64_t)m * a.batch + b) * (kc - 1) + j) * d + c0;
+                const int64_t off = (((int64_t)m * a.batch + b) * (kc - 1) + j) * d + c0;
                 const int s = kc - 1 - j;  // u_{T-s}
+                float u4[kVec];
 #pragma unroll
-                for (int c = 0; c < kVec; ++c) st[c] = s == 1 ? win[m][0][c] : (s == 2 ? win[m][1][c] : win[m][2][c]);
+                for (int c = 0; c < kVec; ++c) u4[c] = s == 1 ? win[m][0][c] : (s == 2 ? win[m][1][c] : win[m][2][c]);
+                if (a.stage_bf16)
+                    *reinterpret_cast<u32x2_t *>(reinterpret_cast<uint16_t *>(a.state_stage) + off) =
+                        u32x2_t{pack_bf16x2(u4[0], u4[1]), pack_bf16x2(u4[2], u4[3])};
+                else
+                    *reinterpret_cast<f32x4_t *>(reinterpret_cast<float *>(a.state_stage) + off) =
+                        f32x4_t{u4[0], u4[1], u4[2], u4[3]};
             }
         }
     }
@@ -325,7 +344,8 @@ __global__ __launch_bounds__(256) void seam_kernel(SeamArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) u[s][r] = al[m][s] * vs[s][r];
             } else if (a.conv_state && s <= kc - 1) {
-                const float *st = a.conv_state + (((int64_t)m * a.batch + b) * (kc - 1) + (kc - 1) + pos - s) * d + c0;
+                const f32x4_t st = load_state4(a.conv_state, a.state_bf16 != 0,
+                                               (((int64_t)m * a.batch + b) * (kc - 1) + (kc - 1) + pos - s) * d + c0);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) u[s][r] = st[r];
             } else {
@@ -371,6 +391,22 @@ void launch_seam(const SeamArgs &a, hipStream_t s) {
 __global__ __launch_bounds__(256) void copy_f32_kernel(const f32x4_t *src, f32x4_t *dst, int64_t n4) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x)
         dst[i] = src[i];
+}
+
+__global__ __launch_bounds__(256) void f32_to_bf16_kernel(const f32x4_t *src, u32x2_t *dst, int64_t n4) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+        const f32x4_t x = src[i];
+        dst[i] = u32x2_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+    }
+}
+
+void launch_f32_to_bf16(const float *src, uint16_t *dst, int64_t n, hipStream_t s) {
+    const int64_t n4 = n / 4;
+    int64_t blocks = (n4 + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks < 1) blocks = 1;
+    launch_kernel(f32_to_bf16_kernel, dim3((unsigned)blocks), dim3(256), s, reinterpret_cast<const f32x4_t *>(src),
+                  reinterpret_cast<u32x2_t *>(dst), n4);
 }
 
 void launch_copy_f32(const float *src, float *dst, int64_t n, hipStream_t s) {

@@ -18,6 +18,7 @@ struct engram_plan_s {
     int32_t n_tables = 0;
     int32_t emb_dim = 0;    // D_e
     int32_t elem = 0;       // bytes per element of the plan dtype
+    bool state_bf16 = false;  // the carried conv state is bf16
     engram::HashConsts hc{};
     // profiling
     bool prof_on = false;

@@ -293,7 +293,9 @@ __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t 
     const uint32_t state_row_bytes = (uint32_t)d * 4u;
     const __amdgpu_buffer_rsrc_t hres = make_rsrc(a.h, branch_bytes * BR);
     const __amdgpu_buffer_rsrc_t ores = make_rsrc(a.out, branch_bytes * BR);
-    const __amdgpu_buffer_rsrc_t cres = make_rsrc(a.conv_state, state_branch_bytes * BR);
+    // a bf16 state has every byte offset of the fp32 layout halved
+    const bool state_bf16 = a.state_bf16 != 0;
+    const __amdgpu_buffer_rsrc_t cres = make_rsrc(a.conv_state, (state_branch_bytes * BR) >> (state_bf16 ? 1 : 0));
     const __amdgpu_buffer_rsrc_t sres = make_rsrc(a.state_stage, state_branch_bytes * BR);
     // the new state's rows are the gated values of the last K_c-1 positions
     const uint32_t stage_shift = (uint32_t)(a.seqlen - (kc - 1)) * state_row_bytes;
@@ -407,8 +409,15 @@ __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t 
                         f32x4_t c = {0.f, 0.f, 0.f, 0.f};
                         if (a.conv_state && s <= kc - 1) {
                             const uint32_t off = pos[j] < s ? sr + 64u * i : 0u;
-                            c = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                                cres, off, smoff + (kc - 1 - s) * (int)state_row_bytes, 0));
+                            const int soff = smoff + (kc - 1 - s) * (int)state_row_bytes;
+                            if (state_bf16) {
+                                const u32x2_t x = __builtin_bit_cast(
+                                    u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(cres, off >> 1, soff >> 1, 0));
+                                c = f32x4_t{bf16_to_f32(x[0] & 0xFFFFu), bf16_to_f32(x[0] >> 16),
+                                            bf16_to_f32(x[1] & 0xFFFFu), bf16_to_f32(x[1] >> 16)};
+                            } else {
+                                c = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(cres, off, soff, 0));
+                            }
                         }
                         if (pos[j] < s) sh[s - 1] = c;
                     }

@@ -90,6 +90,13 @@ typedef struct {
     int32_t conv_mode;   /* ENGRAM_CONV_LINEAR or ENGRAM_CONV_SILU_SKIP         */
     float rms_eps;       /* epsilon inside both RMSNorms (e.g. 1e-6)            */
     engram_dtype dtype;  /* dtype of tables, E, h, W_k, W_v and out             */
+    engram_dtype state_dtype; /* element type of the carried conv state: ENGRAM_F32
+                            (0, the default of a zeroed struct) or ENGRAM_BF16
+                            (bf16 plans only): the gated values a chunk carries
+                            are rounded to nearest-even bf16, which halves the
+                            state's traffic at decode; chunked calls then agree
+                            with one whole call within the bf16 tolerance
+                            rather than bit for bit                          */
 } engram_config;
 
 /* Device pointers to one layer's weights; all caller-owned and read-only.
@@ -287,11 +294,12 @@ ENGRAM_API engram_status engram_prefetch_finish(engram_prefetcher f, void *d_emb
  * with RMSNorm_g(x) = g * x / sqrt(mean(x^2) + eps).
  *   d_emb        [batch*seqlen][D_e], D_e = n_tables*d_e
  *   d_h, d_out   [n_branches][batch*seqlen][d]; d_out may alias d_h
- *   d_conv_state [n_branches][batch][K_c-1][d] fp32 gated values preceding
- *                position 0 (oldest first), or NULL for zeros.  When given it
- *                is replaced by the last K_c-1 gated values of the sequence
+ *   d_conv_state [n_branches][batch][K_c-1][d] gated values preceding
+ *                position 0 (oldest first), fp32 or bf16 as the plan's
+ *                state_dtype says, or NULL for zeros.  When given it is
+ *                replaced by the last K_c-1 gated values of the sequence
  *                extended by this chunk, so chunked prefill and decode equal
- *                one full prefill.
+ *                one full prefill (bit for bit with an fp32 state).
  *   d_alpha      optional [n_branches][batch*seqlen] fp32 gate values
  *   d_workspace  >= engram_workspace_size(p, batch, seqlen) bytes, 256-byte aligned
  * Supported: bf16 with d % 256 == 0, D_e % 128 == 0 and one branch of h
@@ -300,7 +308,7 @@ ENGRAM_API engram_status engram_prefetch_finish(engram_prefetcher f, void *d_emb
  * ENGRAM_E_UNSUPPORTED and launches nothing.
  */
 ENGRAM_API engram_status engram_gate_fuse(engram_plan p, const void *d_emb, const void *d_h, int32_t batch,
-                               int32_t seqlen, const engram_weights *w, float *d_conv_state,
+                               int32_t seqlen, const engram_weights *w, void *d_conv_state,
                                void *d_out, float *d_alpha, uint32_t flags, void *d_workspace,
                                size_t workspace_bytes, hipStream_t stream);
 
@@ -313,7 +321,7 @@ ENGRAM_API engram_status engram_gate_fuse(engram_plan p, const void *d_emb, cons
 ENGRAM_API engram_status engram_forward(engram_plan p, const int32_t *d_tokens, int32_t batch, int32_t seqlen,
                              const int32_t *d_comp_map, int32_t *d_prev_ctx,
                              const void *const *table_ptrs, const void *d_h,
-                             const engram_weights *w, float *d_conv_state, void *d_out,
+                             const engram_weights *w, void *d_conv_state, void *d_out,
                              float *d_alpha, uint32_t flags, void *d_workspace,
                              size_t workspace_bytes, uint32_t *d_bad_tokens, hipStream_t stream);
 
@@ -341,7 +349,7 @@ ENGRAM_API engram_status engram_forward(engram_plan p, const int32_t *d_tokens, 
 ENGRAM_API engram_status engram_forward_noalloc(engram_plan p, const int32_t *d_tokens, int32_t batch,
                                                 int32_t seqlen, const int32_t *d_comp_map, int32_t *d_prev_ctx,
                                                 const void *const *table_ptrs, const void *d_h,
-                                                const engram_weights *w, float *d_conv_state, void *d_out,
+                                                const engram_weights *w, void *d_conv_state, void *d_out,
                                                 float *d_alpha, uint32_t flags, uint32_t *d_bad_tokens,
                                                 hipStream_t stream);
 

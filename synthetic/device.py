@@ -52,7 +52,8 @@ def make_device_layer(wl: W.Workload, layer_slot: int = 0, device="cuda", batch:
     plan = B.Plan(vocab=wl.vocab, vocab_comp=wl.vocab_comp, heads=wl.heads, head_dim=wl.head_dim,
                   table_rows=primes, hash_seed=li.hash_seed, d_model=wl.d_model,
                   n_branches=wl.n_branches, conv_kernel=wl.conv_kernel, conv_mode=conv_mode,
-                  rms_eps=rms_eps, dtype=dt, orders=wl.orders)
+                  rms_eps=rms_eps, dtype=dt, orders=wl.orders,
+                  state_dtype=B.BF16 if wl.state_dtype == "bf16" else B.F32)
     tables = []
     if with_tables:
         for tau, p in enumerate(primes):

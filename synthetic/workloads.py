@@ -61,6 +61,7 @@ class Workload:
     layers: tuple = (0,)     # Engram insertion layers (hash seed low byte)
     decode: bool = False     # carries prev_ctx / conv_state from a context
     orders: tuple = (2, 3)
+    state_dtype: str = "f32"  # element type of the carried conv state ("f32" or "bf16")
 
     @property
     def vocab_comp(self) -> int:
@@ -130,7 +131,7 @@ WORKLOADS: Dict[str, Workload] = {
            dtype="bf16", d_model=2560, n_branches=4, layers=(2, 6)),
         _w(name="multibranch_decode", index=5, vocab=129280, batch=256, seqlen=1, zipf_s=1.05,
            heads=8, head_dim=80, table_target=2226562, same_prime=False,
-           dtype="bf16", d_model=2560, n_branches=4, layers=(2, 6), decode=True),
+           dtype="bf16", d_model=2560, n_branches=4, layers=(2, 6), decode=True, state_dtype="bf16"),
     ]
 }
 
@@ -285,4 +286,6 @@ def make_layer_inputs(wl: Workload, layer_slot: int = 0, batch: Optional[int] = 
                 np.int32).reshape(batch, 2)
         li.conv_state = rng_s.standard_normal(
             (Br, batch, wl.conv_kernel - 1, d), dtype=np.float32)
+        if wl.state_dtype == "bf16":  # a bf16 state holds bf16 values exactly
+            li.conv_state = round_to_bf16(li.conv_state)
     return li

@@ -74,6 +74,10 @@ def test_plan_validation(B):
     c = _cfg(B)
     c.orders[1] = 4
     assert _create(B, c) == B.E_INVALID_ARG
+    # the carried state may be bf16 only on bf16 plans
+    assert _create(B, _cfg(B, dtype=B.BF16, state_dtype=B.BF16)) == B.OK
+    assert _create(B, _cfg(B, dtype=B.F32, state_dtype=B.BF16)) == B.E_INVALID_ARG
+    assert _create(B, _cfg(B, dtype=B.BF16, state_dtype=7)) == B.E_INVALID_ARG
     # bf16 rows of 32 dims are 64 bytes: fine; 4 dims are 8 bytes: rejected
     assert _create(B, _cfg(B, dtype=B.BF16)) == B.OK
     assert _create(B, _cfg(B, dtype=B.BF16, head_dim=4)) == B.E_INVALID_ARG

@@ -353,14 +353,15 @@ def test_forward_multibranch_prefill_two_layers_sampled(B):
         torch.cuda.empty_cache()
 
 
-def test_forward_multibranch_decode_with_state(B):
-    wl = W.workload("multibranch_decode")
+@pytest.mark.parametrize("state_dtype", ["bf16", "f32"])
+def test_forward_multibranch_decode_with_state(B, state_dtype):
+    wl = dataclasses.replace(W.workload("multibranch_decode"), state_dtype=state_dtype)
     toks = W.make_tokens(wl)
     for slot in range(len(wl.layers)):
-        say("forward multibranch decode layer", wl.layers[slot])
+        say("forward multibranch decode layer", wl.layers[slot], "state", state_dtype)
         dl = make_device_layer(wl, layer_slot=slot)
         ctx = dev_i32(dl.li.prev_ctx)
-        state = to_device(dl.li.conv_state, torch.float32, "cuda")
+        state = to_device(dl.li.conv_state, dl.plan.state_torch_dtype, "cuda")
         out, alpha, bad = forward(dl, toks, prev_ctx=ctx, conv_state=state)
         assert bad == 0
         rows = np.arange(0, wl.batch, 7)
@@ -371,7 +372,7 @@ def test_forward_multibranch_decode_with_state(B):
         assert np.abs(host(alpha)[:, rows] - ref_alpha).max() <= alpha_tol("bf16")
         assert np.array_equal(ctx.cpu().numpy(), new_ctx)
         # new conv state = [old rows 1, 2, u_0]
-        st = state.cpu().numpy()
+        st = state.float().cpu().numpy()
         assert np.array_equal(st[:, :, :2], dl.li.conv_state[:, :, 1:])
         for r in rows[:8]:
             _, _, u = L.forward_range(int(r), 0, 1, want_u=True)
@@ -435,6 +436,68 @@ def test_forward_other_shapes_all_positions(B, dtype, d, heads, head_dim, orders
         assert_within(st.cpu().numpy(), L.new_conv_state(u), dtype, "new conv state")
     del dl
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("br,batch,seqlen", [
+    (2, 3, 255),   # sequences start 1 and 2 tokens before tile seams: the seam rows read the state
+    (1, 4, 254),
+    (3, 2, 40),    # the fused W_v path reads the state at sequence starts, stages, converts
+    (4, 5, 1),     # one-token chunks: the fusion kernel updates the bf16 state in place
+    (2, 3, 2),
+])
+def test_forward_bf16_state_all_positions(B, br, batch, seqlen):
+    """A bf16 conv state: the carried rows are read in bf16 on every route
+    (fused W_v epilogue, seam rows, fusion kernel) and the new state is the
+    last K_c-1 gated values rounded to bf16; every position against the
+    oracle run on the same (bf16-exact) carried values."""
+    say("bf16 state", br, batch, seqlen)
+    wl = dataclasses.replace(small_wl(n_branches=br, batch=batch, seqlen=seqlen), state_dtype="bf16")
+    dl = make_device_layer(wl)
+    assert dl.plan.state_torch_dtype == torch.bfloat16
+    toks = W.make_tokens(wl)
+    rng = np.random.default_rng(31 + seqlen)
+    ctx0 = rng.integers(0, wl.vocab_comp + 1, (batch, 2)).astype(np.int32)
+    st0 = W.round_to_bf16((0.5 * rng.standard_normal((br, batch, 3, wl.d_model))).astype(np.float32))
+    ctx = dev_i32(ctx0)
+    st = to_device(st0, torch.bfloat16, "cuda")
+    out, alpha, bad = forward(dl, toks, prev_ctx=ctx, conv_state=st)
+    assert bad == 0
+    idx, _, new_ctx = oracle_indices(wl, dl.li, toks, dl.comp_map_host, prev_ctx=ctx0)
+    L = oracle_layer(wl, dl.li, idx, batch, seqlen, conv_state=st0)
+    ref, ref_alpha, u = L.forward_all(want_u=True)
+    assert_within(host(out), ref, "bf16", "out (bf16 state)")
+    assert np.abs(host(alpha) - ref_alpha).max() <= alpha_tol("bf16")
+    assert np.array_equal(ctx.cpu().numpy(), new_ctx)
+    assert_within(st.float().cpu().numpy(), L.new_conv_state(u), "bf16", "new bf16 conv state")
+    del dl
+    torch.cuda.empty_cache()
+
+
+def test_chunked_prefill_and_decode_with_bf16_state(B):
+    """With a bf16 state the chunks carry rounded gated values: chunked calls
+    agree with one whole call, and with the oracle's unchunked pass, within
+    the bf16 tolerance (bit equality holds for the fp32 state)."""
+    say("chunks, bf16 state")
+    wl = dataclasses.replace(small_wl(n_branches=2, batch=3, seqlen=300), state_dtype="bf16")
+    dl = make_device_layer(wl)
+    toks = W.make_tokens(wl)
+    Br, d = wl.n_branches, wl.d_model
+    pad = np.full((wl.batch, 2), wl.vocab_comp, np.int32)
+    full, alpha_full, _ = forward(dl, toks, prev_ctx=dev_i32(pad),
+                                  conv_state=torch.zeros((Br, wl.batch, 3, d), dtype=torch.bfloat16, device="cuda"))
+    ctx = dev_i32(pad)
+    st = torch.zeros((Br, wl.batch, 3, d), dtype=torch.bfloat16, device="cuda")
+    parts = []
+    for a, b in [(0, 1), (1, 2), (2, 5), (5, 261), (261, 262), (262, 300)]:
+        h = _split(dl.h, Br, wl.batch, wl.seqlen, a, b)
+        o, _, _ = forward(dl, np.ascontiguousarray(toks[:, a:b]), prev_ctx=ctx, conv_state=st, h=h)
+        parts.append(o.view(Br, wl.batch, b - a, d))
+    chunked = host(torch.cat(parts, 2).view(Br, -1, d))
+    idx, _, _ = oracle_indices(wl, dl.li, toks, dl.comp_map_host)
+    ref, _, _ = oracle_layer(wl, dl.li, idx, wl.batch, wl.seqlen).forward_all()
+    assert_within(chunked, ref, "bf16", "chunked (bf16 state) vs oracle")
+    assert_within(host(full), ref, "bf16", "whole call vs oracle")
+    assert np.array_equal(ctx.cpu().numpy(), dl.comp_map_host[toks[:, -2:]])
 
 
 # ----------------------------------------------------------------------------

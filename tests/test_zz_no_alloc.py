@@ -46,7 +46,7 @@ def _run(B, dl, toks, ctx, state, h, noalloc):
     alpha = torch.full((Br, batch * seqlen), -1.0, dtype=torch.float32, device="cuda")
     bad = torch.zeros(1, dtype=torch.int32, device="cuda")
     ctx_d = None if ctx is None else dev_i32(ctx)
-    st_d = None if state is None else to_device(state, torch.float32, "cuda")
+    st_d = None if state is None else to_device(state, dl.plan.state_torch_dtype, "cuda")
     tok_d = dev_i32(toks)
     if noalloc:
         dl.plan.engram_forward_noalloc(tok_d, dl.comp_map, dl.tables, h, dl.weights, out, prev_ctx=ctx_d,
@@ -78,6 +78,8 @@ def _case(B, wl, shapes, with_state, bad_ids=False):
         if with_state:
             ctx = rng.integers(0, wl.vocab_comp + 1, (batch, 2)).astype(np.int32)
             state = rng.standard_normal((Br, batch, wl.conv_kernel - 1, d)).astype(np.float32)
+            if wl.state_dtype == "bf16":
+                state = W.round_to_bf16(state)
         ref = _run(B, dl, toks, ctx, state, h, noalloc=False)
         got = _run(B, dl, toks, ctx, state, h, noalloc=True)
         names = ("out", "alpha", "conv_state", "prev_ctx")
