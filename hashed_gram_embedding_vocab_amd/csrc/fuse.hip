@@ -282,39 +282,35 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
 
 }  // namespace
 
-// One thread per (seam row, 4 channels), branches in a loop.  Tile T > 0,
-// row rho < 3 (token t = 256 T + rho) belongs here when its sequence started
-// before the tile (position > rho): u_{t-s} for s > rho then comes from the
-// previous tile's last rows.  Same expressions, in the same order, as the
-// projection kernel's epilogue, so the bits match the unsplit computation.
+// One thread per (tile seam, 4 channels): the seam's three rows, every
+// branch.  Tile T > 0, row rho < 3 (token t = 256 T + rho) belongs here when
+// its sequence started before the tile (position > rho): u_{t-s} for s > rho
+// then comes from the previous tile's last rows.  The six v rows around the
+// seam (the previous tile's last three, this tile's first three), the taps
+// and the six gates per branch are requested once for all three rows, before
+// any arithmetic.  Same expressions, in the same order, as the projection
+// kernel's epilogue, so the bits match the unsplit computation.
 template <int BR, bool SILU>
 __global__ __launch_bounds__(256) void seam_kernel(SeamArgs a) {
     const int d = a.d;
     const int quads = d / 4;
     const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (x >= (int64_t)(a.n_tiles - 1) * 3 * quads) return;
+    if (x >= (int64_t)(a.n_tiles - 1) * quads) return;
     const int c0 = 4 * (int)(x % quads);
-    const int64_t rt = x / quads;
-    const int rho = (int)(rt % 3);
-    const int T = 1 + (int)(rt / 3);
-    const int64_t t = (int64_t)T * kTokTile + rho;
-    if (t >= a.n_tok) return;
-    const int b = (int)(t / a.seqlen);
-    const int pos = (int)(t - (int64_t)b * a.seqlen);
-    if (pos <= rho) return;  // the projection kernel finished this row
+    const int T = 1 + (int)(x / quads);
+    const int64_t tb = (int64_t)T * kTokTile;  // the tile's first token
+    if (tb >= a.n_tok) return;
     const int kc = a.conv_k;
     const int64_t n_tok = a.n_tok;
 
-    // Every load below is issued unconditionally from an index that is
-    // always valid (t - s >= 253 here), then selected: one memory round trip.
-    // v of tokens t - s (s = 0..3): seam row rho - s of tile T, or row
-    // 6 + rho - s of tile T-1 (its last three rows)
-    f32x4_t vs[4];
+    // vr[k + 3] = v of token tb + k, k = -3 .. 2: rows 3..5 of the previous
+    // tile's seam rows, then rows 0..2 of this tile's (tokens past the end:
+    // any valid row, never used)
+    f32x4_t vr[6];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        const int k = rho - s;
+    for (int k = -3; k < 3; ++k) {
         const int64_t row = k >= 0 ? (int64_t)T * 6 + k : (int64_t)(T - 1) * 6 + 6 + k;
-        vs[s] = *reinterpret_cast<const f32x4_t *>(a.seam_v + row * d + c0);
+        vr[k + 3] = *reinterpret_cast<const f32x4_t *>(a.seam_v + row * d + c0);
     }
     f32x4_t tap[4];  // tap[r][s] multiplies u_{t-s} of channel c0 + r
 #pragma unroll
@@ -324,51 +320,61 @@ __global__ __launch_bounds__(256) void seam_kernel(SeamArgs a) {
             const float w = a.conv_w[(int64_t)(c0 + r) * kc + max(kc - 1 - s, 0)];
             tap[r][s] = s < kc ? w : 0.f;
         }
-    const bool delta = (a.flags & ENGRAM_OUT_DELTA) != 0;
-    float al[BR][4];
-    u32x2_t h2[BR];
+    float al[BR][6];     // al[m][k + 3]: gate of token tb + k
+    u32x2_t h2[BR][3];   // h of rows 0..2
 #pragma unroll
     for (int m = 0; m < BR; ++m) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) al[m][s] = a.alpha[m * n_tok + t - s];
-        h2[m] = *reinterpret_cast<const u32x2_t *>(reinterpret_cast<const uint16_t *>(a.h) +
-                                                   ((int64_t)m * n_tok + t) * d + c0);
+        for (int k = -3; k < 3; ++k) al[m][k + 3] = a.alpha[m * n_tok + min(tb + k, n_tok - 1)];
+#pragma unroll
+        for (int rho = 0; rho < 3; ++rho)
+            h2[m][rho] = *reinterpret_cast<const u32x2_t *>(reinterpret_cast<const uint16_t *>(a.h) +
+                                                            ((int64_t)m * n_tok + min(tb + rho, n_tok - 1)) * d + c0);
     }
+    const bool delta = (a.flags & ENGRAM_OUT_DELTA) != 0;
 
 #pragma unroll
-    for (int m = 0; m < BR; ++m) {
-        float u[4][4];  // u[s][r] = u_{t-s} of channel c0 + r
+    for (int rho = 0; rho < 3; ++rho) {
+        const int64_t t = tb + rho;
+        if (t >= n_tok) break;
+        const int b = (int)(t / a.seqlen);
+        const int pos = (int)(t - (int64_t)b * a.seqlen);
+        if (pos <= rho) continue;  // the projection kernel finished this row
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            if (pos - s >= 0) {
+        for (int m = 0; m < BR; ++m) {
+            float u[4][4];  // u[s][r] = u_{t-s} of channel c0 + r
 #pragma unroll
-                for (int r = 0; r < 4; ++r) u[s][r] = al[m][s] * vs[s][r];
-            } else if (a.conv_state && s <= kc - 1) {
-                const f32x4_t st = load_state4(a.conv_state, a.state_bf16 != 0,
-                                               (((int64_t)m * a.batch + b) * (kc - 1) + (kc - 1) + pos - s) * d + c0);
+            for (int s = 0; s < 4; ++s) {
+                if (pos - s >= 0) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) u[s][r] = st[r];
-            } else {
+                    for (int r = 0; r < 4; ++r) u[s][r] = al[m][rho - s + 3] * vr[rho - s + 3][r];
+                } else if (a.conv_state && s <= kc - 1) {
+                    const f32x4_t st = load_state4(a.conv_state, a.state_bf16 != 0,
+                                                   (((int64_t)m * a.batch + b) * (kc - 1) + (kc - 1) + pos - s) * d + c0);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) u[s][r] = 0.f;
+                    for (int r = 0; r < 4; ++r) u[s][r] = st[r];
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) u[s][r] = 0.f;
+                }
             }
-        }
-        float o[4];
+            float o[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float conv = tap[r][0] * u[0][r] + tap[r][1] * u[1][r] + tap[r][2] * u[2][r] + tap[r][3] * u[3][r];
-            const float y = SILU ? u[0][r] + conv * sigmoidf_(conv) : conv;
-            const uint32_t hw = h2[m][r >> 1];
-            const float hval = bf16_to_f32((r & 1) ? (hw >> 16) : (hw & 0xFFFFu));
-            o[r] = delta ? y : hval + y;
+            for (int r = 0; r < 4; ++r) {
+                const float conv = tap[r][0] * u[0][r] + tap[r][1] * u[1][r] + tap[r][2] * u[2][r] + tap[r][3] * u[3][r];
+                const float y = SILU ? u[0][r] + conv * sigmoidf_(conv) : conv;
+                const uint32_t hw = h2[m][rho][r >> 1];
+                const float hval = bf16_to_f32((r & 1) ? (hw >> 16) : (hw & 0xFFFFu));
+                o[r] = delta ? y : hval + y;
+            }
+            *reinterpret_cast<u32x2_t *>(reinterpret_cast<uint16_t *>(a.out) + ((int64_t)m * n_tok + t) * d + c0) =
+                u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
         }
-        *reinterpret_cast<u32x2_t *>(reinterpret_cast<uint16_t *>(a.out) + ((int64_t)m * n_tok + t) * d + c0) =
-            u32x2_t{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
     }
 }
 
 void launch_seam(const SeamArgs &a, hipStream_t s) {
-    const int64_t items = (int64_t)(a.n_tiles - 1) * 3 * (a.d / 4);
+    const int64_t items = (int64_t)(a.n_tiles - 1) * (a.d / 4);
     if (items <= 0) return;
     const dim3 grid((unsigned)((items + 255) / 256));
     const bool silu = a.conv_mode == ENGRAM_CONV_SILU_SKIP;
