@@ -638,3 +638,15 @@ def test_chunked_forward_equals_full():
     got = np.concatenate(got, 2)
     # the carried state passes through fp32, so allow fp32 rounding of u
     np.testing.assert_allclose(got, full, rtol=1e-6, atol=1e-6)
+
+
+def test_f32_split_errors_parts():
+    """The fp32 parity report splits elements at the row RMS: plain relative
+    error above it, |d| / row RMS below it."""
+    from engram_harness import f32_split_errors
+    ref = np.array([[4.0, -4.0, 0.0, 0.0]])  # row RMS = sqrt(8) ~ 2.83
+    got = ref + np.array([[4e-6, 0.0, 2.83e-6, -1e-7]])
+    rel_large, n_large, abs_small, n_small = f32_split_errors(got, ref)
+    assert (n_large, n_small) == (2, 2)
+    assert abs(rel_large - 1e-6) < 1e-12
+    assert abs(abs_small - 2.83e-6 / np.sqrt(8.0)) < 1e-12
