@@ -18,7 +18,6 @@
 // K-major: the contraction runs over tokens).  No operand is transposed.
 #include <cstring>
 
-#include <rocprim/device/device_scan.hpp>
 
 #include "engram_internal.h"
 
@@ -528,11 +527,63 @@ __global__ __launch_bounds__(kSortThreads) void sort_scatter_kernel(const KeyT *
     }
 }
 
+// Run heads of the sorted keys (head[i] = 1 where a new key starts) and
+// their inclusive prefix count incl[i], the number of heads in [0, i]:
+//   bwd_heads_count_kernel  head flags; heads per block of kHeadItems items
+//   sort_scan_kernel        (one workgroup) exclusive offsets of the blocks
+//   bwd_heads_incl_kernel   each wave ranks 64 items at a time by ballot and
+//                           popcount, offset by its block's and waves' counts
+// Wave w of a block owns items [w * kHeadItems / 4, (w + 1) * kHeadItems / 4).
+constexpr int kHeadItems = 2048;
+constexpr int kHeadRows = kHeadItems / 4 / 64;  // rows of 64 per wave
+
 template <typename KeyT>
-__global__ __launch_bounds__(256) void bwd_heads_kernel(const KeyT *keys, int64_t n, uint32_t *head) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n) return;
-    head[i] = (i == 0 || keys[i] != keys[i - 1]) ? 1u : 0u;
+__global__ __launch_bounds__(256) void bwd_heads_count_kernel(const KeyT *keys, int64_t n, uint32_t *head,
+                                                              uint32_t *bcount) {
+    __shared__ uint32_t wtot[4];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t base = (int64_t)blockIdx.x * kHeadItems + (int64_t)w * (kHeadItems / 4) + lane;
+    uint32_t cnt = 0u;
+#pragma unroll
+    for (int r = 0; r < kHeadRows; ++r) {
+        const int64_t i = base + 64 * r;
+        if (i < n) {
+            const uint32_t hd = (i == 0 || keys[i] != keys[i - 1]) ? 1u : 0u;
+            head[i] = hd;
+            cnt += hd;
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
+    if (lane == 0) wtot[w] = cnt;
+    __syncthreads();
+    if (threadIdx.x == 0) bcount[blockIdx.x] = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+}
+
+__global__ __launch_bounds__(256) void bwd_heads_incl_kernel(const uint32_t *head, int64_t n,
+                                                             const uint32_t *boff, uint32_t *incl) {
+    __shared__ uint32_t wtot[4];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t base = (int64_t)blockIdx.x * kHeadItems + (int64_t)w * (kHeadItems / 4);
+    const uint64_t le = lane == 63 ? ~0ull : ((2ull << lane) - 1ull);  // lanes 0..lane
+    uint32_t hd[kHeadRows];
+    uint32_t tot = 0u;
+#pragma unroll
+    for (int r = 0; r < kHeadRows; ++r) {
+        const int64_t i = base + 64 * r + lane;
+        hd[r] = i < n ? head[i] : 0u;
+        tot += (uint32_t)__popcll(__ballot(hd[r] != 0u));
+    }
+    if (lane == 0) wtot[w] = tot;
+    __syncthreads();
+    uint32_t run = boff[blockIdx.x];
+    for (int ww = 0; ww < w; ++ww) run += wtot[ww];
+#pragma unroll
+    for (int r = 0; r < kHeadRows; ++r) {
+        const uint64_t m = __ballot(hd[r] != 0u);
+        const int64_t i = base + 64 * r + lane;
+        if (i < n) incl[i] = run + (uint32_t)__popcll(m & le);
+        run += (uint32_t)__popcll(m);
+    }
 }
 
 // Per-table row gradients as a segmented sum over the sorted items, in two
@@ -709,10 +760,9 @@ size_t sort_hist_bytes(int64_t n_items) {
 }
 
 size_t table_temp_bytes(int64_t n_items) {
-    size_t scan_bytes = 0;
-    (void)rocprim::inclusive_scan(nullptr, scan_bytes, (uint32_t *)nullptr, (uint32_t *)nullptr, (size_t)n_items,
-                                  rocprim::plus<uint32_t>());
-    return std::max(scan_bytes, sort_hist_bytes(n_items));
+    // the sort's histograms, then the run heads' per-block counts
+    const size_t head_blocks = (size_t)((n_items + kHeadItems - 1) / kHeadItems) * 4u;
+    return std::max(head_blocks, sort_hist_bytes(n_items));
 }
 
 template <typename KeyT>
@@ -740,10 +790,12 @@ hipError_t table_grad(const BwdTableArgs &t, int32_t row_bits, hipStream_t s) {
         cur ^= 1;
     }
     KeyT *keys_out = kb[1];
-    launch_kernel(bwd_heads_kernel<KeyT>, dim3((unsigned)((n + 255) / 256)), dim3(256), s, keys_out, n, t.head);
-    size_t bytes = t.temp_bytes;
-    const hipError_t e = rocprim::inclusive_scan(t.temp, bytes, t.head, t.incl, (size_t)n, rocprim::plus<uint32_t>(), s);
-    if (e != hipSuccess) return e;
+    const int64_t head_blocks = (n + kHeadItems - 1) / kHeadItems;
+    uint32_t *bcount = static_cast<uint32_t *>(t.temp);  // the sort is done with hist
+    launch_kernel(bwd_heads_count_kernel<KeyT>, dim3((unsigned)head_blocks), dim3(256), s, keys_out, n, t.head,
+                  bcount);
+    launch_kernel(sort_scan_kernel, dim3(1), dim3(1024), s, bcount, head_blocks);
+    launch_kernel(bwd_heads_incl_kernel, dim3((unsigned)head_blocks), dim3(256), s, t.head, n, bcount, t.incl);
     const int64_t chunks = bwd_row_chunks(n);
     const dim3 grid((unsigned)((chunks + 3) / 4));
     const uint64_t row_mask = (row_bits >= 64) ? ~0ull : ((1ull << row_bits) - 1ull);
