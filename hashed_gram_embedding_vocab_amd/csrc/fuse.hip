@@ -105,7 +105,10 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
 
 constexpr int kPartCap = 4096;  // gate partials staged in LDS per round
 
-template <bool BF16, int BR>
+// SBF16: the carried conv state is bf16 (else fp32).  A compile-time choice:
+// with a runtime one the compiler widens each bf16 row inside its branch and
+// waits for that load alone, one memory round trip per state row.
+template <bool BF16, int BR, bool SBF16>
 __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
     __shared__ float alpha_s[BR][kPos + 3];
     __shared__ float sums_s[3][BR * (kPos + 3)];
@@ -128,8 +131,10 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
     // partials below: the three values before t0 (v of earlier positions,
     // or the carried state at the sequence start) and the first group's v
     // and h.
+    // (state rows stay in their stored form until first use, so no load
+    // waits for another)
     f32x4_t vprev[3];
-    f32x4_t sprev[BR][3];
+    Raw4<SBF16> sprev[BR][3];
 #pragma unroll
     for (int s = 1; s <= 3; ++s) {
         const int p = t0 - s;
@@ -137,10 +142,9 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
         if (live && p >= 0) vprev[s - 1] = *reinterpret_cast<const f32x4_t *>(a.v + (row0 + p) * d + c0);
 #pragma unroll
         for (int m = 0; m < BR; ++m) {
-            sprev[m][s - 1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            sprev[m][s - 1].w = u32x4_t{0u, 0u, 0u, 0u};
             if (live && p < 0 && a.conv_state && s <= kc - 1)
-                sprev[m][s - 1] = load_state4(a.conv_state, a.state_bf16 != 0,
-                                              (((int64_t)m * a.batch + b) * (kc - 1) + (kc - 1 - s)) * d + c0);
+                sprev[m][s - 1].load(a.conv_state, (((int64_t)m * a.batch + b) * (kc - 1) + (kc - 1 - s)) * d + c0);
         }
     }
     constexpr int kGroup = BR == 1 ? 8 : (BR == 2 ? 4 : 2);
@@ -229,7 +233,7 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
             const bool from_v = t0 - s >= 0;
             const float al = alpha_s[m][3 - s];
 #pragma unroll
-            for (int c = 0; c < kVec; ++c) win[m][s - 1][c] = from_v ? al * vprev[s - 1][c] : sprev[m][s - 1][c];
+            for (int c = 0; c < kVec; ++c) win[m][s - 1][c] = from_v ? al * vprev[s - 1][c] : sprev[m][s - 1].get(c);
         }
 
     for (int tg = t0; tg < t1; tg += kGroup) {
@@ -435,12 +439,15 @@ void launch_fuse(const FuseArgs &a, engram_dtype dt, hipStream_t s) {
     if (threads > 256) threads = 256;
     const int gz = (need + threads - 1) / threads;
     dim3 grid((a.seqlen + kPos - 1) / kPos, a.batch, gz);
+    // (an fp32 plan carries an fp32 state)
 #define ENGRAM_FUSE_LAUNCH(BR)                                                                   \
     do {                                                                                         \
-        if (dt == ENGRAM_BF16)                                                                   \
-            launch_kernel((fuse_kernel<true, BR>), grid, dim3(threads), s, a);            \
+        if (dt != ENGRAM_BF16)                                                                   \
+            launch_kernel((fuse_kernel<false, BR, false>), grid, dim3(threads), s, a);           \
+        else if (a.state_bf16)                                                                   \
+            launch_kernel((fuse_kernel<true, BR, true>), grid, dim3(threads), s, a);             \
         else                                                                                     \
-            launch_kernel((fuse_kernel<false, BR>), grid, dim3(threads), s, a);           \
+            launch_kernel((fuse_kernel<true, BR, false>), grid, dim3(threads), s, a);            \
     } while (0)
     switch (a.n_branches) {
         case 1: ENGRAM_FUSE_LAUNCH(1); break;
