@@ -60,6 +60,9 @@ def parse():
                     help="time only whole steps (no per-launch events; no roofline)")
     ap.add_argument("--retrieve-in-projection", action="store_true",
                     help="engram_forward flag: short chunks retrieve inside the projection launch")
+    ap.add_argument("--overlap-retrieval", action="store_true",
+                    help="with several layers per step: the later layers' rows are retrieved on a second stream "
+                         "while the first layer computes (their slots depend only on the token ids)")
     ap.add_argument("--backward", action="store_true",
                     help="time engram_backward (training) instead of the forward: one JSON line of its own")
     ap.add_argument("--offload", action="store_true",
@@ -211,11 +214,44 @@ def main():
     toks = [to_device(W.make_tokens(wl, seed=wl.seed(2) + 17 * r), torch.int32, "cuda") for r in range(R)]
     torch.cuda.synchronize()
 
+    # Later layers' retrieval on a second stream (default priority): engram_retrieve
+    # into one of two E buffers per layer, handed to engram_gate_fuse on the main
+    # stream by an event; a buffer is refilled only after the fusion two steps
+    # earlier has read it.
+    overlap = args.overlap_retrieval and len(layers) > 1
+    if overlap:
+        side = torch.cuda.Stream()
+        embs = [[torch.empty((n_tok, wl.emb_dim), dtype=layers[l][0].plan.torch_dtype, device="cuda")
+                 for _ in range(2)] for l in range(len(layers))]
+        ready = [[torch.cuda.Event() for _ in range(2)] for _ in layers]
+        free = [[torch.cuda.Event() for _ in range(2)] for _ in layers]
+        used = [[False, False] for _ in layers]
+
     def step(i):
         r = i % R
-        for dl, hs, out, ws, ctx, conv in layers:
-            dl.plan.engram_forward(toks[r], dl.comp_map, dl.tables, hs[r], dl.weights, out, ws,
-                                   prev_ctx=ctx, conv_state=conv, flags=fwd_flags)
+        if not overlap:
+            for dl, hs, out, ws, ctx, conv in layers:
+                dl.plan.engram_forward(toks[r], dl.comp_map, dl.tables, hs[r], dl.weights, out, ws,
+                                       prev_ctx=ctx, conv_state=conv, flags=fwd_flags)
+            return
+        main = torch.cuda.current_stream()
+        par = i % 2
+        for l in range(1, len(layers)):
+            dl, hs, out, ws, ctx, conv = layers[l]
+            if used[l][par]:
+                side.wait_event(free[l][par])
+            dl.plan.engram_retrieve(toks[r], dl.comp_map, dl.tables, embs[l][par], prev_ctx=ctx, stream=side)
+            ready[l][par].record(side)
+        dl, hs, out, ws, ctx, conv = layers[0]
+        dl.plan.engram_forward(toks[r], dl.comp_map, dl.tables, hs[r], dl.weights, out, ws,
+                               prev_ctx=ctx, conv_state=conv, flags=fwd_flags)
+        for l in range(1, len(layers)):
+            dl, hs, out, ws, ctx, conv = layers[l]
+            main.wait_event(ready[l][par])
+            dl.plan.engram_gate_fuse(embs[l][par], hs[r], dl.weights, out, ws, wl.batch, wl.seqlen,
+                                     conv_state=conv)
+            free[l][par].record(main)
+            used[l][par] = True
 
     for i in range(args.warmup):
         step(i)
@@ -397,7 +433,7 @@ def main():
                    "head_dim": wl.head_dim, "emb_dim": De, "table_params": sum(wl.primes()) * wl.head_dim,
                    "rotated_buffers": R, "parallelism": "single GPU",
                    "conv_state_dtype": wl.state_dtype if wl.decode else None,
-                   "retrieval_in_projection": bool(fwd_flags)},
+                   "retrieval_in_projection": bool(fwd_flags), "overlap_retrieval": bool(overlap)},
         "roofline": roofline,
         "gather": gather,
         "gather_uniform": gather_uniform,

@@ -107,6 +107,8 @@ def lib() -> C.CDLL:
         L.engram_forward.restype = C.c_int
         L.engram_forward.argtypes = [P, P, i32, i32, P, P, P, P, C.POINTER(WeightsC), P, P, P, u32,
                                      P, C.c_size_t, P, P]
+        L.engram_retrieve.restype = C.c_int
+        L.engram_retrieve.argtypes = [P, P, i32, i32, P, P, P, P, P, P]
         L.engram_forward_noalloc.restype = C.c_int
         L.engram_forward_noalloc.argtypes = [P, P, i32, i32, P, P, P, P, C.POINTER(WeightsC), P, P, P, u32,
                                              P, P]
@@ -360,6 +362,16 @@ class Plan:
         _check("engram_gather", lib().engram_gather(
             self._h, _ptr(idx, "idx", (torch.int32, torch.uint32)), n_tok, ptrs,
             _ptr(emb, "emb", self.torch_dtype), _stream(stream)))
+
+    def engram_retrieve(self, tokens, comp_map, tables: Sequence[torch.Tensor], emb, prev_ctx=None,
+                        bad_tokens=None, stream=None):
+        """Hash and gather into emb ([batch*seqlen][D_e]); then roll prev_ctx if given."""
+        batch, seqlen = tokens.shape
+        ptrs = (C.c_void_p * len(tables))(*[_table_ptr(t) for t in tables])
+        _check("engram_retrieve", lib().engram_retrieve(
+            self._h, _ptr(tokens, "tokens", torch.int32), batch, seqlen, _ptr(comp_map, "comp_map", torch.int32),
+            _ptr(prev_ctx, "prev_ctx", torch.int32), ptrs, _ptr(emb, "emb", self.torch_dtype),
+            _ptr(bad_tokens, "bad_tokens", (torch.int32, torch.uint32)), _stream(stream)))
 
     def engram_cache_build(self, hot, tables, cache: RowCache, stream=None):
         """hot: [n_tables][n_hot] int32 device tensor of row numbers."""

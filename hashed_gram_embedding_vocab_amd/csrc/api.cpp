@@ -86,11 +86,11 @@ engram_status do_hash(engram_plan_s &p, const int32_t *tokens, int32_t batch, in
 
 engram_status do_hash_gather(engram_plan_s &p, const int32_t *tokens, int32_t batch, int32_t seqlen,
                              const int32_t *comp_map, const int32_t *prev_ctx, uint32_t *bad,
-                             const void *const *tables, void *emb, hipStream_t s) {
+                             const void *const *tables, void *emb, hipStream_t s, int32_t *ctx_out = nullptr) {
     const GatherConsts gc = gather_consts(p, tables);
     {
         Launch l(p, ENGRAM_K_GATHER, s);
-        launch_hash_gather(p.hc, gc, tokens, batch, seqlen, comp_map, prev_ctx, bad, emb, s);
+        launch_hash_gather(p.hc, gc, tokens, batch, seqlen, comp_map, prev_ctx, bad, emb, s, ctx_out);
     }
     return last_launch_status();
 }
@@ -506,6 +506,28 @@ engram_status engram_forward(engram_plan p, const int32_t *d_tokens, int32_t bat
     if (st != ENGRAM_OK) return st;
     return do_fuse(*p, emb, d_h, batch, seqlen, w, d_conv_state, d_out, d_alpha, flags, d_workspace,
                    stream, ctx);
+}
+
+engram_status engram_retrieve(engram_plan p, const int32_t *d_tokens, int32_t batch, int32_t seqlen,
+                              const int32_t *d_comp_map, int32_t *d_prev_ctx, const void *const *table_ptrs,
+                              void *d_emb, uint32_t *d_bad_tokens, hipStream_t stream) {
+    if (!p || !d_tokens || !d_comp_map || !table_ptrs || !d_emb) return ENGRAM_E_INVALID_ARG;
+    if (batch <= 0 || seqlen <= 0) return ENGRAM_E_INVALID_ARG;
+    if ((int64_t)batch * seqlen > (int64_t)INT32_MAX) return ENGRAM_E_UNSUPPORTED;
+    if (!aligned16(d_tokens) || !aligned16(d_comp_map) || !aligned16(d_emb)) return ENGRAM_E_INVALID_ARG;
+    for (int t = 0; t < p->n_tables; ++t)
+        if (!table_ptrs[t] || !aligned16(table_ptrs[t])) return ENGRAM_E_INVALID_ARG;
+    // one token per sequence: the retrieval launch rolls the context itself
+    engram_status st = do_hash_gather(*p, d_tokens, batch, seqlen, d_comp_map, d_prev_ctx, d_bad_tokens,
+                                      table_ptrs, d_emb, stream, seqlen == 1 ? d_prev_ctx : nullptr);
+    if (st != ENGRAM_OK || !d_prev_ctx || seqlen == 1) return st;
+    // after the retrieval has read the old context, on the same stream
+    const CtxUpdate ctx{d_tokens, d_comp_map, d_prev_ctx, p->cfg.vocab, p->cfg.vocab_comp};
+    {
+        Launch l(*p, ENGRAM_K_AUX, stream);
+        launch_ctx_update(ctx, batch, seqlen, stream);
+    }
+    return last_launch_status();
 }
 
 engram_status engram_profile_begin(engram_plan p, int32_t max_launches, uint32_t kind_mask) {

@@ -110,9 +110,12 @@ void launch_prefetch_assemble(const GatherConsts &gc, int64_t n_tok, const uint3
                               const void *staged, void *emb, hipStream_t s);
 // Retrieval in one pass (engram_forward): every lane hashes the n-gram of its
 // own (token, table) pair and copies its 16-byte chunk of that row.
+// ctx_out: roll this carried context (the prev_ctx array) inside the launch;
+// honoured only when seqlen == 1, else ignored
 void launch_hash_gather(const HashConsts &hc, const GatherConsts &gc, const int32_t *tokens,
                         int32_t batch, int32_t seqlen, const int32_t *comp_map,
-                        const int32_t *prev_ctx, uint32_t *bad, void *emb, hipStream_t s);
+                        const int32_t *prev_ctx, uint32_t *bad, void *emb, hipStream_t s,
+                        int32_t *ctx_out = nullptr);
 
 // ---------------------------------------------------------------- projections
 struct ProjArgs {
@@ -228,6 +231,8 @@ __device__ __forceinline__ void ctx_update_one(const CtxUpdate &c, int32_t b, in
     c.prev_ctx[b * 2 + 0] = n0;
     c.prev_ctx[b * 2 + 1] = n1;
 }
+
+void launch_ctx_update(const CtxUpdate &c, int32_t batch, int32_t seqlen, hipStream_t s);
 
 // Gate per branch and token, alpha = sigmoid(<RMSNorm(h), RMSNorm(k)> / sqrt(d)),
 // from the partial sums of the W_k projection (summed in a fixed order).

@@ -82,11 +82,14 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherConsts gc,
 // before a sequence's first token come from prev_ctx, else PAD), hashes it
 // with the table's seed and leaves the slot in LDS.  Phase 2: the block
 // copies the pairs' rows in 16-byte chunks, up to kHGUnroll loads in flight
-// per thread.  The slots never travel through HBM.
+// per thread.  The slots never travel through HBM.  With one token per
+// sequence, ctx_out (the same array as prev_ctx, or null) is rolled by the
+// block after its barrier: every read of a sequence's context is in the block
+// that owns its token.
 __global__ __launch_bounds__(kThreads) void hash_gather_kernel(
     HashConsts hc, GatherConsts gc, const int32_t *__restrict__ tokens, int64_t n_tok, int32_t seqlen,
-    uint64_t magic_seq, int32_t tpb, const int32_t *__restrict__ comp_map,
-    const int32_t *__restrict__ prev_ctx, uint32_t *__restrict__ bad, u32x4_t *__restrict__ emb) {
+    uint64_t magic_seq, int32_t tpb, const int32_t *__restrict__ comp_map, const int32_t *prev_ctx,
+    int32_t *ctx_out, uint32_t *__restrict__ bad, u32x4_t *__restrict__ emb) {
     __shared__ uint32_t slot_s[kThreads];
     const int64_t tok0 = (int64_t)blockIdx.x * tpb;
     const int n_tables = gc.n_tables;
@@ -117,6 +120,12 @@ __global__ __launch_bounds__(kThreads) void hash_gather_kernel(
     }
     __syncthreads();
     const int64_t ntok_here = min<int64_t>(tpb, n_tok - tok0);
+    if (ctx_out && threadIdx.x < ntok_here) {  // seqlen == 1: token tok0 + i is sequence tok0 + i
+        const int64_t b = tok0 + threadIdx.x;
+        const int32_t n1 = compress_id(tokens[b], comp_map, hc.vocab, hc.vocab_comp);
+        ctx_out[b * 2 + 0] = ctx_out[b * 2 + 1];
+        ctx_out[b * 2 + 1] = n1;
+    }
     const int chunks = (int)ntok_here * gc.tok_chunks;
     u32x4_t *dst = emb + tok0 * gc.tok_chunks;
     for (int c0 = threadIdx.x; c0 < chunks; c0 += kThreads * kHGUnroll) {
@@ -139,17 +148,30 @@ __global__ __launch_bounds__(kThreads) void hash_gather_kernel(
     }
 }
 
+// The carried context after a chunk, one thread per sequence (for a
+// retrieval launched on its own, after it has read the old context).
+__global__ __launch_bounds__(kThreads) void ctx_kernel(CtxUpdate c, int32_t batch, int32_t seqlen) {
+    const int32_t b = (int32_t)(blockIdx.x * kThreads + threadIdx.x);
+    if (b < batch) ctx_update_one(c, b, seqlen);
+}
+
 }  // namespace
+
+void launch_ctx_update(const CtxUpdate &c, int32_t batch, int32_t seqlen, hipStream_t s) {
+    launch_kernel(ctx_kernel, dim3((unsigned)((batch + kThreads - 1) / kThreads)), dim3(kThreads), s, c, batch,
+                  seqlen);
+}
 
 void launch_hash_gather(const HashConsts &hc, const GatherConsts &gc, const int32_t *tokens,
                         int32_t batch, int32_t seqlen, const int32_t *comp_map,
-                        const int32_t *prev_ctx, uint32_t *bad, void *emb, hipStream_t s) {
+                        const int32_t *prev_ctx, uint32_t *bad, void *emb, hipStream_t s, int32_t *ctx_out) {
     const int64_t n_tok = (int64_t)batch * seqlen;
     const int tpb = kThreads / gc.n_tables;
     const int64_t blocks = (n_tok + tpb - 1) / tpb;
     const uint64_t magic_seq = seqlen <= 1 ? 0 : (uint64_t)(((unsigned __int128)1 << 64) / (unsigned)seqlen) + 1;
     launch_kernel(hash_gather_kernel, dim3((unsigned)blocks), dim3(kThreads), s, hc, gc, tokens, n_tok,
-                       seqlen, magic_seq, tpb, comp_map, prev_ctx, bad, reinterpret_cast<u32x4_t *>(emb));
+                       seqlen, magic_seq, tpb, comp_map, prev_ctx, seqlen == 1 ? ctx_out : nullptr, bad,
+                       reinterpret_cast<u32x4_t *>(emb));
 }
 
 void launch_gather(const GatherConsts &gc, const uint32_t *idx, int64_t n_tok, void *emb,

@@ -326,6 +326,30 @@ ENGRAM_API engram_status engram_forward(engram_plan p, const int32_t *d_tokens, 
                              size_t workspace_bytes, uint32_t *d_bad_tokens, hipStream_t stream);
 
 /*
+ * Retrieval on its own, ahead of the layer that uses it ([rep]
+ * 工程实现与硬件效率: the slots depend only on the token ids, so a later
+ * layer's rows can be fetched while earlier layers still compute).  Hashes
+ * every (token, table) pair and copies its row into d_emb in one launch, as
+ * engram_forward does (steps 1-4 of engram_hash and engram_gather); then, if
+ * d_prev_ctx is non-NULL, replaces it by the last two compressed ids of the
+ * sequence extended by this chunk (inside that launch when seqlen == 1, else a
+ * second launch, one thread per sequence).
+ * engram_retrieve followed by engram_gate_fuse on d_emb, on one stream or with
+ * d_emb handed over between streams by an event, gives engram_forward's
+ * results bit for bit.
+ *   d_tokens, d_comp_map, d_prev_ctx, d_bad_tokens  as engram_forward
+ *   table_ptrs   HOST array of n_tables DEVICE (or engram_host_alloc) pointers
+ *   d_emb        [batch*seqlen][n_tables*d_e] plan dtype, 16-byte aligned,
+ *                caller-owned; fully overwritten
+ * Bad arguments return ENGRAM_E_INVALID_ARG (batch*seqlen above 2^31-1:
+ * ENGRAM_E_UNSUPPORTED) and launch nothing.
+ */
+ENGRAM_API engram_status engram_retrieve(engram_plan p, const int32_t *d_tokens, int32_t batch, int32_t seqlen,
+                              const int32_t *d_comp_map, int32_t *d_prev_ctx,
+                              const void *const *table_ptrs, void *d_emb, uint32_t *d_bad_tokens,
+                              hipStream_t stream);
+
+/*
  * engram_forward for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * Same arguments and results (bit for bit) as engram_forward, minus the

@@ -124,6 +124,10 @@ int main() {
         EXPECT(engram_forward_noalloc(nullptr, ti, 1, 1, ti, nullptr, tabs, fake, &w, nullptr, fake, nullptr, 0,
                                       nullptr, nullptr),
                ENGRAM_E_INVALID_ARG);
+        EXPECT(engram_retrieve(p, ti, 0, 4, ti, nullptr, tabs, fake, nullptr, nullptr), ENGRAM_E_INVALID_ARG);
+        EXPECT(engram_retrieve(p, ti, 2, 4, ti, nullptr, tabs, odd, nullptr, nullptr), ENGRAM_E_INVALID_ARG);
+        EXPECT(engram_retrieve(nullptr, ti, 2, 4, ti, nullptr, tabs, fake, nullptr, nullptr),
+               ENGRAM_E_INVALID_ARG);
         engram_grads g;
         std::memset(&g, 0, sizeof(g));
         EXPECT(engram_backward(p, tu, tabs, fake, &w, fake, 2, 9, 0, fake, &g, fake, 0, nullptr),

@@ -312,3 +312,31 @@ def test_noalloc_forward_rejects_before_touching_a_device(B):
     # 8 x 4096 tokens at d = 1024 need about 72 MiB of workspace: beyond the scratch
     assert p.engram_workspace_size(8, 4096) > B.NOALLOC_SCRATCH_BYTES
     assert call(p._h, 8, 4096) == B.E_UNSUPPORTED
+
+
+def test_retrieve_rejects_bad_arguments_before_launching(B):
+    """engram_retrieve: null or misaligned buffers, bad shapes and null tables
+    return before any device call."""
+    _no_gpu()
+    L = B.lib()
+    p = B.Plan(vocab=32000, vocab_comp=24640, heads=8, head_dim=64, table_rows=[500009] * 16, hash_seed=1,
+               d_model=1024, dtype=B.BF16)
+    fake = C.c_void_p(0x10000)
+    odd = C.c_void_p(0x10004)
+    tabs = (C.c_void_p * 16)(*([0x10000] * 16))
+    holey = (C.c_void_p * 16)(*([0x10000] * 15 + [0]))
+
+    def call(plan, tokens=fake, batch=4, seqlen=8, comp=fake, tables=tabs, emb=fake):
+        return L.engram_retrieve(plan, tokens, batch, seqlen, comp, None, tables, emb, None, None)
+
+    assert call(None) == B.E_INVALID_ARG
+    assert call(p._h, tokens=None) == B.E_INVALID_ARG
+    assert call(p._h, comp=None) == B.E_INVALID_ARG
+    assert call(p._h, emb=None) == B.E_INVALID_ARG
+    assert call(p._h, tables=None) == B.E_INVALID_ARG
+    assert call(p._h, batch=0) == B.E_INVALID_ARG
+    assert call(p._h, seqlen=-3) == B.E_INVALID_ARG
+    assert call(p._h, batch=1 << 16, seqlen=1 << 16) == B.E_UNSUPPORTED
+    assert call(p._h, emb=odd) == B.E_INVALID_ARG
+    assert call(p._h, tokens=odd) == B.E_INVALID_ARG
+    assert call(p._h, tables=holey) == B.E_INVALID_ARG
