@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--overlap-retrieval", action="store_true",
                     help="with several layers per step: the later layers' rows are retrieved on a second stream "
                          "while the first layer computes (their slots depend only on the token ids)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the forward steps replayed from HIP graphs (captured once per rotation slot): "
+                         "a `graph_replay` entry of its own, whole-step time only")
     ap.add_argument("--backward", action="store_true",
                     help="time engram_backward (training) instead of the forward: one JSON line of its own")
     ap.add_argument("--offload", action="store_true",
@@ -227,18 +230,22 @@ def main():
         free = [[torch.cuda.Event() for _ in range(2)] for _ in layers]
         used = [[False, False] for _ in layers]
 
-    def step(i):
-        r = i % R
+    def enqueue(r, par, captured):
+        """One step on token/h buffers r (E buffers `par` when overlapping).
+        Under graph capture the side stream forks from the capturing stream
+        and joins it again; replays of one graph never overlap, so no buffer
+        needs the cross-step wait."""
         if not overlap:
             for dl, hs, out, ws, ctx, conv in layers:
                 dl.plan.engram_forward(toks[r], dl.comp_map, dl.tables, hs[r], dl.weights, out, ws,
                                        prev_ctx=ctx, conv_state=conv, flags=fwd_flags)
             return
         main = torch.cuda.current_stream()
-        par = i % 2
+        if captured:
+            side.wait_stream(main)
         for l in range(1, len(layers)):
             dl, hs, out, ws, ctx, conv = layers[l]
-            if used[l][par]:
+            if not captured and used[l][par]:
                 side.wait_event(free[l][par])
             dl.plan.engram_retrieve(toks[r], dl.comp_map, dl.tables, embs[l][par], prev_ctx=ctx, stream=side)
             ready[l][par].record(side)
@@ -250,8 +257,37 @@ def main():
             main.wait_event(ready[l][par])
             dl.plan.engram_gate_fuse(embs[l][par], hs[r], dl.weights, out, ws, wl.batch, wl.seqlen,
                                      conv_state=conv)
-            free[l][par].record(main)
-            used[l][par] = True
+            if not captured:
+                free[l][par].record(main)
+                used[l][par] = True
+
+    def step(i):
+        enqueue(i % R, i % 2, False)
+
+    def graph_replay():
+        """The same steps as HIP graphs (one per rotation slot, captured once),
+        replayed: one launch per step from the host.  Whole-step time only."""
+        cap = torch.cuda.Stream()
+        graphs = []
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                enqueue(r, r % 2, True)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record()
+        for i in range(args.steps):
+            graphs[i % R].replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return {"value": n_tok * args.steps / wall, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+                "gpu_event_ms_per_step": round(ev0.elapsed_time(ev1) / args.steps, 4), "graphs": R,
+                "overlap_retrieval": bool(overlap)}
 
     for i in range(args.warmup):
         step(i)
@@ -408,6 +444,8 @@ def main():
         if gather is not None and hbm is not None:
             gather["frac_of_stream_read"] = round(gather["achieved_GBs"] / hbm["read"]["GBs"], 4)
 
+    graphed = graph_replay() if args.graph else None
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.cpu_seconds)
@@ -441,6 +479,7 @@ def main():
         "gate_gemm": gate_gemm,
         "kernels": per_kernel,
         "kernel_avg_us": kernels_us,
+        "graph_replay": graphed,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
