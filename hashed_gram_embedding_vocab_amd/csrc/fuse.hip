@@ -126,26 +126,58 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
 
     if (a.ctx.prev_ctx && blockIdx.x == 0 && blockIdx.z == 0 && tid == 0) ctx_update_one(a.ctx, b, a.seqlen);
 
+    // Gates of positions pa .. t1-1 (the block's and up to three before it).
+    // The whole block stages the partial sums in LDS, as many parts per
+    // round as fit (all of them at decode sizes); one thread per (branch,
+    // position) then adds them in part order, as gate_value does.  Staged
+    // layout: x = ((qq * BR + m) * 3 + k) * npos + pi.
+    const int pa = max(t0 - 3, 0);
+    const int npos = t1 - pa;
+    const int n_sum = BR * npos;
+    const int per_part = 3 * n_sum;
+    const int q_round = max(1, kPartCap / per_part);
+    auto part_at = [&](int x, int q0) -> int64_t {
+        const int pi = x % npos;
+        const int r = x / npos;
+        const int k = r % 3;
+        const int mq = r / 3;
+        const int m = mq % BR, qq = mq / BR;
+        return (((int64_t)m * a.n_parts + q0 + qq) * 3 + k) * n_tok + row0 + pa + pi;
+    };
+    // The first round's partial sums, up to kPre per thread, are requested
+    // before anything else: waiting for them then waits for no other load,
+    // and the gate is taken while the rest is still in flight.
+    constexpr int kPre = 2;
+    const int n_first = min(q_round, a.n_parts) * per_part;
+    float pre[kPre];
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) pre[i] = a.partials[part_at(min(tid + i * (int)blockDim.x, n_first - 1), 0)];
+
     // Everything this thread reads that does not depend on the gate is
-    // requested first, so it arrives in the same round trip as the gate
-    // partials below: the three values before t0 (v of earlier positions,
+    // requested next: the three values before t0 (v of earlier positions,
     // or the carried state at the sequence start) and the first group's v
     // and h.
-    // (state rows stay in their stored form until first use, so no load
-    // waits for another)
+    // Every one of these loads is issued unconditionally: lanes that need no
+    // value read a valid element, and the choice between it and zero is made
+    // where the value is used, past the barriers below, so the compiler can
+    // neither sink a load into a branch nor wait for it early, and the
+    // partial sums above wait for none of them.  State rows stay in their
+    // stored form until first use.
+    const int cc0 = live ? c0 : 0;
+    const void *sbase = a.conv_state ? a.conv_state : static_cast<const void *>(a.v);
     f32x4_t vprev[3];
     Raw4<SBF16> sprev[BR][3];
+    bool vprev_ok[3], sprev_ok[3];
 #pragma unroll
     for (int s = 1; s <= 3; ++s) {
         const int p = t0 - s;
-        vprev[s - 1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (live && p >= 0) vprev[s - 1] = *reinterpret_cast<const f32x4_t *>(a.v + (row0 + p) * d + c0);
+        vprev[s - 1] = *reinterpret_cast<const f32x4_t *>(a.v + (row0 + max(p, 0)) * d + cc0);
+        vprev_ok[s - 1] = live && p >= 0;
+        const bool need = live && p < 0 && a.conv_state && s <= kc - 1;
+        sprev_ok[s - 1] = need;
 #pragma unroll
-        for (int m = 0; m < BR; ++m) {
-            sprev[m][s - 1].w = u32x4_t{0u, 0u, 0u, 0u};
-            if (live && p < 0 && a.conv_state && s <= kc - 1)
-                sprev[m][s - 1].load(a.conv_state, (((int64_t)m * a.batch + b) * (kc - 1) + (kc - 1 - s)) * d + c0);
-        }
+        for (int m = 0; m < BR; ++m)
+            sprev[m][s - 1].load(sbase, need ? (((int64_t)m * a.batch + b) * (kc - 1) + (kc - 1 - s)) * d + c0 : 0);
     }
     constexpr int kGroup = BR == 1 ? 8 : (BR == 2 ? 4 : 2);
     f32x4_t vv[kGroup];
@@ -155,41 +187,32 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
 #pragma unroll
         for (int q = 0; q < kGroup; ++q) {
             const int64_t row = row0 + tg + min(q, n - 1);
-            vv[q] = *reinterpret_cast<const f32x4_t *>(a.v + row * d + c0);
+            vv[q] = *reinterpret_cast<const f32x4_t *>(a.v + row * d + cc0);
 #pragma unroll
-            for (int m = 0; m < BR; ++m) hv[q][m].load(a.h, ((int64_t)m * n_tok + row) * d + c0);
+            for (int m = 0; m < BR; ++m) hv[q][m].load(a.h, ((int64_t)m * n_tok + row) * d + cc0);
         }
     };
-    if (live) load_group(t0);
-    // conv taps, wt[j][c] multiplying u_{t-j}: requested with the rest
+    load_group(t0);
+    // conv taps, wt[j][c] multiplying u_{t-j} (zero for j >= kc, chosen at use)
     float wt[4][kVec];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int c = 0; c < kVec; ++c)
-            wt[j][c] = (live && j < kc) ? a.conv_w[(int64_t)(c0 + c) * kc + (kc - 1 - j)] : 0.f;
+        for (int c = 0; c < kVec; ++c) wt[j][c] = a.conv_w[(int64_t)(cc0 + c) * kc + max(kc - 1 - j, 0)];
 
-    // Gates of positions pa .. t1-1 (the block's and up to three before it).
-    // The whole block stages the partial sums in LDS, as many parts per
-    // round as fit (all of them at decode sizes); one thread per (branch,
-    // position) then adds them in part order, as gate_value does.
-    const int pa = max(t0 - 3, 0);
-    const int npos = t1 - pa;
-    const int n_sum = BR * npos;
-    const int per_part = 3 * n_sum;
-    const int q_round = max(1, kPartCap / per_part);
     for (int w = tid; w < n_sum; w += blockDim.x) sums_s[0][w] = sums_s[1][w] = sums_s[2][w] = 0.f;
     for (int q0 = 0; q0 < a.n_parts; q0 += q_round) {
         const int qn = min(q_round, a.n_parts - q0);
-        // staged layout: x = ((qq * BR + m) * 3 + k) * npos + pi
-        for (int x = tid; x < qn * per_part; x += blockDim.x) {
-            const int pi = x % npos;
-            const int r = x / npos;
-            const int k = r % 3;
-            const int mq = r / 3;
-            const int m = mq % BR, qq = mq / BR;
-            part_s[x] = a.partials[(((int64_t)m * a.n_parts + q0 + qq) * 3 + k) * n_tok + row0 + pa + pi];
+        // (the early values go to LDS on a path with no load of its own, so
+        // their wait covers them alone)
+        int x0 = tid;
+        if (q0 == 0) {
+#pragma unroll
+            for (int i = 0; i < kPre; ++i)
+                if (tid + i * (int)blockDim.x < qn * per_part) part_s[tid + i * blockDim.x] = pre[i];
+            x0 = tid + kPre * blockDim.x;
         }
+        for (int x = x0; x < qn * per_part; x += blockDim.x) part_s[x] = a.partials[part_at(x, q0)];
         __syncthreads();
         for (int w = tid; w < n_sum; w += blockDim.x) {
             const int m = w / npos, pi = w - m * npos;
@@ -224,6 +247,11 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
     const bool silu = a.conv_mode == ENGRAM_CONV_SILU_SKIP;
     const bool delta = (a.flags & ENGRAM_OUT_DELTA) != 0;
 
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int c = 0; c < kVec; ++c) wt[j][c] = j < kc ? wt[j][c] : 0.f;
+
     // win[m][s-1][c] = u_{t-s}
     float win[BR][3][kVec];
 #pragma unroll
@@ -233,7 +261,11 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
             const bool from_v = t0 - s >= 0;
             const float al = alpha_s[m][3 - s];
 #pragma unroll
-            for (int c = 0; c < kVec; ++c) win[m][s - 1][c] = from_v ? al * vprev[s - 1][c] : sprev[m][s - 1].get(c);
+            for (int c = 0; c < kVec; ++c) {
+                const float vp = vprev_ok[s - 1] ? vprev[s - 1][c] : 0.f;
+                const float sp = sprev_ok[s - 1] ? sprev[m][s - 1].get(c) : 0.f;
+                win[m][s - 1][c] = from_v ? al * vp : sp;
+            }
         }
 
     for (int tg = t0; tg < t1; tg += kGroup) {
