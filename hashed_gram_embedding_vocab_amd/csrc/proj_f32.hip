@@ -7,7 +7,9 @@
 namespace engram {
 namespace {
 
-constexpr int TN = 64, TT = 64, TK = 16;
+constexpr int TN = 32, TT = 32, TK = 64;
+constexpr int kOut = TN / 16;  // outputs per thread along n and along t
+constexpr int kPer = TN * TK / 256;  // elements of each operand tile per thread and step
 
 template <typename T, int N>
 __device__ __forceinline__ T pick(const T (&arr)[N], int i) {
@@ -19,46 +21,60 @@ __device__ __forceinline__ T pick(const T (&arr)[N], int i) {
 }
 
 // C^T[n][t] = sum_k W[n][k] E[t][k] over the stacked rows of every W_k^(m)
-// and W_v; k goes to kbuf[m][t][n'], v to v[t][n'].
+// and W_v; k goes to kbuf[m][t][n'], v to v[t][n'].  Each step of TK columns
+// requests all of its operand elements at once (every lane reads a valid
+// element; out-of-range ones become zeros on their way into LDS), so a step
+// costs one memory round trip; each output still adds k in order.
 __global__ __launch_bounds__(256) void proj_f32_kernel(ProjArgs a) {
     __shared__ float ws[TN][TK + 1];
     __shared__ float es[TT][TK + 1];
+    __shared__ const float *wmat_s[kMaxBranches + 1];  // the stacked matrices (a per-lane index into
+                                                      // the kernel arguments would read them from memory)
     const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
     const int d = a.d, K = a.K;
     const int n_total = (a.n_branches + 1) * d;
     const int n0 = blockIdx.x * TN;
     const int64_t t0 = (int64_t)blockIdx.y * TT;
     const float *emb = reinterpret_cast<const float *>(a.emb);
-    float acc[4][4] = {};
+    float acc[kOut][kOut] = {};
+    if (threadIdx.x <= kMaxBranches) wmat_s[threadIdx.x] = reinterpret_cast<const float *>(pick(a.w, threadIdx.x));
+    __syncthreads();
     for (int k0 = 0; k0 < K; k0 += TK) {
-        for (int x = threadIdx.x; x < TN * TK; x += 256) {
+        float wv[kPer], ev[kPer];
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int x = threadIdx.x + 256 * u;
             const int r = x / TK, c = x % TK;
-            const int n = n0 + r, k = k0 + c;
-            float w = 0.f;
-            if (n < n_total && k < K) {
-                const int mat = n / d;
-                w = reinterpret_cast<const float *>(pick(a.w, mat))[(int64_t)(n - mat * d) * K + k];
-            }
-            ws[r][c] = w;
-            const int64_t t = t0 + r;
-            es[r][c] = (t < a.n_tok && k < K) ? emb[t * K + k] : 0.f;
+            const int n = min(n0 + r, n_total - 1), k = min(k0 + c, K - 1);
+            const int mat = n / d;
+            wv[u] = wmat_s[mat][(int64_t)(n - mat * d) * K + k];
+            ev[u] = emb[min(t0 + r, a.n_tok - 1) * K + k];
+        }
+        asm volatile("" ::: "memory");  // every load above is issued before any goes to LDS
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int x = threadIdx.x + 256 * u;
+            const int r = x / TK, c = x % TK;
+            const bool kin = k0 + c < K;
+            ws[r][c] = (n0 + r < n_total && kin) ? wv[u] : 0.f;
+            es[r][c] = (t0 + r < a.n_tok && kin) ? ev[u] : 0.f;
         }
         __syncthreads();
 #pragma unroll
         for (int kk = 0; kk < TK; ++kk)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < kOut; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(ws[tx + 16 * i][kk], es[ty + 16 * j][kk], acc[i][j]);
+                for (int j = 0; j < kOut; ++j) acc[i][j] = fmaf(ws[tx + 16 * i][kk], es[ty + 16 * j][kk], acc[i][j]);
         __syncthreads();
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kOut; ++i) {
         const int n = n0 + tx + 16 * i;
         if (n >= n_total) continue;
         const int mat = n / d, nl = n - mat * d;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < kOut; ++j) {
             const int64_t t = t0 + ty + 16 * j;
             if (t >= a.n_tok) continue;
             if (mat < a.n_branches)
