@@ -7,7 +7,7 @@
 namespace engram {
 namespace {
 
-constexpr int TN = 32, TT = 32, TK = 64;
+constexpr int TN = 16, TT = 16, TK = 64;
 constexpr int kOut = TN / 16;  // outputs per thread along n and along t
 constexpr int kPer = TN * TK / 256;  // elements of each operand tile per thread and step
 
