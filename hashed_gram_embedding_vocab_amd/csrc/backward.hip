@@ -26,6 +26,7 @@ namespace {
 
 constexpr int kConvPos = 32;     // positions per bwd_conv_kernel workgroup
 constexpr int kGateTok = 64;     // tokens per bwd_gate_kernel workgroup
+constexpr int kGateGroup = 8;    // tokens whose loads bwd_gate_kernel issues together
 
 template <typename T, int N>
 __device__ __forceinline__ T pick_arg(const T (&arr)[N], int i) {
@@ -272,29 +273,50 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(BwdArgs a) {
     const f32x4_t gk = *reinterpret_cast<const f32x4_t *>(pick_arg(a.gamma_k, m) + c0);
     const float inv_sqd = rsqrtf((float)d);
     f32x4_t dgh = {0.f, 0.f, 0.f, 0.f}, dgk = {0.f, 0.f, 0.f, 0.f};
-    for (int x = 0; x < kGateTok; ++x) {
-        const int64_t t = tb + x;
-        if (t >= a.n_tok) break;
-        const float rh = sc[0][x], rk = sc[1][x], s = sc[2][x], al = sc[3][x];
-        const float ds = sc[4][x] * al * (1.f - al);
-        const float corr = ds * s / (float)d;
-        const int64_t hi = ((int64_t)m * a.n_tok + t) * d + c0;
-        const f32x4_t hv = load_bf16x4(a.h, hi);
-        const f32x4_t kv = *reinterpret_cast<const f32x4_t *>(a.kv + t * a.kv_ld + (int64_t)m * d + c0);
-        const f32x4_t g = delta ? f32x4_t{0.f, 0.f, 0.f, 0.f} : load_bf16x4(a.dout, hi);
-        f32x4_t dh, dk;
+    // tokens in groups of kGateGroup: the group's h, k and dout are all
+    // requested (rows clamped into the tokens, raw bf16 widened at use)
+    // before any arithmetic, then the tokens are taken in order, so the
+    // gamma sums add them as a plain walk would
+    const u32x2_t zero2 = {0u, 0u};
+    for (int x0 = 0; x0 < kGateTok; x0 += kGateGroup) {
+        u32x2_t hraw[kGateGroup], graw[kGateGroup];
+        f32x4_t kvs[kGateGroup];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float hn = hv[r] / rh, kn = kv[r] / rk;
-            const float da = ds * (gk[r] * kn) * inv_sqd;
-            const float db = ds * (gh[r] * hn) * inv_sqd;
-            dgh[r] += da * hn;
-            dgk[r] += db * kn;
-            dh[r] = g[r] + (gh[r] * da - hn * corr) / rh;
-            dk[r] = (gk[r] * db - kn * corr) / rk;
+        for (int u = 0; u < kGateGroup; ++u) {
+            const int64_t t = min(tb + x0 + u, a.n_tok - 1);
+            const int64_t hi = ((int64_t)m * a.n_tok + t) * d + c0;
+            hraw[u] = *reinterpret_cast<const u32x2_t *>(reinterpret_cast<const uint16_t *>(a.h) + hi);
+            kvs[u] = *reinterpret_cast<const f32x4_t *>(a.kv + t * a.kv_ld + (int64_t)m * d + c0);
+            graw[u] = delta ? zero2 : *reinterpret_cast<const u32x2_t *>(reinterpret_cast<const uint16_t *>(a.dout) + hi);
         }
-        store_bf16x4(a.dh, hi, dh);
-        store_bf16x4(a.dkv, t * a.dkv_ld + (int64_t)m * d + c0, dk);
+#pragma unroll
+        for (int u = 0; u < kGateGroup; ++u) {
+            const int x = x0 + u;
+            const int64_t t = tb + x;
+            if (t >= a.n_tok) break;
+            const float rh = sc[0][x], rk = sc[1][x], s = sc[2][x], al = sc[3][x];
+            const float ds = sc[4][x] * al * (1.f - al);
+            const float corr = ds * s / (float)d;
+            const int64_t hi = ((int64_t)m * a.n_tok + t) * d + c0;
+            const f32x4_t hv = {bf16_to_f32(hraw[u][0] & 0xFFFFu), bf16_to_f32(hraw[u][0] >> 16),
+                                bf16_to_f32(hraw[u][1] & 0xFFFFu), bf16_to_f32(hraw[u][1] >> 16)};
+            const f32x4_t g = {bf16_to_f32(graw[u][0] & 0xFFFFu), bf16_to_f32(graw[u][0] >> 16),
+                               bf16_to_f32(graw[u][1] & 0xFFFFu), bf16_to_f32(graw[u][1] >> 16)};
+            const f32x4_t kv = kvs[u];
+            f32x4_t dh, dk;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float hn = hv[r] / rh, kn = kv[r] / rk;
+                const float da = ds * (gk[r] * kn) * inv_sqd;
+                const float db = ds * (gh[r] * hn) * inv_sqd;
+                dgh[r] += da * hn;
+                dgk[r] += db * kn;
+                dh[r] = g[r] + (gh[r] * da - hn * corr) / rh;
+                dk[r] = (gk[r] * db - kn * corr) / rk;
+            }
+            store_bf16x4(a.dh, hi, dh);
+            store_bf16x4(a.dkv, t * a.dkv_ld + (int64_t)m * d + c0, dk);
+        }
     }
     const int64_t pr = ((int64_t)m * gridDim.x + blockIdx.x) * d + c0;
     *reinterpret_cast<f32x4_t *>(a.dg_part + pr) = dgh;
