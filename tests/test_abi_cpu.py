@@ -4,6 +4,7 @@ and its host-side validation rejects bad arguments without touching a GPU."""
 import ctypes as C
 import os
 import re
+import sys
 
 import pytest
 
@@ -340,3 +341,17 @@ def test_retrieve_rejects_bad_arguments_before_launching(B):
     assert call(p._h, emb=odd) == B.E_INVALID_ARG
     assert call(p._h, tokens=odd) == B.E_INVALID_ARG
     assert call(p._h, tables=holey) == B.E_INVALID_ARG
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 (or a multi-rank launch)
+    exits with a message before touching a device."""
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for extra_env, argv in (({}, ["--gpus", "2"]), ({"WORLD_SIZE": "4"}, [])):
+        env = dict(os.environ, **extra_env)
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py")] + argv, capture_output=True, text=True,
+                           env=env, timeout=120)
+        assert r.returncode == 2, (argv, r.returncode, r.stderr)
+        assert "measures one GPU" in r.stderr
+        assert r.stdout == ""
