@@ -103,13 +103,42 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
     a.alpha[m * a.n_tok + t] = gate_value(a.partials, m, a.n_parts, a.n_tok, t, a.d, a.eps);
 }
 
+// Conv taps of 4 channels, wt[j][c] multiplying u_{t-j} of channel c0 + c
+// (the weight stored at index K_c-1-j; zero for j >= K_c is chosen at use).
+// TAP4: K_c = 4 and the taps 16-byte aligned, so a channel's four taps are
+// one load (else one load per tap; either way the lanes are 16 K_c bytes
+// apart).
+template <bool TAP4>
+__device__ __forceinline__ void load_taps(const float *conv_w, int kc, int c0, float (&wt)[4][kVec]) {
+    if constexpr (TAP4) {
+#pragma unroll
+        for (int c = 0; c < kVec; ++c) {
+            const f32x4_t w4 = *reinterpret_cast<const f32x4_t *>(conv_w + (int64_t)(c0 + c) * 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wt[j][c] = w4[3 - j];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int c = 0; c < kVec; ++c) wt[j][c] = conv_w[(int64_t)(c0 + c) * kc + max(kc - 1 - j, 0)];
+    }
+}
+
 constexpr int kPartCap = 4096;  // gate partials staged in LDS per round
+// Threads per workgroup at most: the channel quads of a token are split into
+// the fewest workgroups of at most five waves (d = 2560: two of 320 threads,
+// where 256-thread workgroups leave a third one half empty).
+constexpr int kFuseMaxThreads = 320;
 
 // SBF16: the carried conv state is bf16 (else fp32).  A compile-time choice:
 // with a runtime one the compiler widens each bf16 row inside its branch and
 // waits for that load alone, one memory round trip per state row.
-template <bool BF16, int BR, bool SBF16>
-__global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
+// TAP4: K_c = 4 with 16-byte aligned taps (one load per channel).  ONE: one
+// position per sequence (a decode step): no earlier rows of v to read and one
+// position per group, so no load is made twice.
+template <bool BF16, int BR, bool SBF16, bool TAP4, bool ONE>
+__global__ __launch_bounds__(kFuseMaxThreads) void fuse_kernel(FuseArgs a) {
     __shared__ float alpha_s[BR][kPos + 3];
     __shared__ float sums_s[3][BR * (kPos + 3)];
     __shared__ float part_s[kPartCap];
@@ -171,15 +200,20 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
 #pragma unroll
     for (int s = 1; s <= 3; ++s) {
         const int p = t0 - s;
-        vprev[s - 1] = *reinterpret_cast<const f32x4_t *>(a.v + (row0 + max(p, 0)) * d + cc0);
-        vprev_ok[s - 1] = live && p >= 0;
+        if constexpr (ONE) {
+            vprev[s - 1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            vprev_ok[s - 1] = false;
+        } else {
+            vprev[s - 1] = *reinterpret_cast<const f32x4_t *>(a.v + (row0 + max(p, 0)) * d + cc0);
+            vprev_ok[s - 1] = live && p >= 0;
+        }
         const bool need = live && p < 0 && a.conv_state && s <= kc - 1;
         sprev_ok[s - 1] = need;
 #pragma unroll
         for (int m = 0; m < BR; ++m)
             sprev[m][s - 1].load(sbase, need ? (((int64_t)m * a.batch + b) * (kc - 1) + (kc - 1 - s)) * d + c0 : 0);
     }
-    constexpr int kGroup = BR == 1 ? 8 : (BR == 2 ? 4 : 2);
+    constexpr int kGroup = ONE ? 1 : (BR == 1 ? 8 : (BR == 2 ? 4 : 2));
     f32x4_t vv[kGroup];
     Raw4<BF16> hv[kGroup][BR];
     auto load_group = [&](int tg) {
@@ -193,12 +227,8 @@ __global__ __launch_bounds__(256) void fuse_kernel(FuseArgs a) {
         }
     };
     load_group(t0);
-    // conv taps, wt[j][c] multiplying u_{t-j} (zero for j >= kc, chosen at use)
     float wt[4][kVec];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int c = 0; c < kVec; ++c) wt[j][c] = a.conv_w[(int64_t)(cc0 + c) * kc + max(kc - 1 - j, 0)];
+    load_taps<TAP4>(a.conv_w, kc, cc0, wt);
 
     for (int w = tid; w < n_sum; w += blockDim.x) sums_s[0][w] = sums_s[1][w] = sums_s[2][w] = 0.f;
     for (int q0 = 0; q0 < a.n_parts; q0 += q_round) {
@@ -467,19 +497,31 @@ void launch_gate(const GateArgs &a, hipStream_t s) {
 
 void launch_fuse(const FuseArgs &a, engram_dtype dt, hipStream_t s) {
     const int need = (a.d + kVec - 1) / kVec;
-    int threads = ((need + 63) / 64) * 64;
-    if (threads > 256) threads = 256;
-    const int gz = (need + threads - 1) / threads;
-    dim3 grid((a.seqlen + kPos - 1) / kPos, a.batch, gz);
+    const int gz = (need + kFuseMaxThreads - 1) / kFuseMaxThreads;
+    const int threads = ((need + gz - 1) / gz + 63) / 64 * 64;
+    const dim3 grid((a.seqlen + kPos - 1) / kPos, a.batch, gz);
+    const bool tap4 = a.conv_k == 4 && (reinterpret_cast<uintptr_t>(a.conv_w) & 15) == 0;
+    const bool one = a.seqlen == 1;
     // (an fp32 plan carries an fp32 state)
+#define ENGRAM_FUSE_SHAPE(BF, BR, SBF)                                                           \
+    do {                                                                                         \
+        if (one && tap4)                                                                         \
+            launch_kernel((fuse_kernel<BF, BR, SBF, true, true>), grid, dim3(threads), s, a);    \
+        else if (one)                                                                            \
+            launch_kernel((fuse_kernel<BF, BR, SBF, false, true>), grid, dim3(threads), s, a);   \
+        else if (tap4)                                                                           \
+            launch_kernel((fuse_kernel<BF, BR, SBF, true, false>), grid, dim3(threads), s, a);   \
+        else                                                                                     \
+            launch_kernel((fuse_kernel<BF, BR, SBF, false, false>), grid, dim3(threads), s, a);  \
+    } while (0)
 #define ENGRAM_FUSE_LAUNCH(BR)                                                                   \
     do {                                                                                         \
         if (dt != ENGRAM_BF16)                                                                   \
-            launch_kernel((fuse_kernel<false, BR, false>), grid, dim3(threads), s, a);           \
+            ENGRAM_FUSE_SHAPE(false, BR, false);                                                 \
         else if (a.state_bf16)                                                                   \
-            launch_kernel((fuse_kernel<true, BR, true>), grid, dim3(threads), s, a);             \
+            ENGRAM_FUSE_SHAPE(true, BR, true);                                                   \
         else                                                                                     \
-            launch_kernel((fuse_kernel<true, BR, false>), grid, dim3(threads), s, a);            \
+            ENGRAM_FUSE_SHAPE(true, BR, false);                                                  \
     } while (0)
     switch (a.n_branches) {
         case 1: ENGRAM_FUSE_LAUNCH(1); break;
@@ -488,6 +530,7 @@ void launch_fuse(const FuseArgs &a, engram_dtype dt, hipStream_t s) {
         default: ENGRAM_FUSE_LAUNCH(4); break;
     }
 #undef ENGRAM_FUSE_LAUNCH
+#undef ENGRAM_FUSE_SHAPE
 }
 
 }  // namespace engram

@@ -353,6 +353,42 @@ def test_forward_multibranch_prefill_two_layers_sampled(B):
         torch.cuda.empty_cache()
 
 
+def test_decode_step_batch_size_invariance(B):
+    """A decode step of 3,328 sequences (260 narrow projection tiles, more
+    than one round) and the same step of its first 128 sequences (10 tiles)
+    give the same bits for those sequences: outputs, gates, conv state and
+    context; sampled rows of the large step against the oracle."""
+    say("decode step batch-size invariance")
+    wl = dataclasses.replace(small_wl(n_branches=4, batch=3328, seqlen=1, head_dim=64), decode=True,
+                             state_dtype="bf16")
+    assert wl.emb_dim % 256 == 0
+    dl = make_device_layer(wl)
+    toks = W.make_tokens(wl)
+    Br, d, nb = wl.n_branches, wl.d_model, 128
+    ctx_a = dev_i32(dl.li.prev_ctx)
+    st_a = to_device(dl.li.conv_state, dl.plan.state_torch_dtype, "cuda")
+    out_a, alpha_a, bad = forward(dl, toks, prev_ctx=ctx_a, conv_state=st_a)
+    assert bad == 0
+    ctx_b = dev_i32(dl.li.prev_ctx[:nb])
+    st_b = st_a.new_empty((Br, nb) + tuple(st_a.shape[2:]))
+    st_b.copy_(to_device(dl.li.conv_state[:, :nb], dl.plan.state_torch_dtype, "cuda"))
+    h_b = dl.h[:, :nb].contiguous()
+    out_b, alpha_b, _ = forward(dl, np.ascontiguousarray(toks[:nb]), prev_ctx=ctx_b, conv_state=st_b, h=h_b)
+    assert torch.equal(out_a[:, :nb], out_b)
+    assert torch.equal(alpha_a[:, :nb], alpha_b)
+    assert torch.equal(st_a[:, :nb], st_b)
+    assert torch.equal(ctx_a[:nb], ctx_b)
+    rows = np.arange(5, wl.batch, 211)
+    idx, _, new_ctx = oracle_indices(wl, dl.li, toks, dl.comp_map_host, prev_ctx=dl.li.prev_ctx)
+    L = oracle_layer(wl, dl.li, idx, wl.batch, 1, rows=rows, conv_state=dl.li.conv_state)
+    ref, ref_alpha = L.forward_positions(rows)
+    assert_within(host(out_a)[:, rows], ref, "bf16", "decode out, 3328 sequences")
+    assert np.abs(host(alpha_a)[:, rows] - ref_alpha).max() <= alpha_tol("bf16")
+    assert np.array_equal(ctx_a.cpu().numpy(), new_ctx)
+    del dl
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("state_dtype", ["bf16", "f32"])
 def test_forward_multibranch_decode_with_state(B, state_dtype):
     wl = dataclasses.replace(W.workload("multibranch_decode"), state_dtype=state_dtype)
@@ -574,22 +610,30 @@ def _split(x, n_branches, batch, seqlen, a, b):
     return x.view(n_branches, batch, seqlen, d)[:, :, a:b].contiguous().view(n_branches, batch * (b - a), d)
 
 
-def test_chunked_prefill_and_decode_equal_full_prefill_bitwise(B):
-    say("chunk invariance")
-    wl = small_wl(n_branches=4, batch=3, seqlen=40)
-    dl = make_device_layer(wl)
+@pytest.mark.parametrize("dt,br,kc,mode,flags", [
+    ("bf16", 4, 4, oracle.CONV_LINEAR, 0),
+    ("f32", 3, 4, oracle.CONV_SILU_SKIP, 0),
+    ("bf16", 2, 2, oracle.CONV_SILU_SKIP, oracle.OUT_DELTA),
+    ("bf16", 1, 3, oracle.CONV_LINEAR, 0),
+])
+def test_chunked_prefill_and_decode_equal_full_prefill_bitwise(B, dt, br, kc, mode, flags):
+    """Chunks of 1, 1, 3, 32, 1 and 2 positions (one-token chunks take the
+    decode-step kernel) against the whole sequence in one call."""
+    say("chunk invariance", dt, br, kc, mode, flags)
+    wl = small_wl(n_branches=br, batch=3, seqlen=40, dtype=dt, conv_kernel=kc)
+    dl = make_device_layer(wl, conv_mode=mode)
     toks = W.make_tokens(wl)
     Br, d = wl.n_branches, wl.d_model
     pad = np.full((wl.batch, 2), wl.vocab_comp, np.int32)
     ctx_full = dev_i32(pad)
-    st_full = torch.zeros((Br, wl.batch, 3, d), dtype=torch.float32, device="cuda")
-    full, alpha_full, _ = forward(dl, toks, prev_ctx=ctx_full, conv_state=st_full)
+    st_full = torch.zeros((Br, wl.batch, kc - 1, d), dtype=torch.float32, device="cuda")
+    full, alpha_full, _ = forward(dl, toks, prev_ctx=ctx_full, conv_state=st_full, flags=flags)
     ctx = dev_i32(pad)
     st = torch.zeros_like(st_full)
     parts, alphas = [], []
     for a, b in [(0, 1), (1, 2), (2, 5), (5, 37), (37, 38), (38, 40)]:
         h = _split(dl.h, Br, wl.batch, wl.seqlen, a, b)
-        o, al, _ = forward(dl, np.ascontiguousarray(toks[:, a:b]), prev_ctx=ctx, conv_state=st, h=h)
+        o, al, _ = forward(dl, np.ascontiguousarray(toks[:, a:b]), prev_ctx=ctx, conv_state=st, h=h, flags=flags)
         parts.append(o.view(Br, wl.batch, b - a, d))
         alphas.append(al.view(Br, wl.batch, b - a))
     chunked = torch.cat(parts, 2).view(Br, -1, d)
