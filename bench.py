@@ -59,7 +59,7 @@ def parse():
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time only whole steps (no per-launch events; no roofline)")
     ap.add_argument("--retrieve-in-projection", action="store_true",
-                    help="engram_forward flag: short chunks retrieve inside the projection launch")
+                    help="engram_forward flag: retrieval inside the projection launches")
     ap.add_argument("--overlap-retrieval", action="store_true",
                     help="with several layers per step: the later layers' rows are retrieved on a second stream "
                          "while the first layer computes (their slots depend only on the token ids)")

@@ -141,12 +141,17 @@ struct InLaunchRetrieval {
 // fusion-kernel route (W_k and W_v in one launch) on 128 x 128 tiles, where
 // a separate retrieval kernel would be a latency-bound launch of its own.
 bool retrieval_in_projection(const engram_plan_s &p, int32_t batch, int32_t seqlen) {
-    if (p.cfg.dtype != ENGRAM_BF16 || fused_value_path(p, batch, seqlen)) return false;
+    if (p.cfg.dtype != ENGRAM_BF16) return false;
     ProjArgs pa{};
-    pa.n_mats = p.cfg.n_branches + 1;
     pa.d = p.cfg.d_model;
     pa.n_tok = (int64_t)batch * seqlen;
     pa.K = p.emb_dim;
+    if (fused_value_path(p, batch, seqlen)) {
+        // the W_k launch and the fused W_v launch both retrieve
+        pa.n_mats = p.cfg.n_branches;
+        return proj_gather_tables_ok(pa, p.n_tables);
+    }
+    pa.n_mats = p.cfg.n_branches + 1;
     return proj_gather_ok(pa, p.n_tables);
 }
 
@@ -201,7 +206,9 @@ engram_status do_fuse(engram_plan_s &p, const void *emb, const void *h, int32_t 
     }
     {
         Launch l(p, ENGRAM_K_GEMM, s);
-        if (rin)
+        if (rin && fused_v)
+            launch_proj_k_gather_bf16(pa, s);
+        else if (rin)
             launch_proj_gather_bf16(pa, s);
         else if (p.cfg.dtype == ENGRAM_BF16)
             launch_proj_bf16(pa, s);
@@ -221,7 +228,9 @@ engram_status do_fuse(engram_plan_s &p, const void *emb, const void *h, int32_t 
         ga.n_branches = Br;
         ga.n_parts = pa.n_parts;
         ga.eps = p.cfg.rms_eps;
-        ga.ctx = ctx;
+        // (with retrieval inside the launches the W_v launch still reads the
+        // old context: it is rolled at the end instead)
+        ga.ctx = rin ? CtxUpdate{} : ctx;
         ga.batch = batch;
         ga.seqlen = seqlen;
         {
@@ -246,9 +255,13 @@ engram_status do_fuse(engram_plan_s &p, const void *emb, const void *h, int32_t 
         pv.conv_k = p.cfg.conv_kernel;
         pv.conv_mode = p.cfg.conv_mode;
         pv.flags = flags;
+        pv.bad = nullptr;  // out-of-range ids were counted by the W_k launch
         {
             Launch l(p, ENGRAM_K_GEMM_V, s);
-            launch_proj_v_fused_bf16(pv, s);
+            if (rin)
+                launch_proj_v_fused_gather_bf16(pv, s);
+            else
+                launch_proj_v_fused_bf16(pv, s);
         }
         const int32_t n_tiles = (int32_t)((n_tok + kTokTile - 1) / kTokTile);
         if (n_tiles > 1) {
@@ -272,6 +285,11 @@ engram_status do_fuse(engram_plan_s &p, const void *emb, const void *h, int32_t 
             sa.flags = flags;
             Launch l(p, ENGRAM_K_SEAM, s);
             launch_seam(sa, s);
+        }
+        if (rin && ctx.prev_ctx) {
+            if (last_launch_status() != ENGRAM_OK) return ENGRAM_E_DEVICE;
+            Launch l(p, ENGRAM_K_AUX, s);
+            launch_ctx_update(ctx, batch, seqlen, s);
         }
     } else {
         // a chunk of at most kFusePositions positions is one fusion-kernel

@@ -187,6 +187,16 @@ void launch_proj_gather_bf16(const ProjArgs &a, hipStream_t s);
 // tile are left to launch_seam.
 constexpr int kTokTile = 256;
 void launch_proj_v_fused_bf16(const ProjArgs &a, hipStream_t s);
+// Retrieval inside the two launches of the route above (W_v separate): the
+// W_k launch of every branch and the fused W_v launch each hash the n-grams
+// of their tiles' tokens and read their E operand from the tables, as
+// launch_proj_gather_bf16 does (E never reaches memory; the W_k launch takes
+// 128 x 128 tiles where launch_proj_bf16 would).  Only the launch given
+// a.bad counts out-of-range ids; neither writes the carried context.  Needs
+// n_tables <= kGatherMaxTables and d_e % 8 == 0 (proj_gather_tables_ok).
+bool proj_gather_tables_ok(const ProjArgs &a, int32_t n_tables);
+void launch_proj_k_gather_bf16(const ProjArgs &a, hipStream_t s);
+void launch_proj_v_fused_gather_bf16(const ProjArgs &a, hipStream_t s);
 // Plain contraction C[t][n] = sum_k W[n][k] E[t][k] (bf16 operands, fp32
 // accumulate and result) on the same MFMA main loop: W rows are the n_mats
 // matrices of a.w stacked (a.d rows each), E has a.n_tok rows, K = a.K

@@ -521,15 +521,17 @@ __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t 
 // 256 x 256 tiles to fill the chip (decode).  A wave always owns 128 output
 // channels in the same MFMA layout, so the gate partial sums come out
 // bit-identical whichever tile computed them.
-template <int MODE, int BR, bool SILU, bool NARROW>
+template <int MODE, int BR, bool SILU, bool NARROW, bool TG = false>
 __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_bf16_kernel(ProjArgs a) {
     static_assert(!(NARROW && MODE == 1), "the fused value epilogue is written for the wide tile");
+    static_assert(!TG || (!NARROW && (MODE == 0 || MODE == 1)), "TG: wide W_k or W_v launch reading the tables");
     static_assert(MODE >= 0 && MODE <= 6, "mode");
     constexpr bool kKMajW = MODE == 4 || MODE == 6;  // weight-side operand stored K-major
     constexpr bool kKMajE = MODE == 4;               // token-side operand stored K-major
     constexpr bool kPlain = MODE == 3 || MODE == 4 || MODE == 5 || MODE == 6;  // fp32 store epilogue
     static_assert(MODE != 2 || NARROW, "retrieval inside the launch is written for the narrow tile");
-    constexpr bool kGather = MODE == 2;
+    // retrieval inside the launch: the narrow mode 2, or a wide W_k / W_v launch with TG
+    constexpr bool kGather = MODE == 2 || TG;
     constexpr bool kGateK = MODE == 0 || MODE == 2 || MODE == 5;  // W_k / W_v launch with the gate-partial epilogue
     typedef TileCfg<NARROW> C;
     constexpr int TBN = C::BN, TBT = C::BT, TTHREADS = C::kThreads, TWAVES = C::kWaves, TWGN = C::kWavesN;
@@ -537,10 +539,20 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
     __shared__ StageT<TOPB> st0, st1, st2, st3;
     __shared__ float alpha_s[MODE == 1 ? BR : 1][TBT];
     __shared__ __attribute__((aligned(16))) float gsm_s[kGateK ? TWAVES * WN : 4];
-    __shared__ uint32_t idx_s[kGather ? 128 * kGatherMaxTables : 1];  // slot of (token of the tile, table)
+    // The W_v launch reading the tables keeps its slot table in the space of
+    // the epilogue's taps and halo rows (LDS would not hold both): the slots
+    // are read only while the ring is filled, the taps and halo rows written
+    // only after the ring's last barrier.
+    // (taps_own is then one buffer: the slots while the ring fills, the taps
+    // and after them the halo rows in the epilogue)
+    constexpr bool kSlotsInEpi = TG && MODE == 1;
+    constexpr int kEpiFloats = 4 * TBN + TWAVES * kHalo * WN;
+    constexpr int kSlots = TBT * kGatherMaxTables;
+    __shared__ uint32_t idx_own[kGather && !kSlotsInEpi ? kSlots : 1];  // slot of (token of the tile, table)
     __shared__ const char *tab_s[kGather ? kGatherMaxTables : 1];
-    __shared__ __attribute__((aligned(16))) float taps_s[MODE == 1 ? 4 * TBN : 4];
-    __shared__ __attribute__((aligned(16))) float halo_s[MODE == 1 ? TWAVES * kHalo * WN : 4];
+    __shared__ __attribute__((aligned(16)))
+    float taps_own[MODE == 1 ? (kSlotsInEpi ? (kEpiFloats > kSlots ? kEpiFloats : kSlots) : 4 * TBN) : 4];
+    __shared__ __attribute__((aligned(16))) float halo_own[MODE == 1 && !kSlotsInEpi ? TWAVES * kHalo * WN : 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -602,8 +614,9 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
         }
     }
 
-    // Mode 2: the slots of the tile's tokens (tokens past n_tok: slot 0) and
-    // the table bases go to LDS before the first stage.  A lane's 16-byte K
+    // Retrieval inside the launch (mode 2, TG): the slots of the tile's
+    // tokens (tokens past n_tok: slot 0) and the table bases go to LDS
+    // before the first stage.  A lane's 16-byte K
     // piece of stage s is element 32 s + 8 lchunk of E, i.e. element goff of
     // table gtau (d_e % 8 == 0: a piece never straddles two tables); the
     // stages are issued in K order, so (gtau, goff) advance by BK each.
@@ -638,7 +651,8 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
             const uint64_t k3 = ((uint64_t)c2 * Bv + (uint64_t)c1) * Bv + (uint64_t)c0;
             for (int tau = 0; tau < g_nt; ++tau) {
                 const uint64_t key = a.hc.order_of[tau] == 2 ? k2 : k3;
-                idx_s[tl * g_nt + tau] =
+                uint32_t *slots = kSlotsInEpi ? reinterpret_cast<uint32_t *>(taps_own) : idx_own;
+                slots[tl * g_nt + tau] =
                     live_tok ? mod_prime(mix64(key ^ a.hc.seed[tau]), a.hc.rows[tau], a.hc.magic[tau]) : 0u;
             }
         }
@@ -661,11 +675,13 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
         const int kbytes = (kbase + (k0)) * 2;                                                   \
         if constexpr (kGather) {                                                                 \
             const char *tb = tab_s[gtau];                                                        \
+            const uint32_t *slots = kSlotsInEpi ? reinterpret_cast<const uint32_t *>(taps_own) : idx_own; \
             _Pragma("unroll") for (int i = 0; i < TBPW; ++i) {                                   \
                 const int blk = wave * TBPW + i;                                                 \
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void_t *)&STG.w[blk * kBlockBytes], \
                                                          16, woff[i], kbytes, 0, 0);             \
-                const uint32_t ix = idx_s[(blk * 16 + lr) * g_nt + gtau];                        \
+                const uint32_t ix = slots[(MODE == 1 ? 64 * (blk >> 2) + 4 * lr + (blk & 3)      \
+                                                      : blk * 16 + lr) * g_nt + gtau];           \
                 __builtin_amdgcn_global_load_lds(tb + (uint64_t)ix * g_row_bytes + 2 * goff,     \
                                                  (lds_void_t *)&STG.e[blk * kBlockBytes], 16, 0, 0); \
             }                                                                                    \
@@ -952,7 +968,12 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
         }
     } else if constexpr (!kGateK) {
         // each wave's two chunk buffers: 8 KB of st0/st1 (A) and of st2/st3 (B)
-        fused_value_epilogue<BR, SILU>(a, acc, alpha_s, halo_s, taps_s, hA, hB, wave, lane, nl, n0, tile_t, t0);
+        if constexpr (kSlotsInEpi)
+            fused_value_epilogue<BR, SILU>(a, acc, alpha_s, taps_own + 4 * TBN, taps_own, hA, hB, wave, lane, nl, n0,
+                                           tile_t, t0);
+        else
+            fused_value_epilogue<BR, SILU>(a, acc, alpha_s, halo_own, taps_own, hA, hB, wave, lane, nl, n0, tile_t,
+                                           t0);
     }
 }
 
@@ -1048,16 +1069,19 @@ int plain_k_splits(int64_t n_tok, int64_t rows, int64_t K) {
     return splits;
 }
 
-void launch_proj_v_fused_bf16(const ProjArgs &a, hipStream_t s) {
+namespace {
+
+template <bool TG>
+void launch_proj_v_fused(const ProjArgs &a, hipStream_t s) {
     const int n_tiles_n = (a.d + BN - 1) / BN;
     const int64_t n_tiles_t = (a.n_tok + BT - 1) / BT;
     const dim3 grid((unsigned)((int64_t)n_tiles_n * n_tiles_t));
 #define ENGRAM_PROJ_V_LAUNCH(BR)                                                                      \
     do {                                                                                              \
         if (a.conv_mode == ENGRAM_CONV_SILU_SKIP)                                                     \
-            launch_kernel((proj_bf16_kernel<1, BR, true, false>), grid, dim3(kThreads), s, a);        \
+            launch_kernel((proj_bf16_kernel<1, BR, true, false, TG>), grid, dim3(kThreads), s, a);    \
         else                                                                                          \
-            launch_kernel((proj_bf16_kernel<1, BR, false, false>), grid, dim3(kThreads), s, a);       \
+            launch_kernel((proj_bf16_kernel<1, BR, false, false, TG>), grid, dim3(kThreads), s, a);   \
     } while (0)
     switch (a.n_branches) {
         case 1: ENGRAM_PROJ_V_LAUNCH(1); break;
@@ -1067,5 +1091,25 @@ void launch_proj_v_fused_bf16(const ProjArgs &a, hipStream_t s) {
     }
 #undef ENGRAM_PROJ_V_LAUNCH
 }
+
+}  // namespace
+
+void launch_proj_v_fused_bf16(const ProjArgs &a, hipStream_t s) { launch_proj_v_fused<false>(a, s); }
+
+bool proj_gather_tables_ok(const ProjArgs &a, int32_t n_tables) {
+    return n_tables >= 1 && n_tables <= kGatherMaxTables && a.K % n_tables == 0 && (a.K / n_tables) % 8 == 0;
+}
+
+void launch_proj_k_gather_bf16(const ProjArgs &a, hipStream_t s) {
+    const int n_total = a.n_mats * a.d;
+    const int64_t wide = (int64_t)((n_total + BN - 1) / BN) * ((a.n_tok + BT - 1) / BT);
+    if (wide < 256) {  // the tiles launch_proj_bf16 would take: 128 x 128
+        launch_proj_gather_bf16(a, s);
+        return;
+    }
+    launch_kernel((proj_bf16_kernel<0, 1, false, false, true>), dim3((unsigned)wide), dim3(kThreads), s, a);
+}
+
+void launch_proj_v_fused_gather_bf16(const ProjArgs &a, hipStream_t s) { launch_proj_v_fused<true>(a, s); }
 
 }  // namespace engram

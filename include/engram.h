@@ -62,14 +62,18 @@ enum { ENGRAM_CONV_LINEAR = 0, ENGRAM_CONV_SILU_SKIP = 1 };
 
 /* engram_gate_fuse / engram_forward flag: write y instead of h + y. */
 enum { ENGRAM_OUT_DELTA = 1u << 0 };
-/* engram_forward flag: on chunks shorter than K_c - 1 (decode), where W_k and
- * W_v go through one launch on 128 x 128 tiles, that launch also retrieves:
- * each workgroup hashes the n-grams of its tokens and loads its E operand
- * straight from the table rows (E never reaches memory; n_tables <= 16).
- * Same results bit for bit.  At a decode step of 256 sequences (four
- * branches, d = 2560) it measured 3.6% faster per step than the separate
- * retrieval kernel; off by default, having been timed at that shape only.
- * Ignored where it does not apply. */
+/* engram_forward flag: retrieval inside the projection launches.  On chunks
+ * shorter than K_c - 1 (decode), where W_k and W_v go through one launch on
+ * 128 x 128 tiles, that launch also retrieves: each workgroup hashes the
+ * n-grams of its tokens and loads its E operand straight from the table
+ * rows.  On longer chunks the W_k launch and the fused W_v launch each do
+ * the same for their tiles.  E never reaches memory; n_tables <= 16 and
+ * d_e % 8 == 0.  Same results bit for bit.  Measured at a decode step of 256
+ * sequences (four branches, d = 2560): 3.6% faster per step than the
+ * separate retrieval kernel.  On prefill chunks: 5% slower at 8 x 4096
+ * tokens with d = 1024, 19-25% slower at d = 2560 (random row pieces from
+ * HBM outrun the operand ring).  Off by default.  Ignored where it does not
+ * apply. */
 enum { ENGRAM_RETRIEVE_IN_PROJECTION = 1u << 1 };
 
 #define ENGRAM_MAX_TABLES 32

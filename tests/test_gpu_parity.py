@@ -287,9 +287,9 @@ def test_forward_bf16_small_shapes_all_positions(B, n_branches, batch, seqlen):
 def test_forward_many_tables_all_positions(B, heads, orders, dtype, batch, seqlen):
     """engram_forward with 24 or 32 tables: fused retrieval and both fusion
     routes (prefill tiles, and the one-token route with its carried state),
-    every position against the oracle; a one-token chunk with the
-    retrieve-in-projection flag (which covers at most 16 tables, so the
-    library keeps the separate retrieval) gives the same bits."""
+    every position against the oracle; the retrieve-in-projection flag
+    (which covers at most 16 tables, so with more the library keeps the
+    separate retrieval) gives the same bits."""
     say("forward many tables", heads, orders, dtype, batch, seqlen)
     wl = many_tables_wl(heads, orders, batch, seqlen, dtype=dtype)
     dl = make_device_layer(wl)
@@ -307,18 +307,18 @@ def test_forward_many_tables_all_positions(B, heads, orders, dtype, batch, seqle
     ref, ref_alpha, _ = L.forward_all()
     assert_within(host(out), ref, dtype, "many tables out")
     assert np.abs(host(alpha) - ref_alpha).max() <= alpha_tol(dtype)
-    if seqlen == 1:
-        st2 = None if state is None else to_device(state, torch.float32, "cuda")
-        out2, _, _ = forward(dl, toks, prev_ctx=dev_i32(ctx), conv_state=st2,
-                             flags=B.RETRIEVE_IN_PROJECTION)
-        assert torch.equal(out2.view(torch.int16) if dtype == "bf16" else out2,
-                           out.view(torch.int16) if dtype == "bf16" else out)
+    st2 = None if state is None else to_device(state, torch.float32, "cuda")
+    out2, _, _ = forward(dl, toks, prev_ctx=None if ctx is None else dev_i32(ctx), conv_state=st2,
+                         flags=B.RETRIEVE_IN_PROJECTION)
+    assert torch.equal(out2.view(torch.int16) if dtype == "bf16" else out2,
+                       out.view(torch.int16) if dtype == "bf16" else out)
 
 
-def _sampled_check(wl, dl, toks, n_pos, what, prev_ctx=None, conv_state=None, seed=0):
+def _sampled_check(wl, dl, toks, n_pos, what, prev_ctx=None, conv_state=None, seed=0, flags=0):
     batch, seqlen = toks.shape
     out, alpha, bad = forward(dl, toks, prev_ctx=None if prev_ctx is None else dev_i32(prev_ctx),
-                              conv_state=None if conv_state is None else to_device(conv_state, torch.float32, "cuda"))
+                              conv_state=None if conv_state is None else to_device(conv_state, torch.float32, "cuda"),
+                              flags=flags)
     assert bad == 0
     pos = sample_positions(batch, seqlen, n_pos, seed)
     idx, _, _ = oracle_indices(wl, dl.li, toks, dl.comp_map_host, prev_ctx=prev_ctx)
@@ -328,16 +328,31 @@ def _sampled_check(wl, dl, toks, n_pos, what, prev_ctx=None, conv_state=None, se
     got = host(out)[:, pos]
     assert_within(got, ref, wl.dtype, what)
     assert np.abs(host(alpha)[:, pos] - ref_alpha).max() <= alpha_tol(wl.dtype)
-    return out
+    return out, alpha
+
+
+def _same_bits_in_projection(dl, toks, out, alpha, flag):
+    """The forward with retrieval inside both projection launches gives the
+    bits of the separate-retrieval forward."""
+    out2, alpha2, bad2 = forward(dl, toks, flags=flag)
+    assert bad2 == 0
+    assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
+    assert torch.equal(alpha2, alpha)
 
 
 @pytest.mark.parametrize("name", ["small", "layer27b"])
 def test_forward_full_size_sampled(B, name):
+    """Sampled positions against the oracle; the same forward with retrieval
+    inside the W_k and W_v launches (256 x 256 tiles at both sizes) gives
+    the same bits, its sampled positions checked against the oracle too."""
     say("forward full size", name)
     wl = W.workload(name)
     dl = make_device_layer(wl)
     toks = W.make_tokens(wl)
-    _sampled_check(wl, dl, toks, 48, name)
+    out, alpha = _sampled_check(wl, dl, toks, 48, name)
+    say("forward full size, retrieval in projection", name)
+    _same_bits_in_projection(dl, toks, out, alpha, B.RETRIEVE_IN_PROJECTION)
+    _sampled_check(wl, dl, toks, 24, name + " (retrieval in projection)", seed=7, flags=B.RETRIEVE_IN_PROJECTION)
     del dl
     torch.cuda.empty_cache()
 
@@ -433,7 +448,9 @@ def test_forward_maxtable_sampled(B, maxtable_layer, name):
     say("forward", name)
     wl = W.workload(name)
     toks = W.make_tokens(wl)
-    _sampled_check(wl, maxtable_layer, toks, 24, name)
+    out, alpha = _sampled_check(wl, maxtable_layer, toks, 24, name)
+    say("forward, retrieval in projection", name)
+    _same_bits_in_projection(maxtable_layer, toks, out, alpha, B.RETRIEVE_IN_PROJECTION)
 
 
 @pytest.mark.parametrize("dtype,d,heads,head_dim,orders,kc,br,batch,seqlen", [
@@ -955,6 +972,66 @@ def test_short_chunks_retrieval_in_projection(B, batch, seqlen, heads, in_proj):
     ref, ref_alpha, _ = L.forward_all()
     assert_within(host(out), ref, "bf16", "short chunks, retrieval in projection")
     assert np.abs(host(alpha) - ref_alpha).max() <= alpha_tol("bf16")
+
+
+@pytest.mark.parametrize("br,batch,seqlen,heads,head_dim,mode,flags,sdt,with_ctx", [
+    (1, 3, 300, 2, 32, oracle.CONV_LINEAR, 0, "f32", True),       # two token tiles, seam rows
+    (4, 2, 257, 4, 32, oracle.CONV_SILU_SKIP, 0, "bf16", True),   # four branches, ragged second tile
+    (2, 1, 600, 8, 16, oracle.CONV_LINEAR, oracle.OUT_DELTA, "f32", False),  # 16 tables of d_e = 16
+    (3, 5, 40, 2, 64, oracle.CONV_SILU_SKIP, oracle.OUT_DELTA, "f32", True),
+])
+def test_prefill_retrieval_in_projection_bitwise(B, br, batch, seqlen, heads, head_dim, mode, flags, sdt,
+                                                 with_ctx):
+    """Chunks on the prefill route (W_v launch separate) with retrieval
+    inside the W_k and W_v launches: out, gates, carried context, new conv
+    state and the out-of-range count equal the separate-retrieval route's
+    bit for bit; out against the oracle within the bf16 bound."""
+    say("prefill, retrieval in projection", br, batch, seqlen, heads, head_dim, mode, flags, sdt, with_ctx)
+    wl = dataclasses.replace(small_wl(n_branches=br, batch=batch, seqlen=seqlen, heads=heads, head_dim=head_dim),
+                             decode=with_ctx, state_dtype=sdt)
+    dl = make_device_layer(wl, conv_mode=mode)
+    toks = W.make_tokens(wl)
+    toks[0, 0] = -5
+    toks[-1, seqlen // 2] = wl.vocab + 3
+    n_bad = int(((toks < 0) | (toks >= wl.vocab)).sum())
+    runs = []
+    for f in (0, B.RETRIEVE_IN_PROJECTION):
+        ctx = dev_i32(dl.li.prev_ctx) if with_ctx else None
+        st = to_device(dl.li.conv_state, dl.plan.state_torch_dtype, "cuda") if with_ctx else None
+        out, alpha, bad = forward(dl, toks, prev_ctx=ctx, conv_state=st, flags=flags | f)
+        runs.append((out, alpha, bad, ctx, st))
+    (o1, a1, b1, c1, s1), (o2, a2, b2, c2, s2) = runs
+    assert b1 == b2 == n_bad
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(a1, a2)
+    idx, _, new_ctx = oracle_indices(wl, dl.li, toks, dl.comp_map_host,
+                                     prev_ctx=dl.li.prev_ctx if with_ctx else None)
+    if with_ctx:
+        assert torch.equal(c1, c2)
+        assert np.array_equal(c2.cpu().numpy(), new_ctx)
+        assert torch.equal(s1.view(torch.int16) if sdt == "bf16" else s1, s2.view(torch.int16) if sdt == "bf16" else s2)
+    L = oracle_layer(wl, dl.li, idx, batch, seqlen, conv_mode=mode, flags=flags,
+                     conv_state=dl.li.conv_state if with_ctx else None)
+    ref, ref_alpha, _ = L.forward_all()
+    assert_within(host(o2), ref, "bf16", "prefill, retrieval in projection")
+    assert np.abs(host(a2) - ref_alpha).max() <= alpha_tol("bf16")
+    del dl
+    torch.cuda.empty_cache()
+
+
+def test_prefill_retrieval_in_projection_profile(B):
+    """With the flag a prefill chunk launches no retrieval kernel: the W_k
+    launch, the gate, the W_v launch, the seam rows and the context update."""
+    wl = dataclasses.replace(small_wl(n_branches=2, batch=2, seqlen=300), decode=True)
+    dl = make_device_layer(wl)
+    toks = W.make_tokens(wl)
+    ctx = dev_i32(dl.li.prev_ctx)
+    dl.plan.engram_profile_begin(64)
+    forward(dl, toks, prev_ctx=ctx, flags=B.RETRIEVE_IN_PROJECTION)
+    torch.cuda.synchronize()
+    prof = dl.plan.engram_profile_end()
+    for k, n in (("hash", 0), ("gather", 0), ("gemm", 1), ("gate", 1), ("gemm_v", 1), ("seam", 1), ("aux", 1)):
+        assert prof[k]["launches"] == n, (k, prof)
 
 
 def test_retrieval_in_projection_profile(B):
