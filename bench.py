@@ -58,11 +58,18 @@ def parse():
                          "in a dispatch delay the launches around it)")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time only whole steps (no per-launch events; no roofline)")
+    ap.add_argument("--unpacked-weights", action="store_true",
+                    help="pass W_k and W_v as [d][D_e] matrices (default: packed once by engram_pack_weight at "
+                         "set-up, outside the timed region, and read with ENGRAM_WEIGHTS_PACKED)")
     ap.add_argument("--retrieve-in-projection", action="store_true",
                     help="engram_forward flag: retrieval inside the projection launches")
     ap.add_argument("--overlap-retrieval", action="store_true",
                     help="with several layers per step: the later layers' rows are retrieved on a second stream "
                          "while the first layer computes (their slots depend only on the token ids)")
+    ap.add_argument("--pipeline-retrieval", action="store_true",
+                    help="retrieve the next step's rows on a second stream while this step's projections run "
+                         "(engram_retrieve one step ahead, engram_gate_fuse on the main stream; every retrieval "
+                         "and fusion of the measured steps lies inside the timed region)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the forward steps replayed from HIP graphs (captured once per rotation slot): "
                          "a `graph_replay` entry of its own, whole-step time only")
@@ -201,7 +208,11 @@ def main():
         return
     n_tok = wl.n_tokens
     R = max(1, args.rotate)
-    fwd_flags = B.RETRIEVE_IN_PROJECTION if args.retrieve_in_projection else 0
+    rip_flag = B.RETRIEVE_IN_PROJECTION if args.retrieve_in_projection else 0
+    # weights packed once into the projections' operand layout (bf16 plans)
+    packed = not args.unpacked_weights and wl.dtype == "bf16"
+    pk_flag = B.WEIGHTS_PACKED if packed else 0
+    fwd_flags = rip_flag | pk_flag
 
     layers = []
     for slot in range(len(wl.layers)):
@@ -213,6 +224,8 @@ def main():
         if wl.decode:
             ctx = to_device(dl.li.prev_ctx, torch.int32, "cuda")
             conv = to_device(dl.li.conv_state, dl.plan.state_torch_dtype, "cuda")
+        if packed:
+            dl.weights = dl.plan.packed_weights(dl.weights)
         layers.append((dl, hs, out, ws, ctx, conv))
     toks = [to_device(W.make_tokens(wl, seed=wl.seed(2) + 17 * r), torch.int32, "cuda") for r in range(R)]
     torch.cuda.synchronize()
@@ -256,13 +269,52 @@ def main():
             dl, hs, out, ws, ctx, conv = layers[l]
             main.wait_event(ready[l][par])
             dl.plan.engram_gate_fuse(embs[l][par], hs[r], dl.weights, out, ws, wl.batch, wl.seqlen,
-                                     conv_state=conv)
+                                     conv_state=conv, flags=pk_flag)
             if not captured:
                 free[l][par].record(main)
                 used[l][par] = True
 
+    # Retrieval one step ahead: step i fuses batch i (E buffers i % 2 of every
+    # layer, retrieved on the side stream during step i-1) and retrieves batch
+    # i+1 into the other buffers.  Step 0 of a run retrieves its own batch
+    # first, and the last step of a run retrieves nothing, so a run of K steps
+    # holds exactly K retrievals and K fusions.
+    pipeline = args.pipeline_retrieval and not overlap and not rip_flag
+    if pipeline:
+        pside = torch.cuda.Stream()
+        pembs = [[torch.empty((n_tok, wl.emb_dim), dtype=L[0].plan.torch_dtype, device="cuda") for _ in range(2)]
+                 for L in layers]
+        pready = [[torch.cuda.Event() for _ in range(2)] for _ in layers]
+        pfree = [[torch.cuda.Event() for _ in range(2)] for _ in layers]
+        pused = [[False, False] for _ in layers]
+        prun = {"steps": 0}
+
+    def pipe_retrieve(b, par):
+        for l, (dl, hs, out, ws, ctx, conv) in enumerate(layers):
+            if pused[l][par]:
+                pside.wait_event(pfree[l][par])
+            dl.plan.engram_retrieve(toks[b % R], dl.comp_map, dl.tables, pembs[l][par], prev_ctx=ctx, stream=pside)
+            pready[l][par].record(pside)
+
+    def pipe_step(i):
+        main = torch.cuda.current_stream()
+        if i == 0:
+            pside.wait_stream(main)
+            pipe_retrieve(0, 0)
+        if i + 1 < prun["steps"]:
+            pipe_retrieve(i + 1, (i + 1) % 2)
+        for l, (dl, hs, out, ws, ctx, conv) in enumerate(layers):
+            main.wait_event(pready[l][i % 2])
+            dl.plan.engram_gate_fuse(pembs[l][i % 2], hs[i % R], dl.weights, out, ws, wl.batch, wl.seqlen,
+                                     conv_state=conv, flags=pk_flag)
+            pfree[l][i % 2].record(main)
+            pused[l][i % 2] = True
+
     def step(i):
-        enqueue(i % R, i % 2, False)
+        if pipeline:
+            pipe_step(i)
+        else:
+            enqueue(i % R, i % 2, False)
 
     def graph_replay():
         """The same steps as HIP graphs (one per rotation slot, captured once),
@@ -289,6 +341,8 @@ def main():
                 "gpu_event_ms_per_step": round(ev0.elapsed_time(ev1) / args.steps, 4), "graphs": R,
                 "overlap_retrieval": bool(overlap)}
 
+    if pipeline:
+        prun["steps"] = args.warmup
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -302,6 +356,8 @@ def main():
                 dl.plan.engram_profile_every(every)
                 dl.plan.engram_profile_begin(8 * steps + 64, kinds)
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if pipeline:
+            prun["steps"] = steps
         if torch.distributed.is_available() and torch.distributed.is_initialized():
             torch.distributed.barrier()
         torch.cuda.synchronize()
@@ -440,7 +496,7 @@ def main():
     if not args.no_hbm_probe:
         hbm = hbm_ceiling(args)
         if wl.name.startswith("maxtable"):
-            gather_uniform = uniform_gather_legs(wl, layers[0][0], args, R, models["gather"][1])
+            gather_uniform = uniform_gather_legs(wl, layers[0][0], args, R, models["gather"][1], pk_flag)
         if gather is not None and hbm is not None:
             gather["frac_of_stream_read"] = round(gather["achieved_GBs"] / hbm["read"]["GBs"], 4)
 
@@ -471,7 +527,9 @@ def main():
                    "head_dim": wl.head_dim, "emb_dim": De, "table_params": sum(wl.primes()) * wl.head_dim,
                    "rotated_buffers": R, "parallelism": "single GPU",
                    "conv_state_dtype": wl.state_dtype if wl.decode else None,
-                   "retrieval_in_projection": bool(fwd_flags), "overlap_retrieval": bool(overlap)},
+                   "retrieval_in_projection": bool(rip_flag), "overlap_retrieval": bool(overlap),
+                   "packed_weights": bool(packed),
+                   "pipeline_retrieval": bool(pipeline)},
         "roofline": roofline,
         "gather": gather,
         "gather_uniform": gather_uniform,
@@ -521,7 +579,7 @@ def hbm_ceiling(args):
     return best
 
 
-def uniform_gather_legs(wl, dl, args, R, fused_bytes):
+def uniform_gather_legs(wl, dl, args, R, fused_bytes, flags=0):
     """On the same 200 GB of tables: the fused retrieval (hash + gather) of
     uniformly drawn token ids, where the caches cannot help, and the
     index-driven gather of uniformly random slots of every table (engram_gather)."""
@@ -539,12 +597,12 @@ def uniform_gather_legs(wl, dl, args, R, fused_bytes):
     h_out = torch.empty_like(dl.h)
     steps = max(8, args.breakdown_steps)
     for i in range(4):
-        dl.plan.engram_forward(toks[i % R], dl.comp_map, dl.tables, dl.h, dl.weights, h_out, ws)
+        dl.plan.engram_forward(toks[i % R], dl.comp_map, dl.tables, dl.h, dl.weights, h_out, ws, flags=flags)
     torch.cuda.synchronize()
     dl.plan.engram_profile_every(1)
     dl.plan.engram_profile_begin(8 * steps + 64, ["gather"])
     for i in range(steps):
-        dl.plan.engram_forward(toks[i % R], dl.comp_map, dl.tables, dl.h, dl.weights, h_out, ws)
+        dl.plan.engram_forward(toks[i % R], dl.comp_map, dl.tables, dl.h, dl.weights, h_out, ws, flags=flags)
     torch.cuda.synchronize()
     p = dl.plan.engram_profile_end()["gather"]
     ms = p["total_ms"] / max(p["launches"], 1)

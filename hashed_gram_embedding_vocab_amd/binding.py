@@ -27,6 +27,7 @@ F32, BF16 = 0, 1
 CONV_LINEAR, CONV_SILU_SKIP = 0, 1
 OUT_DELTA = 1
 RETRIEVE_IN_PROJECTION = 2  # engram_forward: retrieval inside the projection launches
+WEIGHTS_PACKED = 4  # engram_forward / engram_gate_fuse: W_k and W_v as engram_pack_weight wrote them
 MAX_TABLES, MAX_BRANCHES = 32, 4
 NOALLOC_SCRATCH_BYTES = 64 << 20  # ENGRAM_NOALLOC_SCRATCH_BYTES
 KERNEL_NAMES = ("hash", "gather", "gemm", "fuse", "aux", "gemm_v", "gate", "seam", "bwd_gemm", "bwd_fuse",
@@ -97,6 +98,8 @@ def lib() -> C.CDLL:
         L.engram_plan_destroy.argtypes = [P]
         L.engram_workspace_size.restype = C.c_size_t
         L.engram_workspace_size.argtypes = [P, i32, i32]
+        L.engram_pack_weight.restype = C.c_int
+        L.engram_pack_weight.argtypes = [P, P, P, P]
         L.engram_hash.restype = C.c_int
         L.engram_hash.argtypes = [P, P, i32, i32, P, P, P, P, P]
         L.engram_gather.restype = C.c_int
@@ -347,6 +350,20 @@ class Plan:
     # ------------------------------------------------------------------ ABI calls
     def engram_workspace_size(self, batch: int, seqlen: int) -> int:
         return int(lib().engram_workspace_size(self._h, batch, seqlen))
+
+    def engram_pack_weight(self, w, packed, stream=None):
+        """Pack one [d][D_e] weight matrix into packed (same shape and dtype)."""
+        _check("engram_pack_weight", lib().engram_pack_weight(
+            self._h, _ptr(w, "w", self.torch_dtype), _ptr(packed, "packed", self.torch_dtype), _stream(stream)))
+
+    def packed_weights(self, w: "Weights", stream=None) -> "Weights":
+        """The weights with every W_k and W_v packed by engram_pack_weight into
+        new tensors (pass flags=WEIGHTS_PACKED with them)."""
+        def pk(t):
+            out = torch.empty_like(t)
+            self.engram_pack_weight(t, out, stream)
+            return out
+        return Weights([pk(t) for t in w.w_k], pk(w.w_v), w.gamma_h, w.gamma_k, w.conv_w)
 
     def engram_hash(self, tokens, comp_map, idx, prev_ctx=None, bad_tokens=None, stream=None):
         batch, seqlen = tokens.shape

@@ -103,7 +103,9 @@ engram_status check_fuse_args(const engram_plan_s *p, const void *emb, const voi
     if (batch <= 0 || seqlen <= 0) return ENGRAM_E_INVALID_ARG;
     if ((int64_t)batch * seqlen > (int64_t)INT32_MAX) return ENGRAM_E_UNSUPPORTED;
     if (batch > 65535) return ENGRAM_E_UNSUPPORTED;  // one grid row per sequence in the fusion kernel
-    if (flags & ~(uint32_t)ENGRAM_OUT_DELTA) return ENGRAM_E_INVALID_ARG;
+    if (flags & ~(uint32_t)(ENGRAM_OUT_DELTA | ENGRAM_WEIGHTS_PACKED)) return ENGRAM_E_INVALID_ARG;
+    // packed weights are read by the bf16 MFMA projections only
+    if ((flags & ENGRAM_WEIGHTS_PACKED) && p->cfg.dtype != ENGRAM_BF16) return ENGRAM_E_UNSUPPORTED;
     if (!aligned16(emb) || !aligned16(h) || !aligned16(out)) return ENGRAM_E_INVALID_ARG;
     if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return ENGRAM_E_INVALID_ARG;
     if ((alpha && !aligned16(alpha)) || (conv_state && !aligned16(conv_state))) return ENGRAM_E_INVALID_ARG;
@@ -167,6 +169,7 @@ engram_status do_fuse(engram_plan_s &p, const void *emb, const void *h, int32_t 
 
     ProjArgs pa{};
     pa.emb = emb;
+    pa.w_packed = (flags & ENGRAM_WEIGHTS_PACKED) ? 1 : 0;
     for (int m = 0; m < Br; ++m) {
         pa.w[m] = w->w_k[m];
         pa.gamma_h[m] = w->gamma_h[m];
@@ -456,6 +459,22 @@ size_t engram_workspace_size(engram_plan p, int32_t batch, int32_t seqlen) {
     Layout L;
     if (!p || !layout_of(*p, batch, seqlen, L)) return 0;
     return L.total;
+}
+
+engram_status engram_pack_weight(engram_plan p, const void *d_w, void *d_packed, hipStream_t stream) {
+    if (!p || !d_w || !d_packed || !aligned16(d_w) || !aligned16(d_packed)) return ENGRAM_E_INVALID_ARG;
+    if (p->cfg.dtype != ENGRAM_BF16) return ENGRAM_E_UNSUPPORTED;
+    const int64_t rows = p->cfg.d_model, K = p->emb_dim;
+    // the shapes the bf16 projections take (engram_gate_fuse rejects the rest)
+    if (rows % 256 != 0 || K % 128 != 0 || rows * K * 2 >= ((int64_t)1 << 31)) return ENGRAM_E_UNSUPPORTED;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(d_w), b = reinterpret_cast<uintptr_t>(d_packed);
+    const uintptr_t bytes = (uintptr_t)(rows * K * 2);
+    if (a < b + bytes && b < a + bytes) return ENGRAM_E_INVALID_ARG;  // overlapping buffers
+    {
+        Launch l(*p, ENGRAM_K_AUX, stream);
+        launch_pack_weight(d_w, d_packed, (int32_t)rows, (int32_t)K, stream);
+    }
+    return last_launch_status();
 }
 
 engram_status engram_hash(engram_plan p, const int32_t *d_tokens, int32_t batch, int32_t seqlen,

@@ -166,7 +166,14 @@ struct ProjArgs {
     uint32_t *bad;                         // counter of raw ids outside [0, V), or null
     const char *tables[kMaxTables];
     HashConsts hc;
+    // forward modes (0-2): every w[] matrix is in the packed operand layout
+    // (engram_pack_weight), each ring stage's weight blocks one 1 KB read
+    int32_t w_packed;
 };
+
+// [rows][K] bf16 -> the packed operand layout of engram_pack_weight
+// (rows % 16 == 0, K % 32 == 0)
+void launch_pack_weight(const void *w, void *packed, int32_t rows, int32_t K, hipStream_t s);
 
 constexpr int kPartCols = 128;  // columns of d summed into one gate partial (bf16 path)
 

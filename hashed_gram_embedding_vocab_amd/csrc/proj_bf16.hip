@@ -591,6 +591,12 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
     // (a template-dependent bound here keeps the host pass from emitting the
     // kernel's launch stub, so the bound is the namespace constant both tiles share)
     static_assert(TBPW == kBlocksPerWave, "two row blocks per wave and operand in both tiles");
+    // packed weights (forward modes): block blk of the tile is the matrix's
+    // 16-row block (n0 - mat0 d) / 16 + blk, one 1 KB block per K stage; the
+    // lane copies bytes 16 lane .. 16 lane + 15 of it (row lane / 4, already
+    // swizzled), so the stage's weight offset is 1 KB per stage
+    constexpr bool kFwdMode = MODE == 0 || MODE == 1 || MODE == 2;
+    const bool wpk = kFwdMode && a.w_packed != 0;
     uint32_t woff[kBlocksPerWave], eoff[kBlocksPerWave];
 #pragma unroll
     for (int i = 0; i < TBPW; ++i) {
@@ -600,7 +606,8 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
         // order 4 * row + block (see the mode-1 epilogue)
         const int trow = MODE == 1 ? 64 * (blk >> 2) + 4 * lr + (blk & 3) : row;
         const int64_t t = min(max(t0 + trow, (int64_t)0), a.n_tok - 1);
-        woff[i] = (uint32_t)((n0 - mat0 * d + row) * ld + lchunk * 8) * 2u;
+        woff[i] = wpk ? (uint32_t)(((n0 - mat0 * d) / 16 + blk) * (K / 32) * 1024 + lane * 16)
+                      : (uint32_t)((n0 - mat0 * d + row) * ld + lchunk * 8) * 2u;
         eoff[i] = (uint32_t)(t * ld + lchunk * 8) * 2u;
         if constexpr (kKMajW || kKMajE) {
             // instruction i of this wave fills k-rows RPI (TBPW wave + i) + lane / LPR,
@@ -673,13 +680,14 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
 #define ENGRAM_ISSUE(STG, k0)                                                                    \
     do {                                                                                         \
         const int kbytes = (kbase + (k0)) * 2;                                                   \
+        const int kbw = wpk ? (k0) * 32 : kbytes; /* weight side: 1 KB per packed stage */      \
         if constexpr (kGather) {                                                                 \
             const char *tb = tab_s[gtau];                                                        \
             const uint32_t *slots = kSlotsInEpi ? reinterpret_cast<const uint32_t *>(taps_own) : idx_own; \
             _Pragma("unroll") for (int i = 0; i < TBPW; ++i) {                                   \
                 const int blk = wave * TBPW + i;                                                 \
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void_t *)&STG.w[blk * kBlockBytes], \
-                                                         16, woff[i], kbytes, 0, 0);             \
+                                                         16, woff[i], kbw, 0, 0);                \
                 const uint32_t ix = slots[(MODE == 1 ? 64 * (blk >> 2) + 4 * lr + (blk & 3)      \
                                                       : blk * 16 + lr) * g_nt + gtau];           \
                 __builtin_amdgcn_global_load_lds(tb + (uint64_t)ix * g_row_bytes + 2 * goff,     \
@@ -713,7 +721,7 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
             _Pragma("unroll") for (int i = 0; i < TBPW; ++i) {                                   \
                 const int blk = wave * TBPW + i;                                                 \
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void_t *)&STG.w[blk * kBlockBytes], \
-                                                         16, woff[i], kbytes, 0, 0);             \
+                                                         16, woff[i], kbw, 0, 0);                \
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(eres, (lds_void_t *)&STG.e[blk * kBlockBytes], \
                                                          16, eoff[i], kbytes, 0, 0);             \
             }                                                                                    \
@@ -977,7 +985,30 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
     }
 }
 
+// [rows][K] bf16 -> packed operand blocks: thread p writes 16-byte piece p,
+// piece c % 4 of row (c / 4) % 16 of block c / 64 = (row block, K stage),
+// which holds the row's values 8 q .. 8 q + 7 of that stage for
+// q = (c % 4) ^ swz(row).
+__global__ __launch_bounds__(256) void pack_weight_kernel(const u32x4_t *__restrict__ w, u32x4_t *__restrict__ out,
+                                                          int64_t pieces, int32_t K) {
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= pieces) return;
+    const int stages = K / 32;
+    const int64_t blk = c >> 6;
+    const int r = (int)((c >> 2) & 15), pos = (int)(c & 3);
+    const int64_t rb = blk / stages;
+    const int st = (int)(blk - rb * stages);
+    const int q = pos ^ swz(r);
+    out[c] = w[((rb * 16 + r) * K + 32 * st + 8 * q) / 8];
+}
+
 }  // namespace
+
+void launch_pack_weight(const void *w, void *packed, int32_t rows, int32_t K, hipStream_t s) {
+    const int64_t pieces = (int64_t)rows * K / 8;
+    launch_kernel(pack_weight_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), s,
+                  static_cast<const u32x4_t *>(w), static_cast<u32x4_t *>(packed), pieces, K);
+}
 
 void launch_proj_bf16(const ProjArgs &a, hipStream_t s) {
     const int n_total = a.n_mats * a.d;

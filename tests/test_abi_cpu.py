@@ -167,6 +167,45 @@ def test_bf16_shape_support_is_checked(B):
                               C.c_void_p(0x100000), ws, None) == B.E_UNSUPPORTED
 
 
+def test_pack_weight_argument_checks(B):
+    """engram_pack_weight and the packed-weights flag are validated before
+    anything is launched: null, misaligned or overlapping buffers, fp32 plans
+    and unsupported shapes; the fp32 forward and the backward refuse the flag."""
+    _no_gpu()
+    L = B.lib()
+    src, dst = C.c_void_p(0x1000000), C.c_void_p(0x20000000)
+    p = B.Plan(vocab=1000, vocab_comp=770, heads=4, head_dim=32, table_rows=[10007] * 8, hash_seed=1,
+               d_model=256, dtype=B.BF16)  # D_e = 256: a [256][256] matrix, 128 KB
+    assert L.engram_pack_weight(None, src, dst, None) == B.E_INVALID_ARG
+    assert L.engram_pack_weight(p._h, None, dst, None) == B.E_INVALID_ARG
+    assert L.engram_pack_weight(p._h, src, None, None) == B.E_INVALID_ARG
+    assert L.engram_pack_weight(p._h, C.c_void_p(0x1000004), dst, None) == B.E_INVALID_ARG
+    assert L.engram_pack_weight(p._h, src, C.c_void_p(0x20000008), None) == B.E_INVALID_ARG
+    for start in (0x1000000, 0x1000000 + 1024, 0x1000000 + 128 * 1024 - 16, 0x1000000 - 128 * 1024 + 16):
+        assert L.engram_pack_weight(p._h, src, C.c_void_p(start), None) == B.E_INVALID_ARG, hex(start)
+    p32 = B.Plan(vocab=1000, vocab_comp=770, heads=4, head_dim=32, table_rows=[10007] * 8, hash_seed=1,
+                 d_model=256, dtype=B.F32)
+    assert L.engram_pack_weight(p32._h, src, dst, None) == B.E_UNSUPPORTED
+    p200 = B.Plan(vocab=1000, vocab_comp=770, heads=4, head_dim=32, table_rows=[10007] * 8, hash_seed=1,
+                  d_model=200, dtype=B.BF16)
+    assert L.engram_pack_weight(p200._h, src, dst, None) == B.E_UNSUPPORTED
+    # the fp32 projections read [d][D_e] matrices only
+    fake = C.c_void_p(0x10000)
+    w = B.WeightsC()
+    w.w_k[0] = w.w_v = w.gamma_h[0] = w.gamma_k[0] = w.conv_w = 0x10000
+    ws = p32.engram_workspace_size(1, 4)
+    assert L.engram_gate_fuse(p32._h, fake, fake, 1, 4, C.byref(w), None, fake, None, B.WEIGHTS_PACKED,
+                              C.c_void_p(0x100000), ws, None) == B.E_UNSUPPORTED
+    # the backward reads W K-major from the [d][D_e] matrices
+    g = B.GradsC(*([C.c_void_p(0x10000)] * 7))
+    pb = B.Plan(vocab=1000, vocab_comp=770, heads=2, head_dim=32, table_rows=[10007] * 4, hash_seed=1,
+                d_model=256, dtype=B.BF16)
+    tabs = (C.c_void_p * 4)(*([0x10000] * 4))
+    wsb = pb.engram_backward_workspace_size(2, 8)
+    assert L.engram_backward(pb._h, fake, tabs, fake, C.byref(w), fake, 2, 8, B.WEIGHTS_PACKED, fake,
+                             C.byref(g), C.c_void_p(0x100000), wsb, None) == B.E_INVALID_ARG
+
+
 def test_backward_argument_checks(B):
     _no_gpu()
     L = B.lib()
