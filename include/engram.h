@@ -70,7 +70,8 @@ enum { ENGRAM_OUT_DELTA = 1u << 0 };
  * the same for their tiles.  E never reaches memory; n_tables <= 16 and
  * d_e % 8 == 0.  Same results bit for bit.  Measured at a decode step of 256
  * sequences (four branches, d = 2560): 3.6% faster per step than the
- * separate retrieval kernel.  On prefill chunks: 5% slower at 8 x 4096
+ * separate retrieval kernel, 1.3% with packed weights (ENGRAM_WEIGHTS_PACKED
+ * shortens the projection it adds to).  On prefill chunks: 5% slower at 8 x 4096
  * tokens with d = 1024, 19-25% slower at d = 2560 (random row pieces from
  * HBM outrun the operand ring).  Off by default.  Ignored where it does not
  * apply. */

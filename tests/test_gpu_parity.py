@@ -340,6 +340,21 @@ def _same_bits_in_projection(dl, toks, out, alpha, flag):
     assert torch.equal(alpha2, alpha)
 
 
+def _same_bits_packed_weights(B, dl, toks, out, alpha):
+    """The forward on W_k and W_v packed by engram_pack_weight gives the bits
+    of the forward on the [d][D_e] matrices."""
+    packed = dl.plan.packed_weights(dl.weights)
+    saved, dl.weights = dl.weights, packed
+    try:
+        out2, alpha2, bad2 = forward(dl, toks, flags=B.WEIGHTS_PACKED)
+    finally:
+        dl.weights = saved
+    assert bad2 == 0
+    assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
+    assert torch.equal(alpha2, alpha)
+    del packed
+
+
 @pytest.mark.parametrize("name", ["small", "layer27b"])
 def test_forward_full_size_sampled(B, name):
     """Sampled positions against the oracle; the same forward with retrieval
@@ -353,6 +368,8 @@ def test_forward_full_size_sampled(B, name):
     say("forward full size, retrieval in projection", name)
     _same_bits_in_projection(dl, toks, out, alpha, B.RETRIEVE_IN_PROJECTION)
     _sampled_check(wl, dl, toks, 24, name + " (retrieval in projection)", seed=7, flags=B.RETRIEVE_IN_PROJECTION)
+    say("forward full size, packed weights", name)
+    _same_bits_packed_weights(B, dl, toks, out, alpha)
     del dl
     torch.cuda.empty_cache()
 
@@ -363,7 +380,9 @@ def test_forward_multibranch_prefill_two_layers_sampled(B):
     for slot in range(len(wl.layers)):
         say("forward multibranch prefill layer", wl.layers[slot])
         dl = make_device_layer(wl, layer_slot=slot)
-        _sampled_check(wl, dl, toks, 20, "multibranch layer %d" % wl.layers[slot], seed=slot)
+        out, alpha = _sampled_check(wl, dl, toks, 20, "multibranch layer %d" % wl.layers[slot], seed=slot)
+        if slot == 0:  # four stacked W_k matrices and W_v, packed
+            _same_bits_packed_weights(B, dl, toks, out, alpha)
         del dl
         torch.cuda.empty_cache()
 
@@ -451,6 +470,8 @@ def test_forward_maxtable_sampled(B, maxtable_layer, name):
     out, alpha = _sampled_check(wl, maxtable_layer, toks, 24, name)
     say("forward, retrieval in projection", name)
     _same_bits_in_projection(maxtable_layer, toks, out, alpha, B.RETRIEVE_IN_PROJECTION)
+    say("forward, packed weights", name)
+    _same_bits_packed_weights(B, maxtable_layer, toks, out, alpha)
 
 
 @pytest.mark.parametrize("dtype,d,heads,head_dim,orders,kc,br,batch,seqlen", [
