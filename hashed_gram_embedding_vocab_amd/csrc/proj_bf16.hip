@@ -90,7 +90,17 @@ constexpr int kCpolNT = 2;
 #ifndef ENGRAM_PROJ_GROUP_T
 #define ENGRAM_PROJ_GROUP_T 4
 #endif
-constexpr int kGroupT = ENGRAM_PROJ_GROUP_T;  // token tiles sharing each weight tile in the launch order
+#ifndef ENGRAM_PROJ_GROUP_V
+#define ENGRAM_PROJ_GROUP_V 1
+#endif
+// token tiles sharing each weight tile in the launch order: W_k and plain
+// launches, and the fused W_v launch.  The W_v launch walks all channel tiles
+// of one token tile before the next, so the workgroups of an XCD that run at
+// once read and write whole token rows of h and out (measured against groups
+// of four in alternating runs on one box: W_v 226 -> 218 us on the 200 GB
+// tables, 0.462 -> 0.455 ms per step; W_k gains nothing from it).
+constexpr int kGroupT = ENGRAM_PROJ_GROUP_T;
+constexpr int kGroupV = ENGRAM_PROJ_GROUP_V;
 
 static_assert(BN == BT, "one block-load pattern serves both operands");
 static_assert(BT == kTokTile, "the seam kernel assumes this token tile");
@@ -138,18 +148,19 @@ __device__ __forceinline__ bf16x4_t lds_read_tr(const unsigned char *p) {
 
 // Hardware hands consecutive block ids to the 8 XCDs round-robin.  Remap so
 // every XCD walks one contiguous range of the logical tile order (its own
-// L2 then sees neighbouring tiles), then order tiles in groups of kGroupT
-// token tiles sharing each weight tile.
+// L2 then sees neighbouring tiles), then order tiles in groups of G token
+// tiles sharing each weight tile.
+template <int G>
 __device__ __forceinline__ void tile_of(int bid, int nblocks, int n_tiles_n, int n_tiles_t,
                                         int &tile_n, int &tile_t) {
     const int q = nblocks / kXcds, r = nblocks % kXcds;
     const int x = bid % kXcds, slot = bid / kXcds;
     const int logical = (x < r) ? x * (q + 1) + slot : r * (q + 1) + (x - r) * q + slot;
-    const int per_group = kGroupT * n_tiles_n;
+    const int per_group = G * n_tiles_n;
     const int g = logical / per_group;
     const int in = logical - g * per_group;
-    const int t_base = g * kGroupT;
-    const int gt = min(kGroupT, n_tiles_t - t_base);
+    const int t_base = g * G;
+    const int gt = min(G, n_tiles_t - t_base);
     tile_n = in / gt;
     tile_t = t_base + (in - (in / gt) * gt);
 }
@@ -563,7 +574,7 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
     const int n_tiles_n = (n_total + TBN - 1) / TBN;
     const int n_tiles_t = (int)((a.n_tok + TBT - 1) / TBT);
     int tile_n, tile_t;
-    tile_of(blockIdx.x, gridDim.x, n_tiles_n, n_tiles_t, tile_n, tile_t);
+    tile_of<MODE == 1 ? kGroupV : kGroupT>(blockIdx.x, gridDim.x, n_tiles_n, n_tiles_t, tile_n, tile_t);
     const int n0 = tile_n * TBN;
     // first token row of the tile
     // previous tile's last tokens (negative for the first tile: never stored)
