@@ -30,7 +30,11 @@ constexpr int kHGUnroll = ENGRAM_HG_UNROLL; // row chunks in flight per thread i
 constexpr bool kNtRows = (ENGRAM_HG_NT & 1) != 0;  // nontemporal row loads
 constexpr bool kNtEmb = (ENGRAM_HG_NT & 2) != 0;   // nontemporal E stores
 
-__device__ __forceinline__ u32x4_t load_row_chunk(const u32x4_t *p) {
+// Table rows through global-address-space pointers: through generic ones
+// the loads become flat loads, which also count as LDS operations, so the
+// LDS read of the next pointer would wait for the previous row.
+typedef const __attribute__((address_space(1))) u32x4_t *grow_t;
+__device__ __forceinline__ u32x4_t load_row_chunk(grow_t p) {
     if constexpr (kNtRows) return __builtin_nontemporal_load(p);
     return *p;
 }
@@ -44,9 +48,20 @@ __device__ __forceinline__ uint64_t div_magic(uint64_t n, uint64_t magic, int32_
     return d == 1 ? n : __umul64hi(n, magic);
 }
 
+// The table bases (and last rows) go to LDS first: indexed at run time, the
+// kernel-argument arrays would be read from memory by a vector load in front
+// of every row load, each waiting for all earlier loads, so a thread's row
+// loads would go out one at a time instead of together.
 __global__ __launch_bounds__(kThreads) void gather_kernel(GatherConsts gc,
                                                           const uint32_t *__restrict__ idx,
                                                           int64_t total_chunks, u32x4_t *__restrict__ emb) {
+    __shared__ grow_t tab_s[kMaxTables];
+    __shared__ uint32_t last_s[kMaxTables];
+    if (threadIdx.x < (unsigned)gc.n_tables) {
+        tab_s[threadIdx.x] = (grow_t)(gc.table[threadIdx.x]);
+        last_s[threadIdx.x] = gc.last_row[threadIdx.x];
+    }
+    __syncthreads();
     const int64_t base = (int64_t)blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
     uint32_t row[kUnroll];
     int32_t tau[kUnroll], ch[kUnroll];
@@ -64,9 +79,8 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherConsts gc,
     u32x4_t val[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-        const uint32_t r = min(row[u], gc.last_row[tau[u]]);
-        const u32x4_t *src = reinterpret_cast<const u32x4_t *>(gc.table[tau[u]]) +
-                           (int64_t)r * gc.row_chunks + ch[u];
+        const uint32_t r = min(row[u], last_s[tau[u]]);
+        const grow_t src = tab_s[tau[u]] + (int64_t)r * gc.row_chunks + ch[u];
         val[u] = load_row_chunk(src);
     }
 #pragma unroll
@@ -91,8 +105,10 @@ __global__ __launch_bounds__(kThreads) void hash_gather_kernel(
     uint64_t magic_seq, int32_t tpb, const int32_t *__restrict__ comp_map, const int32_t *prev_ctx,
     int32_t *ctx_out, uint32_t *__restrict__ bad, u32x4_t *__restrict__ emb) {
     __shared__ uint32_t slot_s[kThreads];
+    __shared__ grow_t tab_s[kMaxTables];  // table bases (see gather_kernel)
     const int64_t tok0 = (int64_t)blockIdx.x * tpb;
     const int n_tables = gc.n_tables;
+    if (threadIdx.x < (unsigned)n_tables) tab_s[threadIdx.x] = (grow_t)(gc.table[threadIdx.x]);
     const int pairs = tpb * n_tables;
     {
         const int pr = threadIdx.x;
@@ -138,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void hash_gather_kernel(
             const int tau = (int)div_magic((uint64_t)rem, gc.magic_row, gc.row_chunks);
             const int ch = rem - tau * gc.row_chunks;
             const uint32_t r = slot_s[tl * n_tables + tau];
-            val[u] = load_row_chunk(reinterpret_cast<const u32x4_t *>(gc.table[tau]) + (int64_t)r * gc.row_chunks + ch);
+            val[u] = load_row_chunk(tab_s[tau] + (int64_t)r * gc.row_chunks + ch);
         }
 #pragma unroll
         for (int u = 0; u < kHGUnroll; ++u) {

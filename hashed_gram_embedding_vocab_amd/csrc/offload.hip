@@ -73,13 +73,18 @@ __global__ __launch_bounds__(kThreads) void cache_fill_kernel(GatherConsts gc, u
 // capped launch keeps enough bytes in flight on few CUs to fill the host
 // link), the lanes of one row reading one contiguous burst.
 constexpr int kGroups = 4;
+// Row addresses kept in LDS as global-address-space pointers: generic ones
+// make the copies flat loads, which also count as LDS operations, so each
+// LDS read of the next address would wait for the previous row.  (Pinned
+// host tables are reached through the same global addresses.)
+typedef const __attribute__((address_space(1))) u32x4_t *grow_t;
 
 __global__ __launch_bounds__(kThreads) void cached_gather_kernel(GatherConsts gc, uint32_t capacity,
                                                                  const uint32_t *__restrict__ idx, int64_t n_tok,
                                                                  int32_t tpb, const uint32_t *__restrict__ keys,
                                                                  const u32x4_t *__restrict__ cache_rows,
                                                                  u32x4_t *__restrict__ emb) {
-    __shared__ const u32x4_t *src_s[kGroups * kThreads];
+    __shared__ grow_t src_s[kGroups * kThreads];
     const int n_tables = gc.n_tables;
     const int64_t per_iter = (int64_t)tpb * kGroups;
     const int64_t n_iters = (n_tok + per_iter - 1) / per_iter;
@@ -108,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void cached_gather_kernel(GatherConsts gc
                         s = s + 1u == capacity ? 0u : s + 1u;
                     }
                 }
-                src_s[g * kThreads + pr] = src;
+                src_s[g * kThreads + pr] = (grow_t)src;
             }
         }
         __syncthreads();
