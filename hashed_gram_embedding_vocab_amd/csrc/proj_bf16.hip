@@ -343,6 +343,7 @@ __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t 
     }
 
     const bool any_edge = edge[0] || edge[1] || edge[2] || edge[3];
+    const bool carry = a.conv_state != nullptr;
 
     // chunk DMA: instruction k fills LDS rows 8k .. 8k+7 (lane -> row
     // 8k + lane/8, piece lane%8), so lane reads global piece
@@ -381,11 +382,16 @@ __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t 
         ldo[ii] = (uint32_t)(l16 * 512 + (((2 * ii + (sub >> 3)) ^ (l16 & 7)) << 4) + (sub & 4) * 2);
 
     // EDGE: some token block of the wave holds a sequence's first or last
-    // positions.  Without it the body is straight-line code.
-    auto chunk = [&](auto qc, auto ec, unsigned char *buf, int m, int moff, int smoff,
+    // positions.  Without it the body is straight-line code.  CARRY: a
+    // carried conv state is read there (without one, the history before a
+    // sequence start is zero and nothing is loaded or waited for: the wait
+    // would otherwise drain the next chunk's h load and the last chunk's
+    // stores in every wave holding a sequence edge).
+    auto chunk = [&](auto qc, auto ec, auto cc, unsigned char *buf, int m, int moff, int smoff,
                      const float (&al)[FT], const float (&alh)[3]) {
         constexpr int q = decltype(qc)::value;
         constexpr bool EDGE = decltype(ec)::value;
+        constexpr bool CARRY = decltype(cc)::value;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             asm volatile("" ::: "memory");  // one channel group at a time: bounds register use
@@ -429,7 +435,7 @@ __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t 
 #pragma unroll
                     for (int s = 1; s <= 3; ++s) {
                         f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-                        if (a.conv_state && s <= kc - 1) {
+                        if (CARRY && s <= kc - 1) {
                             const uint32_t off = pos[j] < s ? sr + 64u * i : 0u;
                             const int soff = smoff + (kc - 1 - s) * (int)state_row_bytes;
                             if (state_bf16) {
@@ -445,8 +451,10 @@ __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t 
                     }
                     // drain here: left pending, the compiler would wait for
                     // them (and everything before) after the branch, on every path
-                    wait_vmcnt<0>();
-                    asm volatile("" ::: "memory");
+                    if constexpr (CARRY) {
+                        wait_vmcnt<0>();
+                        asm volatile("" ::: "memory");
+                    }
                 }
                 const u32x2_t h2 = *reinterpret_cast<const u32x2_t *>(buf + ldo[ii] + 128 * j);
                 float o[4];
@@ -505,20 +513,24 @@ __device__ __forceinline__ void fused_value_epilogue(const ProjArgs &a, f32x4_t 
         else
             wait_vmcnt<16>();
         asm volatile("" ::: "memory");
-        if (any_edge)
-            chunk(std::integral_constant<int, 0>{}, std::true_type{}, hA, m, moff, smoff, al, alh);
+        if (any_edge && carry)
+            chunk(std::integral_constant<int, 0>{}, std::true_type{}, std::true_type{}, hA, m, moff, smoff, al, alh);
+        else if (any_edge)
+            chunk(std::integral_constant<int, 0>{}, std::true_type{}, std::false_type{}, hA, m, moff, smoff, al, alh);
         else
-            chunk(std::integral_constant<int, 0>{}, std::false_type{}, hA, m, moff, smoff, al, alh);
+            chunk(std::integral_constant<int, 0>{}, std::false_type{}, std::false_type{}, hA, m, moff, smoff, al, alh);
         if (m + 1 < BR) issue(hA, 2 * m + 2);
         if (m + 1 < BR)
             wait_vmcnt<16>();
         else
             wait_vmcnt<8>();
         asm volatile("" ::: "memory");
-        if (any_edge)
-            chunk(std::integral_constant<int, 1>{}, std::true_type{}, hB, m, moff, smoff, al, alh);
+        if (any_edge && carry)
+            chunk(std::integral_constant<int, 1>{}, std::true_type{}, std::true_type{}, hB, m, moff, smoff, al, alh);
+        else if (any_edge)
+            chunk(std::integral_constant<int, 1>{}, std::true_type{}, std::false_type{}, hB, m, moff, smoff, al, alh);
         else
-            chunk(std::integral_constant<int, 1>{}, std::false_type{}, hB, m, moff, smoff, al, alh);
+            chunk(std::integral_constant<int, 1>{}, std::false_type{}, std::false_type{}, hB, m, moff, smoff, al, alh);
         if (m + 1 < BR) issue(hB, 2 * m + 3);
     }
 }
