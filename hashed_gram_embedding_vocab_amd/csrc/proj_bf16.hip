@@ -938,36 +938,51 @@ __global__ __launch_bounds__(NARROW ? 256 : kThreads, NARROW ? 2 : 1) void proj_
         block_barrier();  // every wave is done reading the stage buffers
         h_issue(1);
         unsigned char *h0 = h_half(0), *h1 = h_half(1);
+        // Half 0's channels (i < FN/2) are summed while half 1 is in flight,
+        // then half 1's: each token's sums still add i = 0..FN-1 in order.
+        float s_hk[TFT], s_kk[TFT], s_hh[TFT];
+        auto add_half = [&](auto hc) {
+            constexpr int H = decltype(hc)::value;
+#pragma unroll
+            for (int j = 0; j < TFT; ++j) {
+                const int p = 16 * j + (lane & 15);
+                if (H == 0) s_hk[j] = s_kk[j] = s_hh[j] = 0.f;
+#pragma unroll
+                for (int i = H * (FN / 2); i < (H + 1) * (FN / 2); ++i) {
+                    const u32x2_t x = *reinterpret_cast<const u32x2_t *>(
+                        (H ? h1 : h0) + p * 128 + (((2 * (i & 3) + (sub >> 3)) ^ hswz(p)) << 4) + (sub & 4) * 2);
+                    const f32x4_t g = *reinterpret_cast<const f32x4_t *>(gsm + 16 * i + sub);
+                    const float h4[4] = {bf16_to_f32(x[0] & 0xFFFFu), bf16_to_f32(x[0] >> 16),
+                                         bf16_to_f32(x[1] & 0xFFFFu), bf16_to_f32(x[1] >> 16)};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float kv = acc[i][j][r];
+                        s_hk[j] += h4[r] * g[r] * kv;
+                        s_kk[j] += kv * kv;
+                        s_hh[j] += h4[r] * h4[r];
+                    }
+                }
+            }
+        };
+        static_assert(FN == 8, "two halves of four 16-channel blocks");
+        wait_vmcnt<TWT / 8>();  // half 0 (half 1's TWT/8 loads may be in flight)
+        asm volatile("" ::: "memory");
+        add_half(std::integral_constant<int, 0>{});
         wait_vmcnt<0>();
         asm volatile("" ::: "memory");
+        add_half(std::integral_constant<int, 1>{});
 #pragma unroll
         for (int j = 0; j < TFT; ++j) {
             const int64_t t = tw + 16 * j + (lane & 15);
-            const int p = 16 * j + (lane & 15);
-            float s_hk = 0.f, s_kk = 0.f, s_hh = 0.f;
-#pragma unroll
-            for (int i = 0; i < FN; ++i) {
-                const u32x2_t x = *reinterpret_cast<const u32x2_t *>(
-                    ((i >> 2) ? h1 : h0) + p * 128 + (((2 * (i & 3) + (sub >> 3)) ^ hswz(p)) << 4) + (sub & 4) * 2);
-                const f32x4_t g = *reinterpret_cast<const f32x4_t *>(gsm + 16 * i + sub);
-                const float h4[4] = {bf16_to_f32(x[0] & 0xFFFFu), bf16_to_f32(x[0] >> 16),
-                                     bf16_to_f32(x[1] & 0xFFFFu), bf16_to_f32(x[1] >> 16)};
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float kv = acc[i][j][r];
-                    s_hk += h4[r] * g[r] * kv;
-                    s_kk += kv * kv;
-                    s_hh += h4[r] * h4[r];
-                }
-            }
+            float s_hk_j = s_hk[j], s_kk_j = s_kk[j], s_hh_j = s_hh[j];
             // the four lanes {l, l+16, l+32, l+48} hold the same token
-            s_hk += __shfl_xor(s_hk, 16); s_hk += __shfl_xor(s_hk, 32);
-            s_kk += __shfl_xor(s_kk, 16); s_kk += __shfl_xor(s_kk, 32);
-            s_hh += __shfl_xor(s_hh, 16); s_hh += __shfl_xor(s_hh, 32);
+            s_hk_j += __shfl_xor(s_hk_j, 16); s_hk_j += __shfl_xor(s_hk_j, 32);
+            s_kk_j += __shfl_xor(s_kk_j, 16); s_kk_j += __shfl_xor(s_kk_j, 32);
+            s_hh_j += __shfl_xor(s_hh_j, 16); s_hh_j += __shfl_xor(s_hh_j, 32);
             if (lane < 16 && t < a.n_tok) {
-                pbase[t] = s_hk;
-                pbase[a.n_tok + t] = s_kk;
-                pbase[2 * a.n_tok + t] = s_hh;
+                pbase[t] = s_hk_j;
+                pbase[a.n_tok + t] = s_kk_j;
+                pbase[2 * a.n_tok + t] = s_hh_j;
             }
         }
     } else if constexpr (!kPlain) {
