@@ -69,9 +69,10 @@ enum { ENGRAM_OUT_DELTA = 1u << 0 };
  * rows.  On longer chunks the W_k launch and the fused W_v launch each do
  * the same for their tiles.  E never reaches memory; n_tables <= 16 and
  * d_e % 8 == 0.  Same results bit for bit.  Measured at a decode step of 256
- * sequences (four branches, d = 2560): 3.6% faster per step than the
- * separate retrieval kernel, 1.3% with packed weights (ENGRAM_WEIGHTS_PACKED
- * shortens the projection it adds to).  On prefill chunks: 5% slower at 8 x 4096
+ * sequences (four branches, d = 2560, packed weights): 11% slower per step
+ * than the separate retrieval kernel (0.0820 against 0.0737 ms), whose row
+ * loads all go out together; before that kernel was made so it was 1.3%
+ * faster.  On prefill chunks: 5% slower at 8 x 4096
  * tokens with d = 1024, 19-25% slower at d = 2560 (random row pieces from
  * HBM outrun the operand ring).  Off by default.  Ignored where it does not
  * apply. */
